@@ -1,0 +1,344 @@
+/* ds4o.c — plain scalar CPU oracle for one layer's compressed sparse attention step.
+ *
+ * TEST INFRASTRUCTURE ONLY: called by the tests, the smoke check and the
+ * benchmark's CPU-baseline leg, never by the GPU library.  Slow on purpose:
+ * straight loops in IEEE double, no blocking, no SIMD, no BLAS, one full sort
+ * for the top-k.  Threads run only across independent (unit, query) pairs.
+ *
+ * Source of the method: "Reading the architecture of DwarfStar (ds4.c),
+ * part 1/8" (Qiita), sections 2, 3, 3-1 and 3-3 (cited per function below).
+ */
+#define _GNU_SOURCE
+#include "ds4o.h"
+
+#include <math.h>
+#include <pthread.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---------------------------------------------------------------- dtypes */
+
+/* binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits. */
+double ds4o_f16_to_f64(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int e = (h >> 10) & 0x1f;
+    int m = h & 0x3ff;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);                 /* zero / subnormal: m * 2^-24 */
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m + 1024), e - 25);     /* (1 + m/1024) * 2^(e-15) */
+    return sign ? -v : v;
+}
+
+/* bfloat16 is the upper half of an IEEE binary32. */
+double ds4o_bf16_to_f64(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* Section 3-1 of the article: each raw-window value is stored as
+ * f16_to_f32(f32_to_f16(x)).  The rounding rule is not printed; the reading
+ * taken is IEEE round-to-nearest-even with gradual underflow and overflow to
+ * infinity.  Done in double: the quantum of x's binade is a power of two, so
+ * x / quantum is exact and rint() (ties to even in the default mode) rounds it. */
+uint16_t ds4o_round_f16(float xf)
+{
+    double x = (double)xf;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (isnan(x))
+        return (uint16_t)(sign | 0x7e00);
+    if (isinf(x))
+        return (uint16_t)(sign | 0x7c00);
+    if (a == 0.0)
+        return sign;
+    int e2;
+    frexp(a, &e2);                 /* a in [2^(e2-1), 2^e2) */
+    int E = e2 - 1;
+    if (E < -14)
+        E = -14;                   /* subnormal binade: quantum 2^-24 */
+    double quantum = ldexp(1.0, E - 10);
+    double r = rint(a / quantum) * quantum;
+    if (r >= 65536.0)              /* the largest finite f16 is 65504 */
+        return (uint16_t)(sign | 0x7c00);
+    if (r < ldexp(1.0, -14))       /* stays subnormal (or rounds to zero) */
+        return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    frexp(r, &e2);                 /* rounding may have carried into the next binade */
+    E = e2 - 1;
+    uint16_t frac = (uint16_t)(r / ldexp(1.0, E - 10) - 1024.0);
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | frac);
+}
+
+/* --------------------------------------------------------------- indexer */
+
+/* Section 3-3 of the article: ratio-4 layers keep an indexer with its own
+ * thin query (64 heads of 128 dims) that scores every compressed row; the
+ * scores pick the rows the main attention sees.  The article does not print
+ * the score formula.  Reading taken: per-head dot product, ReLU, then a sum
+ * weighted by per-head weights (without a per-head nonlinearity the 64 heads
+ * would collapse into one 128-dim query).  No scale factor: a positive global
+ * scale does not change the selection. */
+void ds4o_indexer_score(int64_t N, int Hi, int Di, const uint16_t *qI, const float *w,
+                        const uint16_t *kI, int64_t n_vis, double *s)
+{
+    for (int64_t j = 0; j < N; j++) {
+        if (j >= n_vis) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        double total = 0.0;
+        for (int h = 0; h < Hi; h++) {
+            double dot = 0.0;
+            for (int d = 0; d < Di; d++)
+                dot += ds4o_bf16_to_f64(qI[(int64_t)h * Di + d]) * ds4o_bf16_to_f64(kI[j * Di + d]);
+            double relu = dot > 0.0 ? dot : 0.0;
+            total += (double)w[h] * relu;
+        }
+        s[j] = total;
+    }
+}
+
+/* ------------------------------------------------------------------ top-k */
+
+typedef struct {
+    double score;
+    int64_t index;
+} scored_row;
+
+/* Higher score first; equal scores: lower row index first. */
+static int by_score_then_index(const void *pa, const void *pb)
+{
+    const scored_row *a = (const scored_row *)pa, *b = (const scored_row *)pb;
+    if (a->score > b->score) return -1;
+    if (a->score < b->score) return 1;
+    if (a->index < b->index) return -1;
+    if (a->index > b->index) return 1;
+    return 0;
+}
+
+/* Section 3-3 of the article: only the n_indexer_top_k best-scoring compressed
+ * rows (512; Pro 1024, section 2) go on to the main attention.  Brute force:
+ * sort all visible rows, keep the first min(K, n_vis). */
+int ds4o_topk(int64_t n_vis, int K, const double *s, int32_t *idx)
+{
+    if (n_vis < 0)
+        n_vis = 0;
+    scored_row *rows = (scored_row *)malloc((size_t)(n_vis > 0 ? n_vis : 1) * sizeof *rows);
+    for (int64_t j = 0; j < n_vis; j++) {
+        rows[j].score = s[j];
+        rows[j].index = j;
+    }
+    qsort(rows, (size_t)n_vis, sizeof *rows, by_score_then_index);
+    int taken = (int)(n_vis < K ? n_vis : K);
+    for (int k = 0; k < K; k++)
+        idx[k] = k < taken ? (int32_t)rows[k].index : -1;
+    free(rows);
+    return taken;
+}
+
+/* ------------------------------------------------------------------- RoPE */
+
+/* Section 2 of the article: n_rot = 64, RoPE applies to the last 64 of the
+ * 512 head dims only.  Section 3-2 shows compressed rows rotated ("tail
+ * RoPE") when they are emitted, so stored rows are already rotated and only
+ * the query is rotated here.  Readings for what is not printed: adjacent
+ * pairs (D-n_rot+2i, D-n_rot+2i+1), frequency theta^(-2i/n_rot), angle
+ * pos * frequency, no frequency scaling. */
+void ds4o_rope_q(int H, int D, int n_rot, int64_t pos, double theta,
+                 const double *q_in, double *q_out)
+{
+    int first = D - n_rot;
+    for (int h = 0; h < H; h++) {
+        const double *x = q_in + (int64_t)h * D;
+        double *y = q_out + (int64_t)h * D;
+        for (int d = 0; d < first; d++)
+            y[d] = x[d];
+        for (int i = 0; i < n_rot / 2; i++) {
+            double freq = pow(theta, -2.0 * (double)i / (double)n_rot);
+            double angle = (double)pos * freq;
+            double c = cos(angle), sn = sin(angle);
+            double a = x[first + 2 * i], b = x[first + 2 * i + 1];
+            y[first + 2 * i] = a * c - b * sn;
+            y[first + 2 * i + 1] = a * sn + b * c;
+        }
+    }
+}
+
+/* -------------------------------------------------------------- attention */
+
+/* Section 2 of the article: 64 query heads share one KV head of 512 dims
+ * (multi-query attention).  Section 3: the attention reads the recent raw
+ * window at full precision plus the compressed rows the indexer selected.
+ * Readings: each stored row is both key and value (the cache holds one
+ * 512-vector per token, section 3-1); the union is the concatenation of the
+ * raw rows and the selected rows, with no de-duplication; one softmax over
+ * the whole union; no sink or bias terms.  Plain two-pass softmax. */
+int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
+                    const uint16_t *raw, const uint16_t *comp, const int32_t *idx,
+                    double scale, double *out)
+{
+    int n_union = W;
+    for (int k = 0; k < K; k++)
+        if (idx[k] >= 0)
+            n_union++;
+    if (n_union == 0) {
+        memset(out, 0, sizeof(double) * (size_t)H * (size_t)D);
+        return 0;
+    }
+    /* Materialise the union as doubles: rows[r][d]. */
+    double *rows = (double *)malloc(sizeof(double) * (size_t)n_union * (size_t)D);
+    int r = 0;
+    for (int i = 0; i < W; i++, r++)
+        for (int d = 0; d < D; d++)
+            rows[(int64_t)r * D + d] = ds4o_f16_to_f64(raw[(int64_t)i * D + d]);
+    for (int k = 0; k < K; k++) {
+        if (idx[k] < 0)
+            continue;
+        for (int d = 0; d < D; d++)
+            rows[(int64_t)r * D + d] = ds4o_bf16_to_f64(comp[(int64_t)idx[k] * D + d]);
+        r++;
+    }
+    double *logit = (double *)malloc(sizeof(double) * (size_t)n_union);
+    for (int h = 0; h < H; h++) {
+        const double *qh = q_rot + (int64_t)h * D;
+        double m = -INFINITY;
+        for (r = 0; r < n_union; r++) {
+            double dot = 0.0;
+            for (int d = 0; d < D; d++)
+                dot += qh[d] * rows[(int64_t)r * D + d];
+            logit[r] = scale * dot;
+            if (logit[r] > m)
+                m = logit[r];
+        }
+        double z = 0.0;
+        for (r = 0; r < n_union; r++) {
+            logit[r] = exp(logit[r] - m);   /* now the unnormalised probability */
+            z += logit[r];
+        }
+        double *oh = out + (int64_t)h * D;
+        for (int d = 0; d < D; d++) {
+            double acc = 0.0;
+            for (r = 0; r < n_union; r++)
+                acc += logit[r] * rows[(int64_t)r * D + d];
+            oh[d] = acc / z;
+        }
+    }
+    free(logit);
+    free(rows);
+    return n_union;
+}
+
+/* ------------------------------------------------------------- whole step */
+
+typedef struct {
+    int U, T, H, D, n_rot, W, Hi, Di, K, q_is_bf16;
+    int64_t N;
+    const void *q;
+    const int64_t *pos;
+    double theta, scale;
+    const uint16_t *raw, *comp, *kI, *qI;
+    const float *w;
+    const int32_t *n_vis;
+    const int64_t *sel;
+    int64_t n_items;
+    double *scores;
+    int32_t *idx;
+    double *out;
+    int64_t next;
+    pthread_mutex_t lock;
+} step_job;
+
+static void run_one(step_job *j, int64_t item)
+{
+    int64_t ut = j->sel ? j->sel[item] : item;
+    int64_t u = ut / j->T, t = ut % j->T;
+    int H = j->H, D = j->D, W = j->W, K = j->K, Hi = j->Hi, Di = j->Di;
+    int64_t N = j->N;
+
+    double *s = j->scores ? j->scores + item * N : (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    int32_t *ix = j->idx ? j->idx + item * K : (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+
+    ds4o_indexer_score(N, Hi, Di, j->qI + (u * j->T + t) * (int64_t)Hi * Di, j->w + (u * j->T + t) * Hi,
+                       j->kI + u * N * Di, j->n_vis[u * j->T + t], s);
+    ds4o_topk(j->n_vis[u * j->T + t], K, s, ix);
+
+    if (j->out) {
+        double *q64 = (double *)malloc(sizeof(double) * (size_t)H * D);
+        double *qr = (double *)malloc(sizeof(double) * (size_t)H * D);
+        int64_t qoff = (u * j->T + t) * (int64_t)H * D;
+        for (int64_t e = 0; e < (int64_t)H * D; e++)
+            q64[e] = j->q_is_bf16 ? ds4o_bf16_to_f64(((const uint16_t *)j->q)[qoff + e])
+                                  : (double)((const float *)j->q)[qoff + e];
+        ds4o_rope_q(H, D, j->n_rot, j->pos[u * j->T + t], j->theta, q64, qr);
+        const uint16_t *raw_rows = j->raw + (u * (int64_t)(j->T + W - 1) + t) * D;
+        ds4o_sparse_mqa(H, D, W, K, qr, raw_rows, j->comp + u * N * D, ix, j->scale,
+                        j->out + item * (int64_t)H * D);
+        free(qr);
+        free(q64);
+    }
+    if (!j->scores)
+        free(s);
+    if (!j->idx)
+        free(ix);
+}
+
+static void *worker(void *arg)
+{
+    step_job *j = (step_job *)arg;
+    for (;;) {
+        pthread_mutex_lock(&j->lock);
+        int64_t item = j->next++;
+        pthread_mutex_unlock(&j->lock);
+        if (item >= j->n_items)
+            return NULL;
+        run_one(j, item);
+    }
+}
+
+int ds4o_step(int U, int T, int64_t N, int H, int D, int n_rot, int W, int Hi, int Di, int K,
+              const void *q, int q_is_bf16, const int64_t *pos, double theta,
+              const uint16_t *raw, const uint16_t *comp, const uint16_t *kI,
+              const uint16_t *qI, const float *w, const int32_t *n_vis, double scale,
+              const int64_t *sel, int64_t n_sel, int nthreads,
+              double *scores, int32_t *idx, double *out)
+{
+    if (U < 0 || T < 0 || N < 0 || H <= 0 || D <= 0 || n_rot < 0 || n_rot > D || (n_rot & 1) ||
+        W < 0 || Hi <= 0 || Di <= 0 || K <= 0)
+        return -1;
+    step_job j;
+    memset(&j, 0, sizeof j);
+    j.U = U; j.T = T; j.N = N; j.H = H; j.D = D; j.n_rot = n_rot; j.W = W;
+    j.Hi = Hi; j.Di = Di; j.K = K; j.q_is_bf16 = q_is_bf16;
+    j.q = q; j.pos = pos; j.theta = theta; j.scale = scale;
+    j.raw = raw; j.comp = comp; j.kI = kI; j.qI = qI; j.w = w; j.n_vis = n_vis;
+    j.sel = sel;
+    j.n_items = sel ? n_sel : (int64_t)U * T;
+    j.scores = scores; j.idx = idx; j.out = out;
+    for (int64_t i = 0; i < j.n_items; i++) {
+        int64_t ut = sel ? sel[i] : i;
+        if (ut < 0 || ut >= (int64_t)U * T)
+            return -1;
+    }
+    pthread_mutex_init(&j.lock, NULL);
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nthreads > 256)
+        nthreads = 256;
+    pthread_t th[256];
+    int started = 0;
+    for (int i = 1; i < nthreads; i++)
+        if (pthread_create(&th[started], NULL, worker, &j) == 0)
+            started++;
+    worker(&j);
+    for (int i = 0; i < started; i++)
+        pthread_join(th[i], NULL);
+    pthread_mutex_destroy(&j.lock);
+    return 0;
+}

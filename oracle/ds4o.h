@@ -1,0 +1,88 @@
+/* ds4o.h — plain scalar CPU oracle for one layer's compressed sparse attention step.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may call this library.  It shares no code, header, table or
+ * helper with the GPU library (libds4attn) and must never be used as a fallback
+ * for it.
+ *
+ * What it computes follows "Reading the architecture of DwarfStar (ds4.c),
+ * part 1/8" (Qiita), sections 2 and 3:
+ *   - section 2 (model shape): 64 query heads (Pro: 128), one KV head of 512
+ *     dims, RoPE on the last n_rot = 64 dims, 128-row raw window, indexer with
+ *     64 heads x 128 dims and top-k 512 (Pro: 1024);
+ *   - section 3-1: raw-window values are rounded to f16 when pushed;
+ *   - section 3-3: a thin indexer scores the compressed rows and only the
+ *     top-k of them reach the main attention;
+ *   - section 3 (overview): attention runs over the raw window plus the
+ *     selected compressed rows.
+ * Readings of points the article leaves open (ReLU between the per-head dot
+ * product and the weighted head sum, interleaved RoPE pairs, rows stored
+ * already rotated, key = value, one softmax over the concatenated union)
+ * are stated beside each function in ds4o.c.
+ *
+ * All arithmetic is IEEE double; stored inputs are read as the exact real
+ * values of their dtypes (bf16 / f16 bit patterns passed as uint16_t).
+ */
+#ifndef DS4O_H
+#define DS4O_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exact value of an IEEE binary16 / bfloat16 bit pattern. */
+double ds4o_f16_to_f64(uint16_t h);
+double ds4o_bf16_to_f64(uint16_t b);
+
+/* Round a float to IEEE binary16, round-to-nearest-even, gradual underflow,
+ * overflow to infinity, NaN kept (quiet).  Returns the bit pattern. */
+uint16_t ds4o_round_f16(float x);
+
+/* Indexer scores of one query over rows 0..N-1:
+ *   s[j] = sum_h w[h] * max(0, sum_d qI[h][d] * kI[j][d])   for j <  n_vis
+ *   s[j] = -infinity                                         for j >= n_vis
+ * qI: bf16 [Hi][Di], w: f32 [Hi], kI: bf16 [N][Di], s: double [N]. */
+void ds4o_indexer_score(int64_t N, int Hi, int Di, const uint16_t *qI, const float *w,
+                        const uint16_t *kI, int64_t n_vis, double *s);
+
+/* Top-k of one query: rows 0..n_vis-1 sorted by (score descending, index
+ * ascending); the first min(K, n_vis) indices are written to idx[0..], the
+ * remaining slots are -1.  Returns the number of real entries. */
+int ds4o_topk(int64_t n_vis, int K, const double *s, int32_t *idx);
+
+/* RoPE on the tail of every head of one query at absolute position pos:
+ * pairs (D-n_rot+2i, D-n_rot+2i+1), angle pos * theta^(-2i/n_rot). */
+void ds4o_rope_q(int H, int D, int n_rot, int64_t pos, double theta,
+                 const double *q_in, double *q_out);
+
+/* Attention of one query.  Union = W raw rows (f16 [W][D]) followed by the
+ * compressed rows comp[idx[k]] (bf16 [*][D]) for idx[k] >= 0.  One softmax over
+ * the union per head; each row is both key and value.
+ * q_rot: double [H][D] (already rotated), out: double [H][D].
+ * An empty union gives zeros.  Returns the union size. */
+int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
+                    const uint16_t *raw, const uint16_t *comp, const int32_t *idx,
+                    double scale, double *out);
+
+/* Whole step for U units x T queries (the layout of the GPU library's calls),
+ * on nthreads host threads over independent (unit, query) pairs:
+ *   q      : [U][T][H][D]  f32 (q_is_bf16 = 0) or bf16 bits (q_is_bf16 = 1)
+ *   pos    : [U][T] int64      raw : f16 [U][T+W-1][D]  (query t uses rows t..t+W-1)
+ *   comp   : bf16 [U][N][D]    kI  : bf16 [U][N][Di]    qI : bf16 [U][T][Hi][Di]
+ *   w      : f32 [U][T][Hi]    n_vis : int32 [U][T]
+ * Outputs (any may be NULL): scores double [U][T][N], idx int32 [U][T][K],
+ * out double [U][T][H][D].  Only the pairs listed in sel (flattened u*T+t,
+ * n_sel of them) are computed; sel = NULL means all.  Returns 0 on success. */
+int ds4o_step(int U, int T, int64_t N, int H, int D, int n_rot, int W, int Hi, int Di, int K,
+              const void *q, int q_is_bf16, const int64_t *pos, double theta,
+              const uint16_t *raw, const uint16_t *comp, const uint16_t *kI,
+              const uint16_t *qI, const float *w, const int32_t *n_vis, double scale,
+              const int64_t *sel, int64_t n_sel, int nthreads,
+              double *scores, int32_t *idx, double *out);
+
+#ifdef __cplusplus
+}
+#endif
+#endif
