@@ -1,0 +1,145 @@
+/* ds4attn.h — C ABI of libds4attn: one layer's compressed sparse attention step
+ * on an AMD Instinct MI355X (gfx950).
+ *
+ * The step, as "Reading the architecture of DwarfStar (ds4.c), part 1/8"
+ * (Qiita) describes it: in layers with compression ratio 4, a thin indexer
+ * scores every compressed KV row and keeps the best n_indexer_top_k of them
+ * (section 3-3); the main attention then runs its query heads against one
+ * shared 512-dim KV head over the recent raw window plus the selected rows
+ * (sections 2 and 3), with RoPE on the last n_rot = 64 dims (section 2).
+ *
+ * Conventions (all calls):
+ *   - Pointers are DEVICE pointers unless stated otherwise; the caller owns every
+ *     buffer, including the workspace (size it with ds4a_workspace_bytes).  The
+ *     library never allocates or frees device memory.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream) and performs no host synchronisation.
+ *   - Arguments are validated before anything is enqueued.  On a non-zero
+ *     status nothing is enqueued, outputs are untouched, and ds4a_last_error()
+ *     describes the problem.  A launch failure reported by the runtime maps to
+ *     DS4A_E_HIP.  Faults inside kernels surface at the caller's next sync.
+ *     There is no fallback path: unsupported shapes return DS4A_E_UNSUPPORTED.
+ *   - Device pointers must be 16-byte aligned.  Rows are dense and row-major.
+ *   - bf16 / f16 tensors hold IEEE bfloat16 / binary16 bit patterns.
+ *   - Inputs must be finite; the library does not scan data.  Device-side
+ *     integers are clamped to be safe: n_vis to [0, N]; idx values outside
+ *     [0, N) are treated as -1 (skipped).
+ *   - Calls on distinct streams are thread-safe.  Calls that share a
+ *     workspace must be ordered on one stream.
+ */
+#ifndef DS4ATTN_H
+#define DS4ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DS4A_VERSION 1
+
+typedef enum {
+    DS4A_OK = 0,
+    DS4A_E_NULL = -1,        /* a required pointer is NULL                          */
+    DS4A_E_SHAPE = -2,       /* a size is negative, zero where it may not be, or too large */
+    DS4A_E_UNSUPPORTED = -3, /* a valid shape this library does not implement        */
+    DS4A_E_ALIGN = -4,       /* a device pointer is not 16-byte aligned              */
+    DS4A_E_WORKSPACE = -5,   /* workspace missing or smaller than ds4a_workspace_bytes */
+    DS4A_E_DTYPE = -6,       /* unknown dtype code                                   */
+    DS4A_E_HIP = -7          /* the HIP runtime rejected a launch                   */
+} ds4a_status;
+
+typedef enum { DS4A_F32 = 0, DS4A_BF16 = 1, DS4A_F16 = 2 } ds4a_dtype;
+
+/* Supported shapes. */
+#define DS4A_INDEXER_HEADS 64     /* Hi: n_indexer_head (section 2)             */
+#define DS4A_INDEXER_DIM 128      /* Di: n_indexer_head_dim (section 2)         */
+#define DS4A_HEAD_DIM 512         /* D : n_head_dim (section 2)                 */
+#define DS4A_ROPE_DIMS 64         /* n_rot (section 2)                          */
+#define DS4A_MAX_HEADS 128        /* H : a multiple of 16 up to 128 (Flash 64, Pro 128) */
+#define DS4A_MAX_TOPK 2048        /* K : 1..2048 (Flash 512, Pro 1024)          */
+#define DS4A_MAX_WINDOW 1024      /* W : a multiple of 32 up to 1024 (n_swa = 128) */
+
+/* A1 — indexer scores (section 3-3: the indexer's own thin query scores every
+ * compressed row).  For unit u, query t and row j < n_vis[u][t]:
+ *     scores[u][t][j] = sum_h idx_w[u][t][h] * max(0, sum_d idx_q[u][t][h][d] * idx_k[u][j][d])
+ * and scores[u][t][j] = -INFINITY for n_vis[u][t] <= j < N.  The nonlinearity
+ * (ReLU) and the head weighting are this library's reading; the page names only
+ * the head count, head dim and top-k.  Products are exact bf16 x bf16 in fp32,
+ * accumulated in fp32; the head sum is fp32.
+ *   U, T     : units (layers or sessions) and query tokens per unit, >= 1
+ *   N        : compressed rows per unit, >= 1, U*T*N < 2^40, N < 2^31
+ *   Hi, Di   : must be 64 and 128
+ *   idx_q    : bf16 [U][T][Hi][Di]      idx_w : f32 [U][T][Hi]
+ *   idx_k    : bf16 [U][N][Di]          n_vis : int32 [U][T], or NULL for "all N"
+ *   scores   : f32 [U][T][N] (output)
+ */
+int ds4a_indexer_score(int U, int T, int64_t N, int Hi, int Di,
+                       const void *idx_q, const float *idx_w, const void *idx_k,
+                       const int32_t *n_vis, float *scores, void *stream);
+
+/* A2 — top-k selection (section 3-3: only the n_indexer_top_k best-scoring
+ * rows reach the main attention; 512 for Flash, 1024 for Pro per section 2).
+ * For each (u, t): the set of min(K, n_vis) rows j < n_vis with the largest
+ * scores; equal scores (compared as IEEE floats, so -0 == +0) go to the lower j.
+ * idx[u][t][*] receives that set in ascending row order, padded with -1.
+ *   K        : 1..DS4A_MAX_TOPK
+ *   scores   : f32 [U][T][N] (finite for j < n_vis)     n_vis : int32 [U][T] or NULL
+ *   idx      : int32 [U][T][K] (output)
+ *   workspace: ds4a_workspace_bytes(0, U, T, N, K, 0, 0) bytes of device memory
+ */
+int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores,
+                     const int32_t *n_vis, int32_t *idx,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+/* A3-A6 — sparse multi-query attention over the raw window plus the selected
+ * rows (sections 2 and 3; the raw window keeps f16-rounded values, section 3-1).
+ * For unit u, query t, head h:
+ *   q'      = q[u][t][h] with dims D-n_rot+2i, D-n_rot+2i+1 rotated by the angle
+ *             q_pos[u][t] * rope_theta^(-2i/n_rot)   (A3; stored rows are already
+ *             rotated, so only the query is rotated here)
+ *   union   = raw rows raw_kv[u][t + r], r = 0..W-1, then comp_kv[u][idx[u][t][k]]
+ *             for every idx entry in [0, N) (no de-duplication)
+ *   l_r     = scale * <q', row_r>                  (A4; each row is key and value)
+ *   out     = sum_r softmax(l)_r * row_r           (A5, A6: one softmax over the union)
+ * An empty union gives zeros.  MFMA operands are bf16; operands that are not
+ * bf16 (the fp32 query, the f16 raw rows, the probabilities) are carried as
+ * hi + lo bf16 pairs; accumulation is fp32.
+ *   H        : query heads, a multiple of 16 up to 128      D, n_rot : 512, 64
+ *   W        : raw window rows, a multiple of 32, 0..1024     K : 1..DS4A_MAX_TOPK
+ *   q        : [U][T][H][D], q_dtype DS4A_F32 or DS4A_BF16 (pre-RoPE)
+ *   q_pos    : int64 [U][T] absolute positions          rope_theta : > 0 (10000 in the tests)
+ *   raw_kv   : f16 [U][T+W-1][D]   (query t uses rows t..t+W-1)
+ *   comp_kv  : bf16 [U][N][D]      idx : int32 [U][T][K] (from ds4a_topk_select)
+ *   out      : f32 [U][T][H][D] (output)
+ *   workspace: ds4a_workspace_bytes(1, U, T, N, K, H, W) bytes (0 -> NULL allowed)
+ */
+int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K,
+                    const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                    const void *raw_kv, const void *comp_kv, const int32_t *idx,
+                    float scale, float *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* A3 alone, for inspection: writes the rotated query as f32 [U][T][H][D], using
+ * the same device code as ds4a_sparse_mqa's prologue (fp64 angle and rotation,
+ * rounded once to f32).  Same argument rules as ds4a_sparse_mqa. */
+int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtype,
+                const int64_t *q_pos, double rope_theta, float *q_out, void *stream);
+
+/* Workspace bytes for `which` = 0 (ds4a_topk_select; H and W ignored) or
+ * 1 (ds4a_sparse_mqa).  0 means no workspace is needed (NULL is accepted), or
+ * that the arguments are invalid.  Host-only, never touches the GPU. */
+size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W);
+
+/* Text of the last non-zero status returned on the calling thread (host memory
+ * owned by the library, valid until the thread's next call). */
+const char *ds4a_last_error(void);
+
+/* DS4A_VERSION of the loaded library. */
+int ds4a_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,174 @@
+// api.hip — the extern "C" boundary of libds4attn (declared in include/ds4attn.h).
+//
+// Every entry point validates its arguments on the host, before any HIP call,
+// and returns a status; on error nothing is enqueued and ds4a_last_error()
+// holds a message.  Validation is pure host code, so it can be exercised on a
+// machine without a GPU.  Fail closed: unsupported shapes are rejected, there
+// is no alternative code path.
+#include "../../include/ds4attn.h"
+#include "launch.hpp"
+
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+namespace {
+
+thread_local char g_err[512];
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = 0;
+    return DS4A_OK;
+}
+
+bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+#define REQUIRE_PTR(p)                                                              \
+    do {                                                                            \
+        if (!(p)) return fail(DS4A_E_NULL, "%s: %s is NULL", fn, #p);               \
+        if (misaligned(p)) return fail(DS4A_E_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+#define OPTIONAL_PTR(p)                                                             \
+    do {                                                                            \
+        if ((p) && misaligned(p)) return fail(DS4A_E_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
+    } while (0)
+
+constexpr int64_t kMaxRows = (int64_t(1) << 31) - 1;
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+
+int check_units(const char *fn, int U, int T, int64_t N) {
+    if (U < 1 || T < 1) return fail(DS4A_E_SHAPE, "%s: U=%d and T=%d must be >= 1", fn, U, T);
+    if (N < 1 || N > kMaxRows) return fail(DS4A_E_SHAPE, "%s: N=%lld must be in [1, 2^31-1]", fn, (long long)N);
+    if ((int64_t)U * T > (int64_t(1) << 24)) return fail(DS4A_E_SHAPE, "%s: U*T=%lld too large", fn, (long long)U * T);
+    if ((int64_t)U * T * N > kMaxElems) return fail(DS4A_E_SHAPE, "%s: U*T*N too large", fn);
+    return DS4A_OK;
+}
+
+int check_attn_shape(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, int q_dtype,
+                     double theta) {
+    if (int rc = check_units(fn, U, T, N)) return rc;
+    if (q_dtype != DS4A_F32 && q_dtype != DS4A_BF16) {
+        if (q_dtype == DS4A_F16) return fail(DS4A_E_UNSUPPORTED, "%s: f16 queries are not supported", fn);
+        return fail(DS4A_E_DTYPE, "%s: unknown q_dtype %d", fn, q_dtype);
+    }
+    if (H < 1 || D < 1 || n_rot < 0 || W < 0 || K < 1)
+        return fail(DS4A_E_SHAPE, "%s: H=%d D=%d n_rot=%d W=%d K=%d out of range", fn, H, D, n_rot, W, K);
+    if (D != DS4A_HEAD_DIM) return fail(DS4A_E_UNSUPPORTED, "%s: D=%d (only %d)", fn, D, DS4A_HEAD_DIM);
+    if (n_rot != DS4A_ROPE_DIMS) return fail(DS4A_E_UNSUPPORTED, "%s: n_rot=%d (only %d)", fn, n_rot, DS4A_ROPE_DIMS);
+    if (H % 16 != 0 || H > DS4A_MAX_HEADS)
+        return fail(DS4A_E_UNSUPPORTED, "%s: H=%d (multiples of 16 up to %d)", fn, H, DS4A_MAX_HEADS);
+    if (W % 32 != 0 || W > DS4A_MAX_WINDOW)
+        return fail(DS4A_E_UNSUPPORTED, "%s: W=%d (multiples of 32 up to %d)", fn, W, DS4A_MAX_WINDOW);
+    if (K > DS4A_MAX_TOPK) return fail(DS4A_E_UNSUPPORTED, "%s: K=%d (at most %d)", fn, K, DS4A_MAX_TOPK);
+    if (!(theta > 0.0) || theta != theta) return fail(DS4A_E_SHAPE, "%s: rope_theta must be > 0", fn);
+    return DS4A_OK;
+}
+
+int hip_status(const char *fn, hipError_t e) {
+    if (e == hipSuccess) return ok();
+    return fail(DS4A_E_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int ds4a_version(void) { return DS4A_VERSION; }
+
+const char *ds4a_last_error(void) { return g_err; }
+
+size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W) {
+    if (U < 1 || T < 1 || N < 1 || N > kMaxRows || K < 1 || K > DS4A_MAX_TOPK) return 0;
+    if (which == 0) return ds4a::topk_workspace_bytes((int64_t)U * T, N, K);
+    if (which == 1) {
+        if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW) return 0;
+        return ds4a::plan_mqa(U, T, H, W, K).workspace_bytes;
+    }
+    return 0;
+}
+
+int ds4a_indexer_score(int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
+                       const void *idx_k, const int32_t *n_vis, float *scores, void *stream) {
+    const char *fn = "ds4a_indexer_score";
+    if (int rc = check_units(fn, U, T, N)) return rc;
+    if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
+        return fail(DS4A_E_UNSUPPORTED, "%s: Hi=%d Di=%d (only %d x %d)", fn, Hi, Di, DS4A_INDEXER_HEADS,
+                    DS4A_INDEXER_DIM);
+    REQUIRE_PTR(idx_q);
+    REQUIRE_PTR(idx_w);
+    REQUIRE_PTR(idx_k);
+    REQUIRE_PTR(scores);
+    OPTIONAL_PTR(n_vis);
+    return hip_status(fn, ds4a::launch_indexer(U, T, N, static_cast<const uint16_t *>(idx_q), idx_w,
+                                               static_cast<const uint16_t *>(idx_k), n_vis, scores,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores, const int32_t *n_vis, int32_t *idx,
+                     void *workspace, size_t workspace_bytes, void *stream) {
+    const char *fn = "ds4a_topk_select";
+    if (int rc = check_units(fn, U, T, N)) return rc;
+    if (K < 1) return fail(DS4A_E_SHAPE, "%s: K=%d must be >= 1", fn, K);
+    if (K > DS4A_MAX_TOPK) return fail(DS4A_E_UNSUPPORTED, "%s: K=%d (at most %d)", fn, K, DS4A_MAX_TOPK);
+    REQUIRE_PTR(scores);
+    REQUIRE_PTR(idx);
+    OPTIONAL_PTR(n_vis);
+    const size_t need = ds4a::topk_workspace_bytes((int64_t)U * T, N, K);
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, ds4a::launch_topk((int64_t)U * T, N, K, scores, n_vis, idx, workspace,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q, int q_dtype,
+                    const int64_t *q_pos, double rope_theta, const void *raw_kv, const void *comp_kv,
+                    const int32_t *idx, float scale, float *out, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    const char *fn = "ds4a_sparse_mqa";
+    if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, W, N, K, q_dtype, rope_theta)) return rc;
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+        return fail(DS4A_E_SHAPE, "%s: scale must be finite", fn);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_pos);
+    if (W > 0) REQUIRE_PTR(raw_kv);
+    REQUIRE_PTR(comp_kv);
+    REQUIRE_PTR(idx);
+    REQUIRE_PTR(out);
+    const size_t need = ds4a::plan_mqa(U, T, H, W, K).workspace_bytes;
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
+                                           static_cast<const uint16_t *>(raw_kv),
+                                           static_cast<const uint16_t *>(comp_kv), idx, scale, out, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtype, const int64_t *q_pos,
+                double rope_theta, float *q_out, void *stream) {
+    const char *fn = "ds4a_rope_q";
+    if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, 0, 1, 1, q_dtype, rope_theta)) return rc;
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_pos);
+    REQUIRE_PTR(q_out);
+    return hip_status(fn, ds4a::launch_rope(U, T, H, q, q_dtype == DS4A_BF16, q_pos, rope_theta, q_out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// indexer.hip — A1: indexer scores of every compressed row.
+//
+// "Reading the architecture of DwarfStar (ds4.c), part 1/8" (Qiita), section
+// 3-3: ratio-4 layers carry a thin indexer (64 heads x 128 dims, section 2)
+// whose query scores every compressed row; its scores decide which rows the
+// main attention reads.  Score (reading: ReLU between the per-head dot product
+// and the weighted head sum):
+//     s[j] = sum_h w[h] * max(0, <qI[h], kI[j]>)
+//
+// Design (decode and prefill alike): one query per workgroup row-chunk; the
+// query's 64x128 bf16 block sits in VGPRs as the MFMA A operand (64 VGPRs),
+// key rows stream from HBM straight into B-operand registers.  Each wave
+// takes 64 consecutive rows (16 KiB) per iteration: four 16-row blocks, each
+// row read as 4 x 64-byte contiguous segments.  Per 16-row block:
+// 4 head tiles x 4 k-steps = 16 v_mfma_f32_16x16x32_bf16.  The D layout puts
+// 4 heads of one row in each lane, so the fp32 ReLU + weighted head sum is 16
+// in-lane FMAs plus two cross-lane adds.  The op is HBM-bound (64 flop/byte).
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace ds4a {
+
+namespace {
+
+constexpr int kHeads = 64;
+constexpr int kDim = 128;
+constexpr int kThreads = 256;
+constexpr int kWaves = kThreads / kWave;
+constexpr int kBlocksPerIter = 4;                              // 16-row blocks per wave iteration
+constexpr int kRowsPerIter = 16 * kBlocksPerIter * kWaves;     // 256 rows per workgroup iteration
+constexpr int kChunksPerRow = kDim * 2 / 16;                   // 16-byte chunks per key row (16)
+
+__global__ __launch_bounds__(kThreads) void indexer_score_kernel(
+    int T, int64_t N, int64_t rows_per_wg, int64_t wg_per_query,
+    const uint16_t *__restrict__ qI, const float *__restrict__ w, const uint16_t *__restrict__ kI,
+    const int32_t *__restrict__ n_vis, float *__restrict__ scores)
+{
+    const int64_t q = (int64_t)blockIdx.x / wg_per_query;          // flattened (u, t)
+    const int64_t part = (int64_t)blockIdx.x % wg_per_query;
+    const int64_t u = q / T;
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int g = lane >> 4;       // k-group (A/B) and row-group (D) of this lane
+    const int c = lane & 15;       // row of A / column of B and D
+
+    const int64_t nv = clamp_nvis(n_vis, q, N);
+    const int64_t r0 = part * rows_per_wg;
+    const int64_t r1 = r0 + rows_per_wg < N ? r0 + rows_per_wg : N;
+    float *srow = scores + q * N;
+
+    // Invisible rows of this chunk.
+    for (int64_t j = (r0 > nv ? r0 : nv) + threadIdx.x; j < r1; j += kThreads) srow[j] = -INFINITY;
+    const int64_t rv1 = r1 < nv ? r1 : nv;   // visible rows [r0, rv1)
+    if (r0 >= rv1) return;
+
+    // Indexer query -> LDS -> A fragments: aq[ht][s] = qI[16ht + c][32s + 8g .. +7].
+    __shared__ u32x4 sq[kHeads * kDim / 8];
+    const u32x4 *gq = reinterpret_cast<const u32x4 *>(qI + q * (int64_t)(kHeads * kDim));
+    for (int i = threadIdx.x; i < kHeads * kDim / 8; i += kThreads) sq[i] = gq[i];
+    __syncthreads();
+    bf16x8 aq[4][4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + 4 * s + g]);
+
+    // Head weights of the 16 D rows this lane holds: heads 16ht + 4g + r.
+    float wh[4][4];
+    const float *wq = w + q * kHeads;
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wh[ht][r] = wq[16 * ht + 4 * g + r];
+
+    const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
+
+    for (int64_t base = r0 + 16 * kBlocksPerIter * wave; base < rv1; base += kRowsPerIter) {
+        // Issue all loads of this iteration first: B fragment (k-step s) of row base+16bi+c
+        // is the 16-byte chunk 4s+g of that row.
+        u32x4 kb[kBlocksPerIter][4];
+#pragma unroll
+        for (int bi = 0; bi < kBlocksPerIter; ++bi) {
+            const int64_t row = base + 16 * bi + c;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if (row < rv1)
+                    kb[bi][s] = __builtin_nontemporal_load(gk + row * kChunksPerRow + 4 * s + g);
+                else
+                    kb[bi][s] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int bi = 0; bi < kBlocksPerIter; ++bi) {
+            const int64_t blk = base + 16 * bi;
+            if (blk >= rv1) break;                    // uniform across the wave
+            float acc = 0.f;
+#pragma unroll
+            for (int ht = 0; ht < 4; ++ht) {
+                f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s) d = mfma16(aq[ht][s], as_bf16x8(kb[bi][s]), d);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) acc += wh[ht][r] * fmaxf(d[r], 0.f);
+            }
+            // Sum the four row-groups: lanes c, c+16, c+32, c+48 hold the same row.
+            acc = wave_xor_sum(acc, 16);
+            acc = wave_xor_sum(acc, 32);
+            if (g == 0 && blk + c < rv1) srow[blk + c] = acc;
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w,
+                          const uint16_t *idx_k, const int32_t *n_vis, float *scores,
+                          hipStream_t stream)
+{
+    const int64_t Q = (int64_t)U * T;
+    // Aim for >= ~1024 workgroups over the 256 CUs, in multiples of one workgroup iteration.
+    const int64_t total_rows = Q * N;
+    int64_t rows = (total_rows / 1024 + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
+    if (rows < kRowsPerIter) rows = kRowsPerIter;
+    if (rows > 16 * kRowsPerIter) rows = 16 * kRowsPerIter;
+    const int64_t per_q = (N + rows - 1) / rows;
+    const int64_t blocks = per_q * Q;
+    hipLaunchKernelGGL(indexer_score_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       T, N, rows, per_q, idx_q, idx_w, idx_k, n_vis, scores);
+    return hipGetLastError();
+}
+
+}  // namespace ds4a

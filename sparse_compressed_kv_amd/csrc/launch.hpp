@@ -1,0 +1,36 @@
+// launch.hpp — internal launchers behind the C ABI (validated arguments only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ds4a {
+
+// A1: scores f32 [Q][N], Q = U*T.
+hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w,
+                          const uint16_t *idx_k, const int32_t *n_vis, float *scores,
+                          hipStream_t stream);
+
+// A2
+size_t topk_workspace_bytes(int64_t Q, int64_t N, int K);
+hipError_t launch_topk(int64_t Q, int64_t N, int K, const float *scores, const int32_t *n_vis,
+                       int32_t *idx, void *workspace, hipStream_t stream);
+
+// A3-A6
+struct MqaPlan {
+    int n_hg;              // head groups of 16
+    int n_tiles;           // union tiles of 32 rows
+    int tiles_per_chunk;
+    int n_chunks;
+    size_t workspace_bytes;
+};
+MqaPlan plan_mqa(int U, int T, int H, int W, int K);
+hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
+                      const int64_t *q_pos, double theta, const uint16_t *raw, const uint16_t *comp,
+                      const int32_t *idx, float scale, float *out, void *workspace,
+                      hipStream_t stream);
+hipError_t launch_rope(int U, int T, int H, const void *q, int q_bf16, const int64_t *q_pos,
+                       double theta, float *q_out, hipStream_t stream);
+
+}  // namespace ds4a

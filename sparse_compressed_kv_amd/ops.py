@@ -1,0 +1,220 @@
+"""Python binding of libds4attn (ctypes): argument marshalling only.
+
+Every step of the attention path runs in the library's HIP kernels; torch is
+used only to own device memory and to name the stream.  There is no CPU or
+eager fallback: if the library is missing, or no GPU is present, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libds4attn.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "ds4attn.h")
+
+DS4A_F32, DS4A_BF16, DS4A_F16 = 0, 1, 2
+STATUS = {0: "OK", -1: "E_NULL", -2: "E_SHAPE", -3: "E_UNSUPPORTED", -4: "E_ALIGN", -5: "E_WORKSPACE",
+          -6: "E_DTYPE", -7: "E_HIP"}
+
+_lib = None
+
+
+class Ds4aError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} -> {STATUS.get(code, code)}: {msg}")
+        self.code = code
+
+
+def hip_runtimes_mapped() -> list[str]:
+    """Paths of every libamdhip64 mapped into this process (one expected)."""
+    with open("/proc/self/maps") as f:
+        return sorted(set(re.findall(r"\S*libamdhip64\S*", f.read())))
+
+
+def lib() -> ctypes.CDLL:
+    """Load libds4attn.so (built in-tree).  Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is not built: run `python -m sparse_compressed_kv_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, sz, dbl, flt = (ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t,
+                                 ctypes.c_double, ctypes.c_float)
+    L.ds4a_version.argtypes, L.ds4a_version.restype = [], i32
+    L.ds4a_last_error.argtypes, L.ds4a_last_error.restype = [], ctypes.c_char_p
+    L.ds4a_workspace_bytes.argtypes = [i32, i32, i32, i64, i32, i32, i32]
+    L.ds4a_workspace_bytes.restype = sz
+    L.ds4a_indexer_score.argtypes = [i32, i32, i64, i32, i32, P, P, P, P, P, P]
+    L.ds4a_indexer_score.restype = i32
+    L.ds4a_topk_select.argtypes = [i32, i32, i64, i32, P, P, P, P, sz, P]
+    L.ds4a_topk_select.restype = i32
+    L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
+    L.ds4a_sparse_mqa.restype = i32
+    L.ds4a_rope_q.argtypes = [i32, i32, i32, i32, i32, P, i32, P, dbl, P, P]
+    L.ds4a_rope_q.restype = i32
+    _lib = L
+    return L
+
+
+def declared_symbols() -> list[str]:
+    """Function names the public header declares."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(ds4a_[a-z_]+)\s*\(", text)))
+
+
+def last_error() -> str:
+    return lib().ds4a_last_error().decode()
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        raise Ds4aError(fn, rc, last_error())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def workspace_bytes(which: int, U: int, T: int, N: int, K: int, H: int = 0, W: int = 0) -> int:
+    return int(lib().ds4a_workspace_bytes(which, U, T, N, K, H, W))
+
+
+def _workspace(nbytes: int, device, ws):
+    if nbytes == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < nbytes:
+        raise ValueError(f"workspace needs {nbytes} bytes")
+    return ws, ws.numel() * ws.element_size()
+
+
+def indexer_score(idx_q, idx_w, idx_k, n_vis=None, out=None, stream=None):
+    """A1.  idx_q bf16 [U,T,64,128], idx_w f32 [U,T,64], idx_k bf16 [U,N,128] -> f32 [U,T,N]."""
+    U, T, Hi, Di = idx_q.shape
+    N = idx_k.shape[1]
+    _need(idx_q, "idx_q", torch.bfloat16)
+    _need(idx_w, "idx_w", torch.float32, (U, T, Hi))
+    _need(idx_k, "idx_k", torch.bfloat16, (U, N, Di))
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    if out is None:
+        out = torch.empty((U, T, N), dtype=torch.float32, device=idx_q.device)
+    _need(out, "out", torch.float32, (U, T, N))
+    _check("ds4a_indexer_score", lib().ds4a_indexer_score(U, T, N, Hi, Di, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k),
+                                                          _ptr(n_vis), _ptr(out), _stream(stream)))
+    return out
+
+
+def topk_select(scores, K: int, n_vis=None, out=None, workspace=None, stream=None):
+    """A2.  scores f32 [U,T,N] -> int32 [U,T,K]: ascending selected rows, -1 padded."""
+    _need(scores, "scores", torch.float32)
+    U, T, N = scores.shape
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    if out is None:
+        out = torch.empty((U, T, K), dtype=torch.int32, device=scores.device)
+    _need(out, "out", torch.int32, (U, T, K))
+    ws, nb = _workspace(workspace_bytes(0, U, T, N, K), scores.device, workspace)
+    _check("ds4a_topk_select", lib().ds4a_topk_select(U, T, N, K, _ptr(scores), _ptr(n_vis), _ptr(out), _ptr(ws),
+                                                      nb, _stream(stream)))
+    return out
+
+
+def _q_dtype(q):
+    if q.dtype == torch.float32:
+        return DS4A_F32
+    if q.dtype == torch.bfloat16:
+        return DS4A_BF16
+    raise TypeError(f"q must be float32 or bfloat16 (got {q.dtype})")
+
+
+def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 10000.0, W: int = 128,
+               out=None, workspace=None, stream=None):
+    """A3-A6.  q [U,T,H,512] f32|bf16, q_pos i64 [U,T], raw_kv f16 [U,T+W-1,512],
+    comp_kv bf16 [U,N,512], idx i32 [U,T,K] -> f32 [U,T,H,512]."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    U, T, H, D = q.shape
+    N = comp_kv.shape[1]
+    K = idx.shape[2]
+    _need(q, "q", q.dtype)
+    qd = _q_dtype(q)
+    _need(q_pos, "q_pos", torch.int64, (U, T))
+    if W > 0:
+        _need(raw_kv, "raw_kv", torch.float16, (U, T + W - 1, D))
+    _need(comp_kv, "comp_kv", torch.bfloat16, (U, N, D))
+    _need(idx, "idx", torch.int32, (U, T, K))
+    if out is None:
+        out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (U, T, H, D))
+    ws, nb = _workspace(workspace_bytes(1, U, T, N, K, H, W), q.device, workspace)
+    _check("ds4a_sparse_mqa", lib().ds4a_sparse_mqa(
+        U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta),
+        _ptr(raw_kv) if W > 0 else None, _ptr(comp_kv), _ptr(idx), float(scale), _ptr(out), _ptr(ws), nb,
+        _stream(stream)))
+    return out
+
+
+def rope_q(q, q_pos, theta: float = 10000.0, out=None, stream=None):
+    """A3 alone: rotated query as f32 [U,T,H,512]."""
+    U, T, H, D = q.shape
+    qd = _q_dtype(q)
+    _need(q, "q", q.dtype)
+    _need(q_pos, "q_pos", torch.int64, (U, T))
+    if out is None:
+        out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (U, T, H, D))
+    _check("ds4a_rope_q", lib().ds4a_rope_q(U, T, H, D, 64, _ptr(q), qd, _ptr(q_pos), float(theta), _ptr(out),
+                                            _stream(stream)))
+    return out
+
+
+class Step:
+    """The whole hot path for fixed shapes: indexer -> top-k -> attention, with every
+    intermediate, output and workspace allocated once up front."""
+
+    def __init__(self, U, T, N, H=64, K=512, W=128, q_dtype=torch.float32, device="cuda"):
+        self.U, self.T, self.N, self.H, self.K, self.W = U, T, N, H, K, W
+        dev = torch.device(device)
+        self.scores = torch.empty((U, T, N), dtype=torch.float32, device=dev)
+        self.idx = torch.empty((U, T, K), dtype=torch.int32, device=dev)
+        self.out = torch.empty((U, T, H, 512), dtype=torch.float32, device=dev)
+        nb0 = workspace_bytes(0, U, T, N, K)
+        nb1 = workspace_bytes(1, U, T, N, K, H, W)
+        self.ws_topk = torch.empty(max(nb0, 1), dtype=torch.uint8, device=dev)
+        self.ws_mqa = torch.empty(max(nb1, 1), dtype=torch.uint8, device=dev)
+
+    def __call__(self, x: dict, n_vis=None, scale=1.0 / 512 ** 0.5, theta=10000.0, stream=None):
+        indexer_score(x["idx_q"], x["idx_w"], x["idx_k"], n_vis=n_vis, out=self.scores, stream=stream)
+        topk_select(self.scores, self.K, n_vis=n_vis, out=self.idx, workspace=self.ws_topk, stream=stream)
+        sparse_mqa(x["q"], x["pos"], x["raw"], x["comp"], self.idx, scale, theta, W=self.W, out=self.out,
+                   workspace=self.ws_mqa, stream=stream)
+        return self.out

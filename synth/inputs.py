@@ -21,20 +21,26 @@ attention arithmetic.
 """
 from __future__ import annotations
 
+import concurrent.futures
 import dataclasses
 import math
+import os
 
 import numpy as np
 
 TENSOR_IDS = {"q": 0, "raw": 1, "comp": 2, "idx_k": 3, "idx_q": 4, "idx_w": 5, "heavy": 6}
-_CHUNK_ROWS = 65536
+_CHUNK_ELEMS = 1 << 22
 
 
 def bf16_bits_from_f32(x) -> np.ndarray:
     """Round float32 values to bfloat16 (round-to-nearest-even); return the 16-bit patterns."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
-    rounded = b + (np.uint32(0x7FFF) + ((b >> np.uint32(16)) & np.uint32(1)))
-    return (rounded >> np.uint32(16)).astype(np.uint16)
+    t = b >> np.uint32(16)
+    t &= np.uint32(1)
+    t += np.uint32(0x7FFF)
+    t += b
+    t >>= np.uint32(16)
+    return t.astype(np.uint16)
 
 
 def f16_bits_from_f32(x) -> np.ndarray:
@@ -113,10 +119,15 @@ def _rng(w: Workload, seed: int, unit: int, tensor: str) -> np.random.Generator:
 
 
 def _normal_bf16(rng, rows: int, cols: int) -> np.ndarray:
+    """N(0,1) draws rounded to bf16, filled in cache-sized chunks (same stream as one big draw)."""
     out = np.empty((rows, cols), dtype=np.uint16)
-    for r0 in range(0, rows, _CHUNK_ROWS):
-        r1 = min(rows, r0 + _CHUNK_ROWS)
-        out[r0:r1] = bf16_bits_from_f32(rng.standard_normal((r1 - r0, cols), dtype=np.float32))
+    step = max(1, _CHUNK_ELEMS // max(cols, 1))
+    buf = np.empty((step, cols), dtype=np.float32)
+    for r0 in range(0, rows, step):
+        r1 = min(rows, r0 + step)
+        x = buf[: r1 - r0]
+        rng.standard_normal(out=x, dtype=np.float32)
+        out[r0:r1] = bf16_bits_from_f32(x)
     return out
 
 
@@ -145,9 +156,17 @@ def make_unit(w: Workload, unit: int, seed: int = 0) -> dict[str, np.ndarray]:
     }
 
 
-def make_config(w: Workload, seed: int = 0) -> dict[str, np.ndarray]:
-    """All U units stacked on a leading axis (the layout the library's calls take)."""
-    units = [make_unit(w, u, seed) for u in range(w.U)]
+def make_config(w: Workload, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:
+    """All U units stacked on a leading axis (the layout the library's calls take).
+
+    Units are drawn on a thread pool (each unit has its own streams, so the
+    result does not depend on the thread count)."""
+    n = threads or min(16, os.cpu_count() or 1, w.U)
+    if n > 1:
+        with concurrent.futures.ThreadPoolExecutor(max_workers=n) as ex:
+            units = list(ex.map(lambda u: make_unit(w, u, seed), range(w.U)))
+    else:
+        units = [make_unit(w, u, seed) for u in range(w.U)]
     out = {}
     for key in ("q", "raw", "comp", "idx_k", "idx_q", "idx_w", "n_vis", "pos"):
         out[key] = np.stack([x[key] for x in units])

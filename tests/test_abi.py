@@ -1,0 +1,114 @@
+"""The C-ABI library: loads, exports what the header declares, and validates its
+arguments on the host (no GPU needed: every call here is rejected before any HIP call)."""
+import ctypes
+
+import pytest
+
+from sparse_compressed_kv_amd import ops
+
+A = 0x10000          # a 16-byte aligned stand-in for a device pointer (never dereferenced)
+MIS = 0x10004        # misaligned stand-in
+S = None             # null stream
+
+
+@pytest.fixture(scope="module")
+def L():
+    return ops.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    names = ops.declared_symbols()
+    assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_sparse_mqa", "ds4a_rope_q", "ds4a_workspace_bytes",
+            "ds4a_last_error", "ds4a_version"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_version(L):
+    assert L.ds4a_version() == 1
+
+
+def test_indexer_validation(L):
+    f = L.ds4a_indexer_score
+    assert f(0, 1, 10, 64, 128, A, A, A, None, A, S) == -2
+    assert f(1, 1, 0, 64, 128, A, A, A, None, A, S) == -2
+    assert f(1, 1, 10, 32, 128, A, A, A, None, A, S) == -3
+    assert "Hi=32" in ops.last_error()
+    assert f(1, 1, 10, 64, 64, A, A, A, None, A, S) == -3
+    assert f(1, 1, 10, 64, 128, None, A, A, None, A, S) == -1
+    assert "idx_q" in ops.last_error()
+    assert f(1, 1, 10, 64, 128, A, A, A, None, None, S) == -1
+    assert f(1, 1, 10, 64, 128, A, MIS, A, None, A, S) == -4
+    assert f(1, 1, 10, 64, 128, A, A, A, MIS, A, S) == -4
+    assert f(1, 1, 1 << 31, 64, 128, A, A, A, None, A, S) == -2
+
+
+def test_topk_validation(L):
+    f = L.ds4a_topk_select
+    assert f(1, 1, 100, 0, A, None, A, None, 0, S) == -2
+    assert f(1, 1, 100, 4096, A, None, A, None, 0, S) == -3
+    assert f(1, 1, 100, 16, None, None, A, None, 0, S) == -1
+    assert f(1, 1, 100, 16, A, None, MIS, None, 0, S) == -4
+    # the multi-workgroup path needs a workspace
+    need = ops.workspace_bytes(0, 2, 1, 65536, 512)
+    assert need > 0
+    assert f(2, 1, 65536, 512, A, None, A, None, 0, S) == -5
+    assert f(2, 1, 65536, 512, A, None, A, A, need - 1, S) == -5
+    assert "workspace" in ops.last_error()
+    assert f(2, 1, 65536, 512, A, None, A, MIS, need, S) == -4
+
+
+def _mqa(L, **kw):
+    a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, K=512, q=A, q_dtype=0, q_pos=A, theta=10000.0,
+             raw=A, comp=A, idx=A, scale=0.044, out=A, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.ds4a_sparse_mqa(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["K"], a["q"],
+                             a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["comp"], a["idx"], a["scale"],
+                             a["out"], a["ws"], a["ws_bytes"], S)
+
+
+def test_mqa_validation(L):
+    assert _mqa(L, D=256) == -3
+    assert _mqa(L, n_rot=32) == -3
+    assert _mqa(L, H=48 + 1) == -3
+    assert _mqa(L, H=144) == -3
+    assert _mqa(L, W=100) == -3
+    assert _mqa(L, K=0) == -2
+    assert _mqa(L, K=4096) == -3
+    assert _mqa(L, q_dtype=2) == -3
+    assert _mqa(L, q_dtype=7) == -6
+    assert _mqa(L, theta=0.0) == -2
+    assert _mqa(L, scale=float("nan")) == -2
+    assert _mqa(L, q=None) == -1
+    assert _mqa(L, comp=MIS) == -4
+    assert _mqa(L, U=0) == -2
+    need = ops.workspace_bytes(1, 1, 1, 1000, 512, 64, 128)
+    assert need > 0                       # one query: the union is split over workgroups
+    assert _mqa(L, ws=None, ws_bytes=0) == -5
+    assert _mqa(L, ws_bytes=need - 1) == -5
+
+
+def test_rope_validation(L):
+    f = L.ds4a_rope_q
+    assert f(1, 1, 64, 512, 64, None, 0, A, 10000.0, A, S) == -1
+    assert f(1, 1, 64, 512, 32, A, 0, A, 10000.0, A, S) == -3
+    assert f(1, 1, 64, 512, 64, A, 5, A, 10000.0, A, S) == -6
+
+
+def test_workspace_bytes(L):
+    assert ops.workspace_bytes(0, 43, 1, 16384, 512) == 0            # LDS path
+    assert ops.workspace_bytes(0, 8, 1, 262144, 512) >= 8 * 262144 * 8
+    assert ops.workspace_bytes(2, 1, 1, 10, 10) == 0
+    assert ops.workspace_bytes(1, 1, 2048, 8192, 512, 64, 128) == 0   # prefill: no split
+    assert ops.workspace_bytes(1, 1, 1, 10, 512, 64, 100) == 0        # invalid W
+
+
+def test_last_error_is_text(L):
+    L.ds4a_topk_select(1, 1, 100, 0, A, None, A, None, 0, S)
+    assert isinstance(ops.last_error(), str) and "K=0" in ops.last_error()
+
+
+def test_single_hip_runtime_after_torch():
+    import torch  # noqa: F401  torch's runtime is loaded first, the library reuses it
+    ops.lib()
+    assert len(ops.hip_runtimes_mapped()) == 1, ops.hip_runtimes_mapped()

@@ -1,0 +1,283 @@
+"""GPU parity: every step of the HIP path against the CPU oracle on the same seeded inputs.
+
+Bars (from the problem statement): selected index sets bit-exact on identical fp32
+scores, and against the fp64 oracle equal apart from rows whose scores lie within
+1e-5 (relative) of the K-th score; attention outputs within a normwise relative
+error of 2e-3 per (unit, query).  The hi/lo bf16 operand design is also held to
+1e-4, far inside that bar, so that losing one of the split terms is caught.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as orc
+from sparse_compressed_kv_amd import ops
+from synth import inputs as gen
+from tests.util import bits_to_torch, normwise_err, tie_band_ok, upload
+
+pytestmark = pytest.mark.gpu
+
+CONTRACT_ERR = 2e-3
+DESIGN_ERR = 1e-4
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ops.lib()
+    return torch.device("cuda")
+
+
+def bf16_f64(bits):
+    return gen.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+# ------------------------------------------------------------------- RoPE
+
+@pytest.mark.parametrize("qd", ["f32", "bf16"])
+def test_rope_matches_oracle(qd):
+    rng = np.random.default_rng(5)
+    U, T, H = 2, 3, 32
+    qf = rng.standard_normal((U, T, H, 512)).astype(np.float32)
+    pos = np.array([[0, 1, 8191], [262143, 1048575, 4096]], dtype=np.int64)
+    if qd == "bf16":
+        qb = gen.bf16_bits_from_f32(qf)
+        q_dev, q64 = bits_to_torch(qb, torch.bfloat16), bf16_f64(qb)
+    else:
+        q_dev, q64 = torch.from_numpy(qf).cuda(), qf.astype(np.float64)
+    got = ops.rope_q(q_dev, torch.from_numpy(pos).cuda()).cpu().numpy()
+    for u in range(U):
+        for t in range(T):
+            ref = orc.rope_q(q64[u, t], pos[u, t])
+            assert np.all(np.abs(got[u, t] - ref) <= 1e-6 * (1.0 + np.abs(ref))), (u, t)
+            assert np.array_equal(got[u, t, :, :448], ref[:, :448].astype(np.float32))
+
+
+# ---------------------------------------------------------------- indexer
+
+INDEXER_CASES = [
+    dict(U=1, T=1, N=1, nv=None),
+    dict(U=2, T=3, N=700, nv=[[700, 0, 333], [1, 699, 16]]),
+    dict(U=3, T=1, N=4097, nv=None, heavy=0.01),
+    dict(U=1, T=5, N=257, nv=[[0, 1, 128, 256, 257]]),
+]
+
+
+@pytest.mark.parametrize("case", INDEXER_CASES, ids=lambda c: f"U{c['U']}T{c['T']}N{c['N']}")
+def test_indexer_matches_oracle(case):
+    w = gen.Workload("idx", 101, U=case["U"], T=case["T"], N=case["N"], H=16, K=64,
+                     heavy_frac=case.get("heavy", 0.0))
+    x = gen.make_config(w, seed=1)
+    nv = np.array(case["nv"], dtype=np.int32) if case["nv"] is not None else np.full((w.U, w.T), w.N, np.int32)
+    d = upload(x)
+    got = ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=torch.from_numpy(nv).cuda()).cpu().numpy()
+    for u in range(w.U):
+        kabs = np.abs(bf16_f64(x["idx_k"][u]))
+        for t in range(w.T):
+            ref = orc.indexer_score(x["idx_q"][u, t], x["idx_w"][u, t], x["idx_k"][u], n_vis=int(nv[u, t]))
+            v = int(nv[u, t])
+            assert np.all(np.isneginf(got[u, t, v:]))
+            # fp32 accumulation bound: a few ulps of the absolute-value sum of all terms
+            bound = (x["idx_w"][u, t].astype(np.float64)[:, None] *
+                     (np.abs(bf16_f64(x["idx_q"][u, t])) @ kabs.T)).sum(0)[:v]
+            err = np.abs(got[u, t, :v].astype(np.float64) - ref[:v])
+            assert np.all(err <= 2e-6 * bound + 1e-30), (u, t, float((err / np.maximum(bound, 1e-30)).max()))
+
+
+# ------------------------------------------------------------------ top-k
+
+def _scores(pattern, n, rng):
+    if pattern == "normal":
+        return rng.standard_normal(n).astype(np.float32) * np.float32(50.0)
+    if pattern == "ties":
+        return rng.integers(0, 40, n).astype(np.float32)
+    if pattern == "equal":
+        return np.full(n, 3.25, np.float32)
+    if pattern == "zeros":   # +0 and -0 are equal floats
+        s = np.zeros(n, np.float32)
+        s[rng.random(n) < 0.5] = -0.0
+        s[rng.random(n) < 0.01] = 1.0
+        return s
+    if pattern == "heavy":
+        s = np.abs(rng.standard_normal(n)).astype(np.float32) * np.float32(100.0) + np.float32(10.0)
+        s[rng.choice(n, max(1, n // 100), replace=False)] *= np.float32(4.0)
+        return s
+    raise ValueError(pattern)
+
+
+TOPK_CASES = [
+    (1, 1, 1, "normal"), (2, 63, 64, "normal"), (1, 64, 64, "ties"), (3, 511, 512, "normal"),
+    (1, 512, 512, "equal"), (2, 513, 512, "ties"), (2, 4095, 512, "zeros"), (2, 16384, 512, "heavy"),
+    (2, 16384, 2048, "ties"), (2, 16385, 512, "normal"), (2, 40961, 1024, "heavy"), (1, 65537, 512, "equal"),
+    (2, 65537, 1024, "ties"), (1, 262144, 512, "normal"), (1, 100000, 2048, "zeros"), (3, 20000, 7, "normal"),
+]
+
+
+@pytest.mark.parametrize("Q,N,K,pattern", TOPK_CASES, ids=lambda v: str(v))
+def test_topk_bit_exact_on_identical_scores(Q, N, K, pattern):
+    rng = np.random.default_rng(N * 31 + K)
+    s = np.stack([_scores(pattern, N, rng) for _ in range(Q)]).reshape(Q, 1, N)
+    nv = rng.integers(0, N + 1, Q).astype(np.int32)
+    nv[0] = N
+    if Q > 1:
+        nv[1] = min(N, max(0, K - 3))
+    sd = torch.from_numpy(s).cuda()
+    out = torch.full((Q, 1, K), -7, dtype=torch.int32, device="cuda")
+    ops.topk_select(sd, K, n_vis=torch.from_numpy(nv.reshape(Q, 1)).cuda(), out=out)
+    got = out.cpu().numpy()
+    for i in range(Q):
+        ref = orc.topk(s[i, 0].astype(np.float64), K, n_vis=int(nv[i]))
+        n_sel = min(K, int(nv[i]))
+        assert np.array_equal(got[i, 0, :n_sel], np.sort(ref[:n_sel])), (i, int(nv[i]))
+        assert np.all(got[i, 0, n_sel:] == -1)
+
+
+# -------------------------------------------------------------- attention
+
+def _mqa_case(H, q_dtype, W, N, K, seed, U=2, T=2):
+    w = gen.Workload("mqa", 102, U=U, T=T, N=N, H=H, K=K, W=W, q_dtype=q_dtype, heavy_frac=0.01,
+                     pos_base=12345)
+    return w, gen.make_config(w, seed=seed)
+
+
+def _oracle_out(w, x, u, t, idx):
+    q = x["q"][u, t]
+    q64 = bf16_f64(q) if q.dtype == np.uint16 else q.astype(np.float64)
+    qr = orc.rope_q(q64, int(x["pos"][u, t]))
+    raw = x["raw"][u, t:t + w.W] if w.W else np.zeros((0, 512), np.uint16)
+    return orc.sparse_mqa(qr, raw, x["comp"][u], idx, w.scale)
+
+
+@pytest.mark.parametrize("H,qd,W,K", [(64, "f32", 128, 512), (64, "bf16", 128, 512), (128, "f32", 128, 1024),
+                                      (16, "f32", 32, 40), (32, "bf16", 0, 96)])
+def test_mqa_matches_oracle_on_given_sets(H, qd, W, K):
+    N = 3000
+    w, x = _mqa_case(H, qd, W, N, K, seed=3)
+    rng = np.random.default_rng(9)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(w.T)]) for _ in range(w.U)])
+    idx = idx.astype(np.int32)
+    # holes, a duplicate and out-of-range entries (treated as -1)
+    idx[0, 0, 3] = -1
+    idx[0, 0, 5] = idx[0, 0, 6]
+    idx[1, 1, -1] = N + 5
+    idx[1, 0, :K // 2] = -1
+    d = upload(x)
+    out = torch.full((w.U, w.T, H, 512), float("nan"), device="cuda")
+    ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], torch.from_numpy(idx).cuda(), w.scale, W=W, out=out)
+    got = out.cpu().numpy()
+    for u in range(w.U):
+        for t in range(w.T):
+            ix = idx[u, t].copy()
+            ix[(ix < 0) | (ix >= N)] = -1
+            ref = _oracle_out(w, x, u, t, ix)
+            e = normwise_err(got[u, t], ref)
+            assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, e)
+
+
+def test_mqa_empty_union_is_zero():
+    w, x = _mqa_case(16, "f32", 0, 100, 64, seed=4, U=1, T=1)
+    d = upload(x)
+    idx = torch.full((1, 1, 64), -1, dtype=torch.int32, device="cuda")
+    out = torch.full((1, 1, 16, 512), float("nan"), device="cuda")
+    ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], idx, w.scale, W=0, out=out)
+    assert torch.count_nonzero(out).item() == 0
+
+
+# -------------------------------------------------------------- end to end
+
+def _run_step(w, d, nv=True):
+    step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W)
+    step.scores.fill_(float("nan"))
+    step.idx.fill_(-7)
+    step.out.fill_(float("nan"))
+    step(d, n_vis=d["n_vis"] if nv else None, scale=w.scale, theta=w.theta)
+    torch.cuda.synchronize()
+    return step
+
+
+def _check_e2e(w, x, step, sel, nthreads=8):
+    ref = orc.step(w, x, sel=sel, nthreads=nthreads)
+    scores = step.scores.cpu().numpy().reshape(w.U * w.T, w.N)
+    idx = step.idx.cpu().numpy().reshape(w.U * w.T, w.K)
+    out = step.out.cpu().numpy().reshape(w.U * w.T, w.H, 512)
+    assert not np.isnan(out).any() and not np.isnan(scores).any() and (idx != -7).all()
+    compared, worst = 0, 0.0
+    for i, ut in enumerate(sel):
+        nv = int(x["n_vis"].reshape(-1)[ut])
+        r = ref["scores"][i]
+        vis = r[:nv]
+        assert np.all(np.isneginf(scores[ut, nv:]))
+        if nv:
+            den = np.maximum(np.abs(vis), 1e-6 * np.abs(vis).max() + 1e-30)
+            rel = np.abs(scores[ut, :nv].astype(np.float64) - vis) / den
+            assert rel.max() <= 1e-5, (ut, float(rel.max()))
+        ok, ndiff = tie_band_ok(idx[ut], ref["idx"][i], r)
+        assert ok, (ut, ndiff)
+        if ndiff == 0:
+            e = normwise_err(out[ut], ref["out"][i])
+            assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (ut, e)
+            worst = max(worst, e)
+            compared += 1
+    assert compared >= max(1, len(sel) // 2)
+    return worst
+
+
+def test_e2e_c1_decode_1layer():
+    w = gen.CONFIGS["c1"]
+    x = gen.make_config(w)
+    step = _run_step(w, upload(x))
+    _check_e2e(w, x, step, sel=[0])
+
+
+def test_e2e_c2_decode_43layers_full_size_sampled():
+    w = gen.CONFIGS["c2"]
+    x = gen.make_config(w)
+    d = upload(x)
+    step = _run_step(w, d)
+    _check_e2e(w, x, step, sel=[0, 21, 42])
+    # repeat-run determinism (bitwise)
+    s1, i1, o1 = step.scores.clone(), step.idx.clone(), step.out.clone()
+    step(d, n_vis=d["n_vis"], scale=w.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(step.scores, s1) and torch.equal(step.idx, i1) and torch.equal(step.out, o1)
+
+
+def test_e2e_c3_prefill_full_size_sampled():
+    w = gen.CONFIGS["c3"]
+    x = gen.make_config(w)
+    step = _run_step(w, upload(x))
+    _check_e2e(w, x, step, sel=[0, 1, 77, 1023, 1500, 2047])
+
+
+def test_e2e_c4_long_context_full_size_sampled():
+    w = gen.CONFIGS["c4"]
+    x = gen.make_config(w)
+    step = _run_step(w, upload(x), nv=False)
+    _check_e2e(w, x, step, sel=[0, 7])
+
+
+def test_e2e_c5_pro_full_size_sampled():
+    w = gen.CONFIGS["c5"]
+    x = gen.make_config(w)
+    step = _run_step(w, upload(x), nv=False)
+    _check_e2e(w, x, step, sel=[1, 3])
+
+
+def test_e2e_degenerate_all_scores_equal():
+    """idx_q = 0 makes every indexer score 0, so the top-k is rows 0..K-1 (ties to the lower index)."""
+    w = gen.Workload("deg", 103, U=2, T=1, N=20000, K=512)
+    x = gen.make_config(w)
+    x["idx_q"][:] = 0
+    step = _run_step(w, upload(x), nv=False)
+    idx = step.idx.cpu().numpy()
+    assert np.array_equal(idx[:, 0], np.broadcast_to(np.arange(512, dtype=np.int32), (2, 512)))
+    _check_e2e(w, x, step, sel=[0, 1])
+
+
+def test_e2e_ragged_prefill_small():
+    """Several queries per unit, ragged visibility (0 .. N), K above some n_vis."""
+    w = gen.Workload("rag", 104, U=2, T=5, N=777, K=512, q_dtype="bf16", vis_base=0, pos_base=100)
+    x = gen.make_config(w)
+    x["n_vis"] = np.array([[0, 1, 300, 512, 777], [777, 600, 513, 2, 40]], dtype=np.int32)
+    step = _run_step(w, upload(x))
+    _check_e2e(w, x, step, sel=list(range(10)))
