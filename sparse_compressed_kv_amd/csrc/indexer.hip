@@ -7,11 +7,11 @@
 // and the weighted head sum):
 //     s[j] = sum_h w[h] * max(0, <qI[h], kI[j]>)
 //
-// Design (decode and prefill alike): one query per workgroup row-chunk; the
-// query's 64x128 bf16 block sits in VGPRs as the MFMA A operand (64 VGPRs),
-// key rows stream from HBM straight into B-operand registers.  Each wave
-// takes 64 consecutive rows (16 KiB) per iteration: four 16-row blocks, each
-// row read as 4 x 64-byte contiguous segments.  Per 16-row block:
+// Design (decode and prefill alike): one query per workgroup and 1024-row
+// chunk; the query's 64x128 bf16 block sits in VGPRs as the MFMA A operand
+// (64 VGPRs), key rows stream from HBM straight into B-operand registers.
+// Each wave takes 32 consecutive rows (8 KiB) per iteration: two 16-row
+// blocks, each row read as 4 x 64-byte contiguous segments.  Per 16-row block:
 // 4 head tiles x 4 k-steps = 16 v_mfma_f32_16x16x32_bf16.  The D layout puts
 // 4 heads of one row in each lane, so the fp32 ReLU + weighted head sum is 16
 // in-lane FMAs plus two cross-lane adds.  The op is HBM-bound (64 flop/byte).
@@ -26,8 +26,9 @@ constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
-constexpr int kBlocksPerIter = 4;                              // 16-row blocks per wave iteration
-constexpr int kRowsPerIter = 16 * kBlocksPerIter * kWaves;     // 256 rows per workgroup iteration
+constexpr int kBlocksPerIter = 2;                              // 16-row blocks per wave iteration
+constexpr int kRowsPerIter = 16 * kBlocksPerIter * kWaves;     // 128 rows per workgroup iteration
+constexpr int64_t kRowsPerWg = 1024;                          // rows per workgroup (256 KiB of keys)
 constexpr int kChunksPerRow = kDim * 2 / 16;                   // 16-byte chunks per key row (16)
 
 __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
@@ -53,16 +54,21 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     const int64_t rv1 = r1 < nv ? r1 : nv;   // visible rows [r0, rv1)
     if (r0 >= rv1) return;
 
-    // Indexer query -> LDS -> A fragments: aq[ht][s] = qI[16ht + c][32s + 8g .. +7].
+    // Indexer query -> LDS, 16-byte chunk k of head h stored at h*16 + (k ^ (h & 15)) so that the
+    // 16 lanes reading 16 heads at one k hit distinct banks; then A fragments
+    // aq[ht][s] = qI[16ht + c][32s + 8g .. +7].
     __shared__ u32x4 sq[kHeads * kDim / 8];
     const u32x4 *gq = reinterpret_cast<const u32x4 *>(qI + q * (int64_t)(kHeads * kDim));
-    for (int i = threadIdx.x; i < kHeads * kDim / 8; i += kThreads) sq[i] = gq[i];
+    for (int i = threadIdx.x; i < kHeads * kDim / 8; i += kThreads) {
+        const int h = i / kChunksPerRow, k = i % kChunksPerRow;
+        sq[h * kChunksPerRow + (k ^ (h & 15))] = gq[i];
+    }
     __syncthreads();
     bf16x8 aq[4][4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + 4 * s + g]);
+        for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + ((4 * s + g) ^ c)]);
 
     // Head weights of the 16 D rows this lane holds: heads 16ht + 4g + r.
     float wh[4][4];
@@ -76,18 +82,14 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 
     for (int64_t base = r0 + 16 * kBlocksPerIter * wave; base < rv1; base += kRowsPerIter) {
         // Issue all loads of this iteration first: B fragment (k-step s) of row base+16bi+c
-        // is the 16-byte chunk 4s+g of that row.
+        // is the 16-byte chunk 4s+g of that row (16 rows x 64 contiguous bytes per instruction).
         u32x4 kb[kBlocksPerIter][4];
 #pragma unroll
         for (int bi = 0; bi < kBlocksPerIter; ++bi) {
             const int64_t row = base + 16 * bi + c;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                if (row < rv1)
-                    kb[bi][s] = __builtin_nontemporal_load(gk + row * kChunksPerRow + 4 * s + g);
-                else
-                    kb[bi][s] = u32x4{0u, 0u, 0u, 0u};
-            }
+            for (int s = 0; s < 4; ++s)
+                kb[bi][s] = row < rv1 ? gk[row * kChunksPerRow + 4 * s + g] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
         for (int bi = 0; bi < kBlocksPerIter; ++bi) {
@@ -117,11 +119,9 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
                           hipStream_t stream)
 {
     const int64_t Q = (int64_t)U * T;
-    // Aim for >= ~1024 workgroups over the 256 CUs, in multiples of one workgroup iteration.
-    const int64_t total_rows = Q * N;
-    int64_t rows = (total_rows / 1024 + kRowsPerIter - 1) / kRowsPerIter * kRowsPerIter;
-    if (rows < kRowsPerIter) rows = kRowsPerIter;
-    if (rows > 16 * kRowsPerIter) rows = 16 * kRowsPerIter;
+    // 1024-row chunks (256 KiB of keys per workgroup): fastest on MI355X among 256..8192-row chunks,
+    // and faster than persistent or prefetch-ring variants of the same loop.
+    const int64_t rows = kRowsPerWg;
     const int64_t per_q = (N + rows - 1) / rows;
     const int64_t blocks = per_q * Q;
     hipLaunchKernelGGL(indexer_score_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,

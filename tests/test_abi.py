@@ -96,8 +96,10 @@ def test_rope_validation(L):
 
 
 def test_workspace_bytes(L):
-    assert ops.workspace_bytes(0, 43, 1, 16384, 512) == 0            # LDS path
-    assert ops.workspace_bytes(0, 8, 1, 262144, 512) >= 8 * 262144 * 8
+    assert ops.workspace_bytes(0, 43, 1, 8192, 512) == 0             # one workgroup per query
+    assert ops.workspace_bytes(0, 2048, 1, 16384, 512) == 0          # many queries: still direct
+    assert ops.workspace_bytes(0, 43, 1, 16384, 512) > 0             # chunked: candidate lists
+    assert ops.workspace_bytes(0, 8, 1, 262144, 512) >= 2 * 8 * 16 * 512 * 8
     assert ops.workspace_bytes(2, 1, 1, 10, 10) == 0
     assert ops.workspace_bytes(1, 1, 2048, 8192, 512, 64, 128) == 0   # prefill: no split
     assert ops.workspace_bytes(1, 1, 1, 10, 512, 64, 100) == 0        # invalid W
