@@ -47,7 +47,7 @@ constexpr int kTile = 32;                     // union rows per tile
 constexpr int kRowStride = 1040;              // LDS bytes per row (1024 + 16)
 constexpr int kTileBytes = kTile * kRowStride;
 constexpr int kXchBytes = 4 * 2 * kWave * 16; // partial logits of 4 waves
-constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes;
+constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes;   // + 4 bytes per union row of the chunk (row table)
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[16], l[16], O[16][512]
 constexpr int kXcd = 8;
 
@@ -72,10 +72,15 @@ struct MqaArgs {
 };
 
 // Rotate one adjacent pair of the query tail by pos * inv_freq (fp64), round once to f32.
+// The angle (up to ~1e6 rad) is first reduced by a two-part 2*pi in fp64, so that sincos runs
+// on |x| <= pi.
 __device__ __forceinline__ void rope_pair(double inv_freq, int64_t pos, float &a, float &b) {
     const double ang = (double)pos * inv_freq;
+    const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
+    double red = fma(-k, 6.283185307179586, ang);              // 2 pi, high part
+    red = fma(-k, 2.4492935982947064e-16, red);                // 2 pi, low part
     double sn, cs;
-    sincos(ang, &sn, &cs);
+    sincos(red, &sn, &cs);
     const double x = (double)a, y = (double)b;
     a = (float)(x * cs - y * sn);
     b = (float)(x * sn + y * cs);
@@ -117,6 +122,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *tiles = smem;
     f32x4 *xch = reinterpret_cast<f32x4 *>(smem + 2 * kTileBytes);
+    int32_t *s_row = reinterpret_cast<int32_t *>(smem + kLdsBytes);   // per union row: comp row, -2 raw, -1 none
 
     // XCD-aware block order: all head groups of one (query, chunk) share an XCD.
     const int lin = blockIdx.x;
@@ -146,13 +152,27 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const uint16_t *comp_u = a.comp + u * a.N * kD;
     const int32_t *idx_q = a.idx + q * (int64_t)a.K;
 
+    // Row table of this chunk's union rows, read once from idx.
+    const int rho0 = tile0 * kTile;
+    const int n_rows = (tile1 - tile0) * kTile;
+    for (int r = tid; r < n_rows; r += kThreads) {
+        const int rho = rho0 + r;
+        int32_t v = -1;
+        if (rho < a.W) {
+            v = -2;
+        } else if (rho - a.W < a.K) {
+            const int32_t j = idx_q[rho - a.W];
+            if (j >= 0 && (int64_t)j < a.N) v = j;
+        }
+        s_row[r] = v;
+    }
+    __syncthreads();
+
     auto row_ptr = [&](int rho) -> const uint16_t * {
-        if (rho < a.W) return raw_q + (int64_t)rho * kD;
-        const int k = rho - a.W;
-        if (k >= a.K) return nullptr;
-        const int32_t j = idx_q[k];
-        if (j < 0 || (int64_t)j >= a.N) return nullptr;
-        return comp_u + (int64_t)j * kD;
+        const int32_t v = s_row[rho - rho0];
+        if (v == -2) return raw_q + (int64_t)rho * kD;
+        if (v < 0) return nullptr;
+        return comp_u + (int64_t)v * kD;
     };
 
     // Wave w stages rows w + 4i (i = 0..7) of a tile; lane = 16-byte chunk of the row.
@@ -223,7 +243,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int rho = tt * kTile + 16 * rt + 4 * g + r;
-                const bool valid = row_ptr(rho) != nullptr;
+                const bool valid = s_row[rho - rho0] != -1;
                 const float lg = a.scale * (((s0[r] + s1[r]) + s2[r]) + s3[r]);
                 p[rt][r] = valid ? lg : -INFINITY;
                 tmax = fmaxf(tmax, p[rt][r]);
@@ -384,14 +404,15 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
                       const int32_t *idx, float scale, float *out, void *workspace,
                       hipStream_t stream)
 {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_mqa_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     const MqaPlan p = plan_mqa(U, T, H, W, K);
+    const int lds = kLdsBytes + 4 * kTile * p.tiles_per_chunk;
+    static int attr_bytes = 0;
+    if (lds > attr_bytes) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_mqa_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+        if (e != hipSuccess) return e;
+        attr_bytes = lds;
+    }
     MqaArgs a;
     a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_tiles = p.n_tiles;
     a.tiles_per_chunk = p.tiles_per_chunk; a.n_chunks = p.n_chunks;
@@ -401,7 +422,7 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
     a.scale = scale; a.out = out; a.part = static_cast<float *>(workspace);
     fill_inv_freq(theta, a.inv_freq);
     const int64_t blocks = (a.n_items + kXcd - 1) / kXcd * kXcd * p.n_hg;
-    hipLaunchKernelGGL(sparse_mqa_kernel, dim3((unsigned)blocks), dim3(kThreads), kLdsBytes, stream, a);
+    hipLaunchKernelGGL(sparse_mqa_kernel, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1) return e;
     hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg)), dim3(256), 0, stream,
