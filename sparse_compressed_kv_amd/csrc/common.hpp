@@ -7,6 +7,11 @@
 namespace ds4a {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -21,8 +26,25 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, f32x4 
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Same shape with f16 operands (v_mfma_f32_16x16x32_f16).
+__device__ __forceinline__ f32x4 mfma16h(const f16x8 &a, const f16x8 &b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) {
     return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ f16x8 as_f16x8(const u32x4 &v) {
+    return __builtin_bit_cast(f16x8, v);
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, source lane j supplies 4 consecutive
+// 16-bit values of block row j/4 (columns 4*(j%4)..+3) of a 4 x 16 block; lane i receives
+// column i (rows 0..3).  p must point into LDS and be 8-byte aligned.
+__device__ __forceinline__ s16x4 lds_read_tr16(const unsigned char *p) {
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p));
 }
 
 // Round-to-nearest-even fp32 -> bf16 bit pattern (finite inputs).
@@ -42,19 +64,28 @@ __device__ __forceinline__ void split_hi_lo(float x, uint32_t &hi, uint32_t &lo)
     lo = f32_to_bf16_bits(x - bf16_bits_to_f32(hi));
 }
 
-// Pack 8 floats into bf16x8 hi and lo halves.
+// 8 floats -> bf16 hi = rne(v) and lo = rne(v - hi) (v_cvt_pk_bf16_f32, round-to-nearest-even).
 __device__ __forceinline__ void pack_hi_lo8(const float (&v)[8], bf16x8 &hi, bf16x8 &lo) {
-    u32x4 h, l;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        uint32_t h0, l0, h1, l1;
-        split_hi_lo(v[2 * i], h0, l0);
-        split_hi_lo(v[2 * i + 1], h1, l1);
-        h[i] = h0 | (h1 << 16);
-        l[i] = l0 | (l1 << 16);
+        const f32x2 x = {v[2 * i], v[2 * i + 1]};
+        const bf16x2 h = __builtin_convertvector(x, bf16x2);
+        const f32x2 hf = __builtin_convertvector(h, f32x2);
+        const bf16x2 l = __builtin_convertvector(x - hf, bf16x2);
+        hi[2 * i] = h[0];
+        hi[2 * i + 1] = h[1];
+        lo[2 * i] = l[0];
+        lo[2 * i + 1] = l[1];
     }
-    hi = as_bf16x8(h);
-    lo = as_bf16x8(l);
+}
+
+// 8 floats -> f16 hi = rne(v) and lo = rne(v - hi).
+__device__ __forceinline__ void pack_hi_lo8_f16(const float (&v)[8], f16x8 &hi, f16x8 &lo) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        hi[i] = (_Float16)v[i];
+        lo[i] = (_Float16)(v[i] - (float)hi[i]);
+    }
 }
 
 // f16 bit pattern -> float (exact).

@@ -14,17 +14,21 @@
 //
 // Design.  A workgroup (4 waves) owns 16 heads of one query and a contiguous
 // chunk of 32-row union tiles.  Wave w owns dims [128w, 128w+128):
-//   QK  : partial logits L^T[32 rows x 16 heads] over its 128 dims with
-//         v_mfma_f32_16x16x32_bf16 (A = rows from LDS, B = rotated query in
-//         VGPRs); the four partials are summed through LDS in a fixed order;
+//   QK  : partial logits L^T[32 rows x 16 heads] over its 128 dims with 16x16x32
+//         MFMA tiles (A = rows from LDS, B = rotated query in VGPRs); the four
+//         partials are summed through LDS in a fixed order;
 //   softmax: online (running max / sum per head), fp32;
 //   PV  : O^T[128 dims x 16 heads] += V^T * P^T; P^T is already in the
-//         B-operand layout of the QK result, V^T fragments are gathered from
-//         the same LDS tile (swizzled so both access patterns avoid bank
-//         conflicts).
-// Operands that are not bf16 are split into hi + lo bf16 pairs: the fp32 (or
-// rotated) query, the f16 raw rows and the probabilities; compressed rows are
-// exact bf16.  Tiles are double-buffered: the next tile's rows are fetched
+//         B-operand layout of the QK result; V^T fragments come from the same
+//         LDS tile through ds_read_b64_tr_b16 (transposing 4 x 16 blocks).
+// Each row format gets the MFMA of its own type, so rows are never converted:
+// compressed rows are bf16 (v_mfma_f32_16x16x32_bf16), raw-window rows are f16
+// (v_mfma_f32_16x16x32_f16).  What is not already in that type is carried as
+// hi + lo pairs: the fp32 query (a bf16 query only in its rotated tail) and
+// the probabilities.  LDS rows are 1056 bytes apart and their 16-byte
+// chunks are XOR-swizzled by row bit 2, which keeps both the row reads of QK
+// and the transposed reads of PV free of bank conflicts.  Tiles are
+// double-buffered: the next tile's rows are fetched
 // into VGPRs (1 KiB per wave instruction, row-contiguous) while the current
 // tile computes.  When the union is split over several workgroups, each
 // writes (max, sum, unnormalised O) and a merge kernel combines them by
@@ -44,16 +48,21 @@ constexpr int kHG = 16;                       // heads per workgroup
 constexpr int kD = 512;
 constexpr int kRot = 64;
 constexpr int kTile = 32;                     // union rows per tile
-constexpr int kRowStride = 1040;              // LDS bytes per row (1024 + 16)
+constexpr int kRowStride = 1056;              // LDS bytes per row (1024 + 32)
 constexpr int kTileBytes = kTile * kRowStride;
 constexpr int kXchBytes = 4 * 2 * kWave * 16; // partial logits of 4 waves
 constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes;   // + 4 bytes per union row of the chunk (row table)
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[16], l[16], O[16][512]
 constexpr int kXcd = 8;
 
-// Byte offset of 16-byte chunk c (0..63) of tile row r, XOR-swizzled by row bit 3.
+// Byte offset of 16-byte chunk c (0..63) of tile row r, XOR-swizzled by row bit 2.
 __device__ __forceinline__ int chunk_off(int r, int c) {
-    return r * kRowStride + ((c ^ (((r >> 3) & 1) << 1)) << 4);
+    return r * kRowStride + ((c ^ ((r >> 2) & 1)) << 4);
+}
+
+// Byte offset of element d (0..511) of tile row r.
+__device__ __forceinline__ int elem_off(int r, int d) {
+    return chunk_off(r, d >> 3) + ((d & 7) << 1);
 }
 
 struct MqaArgs {
@@ -109,14 +118,6 @@ __device__ __forceinline__ void load_q8(const MqaArgs &a, int64_t q, int h, int 
     }
 }
 
-__device__ __forceinline__ void f16x8_to_f32(const u32x4 &x, float (&v)[8]) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v[2 * i] = f16_bits_to_f32(x[i] & 0xFFFFu);
-        v[2 * i + 1] = f16_bits_to_f32(x[i] >> 16);
-    }
-}
-
 __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -138,15 +139,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const int h0 = hg * kHG;
     const int tile0 = chunk * a.tiles_per_chunk;
     const int tile1 = tile0 + a.tiles_per_chunk < a.n_tiles ? tile0 + a.tiles_per_chunk : a.n_tiles;
-
-    // Rotated query as B fragments: k-step s <-> dims 128*wave + 32s + 8g + (0..7) of head h0 + c.
-    bf16x8 qhi[4], qlo[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        float v[8];
-        load_q8(a, q, h0 + c, 128 * wave + 32 * s + 8 * g, v);
-        pack_hi_lo8(v, qhi[s], qlo[s]);
-    }
 
     const uint16_t *raw_q = a.raw + (u * (int64_t)(a.T + a.W - 1) + t) * kD;
     const uint16_t *comp_u = a.comp + u * a.N * kD;
@@ -189,16 +181,28 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 #pragma unroll
         for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(base + chunk_off(wave + 4 * i, lane)) = stage[i];
     };
+    if (tile0 < tile1) load_tile(tile0);
+
+    // Rotated query as B fragments while the first tile is in flight: k-step s <-> dims
+    // 128*wave + 32s + 8g + (0..7) of head h0 + c; bf16 pair for compressed rows, f16 pair for
+    // raw rows.  The lo halves are zero (and skipped) for a bf16 query outside the rotated tail.
+    bf16x8 qb_hi[4], qb_lo[4];
+    f16x8 qh_hi[4], qh_lo[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        float v[8];
+        load_q8(a, q, h0 + c, 128 * wave + 32 * s + 8 * g, v);
+        pack_hi_lo8(v, qb_hi[s], qb_lo[s]);
+        pack_hi_lo8_f16(v, qh_hi[s], qh_lo[s]);
+    }
+    const bool lo_tail = !a.q_bf16 || wave == 3;      // dims 448..511 belong to wave 3 (s = 2, 3)
 
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[8];
 #pragma unroll
     for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (tile0 < tile1) {
-        load_tile(tile0);
-        store_tile(0);
-    }
+    if (tile0 < tile1) store_tile(0);
     __syncthreads();
 
     for (int tt = tile0; tt < tile1; ++tt) {
@@ -209,27 +213,22 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         const bool is_raw = tt * kTile < a.W;
 
         // ---- QK: partial logits over this wave's dims
-        f32x4 acc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const u32x4 x = *reinterpret_cast<const u32x4 *>(tb + chunk_off(16 * rt + c, 16 * wave + 4 * s + g));
+                const bool lo = !a.q_bf16 || (lo_tail && s >= 2);
                 if (!is_raw) {
-                    acc[rt] = mfma16(as_bf16x8(x), qhi[s], acc[rt]);
-                    acc[rt] = mfma16(as_bf16x8(x), qlo[s], acc[rt]);
+                    acc = mfma16(as_bf16x8(x), qb_hi[s], acc);
+                    if (lo) acc = mfma16(as_bf16x8(x), qb_lo[s], acc);
                 } else {
-                    float v[8];
-                    f16x8_to_f32(x, v);
-                    bf16x8 ahi, alo;
-                    pack_hi_lo8(v, ahi, alo);
-                    acc[rt] = mfma16(ahi, qhi[s], acc[rt]);
-                    acc[rt] = mfma16(ahi, qlo[s], acc[rt]);
-                    acc[rt] = mfma16(alo, qhi[s], acc[rt]);
+                    acc = mfma16h(as_f16x8(x), qh_hi[s], acc);
+                    if (lo) acc = mfma16h(as_f16x8(x), qh_lo[s], acc);
                 }
             }
-            xch[(wave * 2 + rt) * kWave + lane] = acc[rt];
+            xch[(wave * 2 + rt) * kWave + lane] = acc;
         }
         __syncthreads();
 
@@ -273,34 +272,33 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 #pragma unroll
         for (int b = 0; b < 8; ++b) o[b] *= alpha;
 
-        // ---- PV: P^T fragment, element e <-> row e<4 ? 4g+e : 16+4g+(e-4)
+        // ---- PV: P^T fragment, element e <-> row e<4 ? 4g+e : 16+4g+(e-4); V^T fragment by two
+        // transposed reads: source lane (g, c) points at row 4g + c/4 (+16), dims d0 + 4(c%4).
         const float pv[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
-        bf16x8 phi, plo;
-        pack_hi_lo8(pv, phi, plo);
+        const int r1 = 4 * g + (c >> 2);
+        if (!is_raw) {
+            bf16x8 phi, plo;
+            pack_hi_lo8(pv, phi, plo);
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const int d = 128 * wave + 16 * b + c;
-            const int dch = d >> 3, dby = (d & 7) << 1;
-            uint32_t e16[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int r = e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4);
-                e16[e] = *reinterpret_cast<const uint16_t *>(tb + chunk_off(r, dch) + dby);
+            for (int b = 0; b < 8; ++b) {
+                const int d = 128 * wave + 16 * b + 4 * (c & 3);
+                const s16x4 v1 = lds_read_tr16(tb + elem_off(r1, d));
+                const s16x4 v2 = lds_read_tr16(tb + elem_off(r1 + 16, d));
+                const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[b] = mfma16(av, phi, o[b]);
+                o[b] = mfma16(av, plo, o[b]);
             }
-            if (!is_raw) {
-                const u32x4 x = {e16[0] | (e16[1] << 16), e16[2] | (e16[3] << 16), e16[4] | (e16[5] << 16),
-                                 e16[6] | (e16[7] << 16)};
-                o[b] = mfma16(as_bf16x8(x), phi, o[b]);
-                o[b] = mfma16(as_bf16x8(x), plo, o[b]);
-            } else {
-                float v[8];
+        } else {
+            f16x8 phi, plo;
+            pack_hi_lo8_f16(pv, phi, plo);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) v[e] = f16_bits_to_f32(e16[e]);
-                bf16x8 ahi, alo;
-                pack_hi_lo8(v, ahi, alo);
-                o[b] = mfma16(ahi, phi, o[b]);
-                o[b] = mfma16(ahi, plo, o[b]);
-                o[b] = mfma16(alo, phi, o[b]);
+            for (int b = 0; b < 8; ++b) {
+                const int d = 128 * wave + 16 * b + 4 * (c & 3);
+                const s16x4 v1 = lds_read_tr16(tb + elem_off(r1, d));
+                const s16x4 v2 = lds_read_tr16(tb + elem_off(r1 + 16, d));
+                const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+                o[b] = mfma16h(av, phi, o[b]);
+                o[b] = mfma16h(av, plo, o[b]);
             }
         }
         if (has_next) store_tile(buf ^ 1);

@@ -7,8 +7,8 @@
 // the lower row index; the chosen rows are returned in ascending order.
 //
 // Core: block_select, one workgroup radix-selecting `need` of n keys held in
-// LDS (padded one word per 32 so that both the strided sweeps and the
-// per-thread-contiguous sweep are free of bank conflicts):
+// registers (each thread a contiguous run of up to 32 keys, all loaded before
+// first use); LDS holds only the 256-bin histogram and scan scratch:
 //   1. min/max of the keys; the bits above their highest differing bit are
 //      common to all keys and are skipped;
 //   2. 8-bit digit passes: LDS histogram of the keys that match the prefix so
@@ -40,9 +40,6 @@ constexpr int kMergeMax = 12288;              // candidates per workgroup (expli
 constexpr int kLevelChunk = 8192;             // candidates per workgroup in intermediate levels
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4x
-
-__device__ __forceinline__ int pad(int j) { return j + (j >> 5); }
-__host__ __device__ constexpr int padded(int n) { return n + (n >> 5) + 1; }
 
 struct SelectShared {
     uint32_t hist[kBins];
@@ -111,21 +108,25 @@ __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
     __syncthreads();
 }
 
-// Selects the `need` largest of keys[pad(0..n)) (n <= 16384; ties to the lower position) and
-// writes their rows (ids[pad(j)] if ids, else row0 + j) in ascending position order to
-// out[0..need), then -1 up to K.  If out_keys, the selected keys go there too.  Every thread
-// of the workgroup calls it.
-__device__ void block_select(const uint32_t *keys, const int32_t *ids, int64_t row0, int n, int need, int K,
-                             int32_t *out, uint32_t *out_keys, SelectShared &sm)
+// Selects the `need` largest of the n keys held in registers (thread t holds positions
+// t*EPT .. t*EPT+EPT-1; ties go to the lower position) and writes their rows (id[i] if IDS, else
+// row0 + position) in ascending position order to out[0..need), then -1 up to K.  If out_keys,
+// the selected keys go there too.  Every thread of the workgroup calls it.
+template <int EPT, bool IDS>
+__device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int64_t row0, int n, int need,
+                             int K, int32_t *out, uint32_t *out_keys, SelectShared &sm)
 {
     const int lane = threadIdx.x & (kWave - 1);
+    const int j0 = threadIdx.x * EPT;
     uint32_t T = 0, ties = 0xFFFFFFFFu;       // take key > T, and the first `ties` keys == T
     if (need > 0 && need < n) {
         uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-        for (int j = threadIdx.x; j < n; j += kNT) {
-            const uint32_t k = keys[pad(j)];
-            kmin = k < kmin ? k : kmin;
-            kmax = k > kmax ? k : kmax;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            if (j0 + i < n) {
+                kmin = key[i] < kmin ? key[i] : kmin;
+                kmax = key[i] > kmax ? key[i] : kmax;
+            }
         }
         block_minmax(kmin, kmax, sm);
         int bit = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
@@ -139,10 +140,9 @@ __device__ void block_select(const uint32_t *keys, const int32_t *ids, int64_t r
             const uint32_t dmask = (1u << width) - 1u;
             for (int b = threadIdx.x; b < kBins; b += kNT) sm.hist[b] = 0;
             __syncthreads();
-            for (int j = threadIdx.x; j < n; j += kNT) {
-                const uint32_t k = keys[pad(j)];
-                if ((k & pmask) == prefix) atomicAdd(&sm.hist[(k >> shift) & dmask], 1u);
-            }
+#pragma unroll
+            for (int i = 0; i < EPT; ++i)
+                if (j0 + i < n && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> shift) & dmask], 1u);
             __syncthreads();
             if (threadIdx.x < kWave) {
                 // lane l owns bins 255-4l .. 252-4l, highest first
@@ -176,16 +176,15 @@ __device__ void block_select(const uint32_t *keys, const int32_t *ids, int64_t r
         ties = whole_bin ? 0xFFFFFFFFu : remaining;
     }
 
-    // Index-ordered collection: thread t owns positions [t*per, t*per + per).
-    const int per = (n + kNT - 1) / kNT;
-    const int j0 = threadIdx.x * per;
-    const int j1 = j0 + per < n ? j0 + per : n;
+    // Index-ordered collection over each thread's contiguous positions.
     uint32_t gt = 0, eq = 0;
     if (need > 0) {
-        for (int j = j0; j < j1; ++j) {
-            const uint32_t k = keys[pad(j)];
-            gt += k > T;
-            eq += k == T;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            if (j0 + i < n) {
+                gt += key[i] > T;
+                eq += key[i] == T;
+            }
         }
     }
     // gt and eq totals stay below 2^16 (n <= 16384), so one scan carries both.
@@ -193,17 +192,19 @@ __device__ void block_select(const uint32_t *keys, const int32_t *ids, int64_t r
     uint32_t tie_rank = packed & 0xFFFFu;
     uint32_t pos = (packed >> 16) + (tie_rank < ties ? tie_rank : ties);
     if (need > 0) {
-        for (int j = j0; j < j1; ++j) {
-            const uint32_t k = keys[pad(j)];
-            bool take = k > T;
-            if (k == T) {
-                take = tie_rank < ties;
-                ++tie_rank;
-            }
-            if (take && pos < (uint32_t)K) {
-                out[pos] = ids ? ids[pad(j)] : (int32_t)(row0 + j);
-                if (out_keys) out_keys[pos] = k;
-                ++pos;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            if (j0 + i < n) {
+                bool take = key[i] > T;
+                if (key[i] == T) {
+                    take = tie_rank < ties;
+                    ++tie_rank;
+                }
+                if (take && pos < (uint32_t)K) {
+                    out[pos] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
+                    if (out_keys) out_keys[pos] = key[i];
+                    ++pos;
+                }
             }
         }
     }
@@ -217,58 +218,70 @@ __device__ void block_select(const uint32_t *keys, const int32_t *ids, int64_t r
 
 // ---------------------------------------------------------------- kernels
 
-// One workgroup per (query, chunk of `chunk` rows).  Direct path: chunks == 1, out = idx.
-// Chunked path: out/out_keys = the chunk's K candidate slots.
+// One workgroup per (query, chunk of `chunk` <= EPT*kNT rows).  Direct path: chunks == 1,
+// out = idx.  Chunked path: out/out_keys = the chunk's K candidate slots.
+template <int EPT>
 __global__ __launch_bounds__(kNT) void topk_rows_kernel(int64_t N, int K, int chunk, int64_t chunks,
                                                         const float *__restrict__ scores,
                                                         const int32_t *__restrict__ n_vis,
                                                         int32_t *__restrict__ out, uint32_t *__restrict__ out_keys)
 {
-    extern __shared__ uint32_t keys[];
     __shared__ SelectShared sm;
     const int64_t q = blockIdx.x / chunks;
     const int64_t c = blockIdx.x % chunks;
     const int64_t nv = clamp_nvis(n_vis, q, N);
-    const int64_t j0 = c * chunk;
-    const int64_t rem = nv - j0;
+    const int64_t c0 = c * chunk;
+    const int64_t rem = nv - c0;
     const int n = rem <= 0 ? 0 : (rem < chunk ? (int)rem : chunk);
-    const float *s = scores + q * N + j0;
-    for (int j = threadIdx.x; j < n; j += kNT) keys[pad(j)] = float_key(s[j]);
-    __syncthreads();
+    const float *s = scores + q * N + c0;
+    const int j0 = threadIdx.x * EPT;
+    // All loads of the thread's contiguous run are issued before any is used.
+    float v[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = j0 + i < n ? s[j0 + i] : 0.f;
+    uint32_t key[EPT];
+    int32_t id[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        key[i] = float_key(v[i]);
+        id[i] = 0;
+    }
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + c) * K;
-    block_select(keys, nullptr, j0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
+    block_select<EPT, false>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
 }
 
-// One workgroup per (query, chunk of `chunk` candidates).  The candidates of query q are the
-// first cand_count(nv, K, lv) entries of in_keys/in_ids[q * in_stride ...].
+// One workgroup per (query, chunk of `chunk` <= EPT*kNT candidates).  The candidates of query q
+// are the first cand_count(nv, K, lv) entries of in_keys/in_ids[q * in_stride ...].
+template <int EPT>
 __global__ __launch_bounds__(kNT) void topk_cand_kernel(int64_t N, int K, Levels lv, int64_t in_stride, int chunk,
                                                         int64_t chunks, const uint32_t *__restrict__ in_keys,
                                                         const int32_t *__restrict__ in_ids,
                                                         const int32_t *__restrict__ n_vis,
                                                         int32_t *__restrict__ out, uint32_t *__restrict__ out_keys)
 {
-    extern __shared__ uint32_t sh[];
     __shared__ SelectShared sm;
-    uint32_t *keys = sh;
-    int32_t *ids = reinterpret_cast<int32_t *>(sh + padded(chunk));
     const int64_t q = blockIdx.x / chunks;
     const int64_t c = blockIdx.x % chunks;
     int64_t count = cand_count(clamp_nvis(n_vis, q, N), K, lv);
     if (count > in_stride) count = in_stride;
-    const int64_t j0 = c * chunk;
-    const int64_t rem = count - j0;
+    const int64_t c0 = c * chunk;
+    const int64_t rem = count - c0;
     const int n = rem <= 0 ? 0 : (rem < chunk ? (int)rem : chunk);
-    const uint32_t *ik = in_keys + q * in_stride + j0;
-    const int32_t *ii = in_ids + q * in_stride + j0;
-    for (int j = threadIdx.x; j < n; j += kNT) {
-        keys[pad(j)] = ik[j];
-        ids[pad(j)] = ii[j];
+    const uint32_t *ik = in_keys + q * in_stride + c0;
+    const int32_t *ii = in_ids + q * in_stride + c0;
+    const int j0 = threadIdx.x * EPT;
+    uint32_t key[EPT];
+    int32_t id[EPT];
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+        const bool in = j0 + i < n;
+        key[i] = in ? ik[j0 + i] : 0u;
+        id[i] = in ? ii[j0 + i] : -1;
     }
-    __syncthreads();
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + c) * K;
-    block_select(keys, ids, 0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
+    block_select<EPT, true>(key, id, 0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -293,22 +306,13 @@ size_t topk_workspace_bytes(int64_t Q, int64_t N, int K) {
 hipError_t launch_topk(int64_t Q, int64_t N, int K, const float *scores, const int32_t *n_vis,
                        int32_t *idx, void *workspace, hipStream_t stream)
 {
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_rows_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize,
-                                           (int)(sizeof(uint32_t) * padded(kDirectMax)));
-        if (e != hipSuccess) return e;
-        e = hipFuncSetAttribute(reinterpret_cast<const void *>(topk_cand_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize,
-                                (int)(2 * sizeof(uint32_t) * padded(kMergeMax)));
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     if (direct_path(Q, N)) {
-        const size_t lds = sizeof(uint32_t) * padded((int)N);
-        hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)Q), dim3(kNT), lds, stream, N, K, (int)N, (int64_t)1,
-                           scores, n_vis, idx, (uint32_t *)nullptr);
+        if (N <= 8192)
+            hipLaunchKernelGGL(topk_rows_kernel<16>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, (int)N,
+                               (int64_t)1, scores, n_vis, idx, (uint32_t *)nullptr);
+        else
+            hipLaunchKernelGGL(topk_rows_kernel<32>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, (int)N,
+                               (int64_t)1, scores, n_vis, idx, (uint32_t *)nullptr);
         return hipGetLastError();
     }
     const int ch = first_chunk(N, K);
@@ -320,26 +324,28 @@ hipError_t launch_topk(int64_t Q, int64_t N, int K, const float *scores, const i
     uint32_t *keys_b = reinterpret_cast<uint32_t *>(p + 2 * align256(per * 4));
     int32_t *ids_b = reinterpret_cast<int32_t *>(p + 3 * align256(per * 4));
 
-    hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)(Q * chunks)), dim3(kNT), sizeof(uint32_t) * padded(ch),
-                       stream, N, K, ch, chunks, scores, n_vis, ids_a, keys_a);
+    if (ch == 8192)
+        hipLaunchKernelGGL(topk_rows_kernel<16>, dim3((unsigned)(Q * chunks)), dim3(kNT), 0, stream, N, K, ch, chunks,
+                           scores, n_vis, ids_a, keys_a);
+    else
+        hipLaunchKernelGGL(topk_rows_kernel<32>, dim3((unsigned)(Q * chunks)), dim3(kNT), 0, stream, N, K, ch, chunks,
+                           scores, n_vis, ids_a, keys_a);
     Levels lv = {};
     lv.n = 1;
     lv.ch[0] = ch;
     int64_t stride = chunks * K;                 // candidate slots per query in the current list
     while (stride > kMergeMax && lv.n < kMaxLevels) {
         const int64_t chunks2 = (stride + kLevelChunk - 1) / kLevelChunk;
-        hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)(Q * chunks2)), dim3(kNT),
-                           2 * sizeof(uint32_t) * padded(kLevelChunk), stream, N, K, lv, stride, kLevelChunk,
-                           chunks2, keys_a, ids_a, n_vis, ids_b, keys_b);
+        hipLaunchKernelGGL(topk_cand_kernel<16>, dim3((unsigned)(Q * chunks2)), dim3(kNT), 0, stream, N, K, lv,
+                           stride, kLevelChunk, chunks2, keys_a, ids_a, n_vis, ids_b, keys_b);
         lv.ch[lv.n++] = kLevelChunk;
         stride = chunks2 * K;
         uint32_t *tk = keys_a; keys_a = keys_b; keys_b = tk;
         int32_t *ti = ids_a; ids_a = ids_b; ids_b = ti;
     }
     if (stride > kMergeMax) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(topk_cand_kernel, dim3((unsigned)Q), dim3(kNT), 2 * sizeof(uint32_t) * padded(kMergeMax),
-                       stream, N, K, lv, stride, kMergeMax, (int64_t)1, keys_a, ids_a, n_vis, idx,
-                       (uint32_t *)nullptr);
+    hipLaunchKernelGGL(topk_cand_kernel<24>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride, kMergeMax,
+                       (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
     return hipGetLastError();
 }
 
