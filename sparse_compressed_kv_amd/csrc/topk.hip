@@ -41,11 +41,15 @@ constexpr int kLevelChunk = 8192;             // candidates per workgroup in int
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4x
 
+constexpr int kMaxK = 2048;
+
 struct SelectShared {
     uint32_t hist[kBins];
     uint32_t wave_a[kNW];
     uint32_t wave_b[kNW];
     uint32_t res[4];
+    int32_t sel_id[kMaxK];      // the selected set, in row order, before the coalesced copy-out
+    uint32_t sel_key[kMaxK];
 };
 
 // Chunk sizes of the levels that produced a candidate list, first level on rows.
@@ -201,18 +205,19 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
                     ++tie_rank;
                 }
                 if (take && pos < (uint32_t)K) {
-                    out[pos] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
-                    if (out_keys) out_keys[pos] = key[i];
+                    sm.sel_id[pos] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
+                    sm.sel_key[pos] = key[i];
                     ++pos;
                 }
             }
         }
     }
     (void)lane;
+    __syncthreads();
     const int taken = need > 0 ? need : 0;
-    for (int i = taken + threadIdx.x; i < K; i += kNT) {
-        out[i] = -1;
-        if (out_keys) out_keys[i] = 0u;
+    for (int i = threadIdx.x; i < K; i += kNT) {
+        out[i] = i < taken ? sm.sel_id[i] : -1;
+        if (out_keys) out_keys[i] = i < taken ? sm.sel_key[i] : 0u;
     }
 }
 
