@@ -102,6 +102,61 @@ __device__ __forceinline__ uint32_t float_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- DPP (data-parallel primitives on VALU lanes, no LDS round trip)
+// dpp_ctrl codes: row_shr:n = 0x110 + n, row_ror:n = 0x120 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143.
+// Lanes whose DPP source does not exist read 0 (old = 0, bound_ctrl off).
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, ROW_MASK, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_incl_scan_dpp(uint32_t x) {
+    x += dpp_u32<0x111>(x);          // row_shr:1
+    x += dpp_u32<0x112>(x);          // row_shr:2
+    x += dpp_u32<0x114>(x);          // row_shr:4
+    x += dpp_u32<0x118>(x);          // row_shr:8   -> prefix within each row of 16
+    x += dpp_u32<0x142, 0xA>(x);     // row_bcast:15 into rows 1 and 3
+    x += dpp_u32<0x143, 0xC>(x);     // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
+// Sum over the 16 lanes of each row; every lane of the row receives it.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<0x128>(x);          // row_ror:8
+    x += dpp_f32<0x124>(x);          // row_ror:4
+    x += dpp_f32<0x122>(x);          // row_ror:2
+    x += dpp_f32<0x121>(x);          // row_ror:1
+    return x;
+}
+
+// Min and max over the 64 lanes of a wave (uniform result).
+__device__ __forceinline__ void wave_minmax_u32(uint32_t &mn, uint32_t &mx) {
+#define DS4A_ROW_ROR(n)                                                         \
+    {                                                                           \
+        const uint32_t a = (uint32_t)__builtin_amdgcn_update_dpp((int)mn, (int)mn, 0x120 + (n), 0xF, 0xF, false); \
+        const uint32_t b = (uint32_t)__builtin_amdgcn_update_dpp((int)mx, (int)mx, 0x120 + (n), 0xF, 0xF, false); \
+        mn = a < mn ? a : mn;                                                   \
+        mx = b > mx ? b : mx;                                                   \
+    }
+    DS4A_ROW_ROR(8) DS4A_ROW_ROR(4) DS4A_ROW_ROR(2) DS4A_ROW_ROR(1)
+#undef DS4A_ROW_ROR
+    uint32_t m0 = __builtin_amdgcn_readlane(mn, 0), m1 = __builtin_amdgcn_readlane(mn, 16);
+    uint32_t m2 = __builtin_amdgcn_readlane(mn, 32), m3 = __builtin_amdgcn_readlane(mn, 48);
+    uint32_t x0 = __builtin_amdgcn_readlane(mx, 0), x1 = __builtin_amdgcn_readlane(mx, 16);
+    uint32_t x2 = __builtin_amdgcn_readlane(mx, 32), x3 = __builtin_amdgcn_readlane(mx, 48);
+    m0 = m0 < m1 ? m0 : m1;
+    m2 = m2 < m3 ? m2 : m3;
+    mn = m0 < m2 ? m0 : m2;
+    x0 = x0 > x1 ? x0 : x1;
+    x2 = x2 > x3 ? x2 : x3;
+    mx = x0 > x2 ? x0 : x2;
+}
+
 __device__ __forceinline__ float wave_xor_sum(float v, int mask) {
     return v + __shfl_xor(v, mask, kWave);
 }

@@ -12,9 +12,10 @@
 // (64 VGPRs), key rows stream from HBM straight into B-operand registers.
 // Each wave takes 32 consecutive rows (8 KiB) per iteration: two 16-row
 // blocks, each row read as 4 x 64-byte contiguous segments.  Per 16-row block:
-// 4 head tiles x 4 k-steps = 16 v_mfma_f32_16x16x32_bf16.  The D layout puts
-// 4 heads of one row in each lane, so the fp32 ReLU + weighted head sum is 16
-// in-lane FMAs plus two cross-lane adds.  The op is HBM-bound (64 flop/byte).
+// 4 head tiles x 4 k-steps = 16 v_mfma_f32_16x16x32_bf16 with the keys as the
+// A operand, so D holds 4 rows x 1 head per lane; the fp32 ReLU + weighted head
+// sum is 16 in-lane FMAs plus a 4-step DPP butterfly across the 16 lanes of a
+// row.  The op is HBM-bound (64 flop/byte).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -70,15 +71,14 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 #pragma unroll
         for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + ((4 * s + g) ^ c)]);
 
-    // Head weights of the 16 D rows this lane holds: heads 16ht + 4g + r.
-    float wh[4][4];
+    // Head weight of the D column this lane holds in head tile ht: head 16ht + c.
+    float wh[4];
     const float *wq = w + q * kHeads;
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) wh[ht][r] = wq[16 * ht + 4 * g + r];
+    for (int ht = 0; ht < 4; ++ht) wh[ht] = wq[16 * ht + c];
 
     const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
+    const bool row_aligned = ((q * N) & 3) == 0;      // scores of this query start 16-byte aligned
 
     for (int64_t base = r0 + 16 * kBlocksPerIter * wave; base < rv1; base += kRowsPerIter) {
         // Issue all loads of this iteration first: B fragment (k-step s) of row base+16bi+c
@@ -95,19 +95,29 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         for (int bi = 0; bi < kBlocksPerIter; ++bi) {
             const int64_t blk = base + 16 * bi;
             if (blk >= rv1) break;                    // uniform across the wave
-            float acc = 0.f;
+            // D[row 4g + r][head 16ht + c] = <key row, query head> (A = keys, B = query).
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) {
                 f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) d = mfma16(aq[ht][s], as_bf16x8(kb[bi][s]), d);
+                for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(kb[bi][s]), aq[ht][s], d);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc += wh[ht][r] * fmaxf(d[r], 0.f);
+                for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * fmaxf(d[r], 0.f);
             }
-            // Sum the four row-groups: lanes c, c+16, c+32, c+48 hold the same row.
-            acc = wave_xor_sum(acc, 16);
-            acc = wave_xor_sum(acc, 32);
-            if (g == 0 && blk + c < rv1) srow[blk + c] = acc;
+            // Sum over the 16 heads of each row: the 16 lanes of a DPP row.
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
+            const int64_t row0 = blk + 4 * g;
+            if (c == 0) {
+                if (row0 + 3 < rv1 && row_aligned) {
+                    *reinterpret_cast<f32x4 *>(srow + row0) = acc;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (row0 + r < rv1) srow[row0 + r] = acc[r];
+                }
+            }
         }
     }
 }

@@ -12,7 +12,7 @@
 //   1. min/max of the keys; the bits above their highest differing bit are
 //      common to all keys and are skipped;
 //   2. 8-bit digit passes: LDS histogram of the keys that match the prefix so
-//      far, then wave 0 scans the 256 bins (descending, wavefront shuffles)
+//      far, then wave 0 scans the 256 bins (descending, DPP wavefront scan)
 //      for the bin holding the need-th key; stop early once a whole bin is
 //      taken;
 //   3. the result is a threshold key T plus a number of ties (keys == T) to
@@ -69,19 +69,10 @@ __device__ __forceinline__ int64_t cand_count(int64_t nv, int K, const Levels &l
     return c;
 }
 
-__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v, int lane) {
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const uint32_t t = __shfl_up(v, o, kWave);
-        if (lane >= o) v += t;
-    }
-    return v;
-}
-
 // Exclusive prefix sum over the workgroup.
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    const uint32_t incl = wave_incl_scan(v, lane);
+    const uint32_t incl = wave_incl_scan_dpp(v);
     if (lane == kWave - 1) wave_sums[wave] = incl;
     __syncthreads();
     uint32_t off = 0;
@@ -92,12 +83,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
 
 __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-#pragma unroll
-    for (int o = kWave / 2; o > 0; o >>= 1) {
-        const uint32_t a = __shfl_xor(kmin, o, kWave), b = __shfl_xor(kmax, o, kWave);
-        kmin = a < kmin ? a : kmin;
-        kmax = b > kmax ? b : kmax;
-    }
+    wave_minmax_u32(kmin, kmax);
     if (lane == 0) {
         sm.wave_a[wave] = kmin;
         sm.wave_b[wave] = kmax;
@@ -156,7 +142,7 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
                     v[i] = sm.hist[kBins - 1 - (4 * lane + i)];
                     s += v[i];
                 }
-                uint32_t cum = wave_incl_scan(s, lane) - s;
+                uint32_t cum = wave_incl_scan_dpp(s) - s;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (cum < remaining && remaining <= cum + v[i]) {
