@@ -12,28 +12,29 @@
 // Readings: each stored row is both key and value; the union is raw rows then
 // selected rows, not de-duplicated; RoPE pairs are adjacent dims.
 //
-// Design.  A workgroup (4 waves) owns 16 heads of one query and a contiguous
-// chunk of 32-row union tiles.  Wave w owns dims [128w, 128w+128):
-//   QK  : partial logits L^T[32 rows x 16 heads] over its 128 dims with 16x16x32
-//         MFMA tiles (A = rows from LDS, B = rotated query in VGPRs); the four
-//         partials are summed through LDS in a fixed order;
+// Design.  A workgroup (8 waves) owns one query, 64 heads and a contiguous
+// chunk of 32-row union tiles, so every row is brought into LDS once for all
+// 64 heads.  Wave (ht, dh) owns heads 16ht..16ht+15 and dims 256dh..256dh+255:
+//   QK  : partial L^T[32 rows x 16 heads] over its 256 dims with 16x16x32
+//         MFMA tiles (A = rows from LDS, B = rotated query held in VGPRs);
+//         the two halves are added through LDS in a fixed order;
 //   softmax: online (running max / sum per head), fp32;
-//   PV  : O^T[128 dims x 16 heads] += V^T * P^T; P^T is already in the
-//         B-operand layout of the QK result; V^T fragments come from the same
-//         LDS tile through ds_read_b64_tr_b16 (transposing 4 x 16 blocks).
+//   PV  : O^T[256 dims x 16 heads] += V^T * P^T; P^T is already in the
+//         B-operand layout of the QK result, V^T fragments come from the same
+//         LDS tile through ds_read_b64_tr_b16.
 // Each row format gets the MFMA of its own type, so rows are never converted:
 // compressed rows are bf16 (v_mfma_f32_16x16x32_bf16), raw-window rows are f16
-// (v_mfma_f32_16x16x32_f16).  What is not already in that type is carried as
-// hi + lo pairs: the fp32 query (a bf16 query only in its rotated tail) and
-// the probabilities.  LDS rows are 1056 bytes apart and their 16-byte
-// chunks are XOR-swizzled by row bit 2, which keeps both the row reads of QK
-// and the transposed reads of PV free of bank conflicts.  Tiles are
-// double-buffered: the next tile's rows are fetched
-// into VGPRs (1 KiB per wave instruction, row-contiguous) while the current
-// tile computes.  When the union is split over several workgroups, each
+// (v_mfma_f32_16x16x32_f16).  Operands not already in that type are carried
+// as hi + lo pairs: the query (only its rotated tail when it is bf16) and the
+// probabilities.  The raw tiles come first in the union, so the query is held
+// as an f16 pair for them and re-split as a bf16 pair for the compressed tiles.
+// LDS rows are 1056 bytes apart and their 16-byte chunks are XOR-swizzled by
+// row bit 2, which keeps both the row reads of QK and the transposed reads of
+// PV free of bank conflicts.  Loads run two tiles ahead through two register
+// stages (1 KiB of one row per wave instruction) into two LDS buffers; two
+// barriers per tile (logit halves, buffer turnover).  When the union is split over several workgroups each
 // writes (max, sum, unnormalised O) and a merge kernel combines them by
-// log-sum-exp.  Workgroup order is XCD-aware: the head groups that read the
-// same rows are dispatched to the same XCD (same L2).
+// log-sum-exp.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -43,17 +44,23 @@ namespace ds4a {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kHG = 16;                       // heads per workgroup
+constexpr int kThreads = 512;                 // 8 waves: 4 head tiles x 2 halves of the dims
+constexpr int kWaves = kThreads / kWave;
+constexpr int kHW = 16;                       // heads per wave
+constexpr int kHG = 64;                       // heads per workgroup
 constexpr int kD = 512;
+constexpr int kDH = kD / 2;                   // dims per wave
 constexpr int kRot = 64;
+constexpr int kKs = kDH / 32;                 // k-steps of QK per wave (8)
+constexpr int kDB = kDH / 16;                 // 16-dim blocks of PV per wave (16)
 constexpr int kTile = 32;                     // union rows per tile
 constexpr int kRowStride = 1056;              // LDS bytes per row (1024 + 32)
 constexpr int kTileBytes = kTile * kRowStride;
-constexpr int kXchBytes = 4 * 2 * kWave * 16; // partial logits of 4 waves
-constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes;   // + 4 bytes per union row of the chunk (row table)
-constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[16], l[16], O[16][512]
-constexpr int kXcd = 8;
+constexpr int kXchBytes = kWaves * 2 * kWave * 16;           // partial logits of every wave
+constexpr int kStage = kTile / kWaves;        // rows each wave stages per tile (4)
+constexpr int kQtBytes = kHG * kRot * 4;                     // rotated query tails of the 64 heads (f32)
+constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
+constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[64], l[64], O[64][512]
 
 // Byte offset of 16-byte chunk c (0..63) of tile row r, XOR-swizzled by row bit 2.
 __device__ __forceinline__ int chunk_off(int r, int c) {
@@ -77,13 +84,14 @@ struct MqaArgs {
     float scale;
     float *out;
     float *part;
-    double inv_freq[kRot / 2];               // theta^(-2i/n_rot), computed on the host in fp64
+    double log2_theta;                       // log2(rope_theta), computed on the host in fp64
 };
 
-// Rotate one adjacent pair of the query tail by pos * inv_freq (fp64), round once to f32.
-// The angle (up to ~1e6 rad) is first reduced by a two-part 2*pi in fp64, so that sincos runs
-// on |x| <= pi.
-__device__ __forceinline__ void rope_pair(double inv_freq, int64_t pos, float &a, float &b) {
+// Rotate the adjacent pair i of the query tail by pos * theta^(-2i/n_rot) (fp64), round once
+// to f32.  The angle (up to ~1e6 rad) is first reduced by a two-part 2*pi in fp64, so that
+// sincos runs on |x| <= pi.
+__device__ __forceinline__ void rope_pair(double log2_theta, int i, int64_t pos, float &a, float &b) {
+    const double inv_freq = exp2(-(double)(2 * i) / (double)kRot * log2_theta);
     const double ang = (double)pos * inv_freq;
     const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
     double red = fma(-k, 6.283185307179586, ang);              // 2 pi, high part
@@ -95,8 +103,8 @@ __device__ __forceinline__ void rope_pair(double inv_freq, int64_t pos, float &a
     b = (float)(x * sn + y * cs);
 }
 
-// Query dims [d, d+8) of head h of query q as f32, rotated where they fall in the tail.
-__device__ __forceinline__ void load_q8(const MqaArgs &a, int64_t q, int h, int d, float (&v)[8]) {
+// Query dims [d, d+8) of head h of query q as f32, as stored (no rotation).
+__device__ __forceinline__ void load_q8_plain(const MqaArgs &a, int64_t q, int h, int d, float (&v)[8]) {
     const int64_t off = (q * a.H + h) * (int64_t)kD + d;
     if (a.q_bf16) {
         const u32x4 x = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + off);
@@ -111,10 +119,45 @@ __device__ __forceinline__ void load_q8(const MqaArgs &a, int64_t q, int h, int 
         v[0] = x0.x; v[1] = x0.y; v[2] = x0.z; v[3] = x0.w;
         v[4] = x1.x; v[5] = x1.y; v[6] = x1.z; v[7] = x1.w;
     }
+}
+
+// Query dims [d, d+8) of head h of query q as f32, rotated where they fall in the tail.
+__device__ __forceinline__ void load_q8(const MqaArgs &a, int64_t q, int h, int d, float (&v)[8]) {
+    load_q8_plain(a, q, h, d, v);
     if (d >= kD - kRot) {
         const int64_t pos = a.pos[q];
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) rope_pair(a.inv_freq[(d + e - (kD - kRot)) >> 1], pos, v[e], v[e + 1]);
+        for (int e = 0; e < 8; e += 2) rope_pair(a.log2_theta, (d + e - (kD - kRot)) >> 1, pos, v[e], v[e + 1]);
+    }
+}
+
+// The query as MFMA B fragments, k-step s <-> dims d0 + 32s + 8g + (0..7) of head h:
+// hi/lo pairs of one operand type (bf16 or f16).
+// The rotated tail (dims 448..511) comes from `tail`, this head's 64 floats in LDS.
+template <bool F16>
+__device__ __forceinline__ void load_q_frags(const MqaArgs &a, int64_t q, int h, const float *tail, int d0, int g,
+                                             u32x4 (&hi)[kKs], u32x4 (&lo)[kKs]) {
+#pragma unroll
+    for (int s = 0; s < kKs; ++s) {
+        float v[8];
+        const int d = d0 + 32 * s + 8 * g;
+        if (d >= kD - kRot) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[e] = tail[d - (kD - kRot) + e];
+        } else {
+            load_q8_plain(a, q, h, d, v);
+        }
+        if (F16) {
+            f16x8 h8, l8;
+            pack_hi_lo8_f16(v, h8, l8);
+            hi[s] = __builtin_bit_cast(u32x4, h8);
+            lo[s] = __builtin_bit_cast(u32x4, l8);
+        } else {
+            bf16x8 h8, l8;
+            pack_hi_lo8(v, h8, l8);
+            hi[s] = __builtin_bit_cast(u32x4, h8);
+            lo[s] = __builtin_bit_cast(u32x4, l8);
+        }
     }
 }
 
@@ -123,20 +166,21 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *tiles = smem;
     f32x4 *xch = reinterpret_cast<f32x4 *>(smem + 2 * kTileBytes);
+    float *s_qt = reinterpret_cast<float *>(smem + 2 * kTileBytes + kXchBytes);   // [64 heads][64]
     int32_t *s_row = reinterpret_cast<int32_t *>(smem + kLdsBytes);   // per union row: comp row, -2 raw, -1 none
 
-    // XCD-aware block order: all head groups of one (query, chunk) share an XCD.
-    const int lin = blockIdx.x;
-    const int k8 = lin / kXcd;
-    const int hg = k8 % a.n_hg;
-    const int64_t item = (int64_t)(k8 / a.n_hg) * kXcd + (lin % kXcd);
-    if (item >= a.n_items) return;
+    const int64_t lin = blockIdx.x;
+    const int hg = (int)(lin % a.n_hg);
+    const int64_t item = lin / a.n_hg;
     const int64_t q = item / a.n_chunks;
     const int chunk = (int)(item % a.n_chunks);
     const int64_t u = q / a.T, t = q % a.T;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int g = lane >> 4, c = lane & 15;
-    const int h0 = hg * kHG;
+    const int ht = wave >> 1, dh = wave & 1;               // head tile, half of the dims
+    const int h0 = hg * kHG + kHW * ht;                   // this wave's first head
+    const int d0 = kDH * dh;                              // this wave's first dim
+    const bool active = h0 < a.H;                          // H is a multiple of 16
     const int tile0 = chunk * a.tiles_per_chunk;
     const int tile1 = tile0 + a.tiles_per_chunk < a.n_tiles ? tile0 + a.tiles_per_chunk : a.n_tiles;
 
@@ -158,6 +202,29 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         }
         s_row[r] = v;
     }
+    // Rotated query tails of this workgroup's heads: one adjacent pair per thread and step.
+    {
+        const int64_t pos = a.pos[q];
+        for (int i = tid; i < kHG * (kRot / 2); i += kThreads) {
+            const int hl = i / (kRot / 2), pr = i % (kRot / 2);
+            const int h = hg * kHG + hl;
+            if (h >= a.H) break;
+            const int64_t off = (q * a.H + h) * (int64_t)kD + (kD - kRot) + 2 * pr;
+            float x, y;
+            if (a.q_bf16) {
+                const uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.q) + off);
+                x = bf16_bits_to_f32(w & 0xFFFFu);
+                y = bf16_bits_to_f32(w >> 16);
+            } else {
+                const float2 w = *reinterpret_cast<const float2 *>(static_cast<const float *>(a.q) + off);
+                x = w.x;
+                y = w.y;
+            }
+            rope_pair(a.log2_theta, pr, pos, x, y);
+            s_qt[hl * kRot + 2 * pr] = x;
+            s_qt[hl * kRot + 2 * pr + 1] = y;
+        }
+    }
     __syncthreads();
 
     auto row_ptr = [&](int rho) -> const uint16_t * {
@@ -167,176 +234,202 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         return comp_u + (int64_t)v * kD;
     };
 
-    // Wave w stages rows w + 4i (i = 0..7) of a tile; lane = 16-byte chunk of the row.
-    u32x4 stage[8];
-    auto load_tile = [&](int tt) {
+    // Wave w stages rows w + 8i (i = 0..3) of a tile; lane = 16-byte chunk of the row.
+    u32x4 st0[kStage], st1[kStage];
+    auto load_tile = [&](int tt, u32x4 (&st)[kStage]) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint16_t *p = row_ptr(tt * kTile + wave + 4 * i);
-            stage[i] = p ? reinterpret_cast<const u32x4 *>(p)[lane] : u32x4{0u, 0u, 0u, 0u};
+        for (int i = 0; i < kStage; ++i) {
+            const uint16_t *p = row_ptr(tt * kTile + wave + kWaves * i);
+            st[i] = p ? reinterpret_cast<const u32x4 *>(p)[lane] : u32x4{0u, 0u, 0u, 0u};
         }
     };
-    auto store_tile = [&](int buf) {
-        unsigned char *base = tiles + buf * kTileBytes;
+    // Every LDS address below is a per-lane base plus a compile-time offset: the swizzle bit
+    // of the rows a lane touches does not depend on the unrolled index.
+    //   staging: row wave + 8i has swizzle bit (wave >> 2) & 1;
+    //   QK:      row 16rt + c, chunk d0/8 + 4s + g  -> bit (c >> 2) & 1 flips g's low bit;
+    //   PV:      rows 4g + c/4 (+16), dims d0 + 16b + 4(c%4) -> bit g & 1 flips chunk bit (c >> 1) & 1.
+    const int st_base = chunk_off(wave, lane);
+    const int qk_base = c * kRowStride + (((kDH * dh) >> 3) + (g ^ ((c >> 2) & 1))) * 16;
+    const int pv_base = (4 * g + (c >> 2)) * kRowStride + (((kDH * dh) >> 3) + (((c >> 1) & 1) ^ (g & 1))) * 16 +
+                        (c & 1) * 8;
+    auto store_tile = [&](int buf, const u32x4 (&st)[kStage]) {
+        unsigned char *base = tiles + buf * kTileBytes + st_base;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4 *>(base + chunk_off(wave + 4 * i, lane)) = stage[i];
+        for (int i = 0; i < kStage; ++i)
+            *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = st[i];
     };
-    if (tile0 < tile1) load_tile(tile0);
+    if (tile0 < tile1) load_tile(tile0, st0);
+    if (tile0 + 1 < tile1) load_tile(tile0 + 1, st1);
 
-    // Rotated query as B fragments while the first tile is in flight: k-step s <-> dims
-    // 128*wave + 32s + 8g + (0..7) of head h0 + c; bf16 pair for compressed rows, f16 pair for
-    // raw rows.  The lo halves are zero (and skipped) for a bf16 query outside the rotated tail.
-    bf16x8 qb_hi[4], qb_lo[4];
-    f16x8 qh_hi[4], qh_lo[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        float v[8];
-        load_q8(a, q, h0 + c, 128 * wave + 32 * s + 8 * g, v);
-        pack_hi_lo8(v, qb_hi[s], qb_lo[s]);
-        pack_hi_lo8_f16(v, qh_hi[s], qh_lo[s]);
+    // Query fragments for the first phase: f16 pair while the tiles are raw rows, else bf16.
+    // For a bf16 query the lo halves are zero outside the rotated tail (dims 448..511:
+    // the upper half's k-steps 6 and 7).
+    bool q_f16 = tile0 * kTile < a.W;
+    u32x4 qhi[kKs], qlo[kKs];
+    if (active) {
+        if (q_f16) load_q_frags<true>(a, q, h0 + c, s_qt + (kHW * ht + c) * kRot, d0, g, qhi, qlo);
+        else load_q_frags<false>(a, q, h0 + c, s_qt + (kHW * ht + c) * kRot, d0, g, qhi, qlo);
     }
-    const bool lo_tail = !a.q_bf16 || wave == 3;      // dims 448..511 belong to wave 3 (s = 2, 3)
 
     float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[8];
+    f32x4 o[kDB];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < kDB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (tile0 < tile1) store_tile(0);
+    if (tile0 < tile1) store_tile(0, st0);
     __syncthreads();
 
-    for (int tt = tile0; tt < tile1; ++tt) {
-        const int buf = (tt - tile0) & 1;
-        const bool has_next = tt + 1 < tile1;
-        if (has_next) load_tile(tt + 1);
+    // One tile: `ld` is the register stage that held tile tt (already in LDS) and now takes
+    // tile tt+2; `sv` holds tile tt+1, stored into the other buffer at the end.
+    auto step = [&](int tt, int buf, u32x4 (&ld)[kStage], const u32x4 (&sv)[kStage]) {
+        if (tt + 2 < tile1) load_tile(tt + 2, ld);
         const unsigned char *tb = tiles + buf * kTileBytes;
         const bool is_raw = tt * kTile < a.W;
+        if (active && q_f16 && !is_raw) {          // first compressed tile: re-split the query as bf16
+            load_q_frags<false>(a, q, h0 + c, s_qt + (kHW * ht + c) * kRot, d0, g, qhi, qlo);
+            q_f16 = false;
+        }
 
-        // ---- QK: partial logits over this wave's dims
+        // ---- QK: partial logits of 32 rows x this wave's 16 heads over its 256 dims
+        f32x4 acc[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (active) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(tb + chunk_off(16 * rt + c, 16 * wave + 4 * s + g));
-                const bool lo = !a.q_bf16 || (lo_tail && s >= 2);
-                if (!is_raw) {
-                    acc = mfma16(as_bf16x8(x), qb_hi[s], acc);
-                    if (lo) acc = mfma16(as_bf16x8(x), qb_lo[s], acc);
-                } else {
-                    acc = mfma16h(as_f16x8(x), qh_hi[s], acc);
-                    if (lo) acc = mfma16h(as_f16x8(x), qh_lo[s], acc);
+                for (int s = 0; s < kKs; ++s) {
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(tb + qk_base + rt * 16 * kRowStride + s * 64);
+                    const bool lo = !a.q_bf16 || (dh == 1 && s >= kKs - 2);
+                    if (!is_raw) {
+                        acc[rt] = mfma16(as_bf16x8(x), as_bf16x8(qhi[s]), acc[rt]);
+                        if (lo) acc[rt] = mfma16(as_bf16x8(x), as_bf16x8(qlo[s]), acc[rt]);
+                    } else {
+                        acc[rt] = mfma16h(as_f16x8(x), as_f16x8(qhi[s]), acc[rt]);
+                        if (lo) acc[rt] = mfma16h(as_f16x8(x), as_f16x8(qlo[s]), acc[rt]);
+                    }
                 }
             }
-            xch[(wave * 2 + rt) * kWave + lane] = acc;
+            xch[(wave * 2 + rt) * kWave + lane] = acc[rt];
         }
         __syncthreads();
 
-        // ---- full logits (same fixed summation order in every wave), mask, online softmax
-        float p[2][4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const f32x4 s0 = xch[(0 * 2 + rt) * kWave + lane], s1 = xch[(1 * 2 + rt) * kWave + lane];
-            const f32x4 s2 = xch[(2 * 2 + rt) * kWave + lane], s3 = xch[(3 * 2 + rt) * kWave + lane];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rho = tt * kTile + 16 * rt + 4 * g + r;
-                const bool valid = s_row[rho - rho0] != -1;
-                const float lg = a.scale * (((s0[r] + s1[r]) + s2[r]) + s3[r]);
-                p[rt][r] = valid ? lg : -INFINITY;
-                tmax = fmaxf(tmax, p[rt][r]);
-            }
-        }
-        tmax = wave_xor_max(tmax, 16);
-        tmax = wave_xor_max(tmax, 32);
-        const float m_new = fmaxf(m_run, tmax);
-        float alpha = 1.f, psum = 0.f;
-        if (m_new == -INFINITY) {
+        if (active) {
+            // full logits: lower half + upper half, the same order in both waves of the pair
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) p[rt][r] = 0.f;
-        } else {
-            alpha = __expf(m_run - m_new);
+                acc[rt] = xch[((2 * ht) * 2 + rt) * kWave + lane] + xch[((2 * ht + 1) * 2 + rt) * kWave + lane];
+
+            // ---- mask, online softmax (head c; rows 16rt + 4g + r)
+            float p[2][4];
+            float tmax = -INFINITY;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    p[rt][r] = __expf(p[rt][r] - m_new);
-                    psum += p[rt][r];
+                    const int rho = tt * kTile + 16 * rt + 4 * g + r;
+                    p[rt][r] = s_row[rho - rho0] != -1 ? a.scale * acc[rt][r] : -INFINITY;
+                    tmax = fmaxf(tmax, p[rt][r]);
                 }
-        }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
+            tmax = wave_xor_max(tmax, 16);
+            tmax = wave_xor_max(tmax, 32);
+            const float m_new = fmaxf(m_run, tmax);
+            float alpha = 1.f, psum = 0.f;
+            if (m_new == -INFINITY) {
 #pragma unroll
-        for (int b = 0; b < 8; ++b) o[b] *= alpha;
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) p[rt][r] = 0.f;
+            } else {
+                alpha = __expf(m_run - m_new);
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        p[rt][r] = __expf(p[rt][r] - m_new);
+                        psum += p[rt][r];
+                    }
+            }
+            l_run = l_run * alpha + psum;
+            m_run = m_new;
+            if (alpha != 1.f) {
+#pragma unroll
+                for (int b = 0; b < kDB; ++b) o[b] *= alpha;
+            }
 
-        // ---- PV: P^T fragment, element e <-> row e<4 ? 4g+e : 16+4g+(e-4); V^T fragment by two
-        // transposed reads: source lane (g, c) points at row 4g + c/4 (+16), dims d0 + 4(c%4).
-        const float pv[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
-        const int r1 = 4 * g + (c >> 2);
-        if (!is_raw) {
-            bf16x8 phi, plo;
-            pack_hi_lo8(pv, phi, plo);
+            // ---- PV: P^T fragment, element e <-> row e<4 ? 4g+e : 16+4g+(e-4); V^T fragment by two
+            // transposed reads: source lane (g, c) points at row 4g + c/4 (+16), dims d0 + 4(c%4).
+            const float pv[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
+            if (!is_raw) {
+                bf16x8 phi, plo;
+                pack_hi_lo8(pv, phi, plo);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const int d = 128 * wave + 16 * b + 4 * (c & 3);
-                const s16x4 v1 = lds_read_tr16(tb + elem_off(r1, d));
-                const s16x4 v2 = lds_read_tr16(tb + elem_off(r1 + 16, d));
-                const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[b] = mfma16(av, phi, o[b]);
-                o[b] = mfma16(av, plo, o[b]);
-            }
-        } else {
-            f16x8 phi, plo;
-            pack_hi_lo8_f16(pv, phi, plo);
+                for (int b = 0; b < kDB; ++b) {
+                    const s16x4 v1 = lds_read_tr16(tb + pv_base + 32 * b);
+                    const s16x4 v2 = lds_read_tr16(tb + pv_base + 16 * kRowStride + 32 * b);
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[b] = mfma16(av, phi, o[b]);
+                    o[b] = mfma16(av, plo, o[b]);
+                }
+            } else {
+                f16x8 phi, plo;
+                pack_hi_lo8_f16(pv, phi, plo);
 #pragma unroll
-            for (int b = 0; b < 8; ++b) {
-                const int d = 128 * wave + 16 * b + 4 * (c & 3);
-                const s16x4 v1 = lds_read_tr16(tb + elem_off(r1, d));
-                const s16x4 v2 = lds_read_tr16(tb + elem_off(r1 + 16, d));
-                const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-                o[b] = mfma16h(av, phi, o[b]);
-                o[b] = mfma16h(av, plo, o[b]);
+                for (int b = 0; b < kDB; ++b) {
+                    const s16x4 v1 = lds_read_tr16(tb + pv_base + 32 * b);
+                    const s16x4 v2 = lds_read_tr16(tb + pv_base + 16 * kRowStride + 32 * b);
+                    const f16x8 av = __builtin_bit_cast(f16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[b] = mfma16h(av, phi, o[b]);
+                    o[b] = mfma16h(av, plo, o[b]);
+                }
             }
         }
-        if (has_next) store_tile(buf ^ 1);
+        // Tile tt+1 (loaded two steps ago) into the other buffer, whose previous tile
+        // every wave finished reading before the last barrier.
+        if (tt + 1 < tile1) store_tile(buf ^ 1, sv);
         __syncthreads();
+    };
+    // Unrolled by two so that both register stages stay statically named.
+    for (int tt = tile0; tt < tile1; tt += 2) {
+        step(tt, 0, st0, st1);
+        if (tt + 1 < tile1) step(tt + 1, 1, st1, st0);
     }
 
+    if (!active) return;
     // ---- epilogue: per-head sum over the four row groups
     l_run = wave_xor_sum(l_run, 16);
     l_run = wave_xor_sum(l_run, 32);
+    const int hl = kHW * ht + c;                          // head within the workgroup
     if (a.n_chunks == 1) {
         const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-        float *orow = a.out + (q * a.H + h0 + c) * (int64_t)kD + 128 * wave + 4 * g;
+        float *orow = a.out + (q * a.H + h0 + c) * (int64_t)kD + d0 + 4 * g;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) *reinterpret_cast<f32x4 *>(orow + 16 * b) = o[b] * inv;
+        for (int b = 0; b < kDB; ++b) *reinterpret_cast<f32x4 *>(orow + 16 * b) = o[b] * inv;
     } else {
         float *rec = a.part + ((q * a.n_hg + hg) * (int64_t)a.n_chunks + chunk) * kRec;
-        if (wave == 0 && g == 0) {
-            rec[c] = m_run;
-            rec[kHG + c] = l_run;
+        if (g == 0 && dh == 0) {
+            rec[hl] = m_run;
+            rec[kHG + hl] = l_run;
         }
-        float *orow = rec + 2 * kHG + c * kD + 128 * wave + 4 * g;
+        float *orow = rec + 2 * kHG + hl * kD + d0 + 4 * g;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) *reinterpret_cast<f32x4 *>(orow + 16 * b) = o[b];
+        for (int b = 0; b < kDB; ++b) *reinterpret_cast<f32x4 *>(orow + 16 * b) = o[b];
     }
 }
 
-// Combines the per-chunk (max, sum, O) records of one (query, head group).
+// Combines the per-chunk (max, sum, O) records of one (query, head group of 64).
+// One thread per (head, 32 dims): 64 heads x 16 = 1024 threads over 4 workgroups of 256.
 __global__ __launch_bounds__(256) void mqa_merge_kernel(int H, int n_hg, int n_chunks,
                                                         const float *__restrict__ part, float *__restrict__ out)
 {
-    const int64_t qh = blockIdx.x;
+    const int64_t qh = blockIdx.x / 4;                     // (query, head group)
     const int64_t q = qh / n_hg;
     const int hg = (int)(qh % n_hg);
+    const int hl = (int)(blockIdx.x % 4) * 16 + (threadIdx.x >> 4);
+    if (hg * kHG + hl >= H) return;
     const float *base = part + qh * n_chunks * (int64_t)kRec;
-    const int hc = threadIdx.x >> 4;
     const int d0 = (threadIdx.x & 15) * 32;
     float M = -INFINITY;
-    for (int ch = 0; ch < n_chunks; ++ch) M = fmaxf(M, base[ch * (int64_t)kRec + hc]);
+    for (int ch = 0; ch < n_chunks; ++ch) M = fmaxf(M, base[ch * (int64_t)kRec + hl]);
     float L = 0.f;
     f32x4 acc[8];
 #pragma unroll
@@ -344,17 +437,17 @@ __global__ __launch_bounds__(256) void mqa_merge_kernel(int H, int n_hg, int n_c
     if (M != -INFINITY) {
         for (int ch = 0; ch < n_chunks; ++ch) {
             const float *rec = base + ch * (int64_t)kRec;
-            const float m = rec[hc];
+            const float m = rec[hl];
             if (m == -INFINITY) continue;
             const float wgt = __expf(m - M);
-            L += wgt * rec[kHG + hc];
-            const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + 2 * kHG + hc * kD + d0);
+            L += wgt * rec[kHG + hl];
+            const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + 2 * kHG + hl * kD + d0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
         }
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
-    f32x4 *dst = reinterpret_cast<f32x4 *>(out + (q * H + hg * kHG + hc) * (int64_t)kD + d0);
+    f32x4 *dst = reinterpret_cast<f32x4 *>(out + (q * H + hg * kHG + hl) * (int64_t)kD + d0);
 #pragma unroll
     for (int i = 0; i < 8; ++i) dst[i] = acc[i] * inv;
 }
@@ -375,20 +468,18 @@ __global__ __launch_bounds__(256) void rope_q_kernel(MqaArgs a, int64_t total8, 
     dst[1] = make_float4(v[4], v[5], v[6], v[7]);
 }
 
-void fill_inv_freq(double theta, double *inv_freq) {
-    for (int i = 0; i < kRot / 2; ++i) inv_freq[i] = pow(theta, -2.0 * (double)i / (double)kRot);
-}
+
 
 }  // namespace
 
 MqaPlan plan_mqa(int U, int T, int H, int W, int K) {
     MqaPlan p;
-    p.n_hg = H / kHG;
+    p.n_hg = (H + kHG - 1) / kHG;
     p.n_tiles = (W + K + kTile - 1) / kTile;
     const int64_t items = (int64_t)U * T * p.n_hg;
     // Split the union over workgroups only when there are too few (query, head group) items
-    // to give every CU work; aim for ~1024 workgroups.
-    int64_t want = (1024 + items - 1) / items;
+    // to give every CU a workgroup; aim for ~256 workgroups (one per CU at this register use).
+    int64_t want = (256 + items - 1) / items;
     if (want < 1) want = 1;
     if (want > p.n_tiles) want = p.n_tiles;
     p.tiles_per_chunk = (int)((p.n_tiles + want - 1) / want);
@@ -418,12 +509,12 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
     a.n_items = (int64_t)U * T * p.n_chunks;
     a.q = q; a.q_bf16 = q_bf16; a.pos = q_pos; a.raw = raw; a.comp = comp; a.idx = idx;
     a.scale = scale; a.out = out; a.part = static_cast<float *>(workspace);
-    fill_inv_freq(theta, a.inv_freq);
-    const int64_t blocks = (a.n_items + kXcd - 1) / kXcd * kXcd * p.n_hg;
+    a.log2_theta = log2(theta);
+    const int64_t blocks = a.n_items * p.n_hg;
     hipLaunchKernelGGL(sparse_mqa_kernel, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1) return e;
-    hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg * 4)), dim3(256), 0, stream,
                        H, p.n_hg, p.n_chunks, static_cast<const float *>(workspace), out);
     return hipGetLastError();
 }
@@ -433,7 +524,7 @@ hipError_t launch_rope(int U, int T, int H, const void *q, int q_bf16, const int
 {
     MqaArgs a = {};
     a.T = T; a.H = H; a.q = q; a.q_bf16 = q_bf16; a.pos = q_pos;
-    fill_inv_freq(theta, a.inv_freq);
+    a.log2_theta = log2(theta);
     const int64_t total8 = (int64_t)U * T * H * (kD / 8);
     hipLaunchKernelGGL(rope_q_kernel, dim3((unsigned)((total8 + 255) / 256)), dim3(256), 0, stream, a, total8, q_out);
     return hipGetLastError();
