@@ -39,6 +39,7 @@
 #include "launch.hpp"
 
 #include <math.h>
+#include <type_traits>
 
 namespace ds4a {
 
@@ -61,6 +62,7 @@ constexpr int kStage = kTile / kWaves;        // rows each wave stages per tile 
 constexpr int kQtBytes = kHG * kRot * 4;                     // rotated query tails of the 64 heads (f32)
 constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[64], l[64], O[64][512]
+constexpr float kRescale = 8.f;               // softmax reference moves when a logit exceeds it by this
 
 // Byte offset of 16-byte chunk c (0..63) of tile row r, XOR-swizzled by row bit 2.
 __device__ __forceinline__ int chunk_off(int r, int c) {
@@ -132,35 +134,53 @@ __device__ __forceinline__ void load_q8(const MqaArgs &a, int64_t q, int h, int 
 }
 
 // The query as MFMA B fragments, k-step s <-> dims d0 + 32s + 8g + (0..7) of head h:
-// hi/lo pairs of one operand type (bf16 or f16).
-// The rotated tail (dims 448..511) comes from `tail`, this head's 64 floats in LDS.
-template <bool F16>
+// hi/lo pairs of one operand type (bf16 or f16).  The rotated tail (dims 448..511, the
+// k-steps with d0 + 32s >= 448, a wave-uniform test) comes from `tail`, this head's 64
+// floats in LDS; all global loads are issued before any is used.
+template <bool F16, bool QF32>
 __device__ __forceinline__ void load_q_frags(const MqaArgs &a, int64_t q, int h, const float *tail, int d0, int g,
                                              u32x4 (&hi)[kKs], u32x4 (&lo)[kKs]) {
+    float v[kKs][8];
+    const int64_t off = (q * a.H + h) * (int64_t)kD + d0 + 8 * g;
 #pragma unroll
     for (int s = 0; s < kKs; ++s) {
-        float v[8];
-        const int d = d0 + 32 * s + 8 * g;
-        if (d >= kD - kRot) {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v[e] = tail[d - (kD - kRot) + e];
+        if (QF32) {
+            const float4 *p = reinterpret_cast<const float4 *>(static_cast<const float *>(a.q) + off + 32 * s);
+            const float4 x0 = p[0], x1 = p[1];
+            v[s][0] = x0.x; v[s][1] = x0.y; v[s][2] = x0.z; v[s][3] = x0.w;
+            v[s][4] = x1.x; v[s][5] = x1.y; v[s][6] = x1.z; v[s][7] = x1.w;
         } else {
-            load_q8_plain(a, q, h, d, v);
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(static_cast<const uint16_t *>(a.q) + off + 32 * s);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[s][2 * i] = bf16_bits_to_f32(x[i] & 0xFFFFu);
+                v[s][2 * i + 1] = bf16_bits_to_f32(x[i] >> 16);
+            }
+        }
+    }
+#pragma unroll
+    for (int s = 0; s < kKs; ++s) {
+        if (d0 + 32 * s >= kD - kRot) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[s][e] = tail[d0 + 32 * s + 8 * g - (kD - kRot) + e];
         }
         if (F16) {
             f16x8 h8, l8;
-            pack_hi_lo8_f16(v, h8, l8);
+            pack_hi_lo8_f16(v[s], h8, l8);
             hi[s] = __builtin_bit_cast(u32x4, h8);
             lo[s] = __builtin_bit_cast(u32x4, l8);
         } else {
             bf16x8 h8, l8;
-            pack_hi_lo8(v, h8, l8);
+            pack_hi_lo8(v[s], h8, l8);
             hi[s] = __builtin_bit_cast(u32x4, h8);
             lo[s] = __builtin_bit_cast(u32x4, l8);
         }
     }
 }
 
+// LO_ALL: the query is f32, so every k-step carries a lo half; otherwise (bf16 query)
+// only the rotated tail does.
+template <bool LO_ALL>
 __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -183,22 +203,26 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const bool active = h0 < a.H;                          // H is a multiple of 16
     const int tile0 = chunk * a.tiles_per_chunk;
     const int tile1 = tile0 + a.tiles_per_chunk < a.n_tiles ? tile0 + a.tiles_per_chunk : a.n_tiles;
+    const int tile_raw = a.W / kTile;                      // tiles [0, tile_raw) are raw rows
 
     const uint16_t *raw_q = a.raw + (u * (int64_t)(a.T + a.W - 1) + t) * kD;
     const uint16_t *comp_u = a.comp + u * a.N * kD;
     const int32_t *idx_q = a.idx + q * (int64_t)a.K;
 
-    // Row table of this chunk's union rows, read once from idx.
+    // Row table of this chunk's union rows, read once from idx, plus two tiles of padding
+    // for the look-ahead loads past the chunk's end.
     const int rho0 = tile0 * kTile;
-    const int n_rows = (tile1 - tile0) * kTile;
+    const int n_rows = (tile1 - tile0 + 2) * kTile;
     for (int r = tid; r < n_rows; r += kThreads) {
         const int rho = rho0 + r;
         int32_t v = -1;
-        if (rho < a.W) {
-            v = -2;
-        } else if (rho - a.W < a.K) {
-            const int32_t j = idx_q[rho - a.W];
-            if (j >= 0 && (int64_t)j < a.N) v = j;
+        if (rho < tile1 * kTile) {
+            if (rho < a.W) {
+                v = -2;
+            } else if (rho - a.W < a.K) {
+                const int32_t j = idx_q[rho - a.W];
+                if (j >= 0 && (int64_t)j < a.N) v = j;
+            }
         }
         s_row[r] = v;
     }
@@ -227,21 +251,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     }
     __syncthreads();
 
-    auto row_ptr = [&](int rho) -> const uint16_t * {
+    // A row that takes no part (-1) is read from compressed row 0 (N >= 1): it is finite,
+    // its logit is masked to -inf and its probability is 0, so no branch guards the load.
+    auto row_ptr = [&](int rho) __attribute__((always_inline)) -> const uint16_t * {
         const int32_t v = s_row[rho - rho0];
-        if (v == -2) return raw_q + (int64_t)rho * kD;
-        if (v < 0) return nullptr;
-        return comp_u + (int64_t)v * kD;
+        return v == -2 ? raw_q + (int64_t)rho * kD : comp_u + (int64_t)(v < 0 ? 0 : v) * kD;
     };
 
     // Wave w stages rows w + 8i (i = 0..3) of a tile; lane = 16-byte chunk of the row.
     u32x4 st0[kStage], st1[kStage];
-    auto load_tile = [&](int tt, u32x4 (&st)[kStage]) {
+    auto load_tile = [&](int tt, u32x4 (&st)[kStage]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kStage; ++i) {
-            const uint16_t *p = row_ptr(tt * kTile + wave + kWaves * i);
-            st[i] = p ? reinterpret_cast<const u32x4 *>(p)[lane] : u32x4{0u, 0u, 0u, 0u};
-        }
+        for (int i = 0; i < kStage; ++i)
+            st[i] = reinterpret_cast<const u32x4 *>(row_ptr(tt * kTile + wave + kWaves * i))[lane];
     };
     // Every LDS address below is a per-lane base plus a compile-time offset: the swizzle bit
     // of the rows a lane touches does not depend on the unrolled index.
@@ -252,65 +274,60 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const int qk_base = c * kRowStride + (((kDH * dh) >> 3) + (g ^ ((c >> 2) & 1))) * 16;
     const int pv_base = (4 * g + (c >> 2)) * kRowStride + (((kDH * dh) >> 3) + (((c >> 1) & 1) ^ (g & 1))) * 16 +
                         (c & 1) * 8;
-    auto store_tile = [&](int buf, const u32x4 (&st)[kStage]) {
+    auto store_tile = [&](int buf, const u32x4 (&st)[kStage]) __attribute__((always_inline)) {
         unsigned char *base = tiles + buf * kTileBytes + st_base;
 #pragma unroll
         for (int i = 0; i < kStage; ++i)
             *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = st[i];
     };
-    if (tile0 < tile1) load_tile(tile0, st0);
-    if (tile0 + 1 < tile1) load_tile(tile0 + 1, st1);
+    load_tile(tile0, st0);
+    load_tile(tile0 + 1, st1);
 
-    // Query fragments for the first phase: f16 pair while the tiles are raw rows, else bf16.
-    // For a bf16 query the lo halves are zero outside the rotated tail (dims 448..511:
-    // the upper half's k-steps 6 and 7).
-    bool q_f16 = tile0 * kTile < a.W;
+    const float *tail = s_qt + (kHW * ht + c) * kRot;
     u32x4 qhi[kKs], qlo[kKs];
-    if (active) {
-        if (q_f16) load_q_frags<true>(a, q, h0 + c, s_qt + (kHW * ht + c) * kRot, d0, g, qhi, qlo);
-        else load_q_frags<false>(a, q, h0 + c, s_qt + (kHW * ht + c) * kRot, d0, g, qhi, qlo);
-    }
-
     float m_run = -INFINITY, l_run = 0.f;
     f32x4 o[kDB];
 #pragma unroll
     for (int b = 0; b < kDB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    if (tile0 < tile1) store_tile(0, st0);
+    store_tile(0, st0);
     __syncthreads();
 
     // One tile: `ld` is the register stage that held tile tt (already in LDS) and now takes
-    // tile tt+2; `sv` holds tile tt+1, stored into the other buffer at the end.
-    auto step = [&](int tt, int buf, u32x4 (&ld)[kStage], const u32x4 (&sv)[kStage]) {
-        if (tt + 2 < tile1) load_tile(tt + 2, ld);
+    // tile tt+2; `sv` holds tile tt+1, stored into the other buffer at the end.  F16: raw
+    // rows (f16 MFMA), else compressed rows (bf16 MFMA).
+    auto step = [&](auto f16_tag, int tt, int buf, u32x4 (&ld)[kStage], const u32x4 (&sv)[kStage])
+        __attribute__((always_inline)) {
+        constexpr bool F16 = decltype(f16_tag)::value;
+        load_tile(tt + 2, ld);
         const unsigned char *tb = tiles + buf * kTileBytes;
-        const bool is_raw = tt * kTile < a.W;
-        if (active && q_f16 && !is_raw) {          // first compressed tile: re-split the query as bf16
-            load_q_frags<false>(a, q, h0 + c, s_qt + (kHW * ht + c) * kRot, d0, g, qhi, qlo);
-            q_f16 = false;
-        }
 
-        // ---- QK: partial logits of 32 rows x this wave's 16 heads over its 256 dims
-        f32x4 acc[2];
+        // ---- QK: partial logits of 32 rows x this wave's 16 heads over its 256 dims;
+        // hi and lo products go to separate accumulators (two short chains, not one long).
+        f32x4 acc[2], acl[2];
 #pragma unroll
         for (int rt = 0; rt < 2; ++rt) {
             acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (active) {
+            acl[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        if (active) {
 #pragma unroll
-                for (int s = 0; s < kKs; ++s) {
+            for (int s = 0; s < kKs; ++s) {
+#pragma unroll
+                for (int rt = 0; rt < 2; ++rt) {
                     const u32x4 x = *reinterpret_cast<const u32x4 *>(tb + qk_base + rt * 16 * kRowStride + s * 64);
-                    const bool lo = !a.q_bf16 || (dh == 1 && s >= kKs - 2);
-                    if (!is_raw) {
-                        acc[rt] = mfma16(as_bf16x8(x), as_bf16x8(qhi[s]), acc[rt]);
-                        if (lo) acc[rt] = mfma16(as_bf16x8(x), as_bf16x8(qlo[s]), acc[rt]);
-                    } else {
+                    if (F16) {
                         acc[rt] = mfma16h(as_f16x8(x), as_f16x8(qhi[s]), acc[rt]);
-                        if (lo) acc[rt] = mfma16h(as_f16x8(x), as_f16x8(qlo[s]), acc[rt]);
+                        if (LO_ALL || s >= kKs - 2) acl[rt] = mfma16h(as_f16x8(x), as_f16x8(qlo[s]), acl[rt]);
+                    } else {
+                        acc[rt] = mfma16(as_bf16x8(x), as_bf16x8(qhi[s]), acc[rt]);
+                        if (LO_ALL || s >= kKs - 2) acl[rt] = mfma16(as_bf16x8(x), as_bf16x8(qlo[s]), acl[rt]);
                     }
                 }
             }
-            xch[(wave * 2 + rt) * kWave + lane] = acc[rt];
         }
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) xch[(wave * 2 + rt) * kWave + lane] = acc[rt] + acl[rt];
         __syncthreads();
 
         if (active) {
@@ -332,45 +349,34 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
                 }
             tmax = wave_xor_max(tmax, 16);
             tmax = wave_xor_max(tmax, 32);
+            // m_run is a reference, not always the running maximum: it moves (and O and the
+            // sum are rescaled) only when some head of the wave sees a logit more than
+            // kRescale above it, so every exponent stays below e^kRescale.  The result does
+            // not depend on the reference; both waves of a head tile take the same decision
+            // from the same logits.
             const float m_new = fmaxf(m_run, tmax);
-            float alpha = 1.f, psum = 0.f;
-            if (m_new == -INFINITY) {
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) p[rt][r] = 0.f;
-            } else {
-                alpha = __expf(m_run - m_new);
-#pragma unroll
-                for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        p[rt][r] = __expf(p[rt][r] - m_new);
-                        psum += p[rt][r];
-                    }
-            }
-            l_run = l_run * alpha + psum;
-            m_run = m_new;
-            if (alpha != 1.f) {
+            if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescale)) {   // also the first visible row
+                const float alpha = __expf(m_run - m_new);          // 0 while nothing was visible
+                l_run *= alpha;
 #pragma unroll
                 for (int b = 0; b < kDB; ++b) o[b] *= alpha;
+                m_run = m_new;
             }
+            const float m_use = m_run == -INFINITY ? 0.f : m_run;  // nothing visible yet: all p = 0
+            float psum = 0.f;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    p[rt][r] = __expf(p[rt][r] - m_use);
+                    psum += p[rt][r];
+                }
+            l_run += psum;
 
             // ---- PV: P^T fragment, element e <-> row e<4 ? 4g+e : 16+4g+(e-4); V^T fragment by two
             // transposed reads: source lane (g, c) points at row 4g + c/4 (+16), dims d0 + 4(c%4).
             const float pv[8] = {p[0][0], p[0][1], p[0][2], p[0][3], p[1][0], p[1][1], p[1][2], p[1][3]};
-            if (!is_raw) {
-                bf16x8 phi, plo;
-                pack_hi_lo8(pv, phi, plo);
-#pragma unroll
-                for (int b = 0; b < kDB; ++b) {
-                    const s16x4 v1 = lds_read_tr16(tb + pv_base + 32 * b);
-                    const s16x4 v2 = lds_read_tr16(tb + pv_base + 16 * kRowStride + 32 * b);
-                    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
-                    o[b] = mfma16(av, phi, o[b]);
-                    o[b] = mfma16(av, plo, o[b]);
-                }
-            } else {
+            if (F16) {
                 f16x8 phi, plo;
                 pack_hi_lo8_f16(pv, phi, plo);
 #pragma unroll
@@ -381,17 +387,47 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
                     o[b] = mfma16h(av, phi, o[b]);
                     o[b] = mfma16h(av, plo, o[b]);
                 }
+            } else {
+                bf16x8 phi, plo;
+                pack_hi_lo8(pv, phi, plo);
+#pragma unroll
+                for (int b = 0; b < kDB; ++b) {
+                    const s16x4 v1 = lds_read_tr16(tb + pv_base + 32 * b);
+                    const s16x4 v2 = lds_read_tr16(tb + pv_base + 16 * kRowStride + 32 * b);
+                    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(v1, v2, 0, 1, 2, 3, 4, 5, 6, 7));
+                    o[b] = mfma16(av, phi, o[b]);
+                    o[b] = mfma16(av, plo, o[b]);
+                }
             }
         }
-        // Tile tt+1 (loaded two steps ago) into the other buffer, whose previous tile
-        // every wave finished reading before the last barrier.
-        if (tt + 1 < tile1) store_tile(buf ^ 1, sv);
+        // Tile tt+1 (loaded one step ago) into the other buffer, whose previous tile every
+        // wave finished reading before the last barrier.  Past the chunk's end this stores
+        // padding rows that are never read.
+        store_tile(buf ^ 1, sv);
         __syncthreads();
     };
-    // Unrolled by two so that both register stages stay statically named.
-    for (int tt = tile0; tt < tile1; tt += 2) {
-        step(tt, 0, st0, st1);
-        if (tt + 1 < tile1) step(tt + 1, 1, st1, st0);
+    // Tiles [ta, tb) of one row format; unrolled by two so that both register stages stay
+    // statically named; the buffer parity continues across calls.
+    auto run = [&](auto f16_tag, int ta, int tb) __attribute__((always_inline)) {
+        int tt = ta;
+        if (tt < tb && ((tt - tile0) & 1)) {
+            step(f16_tag, tt, 1, st1, st0);
+            ++tt;
+        }
+        for (; tt + 1 < tb; tt += 2) {
+            step(f16_tag, tt, 0, st0, st1);
+            step(f16_tag, tt + 1, 1, st1, st0);
+        }
+        if (tt < tb) step(f16_tag, tt, 0, st0, st1);
+    };
+    const int tmid = tile1 < tile_raw ? tile1 : (tile0 > tile_raw ? tile0 : tile_raw);
+    if (tile0 < tmid) {
+        if (active) load_q_frags<true, LO_ALL>(a, q, h0 + c, tail, d0, g, qhi, qlo);
+        run(std::true_type{}, tile0, tmid);
+    }
+    if (tmid < tile1) {
+        if (active) load_q_frags<false, LO_ALL>(a, q, h0 + c, tail, d0, g, qhi, qlo);
+        run(std::false_type{}, tmid, tile1);
     }
 
     if (!active) return;
@@ -429,17 +465,18 @@ __global__ __launch_bounds__(256) void mqa_merge_kernel(int H, int n_hg, int n_c
     const float *base = part + qh * n_chunks * (int64_t)kRec;
     const int d0 = (threadIdx.x & 15) * 32;
     float M = -INFINITY;
+#pragma unroll 8
     for (int ch = 0; ch < n_chunks; ++ch) M = fmaxf(M, base[ch * (int64_t)kRec + hl]);
     float L = 0.f;
     f32x4 acc[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
+#pragma unroll 2
         for (int ch = 0; ch < n_chunks; ++ch) {
             const float *rec = base + ch * (int64_t)kRec;
             const float m = rec[hl];
-            if (m == -INFINITY) continue;
-            const float wgt = __expf(m - M);
+            const float wgt = m == -INFINITY ? 0.f : __expf(m - M);   // a chunk with no visible row
             L += wgt * rec[kHG + hl];
             const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + 2 * kHG + hl * kD + d0);
 #pragma unroll
@@ -494,13 +531,14 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
                       hipStream_t stream)
 {
     const MqaPlan p = plan_mqa(U, T, H, W, K);
-    const int lds = kLdsBytes + 4 * kTile * p.tiles_per_chunk;
-    static int attr_bytes = 0;
-    if (lds > attr_bytes) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(sparse_mqa_kernel),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    const int lds = kLdsBytes + 4 * kTile * (p.tiles_per_chunk + 2);
+    static int attr_bytes[2] = {0, 0};
+    const void *fn = q_bf16 ? reinterpret_cast<const void *>(sparse_mqa_kernel<false>)
+                            : reinterpret_cast<const void *>(sparse_mqa_kernel<true>);
+    if (lds > attr_bytes[q_bf16 ? 1 : 0]) {
+        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        attr_bytes = lds;
+        attr_bytes[q_bf16 ? 1 : 0] = lds;
     }
     MqaArgs a;
     a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_tiles = p.n_tiles;
@@ -511,7 +549,10 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
     a.scale = scale; a.out = out; a.part = static_cast<float *>(workspace);
     a.log2_theta = log2(theta);
     const int64_t blocks = a.n_items * p.n_hg;
-    hipLaunchKernelGGL(sparse_mqa_kernel, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+    if (q_bf16)
+        hipLaunchKernelGGL(sparse_mqa_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+    else
+        hipLaunchKernelGGL(sparse_mqa_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1) return e;
     hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg * 4)), dim3(256), 0, stream,

@@ -174,6 +174,37 @@ def test_mqa_matches_oracle_on_given_sets(H, qd, W, K):
             assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, e)
 
 
+@pytest.mark.parametrize("order,U,T", [("rising", 1, 1), ("falling", 2, 2)])
+def test_mqa_wide_logit_range(order, U, T):
+    """Selected rows scaled so that logits climb (or fall) by tens across the union: the
+    softmax reference has to move many times inside one workgroup and across the
+    split-union merge."""
+    N, K, W = 2000, 512, 128
+    w, x = _mqa_case(64, "f32", W, N, K, seed=5, U=U, T=T)
+    rng = np.random.default_rng(11)
+    idx = np.stack([np.stack([rng.choice(N, K, replace=False) for _ in range(T)]) for _ in range(U)]).astype(np.int32)
+    comp = bf16_f64(x["comp"]).astype(np.float32)
+    for u in range(U):
+        for t in range(T):
+            for i, j in enumerate(idx[u, t]):
+                f = 1.0 + (i if order == "rising" else K - 1 - i) / 16.0
+                comp[u, j] *= np.float32(f)
+    x = dict(x)
+    x["comp"] = gen.bf16_bits_from_f32(comp.copy())
+    d = upload(x)
+    out = torch.full((U, T, 64, 512), float("nan"), device="cuda")
+    ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], torch.from_numpy(idx).cuda(), w.scale, W=W, out=out)
+    got = out.cpu().numpy()
+    # Logits reach ~100 here, so the split query's 16 significant bits leave ~1e-3 absolute
+    # logit error: the contract bound applies, the unit-scale design bound does not.  A
+    # reference that moved without rescaling O or the sum would be off by O(1).
+    for u in range(U):
+        for t in range(T):
+            ref = _oracle_out(w, x, u, t, idx[u, t])
+            e = normwise_err(got[u, t], ref)
+            assert e <= CONTRACT_ERR, (u, t, e)
+
+
 def test_mqa_empty_union_is_zero():
     w, x = _mqa_case(16, "f32", 0, 100, 64, seed=4, U=1, T=1)
     d = upload(x)
