@@ -226,27 +226,35 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         }
         s_row[r] = v;
     }
-    // Rotated query tails of this workgroup's heads: one adjacent pair per thread and step.
+    // Rotated query tails of this workgroup's heads: four adjacent pairs per thread, all loads
+    // issued first (heads past H read head H-1 and store nothing).
     {
+        constexpr int kPairs = kHG * (kRot / 2) / kThreads;
         const int64_t pos = a.pos[q];
-        for (int i = tid; i < kHG * (kRot / 2); i += kThreads) {
+        float x[kPairs], y[kPairs];
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            const int i = tid + k * kThreads;
             const int hl = i / (kRot / 2), pr = i % (kRot / 2);
-            const int h = hg * kHG + hl;
-            if (h >= a.H) break;
+            const int h = hg * kHG + hl < a.H ? hg * kHG + hl : a.H - 1;
             const int64_t off = (q * a.H + h) * (int64_t)kD + (kD - kRot) + 2 * pr;
-            float x, y;
             if (a.q_bf16) {
                 const uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.q) + off);
-                x = bf16_bits_to_f32(w & 0xFFFFu);
-                y = bf16_bits_to_f32(w >> 16);
+                x[k] = bf16_bits_to_f32(w & 0xFFFFu);
+                y[k] = bf16_bits_to_f32(w >> 16);
             } else {
                 const float2 w = *reinterpret_cast<const float2 *>(static_cast<const float *>(a.q) + off);
-                x = w.x;
-                y = w.y;
+                x[k] = w.x;
+                y[k] = w.y;
             }
-            rope_pair(a.log2_theta, pr, pos, x, y);
-            s_qt[hl * kRot + 2 * pr] = x;
-            s_qt[hl * kRot + 2 * pr + 1] = y;
+        }
+#pragma unroll
+        for (int k = 0; k < kPairs; ++k) {
+            const int i = tid + k * kThreads;
+            const int hl = i / (kRot / 2), pr = i % (kRot / 2);
+            rope_pair(a.log2_theta, pr, pos, x[k], y[k]);
+            s_qt[hl * kRot + 2 * pr] = x[k];
+            s_qt[hl * kRot + 2 * pr + 1] = y[k];
         }
     }
     __syncthreads();
@@ -452,41 +460,60 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     }
 }
 
-// Combines the per-chunk (max, sum, O) records of one (query, head group of 64).
-// One thread per (head, 32 dims): 64 heads x 16 = 1024 threads over 4 workgroups of 256.
+// Combines the per-chunk (reference, sum, O) records of one (query, head group of 64).
+// One thread per (head, 8 dims): 64 heads x 64 = 4096 threads over 16 workgroups of 256.
+// Chunks are taken 8 at a time with every load of a batch issued before any is used
+// (indices past the last chunk are clamped and weighted 0), so a batch costs one round
+// trip to memory.
+constexpr int kMergeBatch = 8;
+constexpr int kMergeWgs = 16;
+
 __global__ __launch_bounds__(256) void mqa_merge_kernel(int H, int n_hg, int n_chunks,
                                                         const float *__restrict__ part, float *__restrict__ out)
 {
-    const int64_t qh = blockIdx.x / 4;                     // (query, head group)
+    const int64_t qh = blockIdx.x / kMergeWgs;             // (query, head group)
     const int64_t q = qh / n_hg;
     const int hg = (int)(qh % n_hg);
-    const int hl = (int)(blockIdx.x % 4) * 16 + (threadIdx.x >> 4);
+    const int hl = (int)(blockIdx.x % kMergeWgs) * 4 + (threadIdx.x >> 6);
     if (hg * kHG + hl >= H) return;
     const float *base = part + qh * n_chunks * (int64_t)kRec;
-    const int d0 = (threadIdx.x & 15) * 32;
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int ch = 0; ch < n_chunks; ++ch) M = fmaxf(M, base[ch * (int64_t)kRec + hl]);
-    float L = 0.f;
-    f32x4 acc[8];
+    const int d0 = (threadIdx.x & 63) * 8;
+    float M = -INFINITY, L = 0.f;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    for (int c0 = 0; c0 < n_chunks; c0 += kMergeBatch) {
+        float m[kMergeBatch], l[kMergeBatch];
+        f32x4 x0[kMergeBatch], x1[kMergeBatch];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-#pragma unroll 2
-        for (int ch = 0; ch < n_chunks; ++ch) {
+        for (int i = 0; i < kMergeBatch; ++i) {
+            const int ch = c0 + i < n_chunks ? c0 + i : n_chunks - 1;
             const float *rec = base + ch * (int64_t)kRec;
-            const float m = rec[hl];
-            const float wgt = m == -INFINITY ? 0.f : __expf(m - M);   // a chunk with no visible row
-            L += wgt * rec[kHG + hl];
+            m[i] = rec[hl];
+            l[i] = rec[kHG + hl];
             const f32x4 *src = reinterpret_cast<const f32x4 *>(rec + 2 * kHG + hl * kD + d0);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += wgt * src[i];
+            x0[i] = src[0];
+            x1[i] = src[1];
         }
+        float mb = M;
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) mb = c0 + i < n_chunks ? fmaxf(mb, m[i]) : mb;
+        const float sc = M == -INFINITY ? 0.f : __expf(M - mb);   // nothing accumulated yet: all zero
+        L *= sc;
+        acc0 *= sc;
+        acc1 *= sc;
+#pragma unroll
+        for (int i = 0; i < kMergeBatch; ++i) {
+            // a chunk past the end, or one with no visible row, weighs 0
+            const float w = (c0 + i < n_chunks && m[i] != -INFINITY) ? __expf(m[i] - mb) : 0.f;
+            L += w * l[i];
+            acc0 += w * x0[i];
+            acc1 += w * x1[i];
+        }
+        M = mb;
     }
     const float inv = L > 0.f ? 1.f / L : 0.f;
     f32x4 *dst = reinterpret_cast<f32x4 *>(out + (q * H + hg * kHG + hl) * (int64_t)kD + d0);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) dst[i] = acc[i] * inv;
+    dst[0] = acc0 * inv;
+    dst[1] = acc1 * inv;
 }
 
 // A3 alone: one thread per 8 dims of one head.
@@ -555,7 +582,7 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
         hipLaunchKernelGGL(sparse_mqa_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1) return e;
-    hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg * 4)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg * kMergeWgs)), dim3(256), 0, stream,
                        H, p.n_hg, p.n_chunks, static_cast<const float *>(workspace), out);
     return hipGetLastError();
 }
