@@ -104,21 +104,13 @@ class Bench:
         stream = torch.cuda.current_stream()
         n = len(self.reps)
 
-        def one(i, ev=None):
+        def one(i):
             d = self.reps[i % n]
             nv = d["n_vis"] if self.nvis else None
-            if ev is not None:
-                ev[0].record(stream)
             ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv, out=st.scores, stream=stream)
-            if ev is not None:
-                ev[1].record(stream)
             ops.topk_select(st.scores, w.K, n_vis=nv, out=st.idx, workspace=st.ws_topk, stream=stream)
-            if ev is not None:
-                ev[2].record(stream)
             ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W, out=st.out,
                            workspace=st.ws_mqa, stream=stream)
-            if ev is not None:
-                ev[3].record(stream)
 
         for i in range(warmup):
             one(i)
@@ -135,14 +127,28 @@ class Bench:
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         total_ms = t_begin.elapsed_time(t_end)
-        # Second timed pass over the same steps with HIP events around each call on the launch
-        # stream: per-kernel averages for the roofline.
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-        torch.cuda.synchronize()
-        for i in range(steps):
-            one(warmup + i, evs[i])
-        torch.cuda.synchronize()
-        k_ms = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps for j in range(3)]
+        # Per-call averages for the roofline: each call launched `steps` times back to back on
+        # the launch stream (inputs rotated as in the step), HIP events at the two ends only.
+        calls = [
+            lambda d, nv: ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv, out=st.scores,
+                                            stream=stream),
+            lambda d, nv: ops.topk_select(st.scores, w.K, n_vis=nv, out=st.idx, workspace=st.ws_topk,
+                                          stream=stream),
+            lambda d, nv: ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta,
+                                         W=w.W, out=st.out, workspace=st.ws_mqa, stream=stream),
+        ]
+        k_ms = []
+        for call in calls:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for i in range(steps):
+                d = self.reps[(warmup + i) % n]
+                call(d, d["n_vis"] if self.nvis else None)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            k_ms.append(e0.elapsed_time(e1) / steps)
         return {"ms_per_step": total_ms / steps, "wall_ms_per_step": 1e3 * wall / steps,
                 "indexer_ms": k_ms[0], "topk_ms": k_ms[1], "mqa_ms": k_ms[2]}
 
