@@ -15,7 +15,8 @@
 // 4 head tiles x 4 k-steps = 16 v_mfma_f32_16x16x32_bf16 with the keys as the
 // A operand, so D holds 4 rows x 1 head per lane; the fp32 ReLU + weighted head
 // sum is 16 in-lane FMAs plus a 4-step DPP butterfly across the 16 lanes of a
-// row.  The op is HBM-bound (64 flop/byte).
+// row.  Scores collect in LDS and are stored once per workgroup.  The op is
+// HBM-bound (64 flop/byte).
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -59,6 +60,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     // 16 lanes reading 16 heads at one k hit distinct banks; then A fragments
     // aq[ht][s] = qI[16ht + c][32s + 8g .. +7].
     __shared__ u32x4 sq[kHeads * kDim / 8];
+    __shared__ __align__(16) float s_sc[kRowsPerWg];   // this chunk's scores, stored at the end
     const u32x4 *gq = reinterpret_cast<const u32x4 *>(qI + q * (int64_t)(kHeads * kDim));
     for (int i = threadIdx.x; i < kHeads * kDim / 8; i += kThreads) {
         const int h = i / kChunksPerRow, k = i % kChunksPerRow;
@@ -108,17 +110,20 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
             // Sum over the 16 heads of each row: the 16 lanes of a DPP row.
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
-            const int64_t row0 = blk + 4 * g;
-            if (c == 0) {
-                if (row0 + 3 < rv1 && row_aligned) {
-                    *reinterpret_cast<f32x4 *>(srow + row0) = acc;
-                } else {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r)
-                        if (row0 + r < rv1) srow[row0 + r] = acc[r];
-                }
-            }
+            if (c == 0) *reinterpret_cast<f32x4 *>(s_sc + (blk - r0) + 4 * g) = acc;
         }
+    }
+
+    // Scores leave in one coalesced burst at the end: a global store inside the loop would make
+    // every later wait for key loads also wait for that store (one in-order counter).
+    __syncthreads();
+    const int n_out = (int)(rv1 - r0);
+    if (row_aligned) {
+        for (int i = threadIdx.x; i < n_out / 4; i += kThreads)
+            reinterpret_cast<f32x4 *>(srow + r0)[i] = reinterpret_cast<const f32x4 *>(s_sc)[i];
+        for (int i = (n_out & ~3) + threadIdx.x; i < n_out; i += kThreads) srow[r0 + i] = s_sc[i];
+    } else {
+        for (int i = threadIdx.x; i < n_out; i += kThreads) srow[r0 + i] = s_sc[i];
     }
 }
 
