@@ -127,6 +127,141 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     }
 }
 
+// ---------------------------------------------------------------- many queries per unit
+
+// Prefill shape (T >= 8 queries of one unit share the same keys).  A workgroup of 8 waves
+// owns 8 consecutive queries and a contiguous range of 128-row key tiles; each key tile is
+// read from HBM once into LDS and used by all 8 waves (one query each), so keys are read
+// T/8 times instead of T times.  Per wave and tile: 8 row blocks x 4 head tiles x 4 k-steps
+// = 128 v_mfma_f32_16x16x32_bf16 (keys as A from LDS, query as B in VGPRs), then the same
+// ReLU + weighted head sum as above.  LDS rows are 256 B with 16-byte chunks XOR-swizzled
+// by the row's low 4 bits, so the 16 rows one A-fragment read touches hit distinct banks.
+constexpr int kPQ = 8;                         // queries per workgroup (one per wave)
+constexpr int kPThreads = kPQ * kWave;
+constexpr int kPTile = 128;                    // key rows per tile
+constexpr int kPTileBytes = kPTile * kDim * 2; // 32 KiB
+
+__global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
+    int T, int64_t N, int n_qb, int n_split,
+    const uint16_t *__restrict__ qI, const float *__restrict__ w, const uint16_t *__restrict__ kI,
+    const int32_t *__restrict__ n_vis, float *__restrict__ scores)
+{
+    __shared__ __align__(16) unsigned char s_k[2 * kPTileBytes];
+    __shared__ __align__(16) float s_sc[kPQ][kPTile];
+
+    const int sp = (int)(blockIdx.x % n_split);
+    const int64_t rest = blockIdx.x / n_split;
+    const int qb = (int)(rest % n_qb);
+    const int64_t u = rest / n_qb;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int g = lane >> 4, c = lane & 15;
+    const int t = qb * kPQ + wave;
+    const bool active = t < T;
+    const int64_t q = u * T + (active ? t : T - 1);
+    const int64_t nv = active ? clamp_nvis(n_vis, q, N) : 0;
+    float *srow = scores + q * N;
+
+    // Rows any query of the workgroup sees, and this split's share of their tiles.
+    int64_t nv_max = 0;
+    for (int i = 0; i < kPQ; ++i) {
+        const int ti = qb * kPQ + i;
+        if (ti < T) {
+            const int64_t v = clamp_nvis(n_vis, u * T + ti, N);
+            nv_max = v > nv_max ? v : nv_max;
+        }
+    }
+    const int64_t n_tiles = (nv_max + kPTile - 1) / kPTile;
+    const int64_t per = (n_tiles + n_split - 1) / n_split;
+    const int64_t tile0 = sp * per;
+    const int64_t tile1 = tile0 + per < n_tiles ? tile0 + per : n_tiles;
+
+    // Rows past every processed tile are invisible to all 8 queries: the last split writes them.
+    if (sp == n_split - 1 && active) {
+        for (int64_t j = n_tiles * kPTile + lane; j < N; j += kWave) srow[j] = -INFINITY;
+    }
+    if (tile0 >= tile1) return;                  // uniform across the workgroup
+
+    // Query block of this wave as B fragments: qf[ht][s] = qI[q][16ht + c][32s + 8g .. +7].
+    const u32x4 *gq = reinterpret_cast<const u32x4 *>(qI + q * (int64_t)(kHeads * kDim));
+    u32x4 qf[4][4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int s = 0; s < 4; ++s) qf[ht][s] = gq[(16 * ht + c) * kChunksPerRow + 4 * s + g];
+    float wh[4];
+#pragma unroll
+    for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
+
+    // Tile staging: thread tid moves chunks 4(tid%4) .. +3 of tile row tid/4 (64 B).
+    const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
+    const int sr = tid >> 2, sc0 = (tid & 3) * 4;
+    u32x4 st[4];
+    auto load_tile = [&](int64_t tile) __attribute__((always_inline)) {
+        const int64_t row = tile * kPTile + sr;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) st[k] = row < N ? gk[row * kChunksPerRow + sc0 + k] : u32x4{0u, 0u, 0u, 0u};
+    };
+    auto store_tile = [&](int buf) __attribute__((always_inline)) {
+        unsigned char *base = s_k + buf * kPTileBytes + sr * 256;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(base + (((sc0 + k) ^ (sr & 15)) << 4)) = st[k];
+    };
+    // A-fragment read offsets: row 16rb + c, chunk (4s + g) ^ c (the row's low 4 bits are c).
+    int a_off[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a_off[s] = c * 256 + (((4 * s + g) ^ c) << 4);
+    const bool row_aligned = ((q * N) & 3) == 0;
+
+    load_tile(tile0);
+    store_tile(0);
+    __syncthreads();
+    for (int64_t tile = tile0; tile < tile1; ++tile) {
+        const int buf = (int)((tile - tile0) & 1);
+        if (tile + 1 < tile1) load_tile(tile + 1);
+        const int64_t trow0 = tile * kPTile;
+        if (active) {
+            const unsigned char *tb = s_k + buf * kPTileBytes;
+#pragma unroll
+            for (int rb = 0; rb < kPTile / 16; ++rb) {
+                u32x4 a[4];
+#pragma unroll
+                for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4 *>(tb + a_off[s] + rb * 16 * 256);
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) {
+                    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(a[s]), as_bf16x8(qf[ht][s]), d);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * fmaxf(d[r], 0.f);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    acc[r] = row16_sum(acc[r]);
+                    if (trow0 + rb * 16 + 4 * g + r >= nv) acc[r] = -INFINITY;
+                }
+                if (c == 0) *reinterpret_cast<f32x4 *>(&s_sc[wave][rb * 16 + 4 * g]) = acc;
+            }
+        }
+        if (tile + 1 < tile1) store_tile(buf ^ 1);
+        // This tile's 128 scores of the wave's query (the LDS writes above are the same wave's).
+        if (active) {
+            const int64_t j = trow0 + 4 * lane;
+            if (lane < kPTile / 4) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(&s_sc[wave][4 * lane]);
+                if (row_aligned && j + 3 < N) {
+                    *reinterpret_cast<f32x4 *>(srow + j) = v;
+                } else {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (j + r < N) srow[j + r] = v[r];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w,
@@ -134,6 +269,18 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
                           hipStream_t stream)
 {
     const int64_t Q = (int64_t)U * T;
+    if (T >= kPQ) {
+        const int n_qb = (T + kPQ - 1) / kPQ;
+        const int64_t wgs = (int64_t)U * n_qb;
+        // about two workgroups per CU in all, never a split shorter than 4 tiles
+        int n_split = (int)((512 + wgs - 1) / wgs);
+        const int64_t max_split = (N + 4 * kPTile - 1) / (4 * kPTile);
+        if (n_split > max_split) n_split = (int)max_split;
+        if (n_split < 1) n_split = 1;
+        hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)(wgs * n_split)), dim3(kPThreads), 0, stream,
+                           T, N, n_qb, n_split, idx_q, idx_w, idx_k, n_vis, scores);
+        return hipGetLastError();
+    }
     // 1024-row chunks (256 KiB of keys per workgroup): fastest on MI355X among 256..8192-row chunks,
     // and faster than persistent or prefetch-ring variants of the same loop.
     const int64_t rows = kRowsPerWg;

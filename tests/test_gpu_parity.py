@@ -60,7 +60,25 @@ INDEXER_CASES = [
     dict(U=2, T=3, N=700, nv=[[700, 0, 333], [1, 699, 16]]),
     dict(U=3, T=1, N=4097, nv=None, heavy=0.01),
     dict(U=1, T=5, N=257, nv=[[0, 1, 128, 256, 257]]),
+    # many queries per unit: the key-tile-sharing path (8 queries per workgroup, split key ranges)
+    dict(U=2, T=9, N=700, nv="rand"),
+    dict(U=1, T=16, N=1001, nv="rand"),
+    dict(U=1, T=8, N=4096, nv="full"),
+    dict(U=1, T=24, N=2048, nv="causal"),
 ]
+
+
+def _indexer_nv(case, U, T, N):
+    nv = case["nv"]
+    if nv is None or nv == "full":
+        return np.full((U, T), N, np.int32)
+    if nv == "rand":
+        r = np.random.default_rng(5).integers(0, N + 1, (U, T)).astype(np.int32)
+        r.flat[0], r.flat[-1] = 0, N
+        return r
+    if nv == "causal":
+        return np.tile((N // 2 + 37 * np.arange(T)).clip(0, N).astype(np.int32), (U, 1))
+    return np.array(nv, dtype=np.int32)
 
 
 @pytest.mark.parametrize("case", INDEXER_CASES, ids=lambda c: f"U{c['U']}T{c['T']}N{c['N']}")
@@ -68,7 +86,7 @@ def test_indexer_matches_oracle(case):
     w = gen.Workload("idx", 101, U=case["U"], T=case["T"], N=case["N"], H=16, K=64,
                      heavy_frac=case.get("heavy", 0.0))
     x = gen.make_config(w, seed=1)
-    nv = np.array(case["nv"], dtype=np.int32) if case["nv"] is not None else np.full((w.U, w.T), w.N, np.int32)
+    nv = _indexer_nv(case, w.U, w.T, w.N)
     d = upload(x)
     got = ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=torch.from_numpy(nv).cuda()).cpu().numpy()
     for u in range(w.U):
