@@ -24,6 +24,14 @@ namespace ds4a {
 
 namespace {
 
+// max(x, 0) as one integer max on the bit pattern (negative floats, -0 included, have
+// negative int bits): no NaN-quieting pass, which fmaxf needs in IEEE mode.  MFMA outputs
+// of finite inputs are finite.
+__device__ __forceinline__ float relu(float x) {
+    const int b = __float_as_int(x);
+    return __int_as_float(b > 0 ? b : 0);
+}
+
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kThreads = 256;
@@ -105,7 +113,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 #pragma unroll
                 for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(kb[bi][s]), aq[ht][s], d);
 #pragma unroll
-                for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * fmaxf(d[r], 0.f);
+                for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * relu(d[r]);
             }
             // Sum over the 16 heads of each row: the 16 lanes of a DPP row.
 #pragma unroll
@@ -133,8 +141,9 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 // owns 8 consecutive queries and a contiguous range of 128-row key tiles; each key tile is
 // read from HBM once into LDS and used by all 8 waves (one query each), so keys are read
 // T/8 times instead of T times.  Per wave and tile: 8 row blocks x 4 head tiles x 4 k-steps
-// = 128 v_mfma_f32_16x16x32_bf16 (keys as A from LDS, query as B in VGPRs), then the same
-// ReLU + weighted head sum as above.  LDS rows are 256 B with 16-byte chunks XOR-swizzled
+// = 128 v_mfma_f32_16x16x32_bf16 with the query as A (VGPRs) and the keys as B (LDS), so a
+// lane's D values are 4 heads of one row: ReLU and weighting are in-lane FMAs and only the
+// 4 lane groups need a cross-lane sum, once per tile.  LDS rows are 256 B with 16-byte chunks XOR-swizzled
 // by the row's low 4 bits, so the 16 rows one A-fragment read touches hit distinct banks.
 constexpr int kPQ = 8;                         // queries per workgroup (one per wave)
 constexpr int kPThreads = kPQ * kWave;
@@ -188,9 +197,12 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
         for (int s = 0; s < 4; ++s) qf[ht][s] = gq[(16 * ht + c) * kChunksPerRow + 4 * s + g];
-    float wh[4];
+    // Head weights of the D rows this lane holds: head 16ht + 4g + r.
+    float wh[4][4];
 #pragma unroll
-    for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
+    for (int ht = 0; ht < 4; ++ht)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) wh[ht][r] = w[q * kHeads + 16 * ht + 4 * g + r];
 
     // Tile staging: thread tid moves chunks 4(tid%4) .. +3 of tile row tid/4 (64 B).
     const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
@@ -221,26 +233,39 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
         const int64_t trow0 = tile * kPTile;
         if (active) {
             const unsigned char *tb = s_k + buf * kPTileBytes;
+            // D[head 16ht + 4g + r][row 16rb + c] (A = query, B = keys): the head sum is mostly
+            // in-lane; the 4 lane groups g are added once per tile.
+            float part[kPTile / 16];
 #pragma unroll
             for (int rb = 0; rb < kPTile / 16; ++rb) {
-                u32x4 a[4];
+                u32x4 b[4];
 #pragma unroll
-                for (int s = 0; s < 4; ++s) a[s] = *reinterpret_cast<const u32x4 *>(tb + a_off[s] + rb * 16 * 256);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const u32x4 *>(tb + a_off[s] + rb * 16 * 256);
+                float acc = 0.f;
 #pragma unroll
                 for (int ht = 0; ht < 4; ++ht) {
                     f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(a[s]), as_bf16x8(qf[ht][s]), d);
+                    for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(qf[ht][s]), as_bf16x8(b[s]), d);
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * fmaxf(d[r], 0.f);
+                    for (int r = 0; r < 4; ++r) acc += wh[ht][r] * relu(d[r]);
                 }
+                part[rb] = acc;
+            }
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    acc[r] = row16_sum(acc[r]);
-                    if (trow0 + rb * 16 + 4 * g + r >= nv) acc[r] = -INFINITY;
-                }
-                if (c == 0) *reinterpret_cast<f32x4 *>(&s_sc[wave][rb * 16 + 4 * g]) = acc;
+            for (int rb = 0; rb < kPTile / 16; ++rb) {
+                part[rb] = wave_xor_sum(part[rb], 16);
+                part[rb] = wave_xor_sum(part[rb], 32);
+            }
+            // lane (g, c) stores rows 16rb + c of blocks rb = 2g, 2g + 1
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int rb = 2 * g + k;
+                float v = part[0];
+#pragma unroll
+                for (int i = 1; i < kPTile / 16; ++i) v = rb == i ? part[i] : v;
+                if (trow0 + rb * 16 + c >= nv) v = -INFINITY;
+                s_sc[wave][rb * 16 + c] = v;
             }
         }
         if (tile + 1 < tile1) store_tile(buf ^ 1);
