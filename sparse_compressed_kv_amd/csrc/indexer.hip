@@ -137,18 +137,21 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 
 // ---------------------------------------------------------------- many queries per unit
 
-// Prefill shape (T >= 8 queries of one unit share the same keys).  A workgroup of 8 waves
-// owns 8 consecutive queries and a contiguous range of 128-row key tiles; each key tile is
-// read from HBM once into LDS and used by all 8 waves (one query each), so keys are read
-// T/8 times instead of T times.  Per wave and tile: 8 row blocks x 4 head tiles x 4 k-steps
-// = 128 v_mfma_f32_16x16x32_bf16 with the query as A (VGPRs) and the keys as B (LDS), so a
+// Prefill shape (T >= 4 queries of one unit share the same keys).  A workgroup of 4 waves
+// owns 4 consecutive queries and a contiguous range of 64-row key tiles; each key tile is
+// read once into LDS and used by all 4 waves (one query each), so keys are read T/4 times
+// instead of T times (the repeats hit L2).  Small workgroups let three share a CU, so one
+// waiting at its barrier leaves the MFMA pipes to the others.  Per wave and tile: 4 row
+// blocks x 4 head tiles x 4 k-steps = 64 v_mfma_f32_16x16x32_bf16 with the query as A (VGPRs) and the keys as B (LDS), so a
 // lane's D values are 4 heads of one row: ReLU and weighting are in-lane FMAs and only the
 // 4 lane groups need a cross-lane sum, once per tile.  LDS rows are 256 B with 16-byte chunks XOR-swizzled
 // by the row's low 4 bits, so the 16 rows one A-fragment read touches hit distinct banks.
-constexpr int kPQ = 8;                         // queries per workgroup (one per wave)
+constexpr int kPQ = 4;                         // queries per workgroup (one per wave)
 constexpr int kPThreads = kPQ * kWave;
-constexpr int kPTile = 128;                    // key rows per tile
-constexpr int kPTileBytes = kPTile * kDim * 2; // 32 KiB
+constexpr int kPTile = 64;                     // key rows per tile (4 threads stage a row)
+constexpr int kPTileBytes = kPTile * kDim * 2; // 16 KiB
+constexpr int kPRB = kPTile / 16;              // 16-row blocks per tile
+static_assert(kPThreads == 4 * kPTile && kPRB % 4 == 0, "staging and score-store mappings");
 
 __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
     int T, int64_t N, int n_qb, int n_split,
@@ -235,35 +238,42 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
             const unsigned char *tb = s_k + buf * kPTileBytes;
             // D[head 16ht + 4g + r][row 16rb + c] (A = query, B = keys): the head sum is mostly
             // in-lane; the 4 lane groups g are added once per tile.
-            float part[kPTile / 16];
+            float part[kPRB];
 #pragma unroll
-            for (int rb = 0; rb < kPTile / 16; ++rb) {
+            for (int rb = 0; rb < kPRB; ++rb) {
                 u32x4 b[4];
 #pragma unroll
                 for (int s = 0; s < 4; ++s) b[s] = *reinterpret_cast<const u32x4 *>(tb + a_off[s] + rb * 16 * 256);
-                float acc = 0.f;
+                // four independent accumulation chains (one per head tile), k-step outermost
+                f32x4 d[4];
+#pragma unroll
+                for (int ht = 0; ht < 4; ++ht) d[ht] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int ht = 0; ht < 4; ++ht) d[ht] = mfma16(as_bf16x8(qf[ht][s]), as_bf16x8(b[s]), d[ht]);
+                __builtin_amdgcn_sched_barrier(0);   // keep the 4 chains interleaved as written
+                float acc[4];
 #pragma unroll
                 for (int ht = 0; ht < 4; ++ht) {
-                    f32x4 d = {0.f, 0.f, 0.f, 0.f};
+                    acc[ht] = wh[ht][0] * relu(d[ht][0]);
 #pragma unroll
-                    for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(qf[ht][s]), as_bf16x8(b[s]), d);
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) acc += wh[ht][r] * relu(d[r]);
+                    for (int r = 1; r < 4; ++r) acc[ht] += wh[ht][r] * relu(d[ht][r]);
                 }
-                part[rb] = acc;
+                part[rb] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
             }
 #pragma unroll
-            for (int rb = 0; rb < kPTile / 16; ++rb) {
+            for (int rb = 0; rb < kPRB; ++rb) {
                 part[rb] = wave_xor_sum(part[rb], 16);
                 part[rb] = wave_xor_sum(part[rb], 32);
             }
-            // lane (g, c) stores rows 16rb + c of blocks rb = 2g, 2g + 1
+            // lane (g, c) stores row 16rb + c of blocks rb = (kPRB/4) g + k
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                const int rb = 2 * g + k;
+            for (int k = 0; k < kPRB / 4; ++k) {
+                const int rb = (kPRB / 4) * g + k;
                 float v = part[0];
 #pragma unroll
-                for (int i = 1; i < kPTile / 16; ++i) v = rb == i ? part[i] : v;
+                for (int i = 1; i < kPRB; ++i) v = rb == i ? part[i] : v;
                 if (trow0 + rb * 16 + c >= nv) v = -INFINITY;
                 s_sc[wave][rb * 16 + c] = v;
             }
@@ -297,8 +307,8 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
     if (T >= kPQ) {
         const int n_qb = (T + kPQ - 1) / kPQ;
         const int64_t wgs = (int64_t)U * n_qb;
-        // about two workgroups per CU in all, never a split shorter than 4 tiles
-        int n_split = (int)((512 + wgs - 1) / wgs);
+        // about three workgroups per CU in all, never a split shorter than 4 tiles
+        int n_split = (int)((768 + wgs - 1) / wgs);
         const int64_t max_split = (N + 4 * kPTile - 1) / (4 * kPTile);
         if (n_split > max_split) n_split = (int)max_split;
         if (n_split < 1) n_split = 1;
