@@ -1,8 +1,9 @@
 #!/usr/bin/env python3
 """Benchmark of one layer's compressed sparse attention step on one MI355X.
 
-One step = the whole hot path over one batch: indexer scores -> top-k ->
-RoPE + sparse multi-query attention, for every unit of the workload.
+One step = the whole hot path over one batch: indexer scores + top-k (one
+ds4a_indexer_topk call) -> RoPE + sparse multi-query attention (ds4a_sparse_mqa),
+for every unit of the workload.
 
 Main line: decode at the DeepSeek V4 Flash shape, 43 independent layers with
 N = 65,536 compressed rows each (64 query heads x 512 dims, one KV head,
@@ -33,8 +34,11 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 LLC_BYTES = 256 << 20        # Infinity Cache
 METRIC = "sparse-attn decode tokens/s/layer at 64K rows; prefill query-tok/s; % HBM/MFMA peak"
-INDEXER_SOURCES = ["sparse_compressed_kv_amd/csrc/indexer.hip", "sparse_compressed_kv_amd/csrc/common.hpp"]
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_decode_43layers_n65536_traffic.json")
+# device code behind ds4a_indexer_topk in decode shapes (the step's dominant call)
+SELECT_SOURCES = ["sparse_compressed_kv_amd/csrc/fused.hip", "sparse_compressed_kv_amd/csrc/indexer_core.hpp",
+                  "sparse_compressed_kv_amd/csrc/select.hpp", "sparse_compressed_kv_amd/csrc/topk.hip",
+                  "sparse_compressed_kv_amd/csrc/common.hpp"]
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "indexer_topk_decode_43layers_n65536_traffic.json")
 
 
 def log(*a):
@@ -45,6 +49,12 @@ def indexer_bytes_per_unit(N: int, T: int = 1) -> int:
     """Algorithmic HBM bytes of the indexer for one unit: keys read once, the query block and
     head weights read, scores written."""
     return N * 128 * 2 + T * (64 * 128 * 2 + 64 * 4) + T * N * 4
+
+
+def select_bytes_per_unit(N: int, K: int) -> int:
+    """Algorithmic HBM bytes of the fused A1 + A2 call for one decode unit: keys read once, the
+    query block and head weights read, the K selected rows written."""
+    return N * 128 * 2 + 64 * 128 * 2 + 64 * 4 + K * 4
 
 
 def decode_bytes_per_unit(N: int, H: int, K: int, W: int = 128) -> int:
@@ -86,7 +96,8 @@ def upload(x: dict) -> dict:
 
 
 class Bench:
-    """Device-resident replicas of one workload, and timed steps over them."""
+    """Device-resident replicas of one workload, and timed steps over them.  A step is
+    ds4a_indexer_topk (A1 + A2) then ds4a_sparse_mqa (A3-A6)."""
 
     def __init__(self, w, x, replicas: int):
         import torch
@@ -95,20 +106,20 @@ class Bench:
 
         self.torch, self.ops, self.w = torch, ops, w
         self.reps = [upload(x) for _ in range(replicas)]
-        self.step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W)
+        self.step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=True)
+        self.sep = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=False)
         self.nvis = w.vis_base is not None
 
     def run(self, steps: int, warmup: int):
         torch, ops, w = self.torch, self.ops, self.w
-        st = self.step
+        st, sep = self.step, self.sep
         stream = torch.cuda.current_stream()
         n = len(self.reps)
 
         def one(i):
             d = self.reps[i % n]
             nv = d["n_vis"] if self.nvis else None
-            ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv, out=st.scores, stream=stream)
-            ops.topk_select(st.scores, w.K, n_vis=nv, out=st.idx, workspace=st.ws_topk, stream=stream)
+            st.select(d, n_vis=nv, stream=stream)
             ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W, out=st.out,
                            workspace=st.ws_mqa, stream=stream)
 
@@ -127,18 +138,20 @@ class Bench:
         torch.cuda.synchronize()
         wall = time.perf_counter() - wall0
         total_ms = t_begin.elapsed_time(t_end)
-        # Per-call averages for the roofline: each call launched `steps` times back to back on
-        # the launch stream (inputs rotated as in the step), HIP events at the two ends only.
-        calls = [
-            lambda d, nv: ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv, out=st.scores,
-                                            stream=stream),
-            lambda d, nv: ops.topk_select(st.scores, w.K, n_vis=nv, out=st.idx, workspace=st.ws_topk,
-                                          stream=stream),
-            lambda d, nv: ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta,
-                                         W=w.W, out=st.out, workspace=st.ws_mqa, stream=stream),
-        ]
-        k_ms = []
-        for call in calls:
+        # Per-call averages: each call launched `steps` times back to back on the launch stream
+        # (inputs rotated as in the step), HIP events at the two ends only.  The separate A1 and
+        # A2 calls are timed too, for comparison with the fused call the step uses.
+        calls = {
+            "select": lambda d, nv: st.select(d, n_vis=nv, stream=stream),
+            "mqa": lambda d, nv: ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta,
+                                                W=w.W, out=st.out, workspace=st.ws_mqa, stream=stream),
+            "indexer": lambda d, nv: ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv,
+                                                       out=sep.scores, stream=stream),
+            "topk": lambda d, nv: ops.topk_select(sep.scores, w.K, n_vis=nv, out=sep.idx, workspace=sep.ws_topk,
+                                                  stream=stream),
+        }
+        k_ms = {}
+        for name, call in calls.items():
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             torch.cuda.synchronize()
@@ -148,9 +161,9 @@ class Bench:
                 call(d, d["n_vis"] if self.nvis else None)
             e1.record(stream)
             torch.cuda.synchronize()
-            k_ms.append(e0.elapsed_time(e1) / steps)
+            k_ms[name] = e0.elapsed_time(e1) / steps
         return {"ms_per_step": total_ms / steps, "wall_ms_per_step": 1e3 * wall / steps,
-                "indexer_ms": k_ms[0], "topk_ms": k_ms[1], "mqa_ms": k_ms[2]}
+                **{f"{k}_ms": v for k, v in k_ms.items()}}
 
 
 def replicas_for(w) -> int:
@@ -179,8 +192,9 @@ def cpu_baseline(w, x, budget_s: float = 20.0):
 
 
 def traffic_for(kernel_hash: str, units: int):
-    """HBM bytes per indexer launch from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters, scaled by
-    the same counters' reading of a plain copy of known size; None if taken on other kernel code."""
+    """HBM bytes per ds4a_indexer_topk call from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters
+    (both kernels of the call), scaled by the same counters' reading of a plain copy of known size;
+    None if taken on other kernel code."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -229,9 +243,11 @@ def main():
     log(f"[bench] {w.name}: {r}")
     units = w.U * w.T
     value = units / (r["ms_per_step"] / 1e3)
+    sel_bytes = units * select_bytes_per_unit(w.N, w.K)
+    achieved = sel_bytes / (r["select_ms"] / 1e3) / 1e9
+    khash = source_hash(SELECT_SOURCES)
     idx_bytes = units * indexer_bytes_per_unit(w.N)
-    achieved = idx_bytes / (r["indexer_ms"] / 1e3) / 1e9
-    khash = source_hash(INDEXER_SOURCES)
+    idx_gbs = idx_bytes / (r["indexer_ms"] / 1e3) / 1e9
     step_bytes = units * decode_bytes_per_unit(w.N, w.H, w.K, w.W)
     rec = {
         "metric": METRIC,
@@ -248,14 +264,16 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "units": w.U, "rows_per_unit": w.N, "query_heads": w.H, "head_dim": 512,
                    "top_k": w.K, "raw_window": w.W, "indexer": "64x128", "input_replicas": reps},
-        "roofline": {"kernel": "indexer_score_kernel", "bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic_for(khash, units), "algorithmic_bytes": idx_bytes,
-                     "avg_launch_us": r["indexer_ms"] * 1e3, "kernel_hash": khash},
+        "roofline": {"kernel": "ds4a_indexer_topk (indexer_select_kernel + topk_cand_kernel)", "bound": "hbm",
+                     "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic_for(khash, units), "algorithmic_bytes": sel_bytes,
+                     "avg_launch_us": r["select_ms"] * 1e3, "kernel_hash": khash},
+        "indexer_alone": {"kernel": "indexer_score_kernel", "achieved": idx_gbs, "frac": idx_gbs / HBM_PEAK_GBS,
+                          "algorithmic_bytes": idx_bytes, "avg_launch_us": r["indexer_ms"] * 1e3},
         "step": {"algorithmic_bytes": step_bytes, "GB_per_s": step_bytes / (r["ms_per_step"] / 1e3) / 1e9,
                  "frac_hbm": step_bytes / (r["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                 "kernel_us": {"indexer": r["indexer_ms"] * 1e3, "topk": r["topk_ms"] * 1e3,
-                               "mqa": r["mqa_ms"] * 1e3},
+                 "kernel_us": {"indexer_topk": r["select_ms"] * 1e3, "mqa": r["mqa_ms"] * 1e3,
+                               "indexer_alone": r["indexer_ms"] * 1e3, "topk_alone": r["topk_ms"] * 1e3},
                  "wall_ms_per_step": r["wall_ms_per_step"]},
     }
     del b
@@ -272,8 +290,10 @@ def main():
         rec["decode_n16384"] = {
             "workload": w2.name, "value": w2.U / (r2["ms_per_step"] / 1e3), "unit": "decode tokens/s/layer",
             "ms_per_step": r2["ms_per_step"], "frac_hbm": by2 / (r2["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "indexer_frac_hbm": w2.U * indexer_bytes_per_unit(w2.N) / (r2["indexer_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "kernel_us": {"indexer": r2["indexer_ms"] * 1e3, "topk": r2["topk_ms"] * 1e3, "mqa": r2["mqa_ms"] * 1e3},
+            "indexer_topk_frac_hbm": w2.U * select_bytes_per_unit(w2.N, w2.K) / (r2["select_ms"] / 1e3) / 1e9
+            / HBM_PEAK_GBS,
+            "kernel_us": {"indexer_topk": r2["select_ms"] * 1e3, "mqa": r2["mqa_ms"] * 1e3,
+                          "indexer_alone": r2["indexer_ms"] * 1e3, "topk_alone": r2["topk_ms"] * 1e3},
         }
         del b2, x2
         torch.cuda.empty_cache()
@@ -291,7 +311,8 @@ def main():
             "steps": steps3, "ms_per_step": r3["ms_per_step"], "algorithmic_flops": fl,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / MFMA_BF16_PEAK_TFLOPS},
-            "kernel_us": {"indexer": r3["indexer_ms"] * 1e3, "topk": r3["topk_ms"] * 1e3, "mqa": r3["mqa_ms"] * 1e3},
+            "kernel_us": {"indexer_topk": r3["select_ms"] * 1e3, "mqa": r3["mqa_ms"] * 1e3,
+                          "indexer_alone": r3["indexer_ms"] * 1e3, "topk_alone": r3["topk_ms"] * 1e3},
         }
         del b3, x3
 

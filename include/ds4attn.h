@@ -93,6 +93,21 @@ int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores,
                      const int32_t *n_vis, int32_t *idx,
                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* A1 + A2 in one call (section 3-3: the indexer's scores serve only to pick the
+ * rows that reach the main attention).  idx receives exactly the set that
+ * ds4a_topk_select returns on the scores of ds4a_indexer_score for the same
+ * arguments (the scores are computed by the same device code, bit for bit).
+ * With T < 4 the scores never reach memory: each 4096-row chunk of a query is
+ * scored and its top-K selected on chip, and only (score, row) candidates are
+ * kept in the workspace; with T >= 4 the scores are written to the workspace.
+ * Arguments as for ds4a_indexer_score and ds4a_topk_select.
+ *   workspace: ds4a_workspace_bytes(2, U, T, N, K, 0, 0) bytes (0 -> NULL allowed)
+ */
+int ds4a_indexer_topk(int U, int T, int64_t N, int Hi, int Di, int K,
+                      const void *idx_q, const float *idx_w, const void *idx_k,
+                      const int32_t *n_vis, int32_t *idx,
+                      void *workspace, size_t workspace_bytes, void *stream);
+
 /* A3-A6 — sparse multi-query attention over the raw window plus the selected
  * rows (sections 2 and 3; the raw window keeps f16-rounded values, section 3-1).
  * For unit u, query t, head h:
@@ -103,9 +118,10 @@ int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores,
  *             for every idx entry in [0, N) (no de-duplication)
  *   l_r     = scale * <q', row_r>                  (A4; each row is key and value)
  *   out     = sum_r softmax(l)_r * row_r           (A5, A6: one softmax over the union)
- * An empty union gives zeros.  MFMA operands are bf16; operands that are not
- * bf16 (the fp32 query, the f16 raw rows, the probabilities) are carried as
- * hi + lo bf16 pairs; accumulation is fp32.
+ * An empty union gives zeros.  Rows enter the MFMAs in their stored type (bf16
+ * compressed rows, f16 raw rows); the query and the probabilities are carried as
+ * hi + lo pairs of that type (a bf16 query only in its rotated tail); accumulation
+ * is fp32.
  *   H        : query heads, a multiple of 16 up to 128      D, n_rot : 512, 64
  *   W        : raw window rows, a multiple of 32, 0..1024     K : 1..DS4A_MAX_TOPK
  *   q        : [U][T][H][D], q_dtype DS4A_F32 or DS4A_BF16 (pre-RoPE)
@@ -127,9 +143,10 @@ int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int
 int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtype,
                 const int64_t *q_pos, double rope_theta, float *q_out, void *stream);
 
-/* Workspace bytes for `which` = 0 (ds4a_topk_select; H and W ignored) or
- * 1 (ds4a_sparse_mqa).  0 means no workspace is needed (NULL is accepted), or
- * that the arguments are invalid.  Host-only, never touches the GPU. */
+/* Workspace bytes for `which` = 0 (ds4a_topk_select; H and W ignored),
+ * 1 (ds4a_sparse_mqa) or 2 (ds4a_indexer_topk; H and W ignored).  0 means no
+ * workspace is needed (NULL is accepted), or that the arguments are invalid.
+ * Host-only, never touches the GPU. */
 size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W);
 
 /* Text of the last non-zero status returned on the calling thread (host memory

@@ -89,6 +89,7 @@ const char *ds4a_last_error(void) { return g_err; }
 size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W) {
     if (U < 1 || T < 1 || N < 1 || N > kMaxRows || K < 1 || K > DS4A_MAX_TOPK) return 0;
     if (which == 0) return ds4a::topk_workspace_bytes((int64_t)U * T, N, K);
+    if (which == 2) return ds4a::indexer_topk_workspace_bytes(U, T, N, K);
     if (which == 1) {
         if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW) return 0;
         return ds4a::plan_mqa(U, T, H, W, K).workspace_bytes;
@@ -131,6 +132,33 @@ int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores, const 
     }
     return hip_status(fn, ds4a::launch_topk((int64_t)U * T, N, K, scores, n_vis, idx, workspace,
                                             static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_indexer_topk(int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q, const float *idx_w,
+                      const void *idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
+                      size_t workspace_bytes, void *stream) {
+    const char *fn = "ds4a_indexer_topk";
+    if (int rc = check_units(fn, U, T, N)) return rc;
+    if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
+        return fail(DS4A_E_UNSUPPORTED, "%s: Hi=%d Di=%d (only %d x %d)", fn, Hi, Di, DS4A_INDEXER_HEADS,
+                    DS4A_INDEXER_DIM);
+    if (K < 1) return fail(DS4A_E_SHAPE, "%s: K=%d must be >= 1", fn, K);
+    if (K > DS4A_MAX_TOPK) return fail(DS4A_E_UNSUPPORTED, "%s: K=%d (at most %d)", fn, K, DS4A_MAX_TOPK);
+    REQUIRE_PTR(idx_q);
+    REQUIRE_PTR(idx_w);
+    REQUIRE_PTR(idx_k);
+    REQUIRE_PTR(idx);
+    OPTIONAL_PTR(n_vis);
+    const size_t need = ds4a::indexer_topk_workspace_bytes(U, T, N, K);
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, ds4a::launch_indexer_topk(U, T, N, K, static_cast<const uint16_t *>(idx_q), idx_w,
+                                                    static_cast<const uint16_t *>(idx_k), n_vis, idx, workspace,
+                                                    static_cast<hipStream_t>(stream)));
 }
 
 int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q, int q_dtype,

@@ -7,6 +7,9 @@
 
 namespace ds4a {
 
+// Units with at least this many queries take the many-queries (prefill) indexer.
+constexpr int kIndexerManyQueries = 4;
+
 // A1: scores f32 [Q][N], Q = U*T.
 hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w,
                           const uint16_t *idx_k, const int32_t *n_vis, float *scores,
@@ -16,6 +19,19 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
 size_t topk_workspace_bytes(int64_t Q, int64_t N, int K);
 hipError_t launch_topk(int64_t Q, int64_t N, int K, const float *scores, const int32_t *n_vis,
                        int32_t *idx, void *workspace, hipStream_t stream);
+// Chunked select: level-1 candidate lists ((key, row) pairs, K slots per chunk of `chunk` rows)
+// at the start of the workspace, then the merge levels down to idx.
+size_t topk_cand_workspace_bytes(int64_t Q, int64_t chunks, int K);
+void topk_level1_buffers(void *workspace, int64_t Q, int64_t chunks, int K, uint32_t **keys, int32_t **ids);
+hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chunks, const int32_t *n_vis,
+                             int32_t *idx, void *workspace, hipStream_t stream);
+
+// A1 + A2 fused: the selected set without materialising scores (decode shapes), or through
+// scores kept in the workspace (many queries per unit).
+size_t indexer_topk_workspace_bytes(int U, int T, int64_t N, int K);
+hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *idx_q, const float *idx_w,
+                               const uint16_t *idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
+                               hipStream_t stream);
 
 // A3-A6
 struct MqaPlan {

@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
     L.ds4a_indexer_score.restype = i32
     L.ds4a_topk_select.argtypes = [i32, i32, i64, i32, P, P, P, P, sz, P]
     L.ds4a_topk_select.restype = i32
+    L.ds4a_indexer_topk.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, P, sz, P]
+    L.ds4a_indexer_topk.restype = i32
     L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
     L.ds4a_sparse_mqa.restype = i32
     L.ds4a_rope_q.argtypes = [i32, i32, i32, i32, i32, P, i32, P, dbl, P, P]
@@ -148,6 +150,25 @@ def topk_select(scores, K: int, n_vis=None, out=None, workspace=None, stream=Non
     return out
 
 
+def indexer_topk(idx_q, idx_w, idx_k, K: int, n_vis=None, out=None, workspace=None, stream=None):
+    """A1 + A2 in one call: the selected rows int32 [U,T,K] that topk_select would return on
+    indexer_score's scores, without writing the scores (decode shapes)."""
+    _need(idx_q, "idx_q", torch.bfloat16)
+    U, T, Hi, Di = idx_q.shape
+    N = idx_k.shape[1]
+    _need(idx_w, "idx_w", torch.float32, (U, T, Hi))
+    _need(idx_k, "idx_k", torch.bfloat16, (U, N, Di))
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    if out is None:
+        out = torch.empty((U, T, K), dtype=torch.int32, device=idx_q.device)
+    _need(out, "out", torch.int32, (U, T, K))
+    ws, nb = _workspace(workspace_bytes(2, U, T, N, K), idx_q.device, workspace)
+    _check("ds4a_indexer_topk", lib().ds4a_indexer_topk(U, T, N, Hi, Di, K, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k),
+                                                        _ptr(n_vis), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    return out
+
+
 def _q_dtype(q):
     if q.dtype == torch.float32:
         return DS4A_F32
@@ -199,22 +220,34 @@ def rope_q(q, q_pos, theta: float = 10000.0, out=None, stream=None):
 
 class Step:
     """The whole hot path for fixed shapes: indexer -> top-k -> attention, with every
-    intermediate, output and workspace allocated once up front."""
+    intermediate, output and workspace allocated once up front.  fused=True runs A1 + A2
+    as ds4a_indexer_topk (no score buffer in decode shapes); fused=False runs the separate
+    calls and keeps the scores in self.scores."""
 
-    def __init__(self, U, T, N, H=64, K=512, W=128, q_dtype=torch.float32, device="cuda"):
+    def __init__(self, U, T, N, H=64, K=512, W=128, q_dtype=torch.float32, device="cuda", fused=False):
         self.U, self.T, self.N, self.H, self.K, self.W = U, T, N, H, K, W
+        self.fused = fused
         dev = torch.device(device)
-        self.scores = torch.empty((U, T, N), dtype=torch.float32, device=dev)
+        self.scores = None if fused else torch.empty((U, T, N), dtype=torch.float32, device=dev)
         self.idx = torch.empty((U, T, K), dtype=torch.int32, device=dev)
         self.out = torch.empty((U, T, H, 512), dtype=torch.float32, device=dev)
-        nb0 = workspace_bytes(0, U, T, N, K)
+        nb0 = workspace_bytes(2 if fused else 0, U, T, N, K)
         nb1 = workspace_bytes(1, U, T, N, K, H, W)
         self.ws_topk = torch.empty(max(nb0, 1), dtype=torch.uint8, device=dev)
         self.ws_mqa = torch.empty(max(nb1, 1), dtype=torch.uint8, device=dev)
 
+    def select(self, x: dict, n_vis=None, stream=None):
+        """A1 + A2 into self.idx."""
+        if self.fused:
+            indexer_topk(x["idx_q"], x["idx_w"], x["idx_k"], self.K, n_vis=n_vis, out=self.idx,
+                         workspace=self.ws_topk, stream=stream)
+        else:
+            indexer_score(x["idx_q"], x["idx_w"], x["idx_k"], n_vis=n_vis, out=self.scores, stream=stream)
+            topk_select(self.scores, self.K, n_vis=n_vis, out=self.idx, workspace=self.ws_topk, stream=stream)
+        return self.idx
+
     def __call__(self, x: dict, n_vis=None, scale=1.0 / 512 ** 0.5, theta=10000.0, stream=None):
-        indexer_score(x["idx_q"], x["idx_w"], x["idx_k"], n_vis=n_vis, out=self.scores, stream=stream)
-        topk_select(self.scores, self.K, n_vis=n_vis, out=self.idx, workspace=self.ws_topk, stream=stream)
+        self.select(x, n_vis=n_vis, stream=stream)
         sparse_mqa(x["q"], x["pos"], x["raw"], x["comp"], self.idx, scale, theta, W=self.W, out=self.out,
                    workspace=self.ws_mqa, stream=stream)
         return self.out

@@ -18,8 +18,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = ops.declared_symbols()
-    assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_sparse_mqa", "ds4a_rope_q", "ds4a_workspace_bytes",
-            "ds4a_last_error", "ds4a_version"} <= set(names)
+    assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_rope_q",
+            "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -56,6 +56,23 @@ def test_topk_validation(L):
     assert f(2, 1, 65536, 512, A, None, A, A, need - 1, S) == -5
     assert "workspace" in ops.last_error()
     assert f(2, 1, 65536, 512, A, None, A, MIS, need, S) == -4
+
+
+def test_indexer_topk_validation(L):
+    f = L.ds4a_indexer_topk
+    assert f(0, 1, 10, 64, 128, 8, A, A, A, None, A, None, 0, S) == -2
+    assert f(1, 1, 10, 32, 128, 8, A, A, A, None, A, None, 0, S) == -3
+    assert f(1, 1, 10, 64, 128, 0, A, A, A, None, A, None, 0, S) == -2
+    assert f(1, 1, 10, 64, 128, 4096, A, A, A, None, A, None, 0, S) == -3
+    assert f(1, 1, 10, 64, 128, 8, None, A, A, None, A, None, 0, S) == -1
+    assert f(1, 1, 10, 64, 128, 8, A, A, A, None, None, None, 0, S) == -1
+    assert f(1, 1, 10, 64, 128, 8, A, A, A, MIS, A, None, 0, S) == -4
+    # more than one 8192-row chunk: candidate lists need a workspace
+    need = ops.workspace_bytes(2, 2, 1, 65536, 512)
+    assert need > 0
+    assert f(2, 1, 65536, 64, 128, 512, A, A, A, None, A, None, 0, S) == -5
+    assert f(2, 1, 65536, 64, 128, 512, A, A, A, None, A, A, need - 1, S) == -5
+    assert f(2, 1, 65536, 64, 128, 512, A, A, A, None, A, MIS, need, S) == -4
 
 
 def _mqa(L, **kw):
@@ -103,6 +120,9 @@ def test_workspace_bytes(L):
     assert ops.workspace_bytes(2, 1, 1, 10, 10) == 0
     assert ops.workspace_bytes(1, 1, 2048, 8192, 512, 64, 128) == 0   # prefill: no split
     assert ops.workspace_bytes(1, 1, 1, 10, 512, 64, 100) == 0        # invalid W
+    assert ops.workspace_bytes(2, 43, 1, 4096, 512) == 0             # fused: one chunk, no candidates
+    assert ops.workspace_bytes(2, 43, 1, 65536, 512) >= 2 * 43 * 16 * 512 * 8  # 16 chunks of candidates
+    assert ops.workspace_bytes(2, 1, 2048, 8192, 512) >= 2048 * 8192 * 4       # many queries: scores
 
 
 def test_last_error_is_text(L):

@@ -150,6 +150,48 @@ def test_topk_bit_exact_on_identical_scores(Q, N, K, pattern):
         assert np.all(got[i, 0, n_sel:] == -1)
 
 
+# ------------------------------------------------------- fused indexer + top-k
+
+FUSED_CASES = [
+    dict(U=3, T=1, N=1, K=1, nv=None),
+    dict(U=2, T=1, N=8192, K=512, nv=None),
+    dict(U=3, T=1, N=8193, K=512, nv=[[8193], [0], [300]]),
+    dict(U=4, T=1, N=65536, K=512, nv=None, heavy=0.01),
+    dict(U=2, T=1, N=65537, K=1024, nv=[[65537], [40000]]),
+    dict(U=1, T=1, N=262144, K=512, nv=None),
+    dict(U=1, T=2, N=100000, K=2048, nv=[[100000, 2047]]),
+    dict(U=2, T=3, N=20000, K=7, nv=None),
+    dict(U=1, T=5, N=3000, K=64, nv=[[0, 1, 64, 2999, 3000]]),
+]
+
+
+@pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"U{c['U']}T{c['T']}N{c['N']}K{c['K']}")
+def test_indexer_topk_equals_separate_calls(case):
+    """ds4a_indexer_topk returns exactly topk_select(indexer_score(...)): same bits, same set."""
+    w = gen.Workload("fus", 105, U=case["U"], T=case["T"], N=case["N"], H=16, K=case["K"],
+                     heavy_frac=case.get("heavy", 0.0))
+    x = gen.make_config(w, seed=2)
+    nv = (np.array(case["nv"], dtype=np.int32) if case["nv"] is not None
+          else np.full((w.U, w.T), w.N, np.int32))
+    d = upload(x)
+    nvd = torch.from_numpy(nv).cuda()
+    scores = ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nvd)
+    ref = ops.topk_select(scores, w.K, n_vis=nvd)
+    got = torch.full_like(ref, -7)
+    ops.indexer_topk(d["idx_q"], d["idx_w"], d["idx_k"], w.K, n_vis=nvd, out=got)
+    assert torch.equal(got, ref)
+
+
+def test_indexer_topk_all_tied():
+    """Every score equal (zero query): the set is rows 0..K-1 across chunk boundaries."""
+    w = gen.Workload("fut", 106, U=2, T=1, N=30000, H=16, K=512)
+    x = gen.make_config(w, seed=3)
+    x["idx_q"][:] = 0
+    d = upload(x)
+    got = ops.indexer_topk(d["idx_q"], d["idx_w"], d["idx_k"], w.K).cpu().numpy()
+    assert np.array_equal(got[:, 0], np.broadcast_to(np.arange(512, dtype=np.int32), (2, 512)))
+
+
 # -------------------------------------------------------------- attention
 
 def _mqa_case(H, q_dtype, W, N, K, seed, U=2, T=2):
@@ -234,9 +276,10 @@ def test_mqa_empty_union_is_zero():
 
 # -------------------------------------------------------------- end to end
 
-def _run_step(w, d, nv=True):
-    step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W)
-    step.scores.fill_(float("nan"))
+def _run_step(w, d, nv=True, fused=False):
+    step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=fused)
+    if step.scores is not None:
+        step.scores.fill_(float("nan"))
     step.idx.fill_(-7)
     step.out.fill_(float("nan"))
     step(d, n_vis=d["n_vis"] if nv else None, scale=w.scale, theta=w.theta)
@@ -246,17 +289,19 @@ def _run_step(w, d, nv=True):
 
 def _check_e2e(w, x, step, sel, nthreads=8):
     ref = orc.step(w, x, sel=sel, nthreads=nthreads)
-    scores = step.scores.cpu().numpy().reshape(w.U * w.T, w.N)
+    scores = None if step.scores is None else step.scores.cpu().numpy().reshape(w.U * w.T, w.N)
     idx = step.idx.cpu().numpy().reshape(w.U * w.T, w.K)
     out = step.out.cpu().numpy().reshape(w.U * w.T, w.H, 512)
-    assert not np.isnan(out).any() and not np.isnan(scores).any() and (idx != -7).all()
+    assert not np.isnan(out).any() and (idx != -7).all()
+    assert scores is None or not np.isnan(scores).any()
     compared, worst = 0, 0.0
     for i, ut in enumerate(sel):
         nv = int(x["n_vis"].reshape(-1)[ut])
         r = ref["scores"][i]
         vis = r[:nv]
-        assert np.all(np.isneginf(scores[ut, nv:]))
-        if nv:
+        if scores is not None:
+            assert np.all(np.isneginf(scores[ut, nv:]))
+        if nv and scores is not None:
             den = np.maximum(np.abs(vis), 1e-6 * np.abs(vis).max() + 1e-30)
             rel = np.abs(scores[ut, :nv].astype(np.float64) - vis) / den
             assert rel.max() <= 1e-5, (ut, float(rel.max()))
@@ -289,6 +334,17 @@ def test_e2e_c2_decode_43layers_full_size_sampled():
     step(d, n_vis=d["n_vis"], scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(step.scores, s1) and torch.equal(step.idx, i1) and torch.equal(step.out, o1)
+    # the fused A1 + A2 path gives the same set and so the same output, bit for bit
+    fs = _run_step(w, d, fused=True)
+    assert torch.equal(fs.idx, i1) and torch.equal(fs.out, o1)
+
+
+def test_e2e_c2_64k_decode_fused():
+    """The bench's main workload through the fused path, checked against the oracle."""
+    w = gen.CONFIGS["c2_64k"]
+    x = gen.make_config(w)
+    step = _run_step(w, upload(x), fused=True)
+    _check_e2e(w, x, step, sel=[0, 42])
 
 
 def test_e2e_c3_prefill_full_size_sampled():
