@@ -23,6 +23,7 @@ namespace {
 constexpr int kFRows = 4096;                  // rows per workgroup = 8 keys x 512 threads
 constexpr int kFEpt = kFRows / kNT;
 constexpr int kFWaves = kNT / kWave;
+constexpr int kFBpi = 2;                      // 16-row blocks in flight per wave
 
 __global__ __launch_bounds__(kNT) void indexer_select_kernel(
     int T, int64_t N, int K, int64_t chunks,
@@ -50,7 +51,7 @@ __global__ __launch_bounds__(kNT) void indexer_select_kernel(
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
         const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
-        indexer_score_rows<kFWaves>(aq, wh, gk, c0, c0 + n, wave, g, c, s_sc);
+        indexer_score_rows<kFWaves, kFBpi>(aq, wh, gk, c0, c0 + n, wave, g, c, s_sc);
     }
     __syncthreads();
 

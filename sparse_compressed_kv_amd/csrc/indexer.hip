@@ -53,7 +53,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
     const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
-    indexer_score_rows<kWaves>(aq, wh, gk, r0, rv1, wave, g, c, s_sc);
+    indexer_score_rows<kWaves, 2>(aq, wh, gk, r0, rv1, wave, g, c, s_sc);
 
     __syncthreads();
     const bool row_aligned = ((q * N) & 3) == 0;      // scores of this query start 16-byte aligned

@@ -4,8 +4,8 @@
 // Score (reading: ReLU between the per-head dot product and the weighted head sum):
 //     s[j] = sum_h w[h] * max(0, <qI[h], kI[j]>)
 // The query's 64x128 bf16 block sits in VGPRs as MFMA B fragments; key rows stream from
-// HBM straight into A-operand registers.  Each wave takes 32 consecutive rows (8 KiB) per
-// iteration: two 16-row blocks, all loads issued before either is used, each row read as
+// HBM straight into A-operand registers.  Each wave takes 16*BPI consecutive rows per
+// iteration: BPI 16-row blocks, all loads issued before any is used, each row read as
 // 4 x 64-byte contiguous segments.  Per 16-row block: 4 head tiles x 4 k-steps = 16
 // v_mfma_f32_16x16x32_bf16 with the keys as A, so D holds 4 rows x 1 head per lane; the fp32
 // ReLU + weighted head sum is 16 in-lane FMAs plus a 4-step DPP butterfly across the 16
@@ -21,7 +21,6 @@ namespace {
 constexpr int kHeads = 64;
 constexpr int kDim = 128;
 constexpr int kChunksPerRow = kDim * 2 / 16;                   // 16-byte chunks per key row (16)
-constexpr int kBlocksPerIter = 2;                              // 16-row blocks per wave iteration
 
 // max(x, 0) as one integer max on the bit pattern (negative floats, -0 included, have
 // negative int bits): no NaN-quieting pass, which fmaxf needs in IEEE mode.  MFMA outputs
@@ -50,23 +49,25 @@ __device__ __forceinline__ void indexer_query_frags(const uint16_t *__restrict__
 }
 
 // Scores of the visible rows [r0, rv1) of one query into s_out[row - r0] (LDS), by the
-// WAVES waves of the workgroup; wh[ht] is the weight of head 16ht + c.
-template <int WAVES>
+// WAVES waves of the workgroup, BPI 16-row blocks per wave iteration (loads of all BPI
+// blocks issued first); wh[ht] is the weight of head 16ht + c.  A row's score does not
+// depend on WAVES or BPI.
+template <int WAVES, int BPI>
 __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], const float (&wh)[4],
                                                    const u32x4 *__restrict__ gk, int64_t r0, int64_t rv1,
                                                    int wave, int g, int c, float *s_out) {
-    constexpr int kRowsPerIter = 16 * kBlocksPerIter * WAVES;
-    for (int64_t base = r0 + 16 * kBlocksPerIter * wave; base < rv1; base += kRowsPerIter) {
-        u32x4 kb[kBlocksPerIter][4];
+    constexpr int kRowsPerIter = 16 * BPI * WAVES;
+    for (int64_t base = r0 + 16 * BPI * wave; base < rv1; base += kRowsPerIter) {
+        u32x4 kb[BPI][4];
 #pragma unroll
-        for (int bi = 0; bi < kBlocksPerIter; ++bi) {
+        for (int bi = 0; bi < BPI; ++bi) {
             const int64_t row = base + 16 * bi + c;
 #pragma unroll
             for (int s = 0; s < 4; ++s)
                 kb[bi][s] = row < rv1 ? gk[row * kChunksPerRow + 4 * s + g] : u32x4{0u, 0u, 0u, 0u};
         }
 #pragma unroll
-        for (int bi = 0; bi < kBlocksPerIter; ++bi) {
+        for (int bi = 0; bi < BPI; ++bi) {
             const int64_t blk = base + 16 * bi;
             if (blk >= rv1) break;                    // uniform across the wave
             // D[row 4g + r][head 16ht + c] = <key row, query head> (A = keys, B = query).
