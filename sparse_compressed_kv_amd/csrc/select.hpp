@@ -45,6 +45,30 @@ __device__ __forceinline__ int64_t cand_count(int64_t nv, int K, const Levels &l
     return c;
 }
 
+// Thread t receives src[t*EPT .. t*EPT + EPT - 1] (0 past n, n <= EPT*kNT, n uniform across
+// the workgroup) through an LDS stage of EPT*kNT words: the global loads are lane-consecutive
+// (one 256-byte run per wave instruction) and issued all at once; indices past n are clamped
+// to n - 1, so no load is conditional.  Every thread of the workgroup calls it.
+template <int EPT>
+__device__ __forceinline__ void load_blocked(const uint32_t *__restrict__ src, int n, uint32_t (&v)[EPT],
+                                             uint32_t *stage) {
+    if (n > 0) {
+        uint32_t x[EPT];
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const int j = (int)threadIdx.x + i * kNT;
+            x[i] = src[j < n ? j : n - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) stage[(int)threadIdx.x + i * kNT] = x[i];
+    }
+    __syncthreads();
+    const int j0 = (int)threadIdx.x * EPT;
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) v[i] = j0 + i < n ? stage[j0 + i] : 0u;
+    __syncthreads();
+}
+
 // Exclusive prefix sum over the workgroup.
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;

@@ -53,7 +53,8 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(int64_t N, int K, int ch
     const int n = rem <= 0 ? 0 : (rem < chunk ? (int)rem : chunk);
     const float *s = scores + q * N + c0;
     const int j0 = threadIdx.x * EPT;
-    // All loads of the thread's contiguous run are issued before any is used.
+    // All loads of the thread's contiguous run are issued before any is used (scores of one
+    // query are contiguous, so the run is a few full cache lines per thread).
     float v[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) v[i] = j0 + i < n ? s[j0 + i] : 0.f;
@@ -88,14 +89,15 @@ __global__ __launch_bounds__(kNT) void topk_cand_kernel(int64_t N, int K, Levels
     const int n = rem <= 0 ? 0 : (rem < chunk ? (int)rem : chunk);
     const uint32_t *ik = in_keys + q * in_stride + c0;
     const int32_t *ii = in_ids + q * in_stride + c0;
-    const int j0 = threadIdx.x * EPT;
+    __shared__ uint32_t stage[EPT * kNT];
     uint32_t key[EPT];
     int32_t id[EPT];
+    load_blocked<EPT>(ik, n, key, stage);
+    {
+        uint32_t tmp[EPT];
+        load_blocked<EPT>(reinterpret_cast<const uint32_t *>(ii), n, tmp, stage);
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        const bool in = j0 + i < n;
-        key[i] = in ? ik[j0 + i] : 0u;
-        id[i] = in ? ii[j0 + i] : -1;
+        for (int i = 0; i < EPT; ++i) id[i] = (int32_t)tmp[i];
     }
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + c) * K;
