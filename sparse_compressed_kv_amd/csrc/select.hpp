@@ -81,6 +81,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
     return off + incl - v;
 }
 
+template <int NT>
 __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     wave_minmax_u32(kmin, kmax);
@@ -91,7 +92,7 @@ __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
     __syncthreads();
     kmin = 0xFFFFFFFFu;
     kmax = 0u;
-    for (int i = 0; i < kNW; ++i) {
+    for (int i = 0; i < NT / kWave; ++i) {
         kmin = sm.wave_a[i] < kmin ? sm.wave_a[i] : kmin;
         kmax = sm.wave_b[i] > kmax ? sm.wave_b[i] : kmax;
     }
@@ -101,8 +102,8 @@ __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
 // Selects the `need` largest of the n keys held in registers (thread t holds positions
 // t*EPT .. t*EPT+EPT-1; ties go to the lower position) and writes their rows (id[i] if IDS, else
 // row0 + position) in ascending position order to out[0..need), then -1 up to K.  If out_keys,
-// the selected keys go there too.  Every thread of the workgroup calls it.
-template <int EPT, bool IDS>
+// the selected keys go there too.  Every thread of the NT-thread workgroup calls it.
+template <int EPT, bool IDS, int NT = kNT>
 __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int64_t row0, int n, int need,
                              int K, int32_t *out, uint32_t *out_keys, SelectShared &sm)
 {
@@ -118,7 +119,8 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
                 kmax = key[i] > kmax ? key[i] : kmax;
             }
         }
-        block_minmax(kmin, kmax, sm);
+        static_assert(NT % kWave == 0 && NT <= kNT && NT >= kWave * 2, "workgroup size");
+        block_minmax<NT>(kmin, kmax, sm);
         int bit = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
         uint32_t pmask = bit >= 32 ? 0u : ~((1u << bit) - 1u);
         uint32_t prefix = kmin & pmask;
@@ -128,7 +130,7 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
             const int width = bit < 8 ? bit : 8;
             const int shift = bit - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int b = threadIdx.x; b < kBins; b += kNT) sm.hist[b] = 0;
+            for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[b] = 0;
             __syncthreads();
 #pragma unroll
             for (int i = 0; i < EPT; ++i)
@@ -201,7 +203,7 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
     (void)lane;
     __syncthreads();
     const int taken = need > 0 ? need : 0;
-    for (int i = threadIdx.x; i < K; i += kNT) {
+    for (int i = threadIdx.x; i < K; i += NT) {
         out[i] = i < taken ? sm.sel_id[i] : -1;
         if (out_keys) out_keys[i] = i < taken ? sm.sel_key[i] : 0u;
     }
