@@ -9,7 +9,9 @@ Main line: decode at the DeepSeek V4 Flash shape, 43 independent layers with
 N = 65,536 compressed rows each (64 query heads x 512 dims, one KV head,
 128-row raw window, indexer 64 x 128, top-k 512).  `value` is decode
 tokens/s/layer = layer-units per second.  Also measured in the same run: the
-same decode at N = 16,384 rows, and chunked prefill (2,048 queries, N = 8,192).
+same decode at N = 16,384 rows, 8 sessions at N = 262,144, the Pro shape (4
+sessions, 128 heads, top-1024, N = 65,536), and chunked prefill (2,048 queries,
+N = 8,192).
 
 Inputs are synthetic (synth.inputs), uploaded to HBM before timing.  Several
 replicas of each input set are rotated step by step so that no step finds its
@@ -297,6 +299,24 @@ def main():
         }
         del b2, x2
         torch.cuda.empty_cache()
+        # ---- long context (8 sessions x 262,144 rows) and the Pro shape (128 heads, top-1024)
+        for key, name in (("c4", "decode_8sessions_n262144"), ("c5", "pro_decode_4sessions_n65536")):
+            w4 = gen.CONFIGS[key]
+            x4 = gen.make_config(w4)
+            b4 = Bench(w4, x4, replicas_for(w4))
+            r4 = b4.run(args.steps, args.warmup)
+            log(f"[bench] {w4.name}: {r4}")
+            by4 = w4.U * decode_bytes_per_unit(w4.N, w4.H, w4.K, w4.W)
+            rec[name] = {
+                "workload": w4.name, "value": w4.U / (r4["ms_per_step"] / 1e3), "unit": "decode tokens/s/layer",
+                "ms_per_step": r4["ms_per_step"], "frac_hbm": by4 / (r4["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                "indexer_topk_frac_hbm": w4.U * select_bytes_per_unit(w4.N, w4.K) / (r4["select_ms"] / 1e3) / 1e9
+                / HBM_PEAK_GBS,
+                "kernel_us": {"indexer_topk": r4["select_ms"] * 1e3, "mqa": r4["mqa_ms"] * 1e3,
+                              "indexer_alone": r4["indexer_ms"] * 1e3, "topk_alone": r4["topk_ms"] * 1e3},
+            }
+            del b4, x4
+            torch.cuda.empty_cache()
         # ---- chunked prefill: 2,048 queries, 8,192 rows
         w3 = gen.CONFIGS["c3"]
         x3 = gen.make_config(w3)

@@ -97,9 +97,10 @@ int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores,
  * rows that reach the main attention).  idx receives exactly the set that
  * ds4a_topk_select returns on the scores of ds4a_indexer_score for the same
  * arguments (the scores are computed by the same device code, bit for bit).
- * With T < 4 the scores never reach memory: each 4096-row chunk of a query is
- * scored and its top-K selected on chip, and only (score, row) candidates are
- * kept in the workspace; with T >= 4 the scores are written to the workspace.
+ * With T < 4 and at least 128 chunks of 4096 rows in the call, the scores never
+ * reach memory: each chunk of a query is scored and its top-K selected on chip,
+ * and only (score, row) candidates are kept in the workspace; otherwise the
+ * scores are written to the workspace and selected from there.
  * Arguments as for ds4a_indexer_score and ds4a_topk_select.
  *   workspace: ds4a_workspace_bytes(2, U, T, N, K, 0, 0) bytes (0 -> NULL allowed)
  */

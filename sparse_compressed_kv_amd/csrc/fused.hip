@@ -9,8 +9,9 @@
 // are merged as in the chunked top-k.  A chunk's own top-K contains every global
 // top-K row of that chunk (one total order: score, then lower row), so the
 // result is exactly the top-k of the full score vector.
-// Many queries per unit (prefill shapes) go through the score kernel into the
-// workspace and the top-k on it.
+// Many queries per unit (prefill shapes), and calls too small to fill the GPU
+// with chunk workgroups, go through the score kernel into the workspace and the
+// top-k on it.
 #include "common.hpp"
 #include "indexer_core.hpp"
 #include "launch.hpp"
@@ -74,13 +75,18 @@ __global__ __launch_bounds__(kNT) void indexer_select_kernel(
 
 int64_t fused_chunks(int64_t N) { return (N + kFRows - 1) / kFRows; }
 
+// The fused kernel needs enough chunk workgroups to stream the keys at full rate; with fewer
+// (a handful of units) the score kernel's smaller 1024-row chunks plus the separate top-k
+// are faster, and so are many queries per unit (prefill shapes).
+bool use_fused(int T, int64_t Q, int64_t N) { return T < kIndexerManyQueries && Q * fused_chunks(N) >= 128; }
+
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
 
 size_t indexer_topk_workspace_bytes(int U, int T, int64_t N, int K) {
     const int64_t Q = (int64_t)U * T;
-    if (T >= kIndexerManyQueries) return align256((size_t)Q * (size_t)N * 4) + topk_workspace_bytes(Q, N, K);
+    if (!use_fused(T, Q, N)) return align256((size_t)Q * (size_t)N * 4) + topk_workspace_bytes(Q, N, K);
     const int64_t chunks = fused_chunks(N);
     return chunks > 1 ? topk_cand_workspace_bytes(Q, chunks, K) : 0;
 }
@@ -90,7 +96,7 @@ hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *i
                                hipStream_t stream)
 {
     const int64_t Q = (int64_t)U * T;
-    if (T >= kIndexerManyQueries) {
+    if (!use_fused(T, Q, N)) {
         float *scores = static_cast<float *>(workspace);
         void *ws2 = static_cast<char *>(workspace) + align256((size_t)Q * (size_t)N * 4);
         hipError_t e = launch_indexer(U, T, N, idx_q, idx_w, idx_k, n_vis, scores, stream);

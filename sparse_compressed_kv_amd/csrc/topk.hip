@@ -156,8 +156,12 @@ hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chu
         int32_t *ti = ids_a; ids_a = ids_b; ids_b = ti;
     }
     if (stride > kMergeMax) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(topk_cand_kernel<24>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride, kMergeMax,
-                       (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
+    if (stride <= kLevelChunk)            // 16 candidates per thread suffice
+        hipLaunchKernelGGL(topk_cand_kernel<16>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride,
+                           kLevelChunk, (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
+    else
+        hipLaunchKernelGGL(topk_cand_kernel<24>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride, kMergeMax,
+                           (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
     return hipGetLastError();
 }
 

@@ -117,10 +117,11 @@ def test_workspace_bytes(L):
     assert ops.workspace_bytes(0, 2048, 1, 16384, 512) == 0          # many queries: still direct
     assert ops.workspace_bytes(0, 43, 1, 16384, 512) > 0             # chunked: candidate lists
     assert ops.workspace_bytes(0, 8, 1, 262144, 512) >= 2 * 8 * 16 * 512 * 8
-    assert ops.workspace_bytes(2, 1, 1, 10, 10) == 0
+    assert ops.workspace_bytes(3, 1, 1, 10, 10) == 0                  # unknown `which`
     assert ops.workspace_bytes(1, 1, 2048, 8192, 512, 64, 128) == 0   # prefill: no split
     assert ops.workspace_bytes(1, 1, 1, 10, 512, 64, 100) == 0        # invalid W
-    assert ops.workspace_bytes(2, 43, 1, 4096, 512) == 0             # fused: one chunk, no candidates
+    assert ops.workspace_bytes(2, 200, 1, 4096, 512) == 0            # fused: one chunk, no candidates
+    assert ops.workspace_bytes(2, 4, 1, 65536, 1024) >= 4 * 65536 * 4  # too few chunks: scores kept
     assert ops.workspace_bytes(2, 43, 1, 65536, 512) >= 2 * 43 * 16 * 512 * 8  # 16 chunks of candidates
     assert ops.workspace_bytes(2, 1, 2048, 8192, 512) >= 2048 * 8192 * 4       # many queries: scores
 
