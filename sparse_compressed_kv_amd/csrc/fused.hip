@@ -3,7 +3,7 @@
 // "Reading the architecture of DwarfStar (ds4.c), part 1/8" (Qiita), section
 // 3-3: the indexer's scores exist only to pick the top-k rows that reach the
 // main attention.  So in decode shapes the scores need not leave the chip: a
-// workgroup scores a 4096-row chunk of one query into LDS (the same row loop,
+// workgroup scores a chunk of one query's rows into LDS (the same row loop,
 // hence the same bits, as the score kernel) and selects the chunk's top-K there;
 // only K (key, row) candidates per chunk go to memory, and the candidate lists
 // are merged as in the chunked top-k.  A chunk's own top-K contains every global
@@ -21,18 +21,25 @@ namespace ds4a {
 
 namespace {
 
-constexpr int kFRows = 4096;                  // rows per workgroup = 8 keys x 512 threads
-constexpr int kFEpt = kFRows / kNT;
 constexpr int kFWaves = kNT / kWave;
 constexpr int kFBpi = 2;                      // 16-row blocks in flight per wave
+// Device figures behind the chunk rule (MI355X): 256 CUs, each holding two chunk workgroups
+// at once (the row loop keeps the query in VGPRs, 125 per lane: 4 waves per SIMD).  Fixed,
+// so that workspace sizes do not depend on the device a call runs on.
+constexpr int64_t kFCUs = 256;
+constexpr int64_t kFSlots = 2 * kFCUs;
 
+// A chunk of up to EPT * 512 rows (`rows` per chunk): each thread selects over EPT keys.
+template <int EPT>
 __global__ __launch_bounds__(kNT) void indexer_select_kernel(
-    int T, int64_t N, int K, int64_t chunks,
+    int T, int64_t N, int K, int rows, int64_t chunks,
     const uint16_t *__restrict__ qI, const float *__restrict__ w, const uint16_t *__restrict__ kI,
     const int32_t *__restrict__ n_vis, int32_t *__restrict__ out, uint32_t *__restrict__ out_keys)
 {
     __shared__ u32x4 sq[kHeads * kDim / 8];
-    __shared__ __align__(16) float s_sc[kFRows];
+    constexpr int kRows = EPT * kNT;
+    static_assert(EPT % 4 == 0, "scores are read from LDS four at a time");
+    __shared__ __align__(16) float s_sc[kRows];
     __shared__ SelectShared sm;
 
     const int64_t q = blockIdx.x / chunks;
@@ -41,26 +48,28 @@ __global__ __launch_bounds__(kNT) void indexer_select_kernel(
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int g = lane >> 4, c = lane & 15;
     const int64_t nv = clamp_nvis(n_vis, q, N);
-    const int64_t c0 = ch * kFRows;
+    const int64_t c0 = ch * rows;
     const int64_t rem = nv - c0;
-    const int n = rem <= 0 ? 0 : (rem < kFRows ? (int)rem : kFRows);   // visible rows of this chunk
+    const int n = rem <= 0 ? 0 : (rem < rows ? (int)rem : rows);     // visible rows of this chunk
 
     if (n > 0) {                                  // uniform across the workgroup
+        const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
+        u32x4 kb[kFBpi][4];
+        indexer_load_keys<kFBpi>(gk, indexer_first_row<kFBpi>(c0, wave), c0 + n, g, c, kb);
         bf16x8 aq[4][4];
         indexer_query_frags<kNT>(qI, q, sq, g, c, aq);
         float wh[4];
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
-        const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
-        indexer_score_rows<kFWaves, kFBpi>(aq, wh, gk, c0, c0 + n, wave, g, c, s_sc);
+        indexer_score_rows<kFWaves, kFBpi>(aq, wh, gk, c0, c0 + n, wave, g, c, s_sc, kb);
     }
     __syncthreads();
 
-    const int j0 = threadIdx.x * kFEpt;
-    uint32_t key[kFEpt];
-    int32_t id[kFEpt];
+    const int j0 = threadIdx.x * EPT;
+    uint32_t key[EPT];
+    int32_t id[EPT];
 #pragma unroll
-    for (int i = 0; i < kFEpt; i += 4) {
+    for (int i = 0; i < EPT; i += 4) {
         const f32x4 v = *reinterpret_cast<const f32x4 *>(s_sc + j0 + i);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -70,15 +79,61 @@ __global__ __launch_bounds__(kNT) void indexer_select_kernel(
     }
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + ch) * K;
-    block_select<kFEpt, false>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
+    block_select<EPT, false>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
 }
 
-int64_t fused_chunks(int64_t N) { return (N + kFRows - 1) / kFRows; }
+struct FusedShape {
+    int ept;                                  // keys per thread: chunk capacity ept * 512 rows
+    int rows;                                 // rows per chunk
+    int64_t chunks;                           // chunks per query
+};
+
+// Chunk rule.  Every CU gets about the same share of HBM bandwidth, so a chunk workgroup
+// streams at a rate set by how many share its CU, and the call lasts as long as its busiest
+// CU: (workgroups per CU) x (rows per chunk), plus a select and the query set-up per
+// resident round, plus the merge: ~0.6 ns per candidate and ~10 us per extra level.  Costs
+// are in rows (one 256-byte key row at a CU's share of the bandwidth, ~10 ns): a select +
+// set-up costs 370 + 24 * ept, a merge candidate 1/16.
+// Chunks hold at most 8192 rows (16 keys per thread) and at least 4 rows per candidate.
+FusedShape fused_shape(int64_t Q, int64_t N, int K) {
+    const int64_t cmin = (N + 8191) / 8192 > 0 ? (N + 8191) / 8192 : 1;
+    int64_t cmax = N / (4 * (int64_t)K);
+    if (cmax > cmin + 32) cmax = cmin + 32;
+    if (cmax < cmin) cmax = cmin;
+    FusedShape best = {16, 8192, cmin};
+    int64_t best_cost = -1;
+    for (int64_t c = cmin; c <= cmax; ++c) {
+        const int64_t rows = ((N + c - 1) / c + 15) / 16 * 16;
+        const int ept = (int)((rows + 2047) / 2048 * 4);
+        const int64_t wgs = Q * c;
+        int64_t levels = 0;
+        for (int64_t stride = c * K; stride > kMergeMax; stride = (stride + kLevelChunk - 1) / kLevelChunk * K)
+            ++levels;
+        const int64_t cost = (wgs + kFCUs - 1) / kFCUs * rows + (wgs + kFSlots - 1) / kFSlots * (370 + 24 * ept) +
+                             c * K / 16 + 1000 * levels;
+        if (best_cost < 0 || cost < best_cost) {
+            best_cost = cost;
+            best = {ept, (int)rows, c};
+        }
+    }
+    return best;
+}
 
 // The fused kernel needs enough chunk workgroups to stream the keys at full rate; with fewer
 // (a handful of units) the score kernel's smaller 1024-row chunks plus the separate top-k
 // are faster, and so are many queries per unit (prefill shapes).
-bool use_fused(int T, int64_t Q, int64_t N) { return T < kIndexerManyQueries && Q * fused_chunks(N) >= 128; }
+bool use_fused(int T, int64_t Q, int64_t N, int K) {
+    return T < kIndexerManyQueries && Q * fused_shape(Q, N, K).chunks >= 128;
+}
+
+template <int EPT>
+void launch_select(int64_t grid, int T, int64_t N, int K, int rows, int64_t chunks, const uint16_t *idx_q,
+                   const float *idx_w, const uint16_t *idx_k, const int32_t *n_vis, int32_t *ids, uint32_t *keys,
+                   hipStream_t stream)
+{
+    hipLaunchKernelGGL(indexer_select_kernel<EPT>, dim3((unsigned)grid), dim3(kNT), 0, stream, T, N, K, rows, chunks,
+                       idx_q, idx_w, idx_k, n_vis, ids, keys);
+}
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -86,8 +141,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 size_t indexer_topk_workspace_bytes(int U, int T, int64_t N, int K) {
     const int64_t Q = (int64_t)U * T;
-    if (!use_fused(T, Q, N)) return align256((size_t)Q * (size_t)N * 4) + topk_workspace_bytes(Q, N, K);
-    const int64_t chunks = fused_chunks(N);
+    if (!use_fused(T, Q, N, K)) return align256((size_t)Q * (size_t)N * 4) + topk_workspace_bytes(Q, N, K);
+    const int64_t chunks = fused_shape(Q, N, K).chunks;
     return chunks > 1 ? topk_cand_workspace_bytes(Q, chunks, K) : 0;
 }
 
@@ -96,27 +151,27 @@ hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *i
                                hipStream_t stream)
 {
     const int64_t Q = (int64_t)U * T;
-    if (!use_fused(T, Q, N)) {
+    if (!use_fused(T, Q, N, K)) {
         float *scores = static_cast<float *>(workspace);
         void *ws2 = static_cast<char *>(workspace) + align256((size_t)Q * (size_t)N * 4);
         hipError_t e = launch_indexer(U, T, N, idx_q, idx_w, idx_k, n_vis, scores, stream);
         if (e != hipSuccess) return e;
         return launch_topk(Q, N, K, scores, n_vis, idx, ws2, stream);
     }
-    const int64_t chunks = fused_chunks(N);
-    if (chunks == 1) {
-        hipLaunchKernelGGL(indexer_select_kernel, dim3((unsigned)Q), dim3(kNT), 0, stream, T, N, K, chunks, idx_q,
-                           idx_w, idx_k, n_vis, idx, (uint32_t *)nullptr);
-        return hipGetLastError();
+    const FusedShape fs = fused_shape(Q, N, K);
+    uint32_t *keys = nullptr;
+    int32_t *ids = idx;                       // one chunk: its selection is the result
+    if (fs.chunks > 1) topk_level1_buffers(workspace, Q, fs.chunks, K, &keys, &ids);
+    const int64_t grid = Q * fs.chunks;
+    switch (fs.ept) {
+    case 4: launch_select<4>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    case 8: launch_select<8>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    case 12: launch_select<12>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    default: launch_select<16>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
     }
-    uint32_t *keys;
-    int32_t *ids;
-    topk_level1_buffers(workspace, Q, chunks, K, &keys, &ids);
-    hipLaunchKernelGGL(indexer_select_kernel, dim3((unsigned)(Q * chunks)), dim3(kNT), 0, stream, T, N, K, chunks,
-                       idx_q, idx_w, idx_k, n_vis, ids, keys);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_topk_merge(Q, N, K, kFRows, chunks, n_vis, idx, workspace, stream);
+    if (e != hipSuccess || fs.chunks == 1) return e;
+    return launch_topk_merge(Q, N, K, fs.rows, fs.chunks, n_vis, idx, workspace, stream);
 }
 
 }  // namespace ds4a

@@ -47,13 +47,15 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 
     __shared__ u32x4 sq[kHeads * kDim / 8];
     __shared__ __align__(16) float s_sc[kRowsPerWg];
+    const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
+    u32x4 kb[2][4];
+    indexer_load_keys<2>(gk, indexer_first_row<2>(r0, wave), rv1, g, c, kb);   // in flight during the query set-up
     bf16x8 aq[4][4];
     indexer_query_frags<kThreads>(qI, q, sq, g, c, aq);
     float wh[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
-    const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
-    indexer_score_rows<kWaves, 2>(aq, wh, gk, r0, rv1, wave, g, c, s_sc);
+    indexer_score_rows<kWaves, 2>(aq, wh, gk, r0, rv1, wave, g, c, s_sc, kb);
 
     __syncthreads();
     const bool row_aligned = ((q * N) & 3) == 0;      // scores of this query start 16-byte aligned

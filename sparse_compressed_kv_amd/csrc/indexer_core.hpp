@@ -48,24 +48,36 @@ __device__ __forceinline__ void indexer_query_frags(const uint16_t *__restrict__
         for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + ((4 * s + g) ^ c)]);
 }
 
+// Keys of the 16*BPI rows from `base` as MFMA A fragments: lane (g, c) takes the 16-byte
+// chunks 4s + g of row base + 16bi + c; rows at or past rv1 read as zero (no load).
+template <int BPI>
+__device__ __forceinline__ void indexer_load_keys(const u32x4 *__restrict__ gk, int64_t base, int64_t rv1, int g,
+                                                  int c, u32x4 (&kb)[BPI][4]) {
+#pragma unroll
+    for (int bi = 0; bi < BPI; ++bi) {
+        const int64_t row = base + 16 * bi + c;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            kb[bi][s] = row < rv1 ? gk[row * kChunksPerRow + 4 * s + g] : u32x4{0u, 0u, 0u, 0u};
+    }
+}
+
+// First row of a wave's first iteration in indexer_score_rows.
+template <int BPI>
+__device__ __forceinline__ int64_t indexer_first_row(int64_t r0, int wave) { return r0 + 16 * BPI * wave; }
+
 // Scores of the visible rows [r0, rv1) of one query into s_out[row - r0] (LDS), by the
-// WAVES waves of the workgroup, BPI 16-row blocks per wave iteration (loads of all BPI
-// blocks issued first); wh[ht] is the weight of head 16ht + c.  A row's score does not
-// depend on WAVES or BPI.
+// WAVES waves of the workgroup, BPI 16-row blocks per wave iteration; wh[ht] is the weight
+// of head 16ht + c.  kb holds the wave's first iteration of keys (indexer_load_keys at
+// indexer_first_row), so a caller can issue those loads before it sets up the query; the
+// next iteration's loads are issued as soon as the current blocks are used.  A row's score
+// does not depend on WAVES or BPI.
 template <int WAVES, int BPI>
 __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], const float (&wh)[4],
                                                    const u32x4 *__restrict__ gk, int64_t r0, int64_t rv1,
-                                                   int wave, int g, int c, float *s_out) {
+                                                   int wave, int g, int c, float *s_out, u32x4 (&kb)[BPI][4]) {
     constexpr int kRowsPerIter = 16 * BPI * WAVES;
-    for (int64_t base = r0 + 16 * BPI * wave; base < rv1; base += kRowsPerIter) {
-        u32x4 kb[BPI][4];
-#pragma unroll
-        for (int bi = 0; bi < BPI; ++bi) {
-            const int64_t row = base + 16 * bi + c;
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                kb[bi][s] = row < rv1 ? gk[row * kChunksPerRow + 4 * s + g] : u32x4{0u, 0u, 0u, 0u};
-        }
+    for (int64_t base = indexer_first_row<BPI>(r0, wave); base < rv1; base += kRowsPerIter) {
 #pragma unroll
         for (int bi = 0; bi < BPI; ++bi) {
             const int64_t blk = base + 16 * bi;
@@ -85,6 +97,7 @@ __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], con
             for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
             if (c == 0) *reinterpret_cast<f32x4 *>(s_out + (blk - r0) + 4 * g) = acc;
         }
+        indexer_load_keys<BPI>(gk, base + kRowsPerIter, rv1, g, c, kb);
     }
 }
 

@@ -143,17 +143,26 @@ def make_unit(w: Workload, unit: int, seed: int = 0) -> dict[str, np.ndarray]:
         raise ValueError(f"q_dtype {w.q_dtype!r}")
     raw = f16_bits_from_f32(_rng(w, seed, unit, "raw").standard_normal((T + W - 1, D), dtype=np.float32))
     comp = _normal_bf16(_rng(w, seed, unit, "comp"), N, D)
+    ix = make_indexer_unit(w, unit, seed)
+    heavy = ix["heavy"]
+    if heavy.size:
+        comp[heavy] = bf16_bits_from_f32(bf16_bits_to_f32(comp[heavy]) * np.float32(4.0))
+    return {
+        "q": q, "raw": raw, "comp": comp, "idx_k": ix["idx_k"], "idx_q": ix["idx_q"], "idx_w": ix["idx_w"],
+        "heavy": heavy, "n_vis": w.n_vis()[unit], "pos": w.positions()[unit],
+    }
+
+
+def make_indexer_unit(w: Workload, unit: int, seed: int = 0) -> dict[str, np.ndarray]:
+    """The indexer inputs of one unit alone (the same values make_unit returns for them)."""
+    T, N, Hi, Di = w.T, w.N, w.Hi, w.Di
     idx_k = _normal_bf16(_rng(w, seed, unit, "idx_k"), N, Di)
     idx_q = bf16_bits_from_f32(_rng(w, seed, unit, "idx_q").standard_normal((T, Hi, Di), dtype=np.float32))
     idx_w = _rng(w, seed, unit, "idx_w").random((T, Hi), dtype=np.float32)
     heavy = np.sort(_rng(w, seed, unit, "heavy").choice(N, size=w.n_heavy(), replace=False)).astype(np.int64)
     if heavy.size:
-        comp[heavy] = bf16_bits_from_f32(bf16_bits_to_f32(comp[heavy]) * np.float32(4.0))
         idx_k[heavy] = bf16_bits_from_f32(bf16_bits_to_f32(idx_k[heavy]) * np.float32(4.0))
-    return {
-        "q": q, "raw": raw, "comp": comp, "idx_k": idx_k, "idx_q": idx_q, "idx_w": idx_w,
-        "heavy": heavy, "n_vis": w.n_vis()[unit], "pos": w.positions()[unit],
-    }
+    return {"idx_k": idx_k, "idx_q": idx_q, "idx_w": idx_w, "heavy": heavy}
 
 
 def make_config(w: Workload, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:
@@ -172,3 +181,11 @@ def make_config(w: Workload, seed: int = 0, threads: int | None = None) -> dict[
         out[key] = np.stack([x[key] for x in units])
     out["heavy"] = [x["heavy"] for x in units]
     return out
+
+
+def make_indexer_config(w: Workload, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:
+    """The indexer inputs (idx_k, idx_q, idx_w) of all U units, stacked, without the attention rows."""
+    n = threads or min(16, os.cpu_count() or 1, w.U)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, n)) as ex:
+        units = list(ex.map(lambda u: make_indexer_unit(w, u, seed), range(w.U)))
+    return {key: np.stack([x[key] for x in units]) for key in ("idx_k", "idx_q", "idx_w")}

@@ -120,10 +120,26 @@ def test_workspace_bytes(L):
     assert ops.workspace_bytes(3, 1, 1, 10, 10) == 0                  # unknown `which`
     assert ops.workspace_bytes(1, 1, 2048, 8192, 512, 64, 128) == 0   # prefill: no split
     assert ops.workspace_bytes(1, 1, 1, 10, 512, 64, 100) == 0        # invalid W
-    assert ops.workspace_bytes(2, 200, 1, 4096, 512) == 0            # fused: one chunk, no candidates
+    assert ops.workspace_bytes(2, 300, 1, 2048, 512) == 0            # fused: one chunk, no candidates
     assert ops.workspace_bytes(2, 4, 1, 65536, 1024) >= 4 * 65536 * 4  # too few chunks: scores kept
-    assert ops.workspace_bytes(2, 43, 1, 65536, 512) >= 2 * 43 * 16 * 512 * 8  # 16 chunks of candidates
+    assert ops.workspace_bytes(2, 43, 1, 65536, 512) >= 2 * 43 * 11 * 512 * 8  # 11 chunks of candidates
     assert ops.workspace_bytes(2, 1, 2048, 8192, 512) >= 2048 * 8192 * 4       # many queries: scores
+
+
+@pytest.mark.parametrize("U,T,N,K", [
+    (300, 1, 2048, 512), (100, 3, 2048, 512), (200, 1, 8197, 512), (43, 1, 65536, 512),
+    (43, 1, 16384, 512), (43, 1, 65537, 1024), (8, 1, 262144, 512), (40, 1, 100000, 2048),
+    (50, 3, 20000, 7), (70, 2, 3000, 64), (130, 1, 9000, 512), (4, 1, 65536, 1024),
+    (3, 1, 8193, 512), (1, 2, 100000, 2048), (1, 4, 65536, 512), (64, 1, 4096, 512),
+])
+def test_indexer_topk_routing_matches_library(U, T, N, K):
+    """The host restatement of the fused call's chunk rule agrees with the library's sizes."""
+    from tests import routing
+    got = ops.workspace_bytes(2, U, T, N, K)
+    if routing.uses_fused(U, T, N, K):
+        assert got == routing.fused_workspace_bytes(U, T, N, K)
+    else:
+        assert got >= ((U * T * N * 4 + 255) & ~255)
 
 
 def test_last_error_is_text(L):

@@ -13,6 +13,7 @@ import torch
 from oracle import oracle as orc
 from sparse_compressed_kv_amd import ops
 from synth import inputs as gen
+from tests import routing
 from tests.util import bits_to_torch, normwise_err, tie_band_ok, upload
 
 pytestmark = pytest.mark.gpu
@@ -153,43 +154,71 @@ def test_topk_bit_exact_on_identical_scores(Q, N, K, pattern):
 # ------------------------------------------------------- fused indexer + top-k
 
 FUSED_CASES = [
-    dict(U=3, T=1, N=1, K=1, nv=None),
-    dict(U=2, T=1, N=8192, K=512, nv=None),
-    dict(U=3, T=1, N=8193, K=512, nv=[[8193], [0], [300]]),
-    dict(U=4, T=1, N=65536, K=512, nv=None, heavy=0.01),
-    dict(U=2, T=1, N=65537, K=1024, nv=[[65537], [40000]]),
-    dict(U=1, T=1, N=262144, K=512, nv=None),
-    dict(U=1, T=2, N=100000, K=2048, nv=[[100000, 2047]]),
-    dict(U=2, T=3, N=20000, K=7, nv=None),
-    dict(U=1, T=5, N=3000, K=64, nv=[[0, 1, 64, 2999, 3000]]),
+    # too few chunk workgroups: scores through the workspace
+    dict(U=3, T=1, N=1, K=1, nv=None, ept=None),
+    dict(U=3, T=1, N=8193, K=512, nv=[[8193], [0], [300]], ept=None),
+    dict(U=1, T=2, N=100000, K=2048, nv=[[100000, 2047]], ept=None),
+    # fused: every chunk size, one chunk (direct output) to two merge levels
+    dict(U=100, T=3, N=2048, K=512, nv="edges", ept=4),
+    dict(U=200, T=1, N=8197, K=512, nv="edges", ept=12),
+    dict(U=43, T=1, N=65536, K=512, nv=None, heavy=0.01, ept=12),
+    dict(U=43, T=1, N=65537, K=1024, nv="edges", ept=12),
+    dict(U=8, T=1, N=262144, K=512, nv="edges", ept=16),
+    dict(U=40, T=1, N=100000, K=2048, nv="edges", ept=16),
+    dict(U=50, T=3, N=20000, K=7, nv=None, ept=8),
+    dict(U=64, T=1, N=4096, K=512, nv="edges", ept=4),
+    dict(U=70, T=2, N=3000, K=64, nv="edges", ept=4),
 ]
+
+
+def _fused_nv(case, rows):
+    """Visible rows per query: random, with the first queries on the edges of K and of a chunk."""
+    U, T, N, K = case["U"], case["T"], case["N"], case["K"]
+    nv = case["nv"]
+    if nv is None:
+        return np.full((U, T), N, np.int32)
+    if nv != "edges":
+        return np.array(nv, dtype=np.int32)
+    r = np.random.default_rng(7).integers(0, N + 1, U * T)
+    edges = [0, 1, K - 1, K, K + 1, rows - 1, rows, rows + 1, 2 * rows + 3, N - 1, N]
+    edges = [e for e in edges if 0 <= e <= N]
+    r[:len(edges)] = edges[:len(r)]
+    return r.reshape(U, T).astype(np.int32)
 
 
 @pytest.mark.parametrize("case", FUSED_CASES, ids=lambda c: f"U{c['U']}T{c['T']}N{c['N']}K{c['K']}")
 def test_indexer_topk_equals_separate_calls(case):
     """ds4a_indexer_topk returns exactly topk_select(indexer_score(...)): same bits, same set."""
-    w = gen.Workload("fus", 105, U=case["U"], T=case["T"], N=case["N"], H=16, K=case["K"],
-                     heavy_frac=case.get("heavy", 0.0))
-    x = gen.make_config(w, seed=2)
-    nv = (np.array(case["nv"], dtype=np.int32) if case["nv"] is not None
-          else np.full((w.U, w.T), w.N, np.int32))
-    d = upload(x)
+    U, T, N, K = case["U"], case["T"], case["N"], case["K"]
+    fused = routing.uses_fused(U, T, N, K)
+    assert fused == (case["ept"] is not None)
+    if fused:
+        assert routing.fused_shape(U * T, N, K)[0] == case["ept"]
+    w = gen.Workload("fus", 105, U=U, T=T, N=N, H=16, K=K, heavy_frac=case.get("heavy", 0.0))
+    x = gen.make_indexer_config(w, seed=2)
+    nv = _fused_nv(case, routing.fused_shape(U * T, N, K)[1])
+    iq = bits_to_torch(x["idx_q"], torch.bfloat16)
+    iw = torch.from_numpy(x["idx_w"]).cuda()
+    ik = bits_to_torch(x["idx_k"], torch.bfloat16)
+    del x
     nvd = torch.from_numpy(nv).cuda()
-    scores = ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nvd)
-    ref = ops.topk_select(scores, w.K, n_vis=nvd)
+    scores = ops.indexer_score(iq, iw, ik, n_vis=nvd)
+    ref = ops.topk_select(scores, K, n_vis=nvd)
+    del scores
     got = torch.full_like(ref, -7)
-    ops.indexer_topk(d["idx_q"], d["idx_w"], d["idx_k"], w.K, n_vis=nvd, out=got)
+    ops.indexer_topk(iq, iw, ik, K, n_vis=nvd, out=got)
     assert torch.equal(got, ref)
 
 
 def test_indexer_topk_all_tied():
     """Every score equal (zero query): the set is rows 0..K-1 across chunk boundaries."""
-    w = gen.Workload("fut", 106, U=2, T=1, N=30000, H=16, K=512)
-    x = gen.make_config(w, seed=3)
+    w = gen.Workload("fut", 106, U=130, T=1, N=9000, H=16, K=512)
+    assert routing.uses_fused(w.U, w.T, w.N, w.K) and routing.fused_shape(w.U, w.N, w.K) == (8, 3008, 3)
+    x = gen.make_indexer_config(w, seed=3)
     x["idx_q"][:] = 0
-    d = upload(x)
-    got = ops.indexer_topk(d["idx_q"], d["idx_w"], d["idx_k"], w.K).cpu().numpy()
-    assert np.array_equal(got[:, 0], np.broadcast_to(np.arange(512, dtype=np.int32), (2, 512)))
+    got = ops.indexer_topk(bits_to_torch(x["idx_q"], torch.bfloat16), torch.from_numpy(x["idx_w"]).cuda(),
+                           bits_to_torch(x["idx_k"], torch.bfloat16), w.K).cpu().numpy()
+    assert np.array_equal(got[:, 0], np.broadcast_to(np.arange(512, dtype=np.int32), (w.U, 512)))
 
 
 # -------------------------------------------------------------- attention

@@ -27,3 +27,14 @@ def test_workload_shapes_match_printed_constants():
         assert w.Di == g["n_indexer_head_dim"][col]
         assert w.K == g["n_indexer_top_k"][col]
     assert g["n_head_kv"] == (1, 1)
+
+
+def test_indexer_only_inputs_equal_full_inputs():
+    """make_indexer_config draws the same indexer values as make_config (own streams per tensor)."""
+    import numpy as np
+
+    from synth.inputs import Workload, make_config, make_indexer_config
+    w = Workload("tiny", 9, U=3, T=2, N=300, heavy_frac=0.05)
+    a, b = make_config(w, seed=4), make_indexer_config(w, seed=4)
+    for key in ("idx_k", "idx_q", "idx_w"):
+        assert np.array_equal(a[key], b[key]), key
