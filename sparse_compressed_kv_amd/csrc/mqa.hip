@@ -61,6 +61,7 @@ constexpr int kXchBytes = kWaves * 2 * kWave * 16;           // partial logits o
 constexpr int kStage = kTile / kWaves;        // rows each wave stages per tile (4)
 constexpr int kQtBytes = kHG * kRot * 4;                     // rotated query tails of the 64 heads (f32)
 constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
+constexpr int kRowRegs = 2;            // row-table entries per thread loaded ahead of the first gathers
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[64], l[64], O[64][512]
 constexpr float kRescale = 8.f;               // softmax reference moves when a logit exceeds it by this
 
@@ -89,20 +90,29 @@ struct MqaArgs {
     double log2_theta;                       // log2(rope_theta), computed on the host in fp64
 };
 
-// Rotate the adjacent pair i of the query tail by pos * theta^(-2i/n_rot) (fp64), round once
-// to f32.  The angle (up to ~1e6 rad) is first reduced by a two-part 2*pi in fp64, so that
+// The angle of the adjacent pair i of the query tail, pos * theta^(-2i/n_rot), as (cos, sin)
+// in fp64.  The angle (up to ~1e6 rad) is first reduced by a two-part 2*pi in fp64, so that
 // sincos runs on |x| <= pi.
-__device__ __forceinline__ void rope_pair(double log2_theta, int i, int64_t pos, float &a, float &b) {
+__device__ __forceinline__ void rope_angle(double log2_theta, int i, int64_t pos, double &cs, double &sn) {
     const double inv_freq = exp2(-(double)(2 * i) / (double)kRot * log2_theta);
     const double ang = (double)pos * inv_freq;
     const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
     double red = fma(-k, 6.283185307179586, ang);              // 2 pi, high part
     red = fma(-k, 2.4492935982947064e-16, red);                // 2 pi, low part
-    double sn, cs;
     sincos(red, &sn, &cs);
+}
+
+// Rotate the pair (a, b) by the angle (cs, sn) in fp64 and round once to f32.
+__device__ __forceinline__ void rope_rotate(double cs, double sn, float &a, float &b) {
     const double x = (double)a, y = (double)b;
     a = (float)(x * cs - y * sn);
     b = (float)(x * sn + y * cs);
+}
+
+__device__ __forceinline__ void rope_pair(double log2_theta, int i, int64_t pos, float &a, float &b) {
+    double cs, sn;
+    rope_angle(log2_theta, i, pos, cs, sn);
+    rope_rotate(cs, sn, a, b);
 }
 
 // Query dims [d, d+8) of head h of query q as f32, as stored (no rotation).
@@ -134,13 +144,12 @@ __device__ __forceinline__ void load_q8(const MqaArgs &a, int64_t q, int h, int 
 }
 
 // The query as MFMA B fragments, k-step s <-> dims d0 + 32s + 8g + (0..7) of head h:
-// hi/lo pairs of one operand type (bf16 or f16).  The rotated tail (dims 448..511, the
-// k-steps with d0 + 32s >= 448, a wave-uniform test) comes from `tail`, this head's 64
-// floats in LDS; all global loads are issued before any is used.
-template <bool F16, bool QF32>
-__device__ __forceinline__ void load_q_frags(const MqaArgs &a, int64_t q, int h, const float *tail, int d0, int g,
-                                             u32x4 (&hi)[kKs], u32x4 (&lo)[kKs]) {
-    float v[kKs][8];
+// hi/lo pairs of one operand type (bf16 or f16).  load_q_plain issues every global load
+// (the stored values as f32); pack_q_frags takes the rotated tail (dims 448..511, the k-steps
+// with d0 + 32s >= 448, a wave-uniform test) from `tail`, this head's 64 floats in LDS.
+template <bool QF32>
+__device__ __forceinline__ void load_q_plain(const MqaArgs &a, int64_t q, int h, int d0, int g,
+                                             float (&v)[kKs][8]) {
     const int64_t off = (q * a.H + h) * (int64_t)kD + d0 + 8 * g;
 #pragma unroll
     for (int s = 0; s < kKs; ++s) {
@@ -158,20 +167,25 @@ __device__ __forceinline__ void load_q_frags(const MqaArgs &a, int64_t q, int h,
             }
         }
     }
+}
+
+template <bool F16>
+__device__ __forceinline__ void pack_q_frags(const float (&v)[kKs][8], const float *tail, int d0, int g,
+                                             u32x4 (&hi)[kKs], u32x4 (&lo)[kKs]) {
 #pragma unroll
     for (int s = 0; s < kKs; ++s) {
-        if (d0 + 32 * s >= kD - kRot) {
+        float x[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) v[s][e] = tail[d0 + 32 * s + 8 * g - (kD - kRot) + e];
-        }
+        for (int e = 0; e < 8; ++e)
+            x[e] = d0 + 32 * s >= kD - kRot ? tail[d0 + 32 * s + 8 * g - (kD - kRot) + e] : v[s][e];
         if (F16) {
             f16x8 h8, l8;
-            pack_hi_lo8_f16(v[s], h8, l8);
+            pack_hi_lo8_f16(x, h8, l8);
             hi[s] = __builtin_bit_cast(u32x4, h8);
             lo[s] = __builtin_bit_cast(u32x4, l8);
         } else {
             bf16x8 h8, l8;
-            pack_hi_lo8(v[s], h8, l8);
+            pack_hi_lo8(x, h8, l8);
             hi[s] = __builtin_bit_cast(u32x4, h8);
             lo[s] = __builtin_bit_cast(u32x4, l8);
         }
@@ -189,12 +203,17 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     float *s_qt = reinterpret_cast<float *>(smem + 2 * kTileBytes + kXchBytes);   // [64 heads][64]
     int32_t *s_row = reinterpret_cast<int32_t *>(smem + kLdsBytes);   // per union row: comp row, -2 raw, -1 none
 
-    const int64_t lin = blockIdx.x;
-    const int hg = (int)(lin % a.n_hg);
-    const int64_t item = lin / a.n_hg;
-    const int64_t q = item / a.n_chunks;
-    const int chunk = (int)(item % a.n_chunks);
-    const int64_t u = q / a.T, t = q % a.T;
+    // Workgroup -> (query, chunk, head group), in 32-bit arithmetic: the grid is below 2^31
+    // workgroups (U*T <= 2^24, and the union is split only when there are fewer than 256
+    // queries), and 64-bit divisions by runtime values cost hundreds of scalar instructions
+    // ahead of the first load.
+    const uint32_t lin = blockIdx.x;
+    const int hg = a.n_hg == 1 ? 0 : (int)(lin % (uint32_t)a.n_hg);
+    const uint32_t item = a.n_hg == 1 ? lin : lin / (uint32_t)a.n_hg;
+    const uint32_t q32 = item / (uint32_t)a.n_chunks;
+    const int chunk = (int)(item - q32 * (uint32_t)a.n_chunks);
+    const uint32_t u32 = q32 / (uint32_t)a.T;
+    const int64_t q = q32, u = u32, t = q32 - u32 * (uint32_t)a.T;
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
     const int g = lane >> 4, c = lane & 15;
     const int ht = wave >> 1, dh = wave & 1;               // head tile, half of the dims
@@ -209,69 +228,114 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const uint16_t *comp_u = a.comp + u * a.N * kD;
     const int32_t *idx_q = a.idx + q * (int64_t)a.K;
 
-    // Row table of this chunk's union rows, read once from idx, plus two tiles of padding
-    // for the look-ahead loads past the chunk's end.
+    // Union row rho of this chunk: a compressed row, -2 for a raw row, -1 for none (past the
+    // chunk's end, a -1 or out-of-range index, past K).  idx is always read, at a clamped
+    // position (idx_at), so a run of these loads issues back to back with no branch.
+    auto idx_at = [&](int rho) __attribute__((always_inline)) -> int32_t {
+        const int k = rho - a.W;
+        return idx_q[k < 0 ? 0 : (k < a.K ? k : a.K - 1)];
+    };
+    auto union_row = [&](int rho, int32_t j) __attribute__((always_inline)) -> int32_t {
+        const int k = rho - a.W;
+        const int32_t comp = (k < a.K && j >= 0 && (int64_t)j < a.N) ? j : -1;
+        return rho >= tile1 * kTile ? -1 : (k < 0 ? -2 : comp);
+    };
+    // A row that takes no part (-1) is read from compressed row 0 (N >= 1): it is finite,
+    // its logit is masked to -inf and its probability is 0, so no branch guards the load.
+    auto union_ptr = [&](int rho, int32_t v) __attribute__((always_inline)) -> const uint16_t * {
+        return v == -2 ? raw_q + (int64_t)rho * kD : comp_u + (int64_t)(v < 0 ? 0 : v) * kD;
+    };
+    // Set-up loads first, then the first two tiles' row gathers, then the set-up's use of its
+    // loads: vector loads complete in issue order, so a gather issued before the set-up's own
+    // loads would hold the set-up up until the rows arrive.
+    //  - row table of this chunk's union rows from idx, plus two tiles of padding for the
+    //    look-ahead loads past the chunk's end (the first kRowRegs entries per thread are
+    //    loaded into registers here, any further ones after the gathers);
+    const int64_t pos = a.pos[q];
     const int rho0 = tile0 * kTile;
     const int n_rows = (tile1 - tile0 + 2) * kTile;
-    for (int r = tid; r < n_rows; r += kThreads) {
-        const int rho = rho0 + r;
-        int32_t v = -1;
-        if (rho < tile1 * kTile) {
-            if (rho < a.W) {
-                v = -2;
-            } else if (rho - a.W < a.K) {
-                const int32_t j = idx_q[rho - a.W];
-                if (j >= 0 && (int64_t)j < a.N) v = j;
-            }
-        }
-        s_row[r] = v;
+    int32_t rv[kRowRegs];
+#pragma unroll
+    for (int k = 0; k < kRowRegs; ++k) {
+        const int r = tid + k * kThreads < n_rows ? tid + k * kThreads : n_rows - 1;
+        rv[k] = idx_at(rho0 + r);
     }
-    // Rotated query tails of this workgroup's heads: four adjacent pairs per thread, all loads
-    // issued first (heads past H read head H-1 and store nothing).
-    {
-        constexpr int kPairs = kHG * (kRot / 2) / kThreads;
-        const int64_t pos = a.pos[q];
-        float x[kPairs], y[kPairs];
+    //  - the query tail of this workgroup's heads, four adjacent pairs per thread (heads past H
+    //    read head H-1 and store nothing);
+    constexpr int kPairs = kHG * (kRot / 2) / kThreads;
+    float qx[kPairs], qy[kPairs];
 #pragma unroll
-        for (int k = 0; k < kPairs; ++k) {
-            const int i = tid + k * kThreads;
-            const int hl = i / (kRot / 2), pr = i % (kRot / 2);
-            const int h = hg * kHG + hl < a.H ? hg * kHG + hl : a.H - 1;
-            const int64_t off = (q * a.H + h) * (int64_t)kD + (kD - kRot) + 2 * pr;
-            if (a.q_bf16) {
-                const uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.q) + off);
-                x[k] = bf16_bits_to_f32(w & 0xFFFFu);
-                y[k] = bf16_bits_to_f32(w >> 16);
-            } else {
-                const float2 w = *reinterpret_cast<const float2 *>(static_cast<const float *>(a.q) + off);
-                x[k] = w.x;
-                y[k] = w.y;
-            }
+    for (int k = 0; k < kPairs; ++k) {
+        const int i = tid + k * kThreads;
+        const int hl = i / (kRot / 2), pr = i % (kRot / 2);
+        const int h = hg * kHG + hl < a.H ? hg * kHG + hl : a.H - 1;
+        const int64_t off = (q * a.H + h) * (int64_t)kD + (kD - kRot) + 2 * pr;
+        if (!LO_ALL) {                                    // bf16 query
+            const uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(a.q) + off);
+            qx[k] = bf16_bits_to_f32(w & 0xFFFFu);
+            qy[k] = bf16_bits_to_f32(w >> 16);
+        } else {
+            const float2 w = *reinterpret_cast<const float2 *>(static_cast<const float *>(a.q) + off);
+            qx[k] = w.x;
+            qy[k] = w.y;
         }
+    }
+    //  - this wave's query values (packed into MFMA fragments once the tail is rotated; a
+    //    wave past H reads head H-1 and never uses it);
+    float qv[kKs][8];
+    load_q_plain<LO_ALL>(a, q, active ? h0 + c : a.H - 1, d0, g, qv);
+    //  - wave w stages rows w + 8i (i = 0..3) of a tile, lane = 16-byte chunk of the row; the
+    //    first two tiles' rows come straight from idx (wave-uniform reads).
+    u32x4 st0[kStage], st1[kStage];
+    {
+        const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+        int32_t j0[kStage], j1[kStage];
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            j0[i] = idx_at(tile0 * kTile + wave_u + kWaves * i);
+            j1[i] = idx_at((tile0 + 1) * kTile + wave_u + kWaves * i);
+        }
+        // The position arrives with these reads, not after the gathers (the compiler would
+        // otherwise issue its load at its first use, behind them).
+        asm volatile("" : : "s"(pos));
+#pragma unroll
+        for (int i = 0; i < kStage; ++i) {
+            const int r0 = tile0 * kTile + wave_u + kWaves * i, r1 = r0 + kTile;
+            st0[i] = reinterpret_cast<const u32x4 *>(union_ptr(r0, union_row(r0, j0[i])))[lane];
+            st1[i] = reinterpret_cast<const u32x4 *>(union_ptr(r1, union_row(r1, j1[i])))[lane];
+        }
+    }
+    // (stored at the same clamped position, with no branch, so that the compiler does not move
+    // the load down here, behind the gathers)
+#pragma unroll
+    for (int k = 0; k < kRowRegs; ++k) {
+        const int r = tid + k * kThreads < n_rows ? tid + k * kThreads : n_rows - 1;
+        s_row[r] = union_row(rho0 + r, rv[k]);
+    }
+    for (int r = tid + kRowRegs * kThreads; r < n_rows; r += kThreads) s_row[r] = union_row(rho0 + r, idx_at(rho0 + r));
+    // Rotated query tails into LDS.  A thread's pairs are all pair tid % 32 of their heads
+    // (kThreads is a multiple of 32), so one angle serves them all.
+    {
+        static_assert(kThreads % (kRot / 2) == 0, "one pair index per thread");
+        double cs, sn;
+        rope_angle(a.log2_theta, tid % (kRot / 2), pos, cs, sn);
 #pragma unroll
         for (int k = 0; k < kPairs; ++k) {
             const int i = tid + k * kThreads;
             const int hl = i / (kRot / 2), pr = i % (kRot / 2);
-            rope_pair(a.log2_theta, pr, pos, x[k], y[k]);
-            s_qt[hl * kRot + 2 * pr] = x[k];
-            s_qt[hl * kRot + 2 * pr + 1] = y[k];
+            rope_rotate(cs, sn, qx[k], qy[k]);
+            s_qt[hl * kRot + 2 * pr] = qx[k];
+            s_qt[hl * kRot + 2 * pr + 1] = qy[k];
         }
     }
     __syncthreads();
 
-    // A row that takes no part (-1) is read from compressed row 0 (N >= 1): it is finite,
-    // its logit is masked to -inf and its probability is 0, so no branch guards the load.
-    auto row_ptr = [&](int rho) __attribute__((always_inline)) -> const uint16_t * {
-        const int32_t v = s_row[rho - rho0];
-        return v == -2 ? raw_q + (int64_t)rho * kD : comp_u + (int64_t)(v < 0 ? 0 : v) * kD;
-    };
-
-    // Wave w stages rows w + 8i (i = 0..3) of a tile; lane = 16-byte chunk of the row.
-    u32x4 st0[kStage], st1[kStage];
     auto load_tile = [&](int tt, u32x4 (&st)[kStage]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int i = 0; i < kStage; ++i)
-            st[i] = reinterpret_cast<const u32x4 *>(row_ptr(tt * kTile + wave + kWaves * i))[lane];
+        for (int i = 0; i < kStage; ++i) {
+            const int rho = tt * kTile + wave + kWaves * i;
+            st[i] = reinterpret_cast<const u32x4 *>(union_ptr(rho, s_row[rho - rho0]))[lane];
+        }
     };
     // Every LDS address below is a per-lane base plus a compile-time offset: the swizzle bit
     // of the rows a lane touches does not depend on the unrolled index.
@@ -288,9 +352,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         for (int i = 0; i < kStage; ++i)
             *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = st[i];
     };
-    load_tile(tile0, st0);
-    load_tile(tile0 + 1, st1);
-
     const float *tail = s_qt + (kHW * ht + c) * kRot;
     u32x4 qhi[kKs], qlo[kKs];
     float m_run = -INFINITY, l_run = 0.f;
@@ -298,6 +359,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 #pragma unroll
     for (int b = 0; b < kDB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // Fragments for the first row format.
+    const int tmid = tile1 < tile_raw ? tile1 : (tile0 > tile_raw ? tile0 : tile_raw);
+    if (active) {
+        if (tile0 < tmid) pack_q_frags<true>(qv, tail, d0, g, qhi, qlo);
+        else pack_q_frags<false>(qv, tail, d0, g, qhi, qlo);
+    }
     store_tile(0, st0);
     __syncthreads();
 
@@ -428,13 +495,13 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         }
         if (tt < tb) step(f16_tag, tt, 0, st0, st1);
     };
-    const int tmid = tile1 < tile_raw ? tile1 : (tile0 > tile_raw ? tile0 : tile_raw);
-    if (tile0 < tmid) {
-        if (active) load_q_frags<true, LO_ALL>(a, q, h0 + c, tail, d0, g, qhi, qlo);
-        run(std::true_type{}, tile0, tmid);
-    }
+    if (tile0 < tmid) run(std::true_type{}, tile0, tmid);
     if (tmid < tile1) {
-        if (active) load_q_frags<false, LO_ALL>(a, q, h0 + c, tail, d0, g, qhi, qlo);
+        if (active && tile0 < tmid) {
+            float qv2[kKs][8];
+            load_q_plain<LO_ALL>(a, q, h0 + c, d0, g, qv2);
+            pack_q_frags<false>(qv2, tail, d0, g, qhi, qlo);
+        }
         run(std::false_type{}, tmid, tile1);
     }
 
@@ -567,7 +634,7 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
         if (e != hipSuccess) return e;
         attr_bytes[q_bf16 ? 1 : 0] = lds;
     }
-    MqaArgs a;
+    MqaArgs a = {};
     a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_tiles = p.n_tiles;
     a.tiles_per_chunk = p.tiles_per_chunk; a.n_chunks = p.n_chunks;
     a.N = N;

@@ -45,28 +45,36 @@ __device__ __forceinline__ int64_t cand_count(int64_t nv, int K, const Levels &l
     return c;
 }
 
-// Thread t receives src[t*EPT .. t*EPT + EPT - 1] (0 past n, n <= EPT*kNT, n uniform across
-// the workgroup) through an LDS stage of EPT*kNT words: the global loads are lane-consecutive
-// (one 256-byte run per wave instruction) and issued all at once; indices past n are clamped
-// to n - 1, so no load is conditional.  Every thread of the workgroup calls it.
+// Thread t receives src_a/src_b[t*EPT .. t*EPT + EPT - 1] (0 past n, n <= EPT*kNT, n uniform
+// across the workgroup) through LDS stages of EPT*kNT words each: the global loads of both
+// arrays are lane-consecutive (one 256-byte run per wave instruction) and all issued before
+// any is used; indices past n are clamped to n - 1, so no load is conditional.  Every thread
+// of the workgroup calls it.
 template <int EPT>
-__device__ __forceinline__ void load_blocked(const uint32_t *__restrict__ src, int n, uint32_t (&v)[EPT],
-                                             uint32_t *stage) {
+__device__ __forceinline__ void load_blocked2(const uint32_t *__restrict__ src_a, const uint32_t *__restrict__ src_b,
+                                              int n, uint32_t (&va)[EPT], uint32_t (&vb)[EPT], uint32_t *stage_a,
+                                              uint32_t *stage_b) {
     if (n > 0) {
-        uint32_t x[EPT];
+        uint32_t xa[EPT], xb[EPT];
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const int j = (int)threadIdx.x + i * kNT;
-            x[i] = src[j < n ? j : n - 1];
+            xa[i] = src_a[j < n ? j : n - 1];
+            xb[i] = src_b[j < n ? j : n - 1];
         }
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) stage[(int)threadIdx.x + i * kNT] = x[i];
+        for (int i = 0; i < EPT; ++i) {
+            stage_a[(int)threadIdx.x + i * kNT] = xa[i];
+            stage_b[(int)threadIdx.x + i * kNT] = xb[i];
+        }
     }
     __syncthreads();
     const int j0 = (int)threadIdx.x * EPT;
 #pragma unroll
-    for (int i = 0; i < EPT; ++i) v[i] = j0 + i < n ? stage[j0 + i] : 0u;
-    __syncthreads();
+    for (int i = 0; i < EPT; ++i) {
+        va[i] = j0 + i < n ? stage_a[j0 + i] : 0u;
+        vb[i] = j0 + i < n ? stage_b[j0 + i] : 0u;
+    }
 }
 
 // Exclusive prefix sum over the workgroup.

@@ -89,13 +89,12 @@ __global__ __launch_bounds__(kNT) void topk_cand_kernel(int64_t N, int K, Levels
     const int n = rem <= 0 ? 0 : (rem < chunk ? (int)rem : chunk);
     const uint32_t *ik = in_keys + q * in_stride + c0;
     const int32_t *ii = in_ids + q * in_stride + c0;
-    __shared__ uint32_t stage[EPT * kNT];
+    __shared__ uint32_t stage[2][EPT * kNT];
     uint32_t key[EPT];
     int32_t id[EPT];
-    load_blocked<EPT>(ik, n, key, stage);
     {
         uint32_t tmp[EPT];
-        load_blocked<EPT>(reinterpret_cast<const uint32_t *>(ii), n, tmp, stage);
+        load_blocked2<EPT>(ik, reinterpret_cast<const uint32_t *>(ii), n, key, tmp, stage[0], stage[1]);
 #pragma unroll
         for (int i = 0; i < EPT; ++i) id[i] = (int32_t)tmp[i];
     }

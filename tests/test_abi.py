@@ -103,6 +103,7 @@ def test_mqa_validation(L):
     assert need > 0                       # one query: the union is split over workgroups
     assert _mqa(L, ws=None, ws_bytes=0) == -5
     assert _mqa(L, ws_bytes=need - 1) == -5
+    assert _mqa(L, U=1 << 16, T=1 << 9) == -2     # U*T above 2^24 (keeps every grid below 2^31)
 
 
 def test_rope_validation(L):
