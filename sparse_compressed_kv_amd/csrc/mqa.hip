@@ -57,10 +57,12 @@ constexpr int kDB = kDH / 16;                 // 16-dim blocks of PV per wave (1
 constexpr int kTile = 32;                     // union rows per tile
 constexpr int kRowStride = 1056;              // LDS bytes per row (1024 + 32)
 constexpr int kTileBytes = kTile * kRowStride;
-constexpr int kXchBytes = kWaves * 2 * kWave * 16;           // partial logits of every wave
+constexpr int kXchBytes = kWaves * 2 * kWave * 16;           // partial logits of every wave (one of two)
 constexpr int kStage = kTile / kWaves;        // rows each wave stages per tile (4)
 constexpr int kQtBytes = kHG * kRot * 4;                     // rotated query tails of the 64 heads (f32)
-constexpr int kLdsBytes = 2 * kTileBytes + kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
+constexpr int kTileBufs = 3;                 // tile buffers in LDS: one barrier per tile
+constexpr int kLdsBytes = kTileBufs * kTileBytes + 2 * kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
+constexpr int kPadTiles = 3;                 // row-table padding for the look-ahead loads past a chunk's end
 constexpr int kRowRegs = 2;            // row-table entries per thread loaded ahead of the first gathers
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[64], l[64], O[64][512]
 constexpr float kRescale = 8.f;               // softmax reference moves when a logit exceeds it by this
@@ -199,8 +201,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *tiles = smem;
-    f32x4 *xch = reinterpret_cast<f32x4 *>(smem + 2 * kTileBytes);
-    float *s_qt = reinterpret_cast<float *>(smem + 2 * kTileBytes + kXchBytes);   // [64 heads][64]
+    f32x4 *xch = reinterpret_cast<f32x4 *>(smem + kTileBufs * kTileBytes);   // two exchange buffers
+    float *s_qt = reinterpret_cast<float *>(smem + kTileBufs * kTileBytes + 2 * kXchBytes);   // [64 heads][64]
     int32_t *s_row = reinterpret_cast<int32_t *>(smem + kLdsBytes);   // per union row: comp row, -2 raw, -1 none
 
     // Workgroup -> (query, chunk, head group), in 32-bit arithmetic: the grid is below 2^31
@@ -248,12 +250,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     // Set-up loads first, then the first two tiles' row gathers, then the set-up's use of its
     // loads: vector loads complete in issue order, so a gather issued before the set-up's own
     // loads would hold the set-up up until the rows arrive.
-    //  - row table of this chunk's union rows from idx, plus two tiles of padding for the
-    //    look-ahead loads past the chunk's end (the first kRowRegs entries per thread are
+    //  - row table of this chunk's union rows from idx, plus kPadTiles tiles of padding for
+    //    the look-ahead loads past the chunk's end (the first kRowRegs entries per thread are
     //    loaded into registers here, any further ones after the gathers);
     const int64_t pos = a.pos[q];
     const int rho0 = tile0 * kTile;
-    const int n_rows = (tile1 - tile0 + 2) * kTile;
+    const int n_rows = (tile1 - tile0 + kPadTiles) * kTile;
     int32_t rv[kRowRegs];
 #pragma unroll
     for (int k = 0; k < kRowRegs; ++k) {
@@ -366,16 +368,28 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         else pack_q_frags<false>(qv, tail, d0, g, qhi, qlo);
     }
     store_tile(0, st0);
+    load_tile(tile0 + 2, st0);
+    // Waves w and w + 4 share a SIMD.  Between two barriers both would otherwise run the
+    // same phases in lock-step (softmax on the VALU while the matrix core idles, then both
+    // queue their MFMAs); a higher issue priority for waves 0-3 lets them run ahead, so one
+    // wave's softmax and LDS work overlap the other's MFMAs.
+    if (wave < kWaves / 2) __builtin_amdgcn_s_setprio(1);
     __syncthreads();
 
-    // One tile: `ld` is the register stage that held tile tt (already in LDS) and now takes
-    // tile tt+2; `sv` holds tile tt+1, stored into the other buffer at the end.  F16: raw
-    // rows (f16 MFMA), else compressed rows (bf16 MFMA).
-    auto step = [&](auto f16_tag, int tt, int buf, u32x4 (&ld)[kStage], const u32x4 (&sv)[kStage])
+    // One tile, one barrier.  Tile i (counted from tile0) sits in LDS buffer i % 3 and is
+    // staged through registers two steps ahead.  On entry `sv` holds tile tt+1: it goes into
+    // buffer `bnext` (whose last tile, tt-2, every wave finished before the barrier of step
+    // tt-1), and `sv` then takes tile tt+3.  The barrier after the logit exchange publishes
+    // both the partial logits (exchange buffer `xb`, alternating by step) and tile tt+1.
+    // F16: raw rows (f16 MFMA), else compressed rows (bf16 MFMA).
+    auto step = [&](auto f16_tag, auto xb_tag, int tt, int bcur, int bnext, u32x4 (&sv)[kStage])
         __attribute__((always_inline)) {
         constexpr bool F16 = decltype(f16_tag)::value;
-        load_tile(tt + 2, ld);
-        const unsigned char *tb = tiles + buf * kTileBytes;
+        constexpr int kXb = decltype(xb_tag)::value;
+        store_tile(bnext, sv);
+        load_tile(tt + 3, sv);
+        const unsigned char *tb = tiles + bcur * kTileBytes;
+        f32x4 *xc = xch + kXb * (kXchBytes / 16);
 
         // ---- QK: partial logits of 32 rows x this wave's 16 heads over its 256 dims;
         // hi and lo products go to separate accumulators (two short chains, not one long).
@@ -402,14 +416,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
             }
         }
 #pragma unroll
-        for (int rt = 0; rt < 2; ++rt) xch[(wave * 2 + rt) * kWave + lane] = acc[rt] + acl[rt];
+        for (int rt = 0; rt < 2; ++rt) xc[(wave * 2 + rt) * kWave + lane] = acc[rt] + acl[rt];
         __syncthreads();
 
         if (active) {
             // full logits: lower half + upper half, the same order in both waves of the pair
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
-                acc[rt] = xch[((2 * ht) * 2 + rt) * kWave + lane] + xch[((2 * ht + 1) * 2 + rt) * kWave + lane];
+                acc[rt] = xc[((2 * ht) * 2 + rt) * kWave + lane] + xc[((2 * ht + 1) * 2 + rt) * kWave + lane];
 
             // ---- mask, online softmax (head c; rows 16rt + 4g + r)
             float p[2][4];
@@ -475,25 +489,32 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
                 }
             }
         }
-        // Tile tt+1 (loaded one step ago) into the other buffer, whose previous tile every
-        // wave finished reading before the last barrier.  Past the chunk's end this stores
-        // padding rows that are never read.
-        store_tile(buf ^ 1, sv);
-        __syncthreads();
     };
-    // Tiles [ta, tb) of one row format; unrolled by two so that both register stages stay
-    // statically named; the buffer parity continues across calls.
+    // Tiles [ta, tb) of one row format; unrolled by two so that the register stages and the
+    // exchange buffers stay statically named (tile i: stage st1 if i is even, st0 if odd;
+    // exchange buffer i & 1); the LDS buffer i % 3 rotates at run time.  Both continue across
+    // calls.
+    using X0 = std::integral_constant<int, 0>;
+    using X1 = std::integral_constant<int, 1>;
+    int bcur = 0;
+    auto next3 = [](int b) __attribute__((always_inline)) { return b == 2 ? 0 : b + 1; };
     auto run = [&](auto f16_tag, int ta, int tb) __attribute__((always_inline)) {
         int tt = ta;
         if (tt < tb && ((tt - tile0) & 1)) {
-            step(f16_tag, tt, 1, st1, st0);
+            step(f16_tag, X1{}, tt, bcur, next3(bcur), st0);
+            bcur = next3(bcur);
             ++tt;
         }
         for (; tt + 1 < tb; tt += 2) {
-            step(f16_tag, tt, 0, st0, st1);
-            step(f16_tag, tt + 1, 1, st1, st0);
+            step(f16_tag, X0{}, tt, bcur, next3(bcur), st1);
+            bcur = next3(bcur);
+            step(f16_tag, X1{}, tt + 1, bcur, next3(bcur), st0);
+            bcur = next3(bcur);
         }
-        if (tt < tb) step(f16_tag, tt, 0, st0, st1);
+        if (tt < tb) {
+            step(f16_tag, X0{}, tt, bcur, next3(bcur), st1);
+            bcur = next3(bcur);
+        }
     };
     if (tile0 < tmid) run(std::true_type{}, tile0, tmid);
     if (tmid < tile1) {
@@ -625,7 +646,7 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
                       hipStream_t stream)
 {
     const MqaPlan p = plan_mqa(U, T, H, W, K);
-    const int lds = kLdsBytes + 4 * kTile * (p.tiles_per_chunk + 2);
+    const int lds = kLdsBytes + 4 * kTile * (p.tiles_per_chunk + kPadTiles);
     static int attr_bytes[2] = {0, 0};
     const void *fn = q_bf16 ? reinterpret_cast<const void *>(sparse_mqa_kernel<false>)
                             : reinterpret_cast<const void *>(sparse_mqa_kernel<true>);
