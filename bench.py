@@ -8,10 +8,13 @@ for every unit of the workload.
 Main line: decode at the DeepSeek V4 Flash shape, 43 independent layers with
 N = 65,536 compressed rows each (64 query heads x 512 dims, one KV head,
 128-row raw window, indexer 64 x 128, top-k 512).  `value` is decode
-tokens/s/layer = layer-units per second.  Also measured in the same run: the
-same decode at N = 16,384 rows, 8 sessions at N = 262,144, the Pro shape (4
-sessions, 128 heads, top-1024, N = 65,536), and chunked prefill (2,048 queries,
-N = 8,192).
+tokens/s/layer = layer-units per second.  The main line is also timed with the
+step captured as a HIP graph (each replay checked against the eager result),
+and per step (p10 / p50 / p90).  Also measured in the same run: the same
+decode at N = 16,384 and 32,768 rows, 8 sessions at N = 262,144, the Pro shape
+(4 sessions, 128 heads, top-1024, N = 65,536), and chunked prefill (2,048
+queries, N = 8,192).  The CPU baseline runs the oracle on the main line's
+units and also reports how the GPU results agree with it.
 
 Inputs are synthetic (synth.inputs), uploaded to HBM before timing.  Several
 replicas of each input set are rotated step by step so that no step finds its
@@ -112,6 +115,15 @@ class Bench:
         self.sep = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=False)
         self.nvis = w.vis_base is not None
 
+    def one(self, i: int, stream):
+        """Step i: both calls on `stream`, over input replica i mod replicas."""
+        w, st = self.w, self.step
+        d = self.reps[i % len(self.reps)]
+        nv = d["n_vis"] if self.nvis else None
+        st.select(d, n_vis=nv, stream=stream)
+        self.ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W, out=st.out,
+                            workspace=st.ws_mqa, stream=stream)
+
     def run(self, steps: int, warmup: int):
         torch, ops, w = self.torch, self.ops, self.w
         st, sep = self.step, self.sep
@@ -119,11 +131,7 @@ class Bench:
         n = len(self.reps)
 
         def one(i):
-            d = self.reps[i % n]
-            nv = d["n_vis"] if self.nvis else None
-            st.select(d, n_vis=nv, stream=stream)
-            ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W, out=st.out,
-                           workspace=st.ws_mqa, stream=stream)
+            self.one(i, stream)
 
         for i in range(warmup):
             one(i)
@@ -167,14 +175,86 @@ class Bench:
         return {"ms_per_step": total_ms / steps, "wall_ms_per_step": 1e3 * wall / steps,
                 **{f"{k}_ms": v for k, v in k_ms.items()}}
 
+    def percentiles(self, steps: int):
+        """Per-step times (an event pair around every step, so this pass is not the headline)."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for i in range(steps):
+            self.one(i, stream)
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        t = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+        return {"p10_ms": t[steps // 10], "p50_ms": t[steps // 2], "p90_ms": t[(9 * steps) // 10]}
+
+    def graph_run(self, steps: int):
+        """The step captured once per input replica as a HIP graph and replayed in rotation.
+        Before timing, every graph is replayed twice with eager steps in between, and each
+        replay's selection and output are compared with the eager result of its replica."""
+        torch = self.torch
+        st = self.step
+        n = len(self.reps)
+        cur = torch.cuda.current_stream()
+        ref = []
+        for j in range(n):
+            self.one(j, cur)
+            torch.cuda.synchronize()
+            ref.append((st.idx.clone(), st.out.clone()))
+        graphs = []
+        side = torch.cuda.Stream()
+        for j in range(n):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                self.one(j, torch.cuda.current_stream())
+            graphs.append(g)
+        torch.cuda.synchronize()
+        same = True
+        for _ in range(2):
+            for j in range(n):
+                graphs[j].replay()
+                torch.cuda.synchronize()
+                same = same and torch.equal(st.idx, ref[j][0]) and torch.equal(st.out, ref[j][1])
+                self.one(j + 1, cur)
+                torch.cuda.synchronize()
+        for i in range(n):
+            graphs[i % n].replay()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0.record(cur)
+        for i in range(steps):
+            graphs[i % n].replay()
+        t1.record(cur)
+        torch.cuda.synchronize()
+        del graphs
+        return {"ms_per_step": t0.elapsed_time(t1) / steps, "replays_match_eager": bool(same)}
+
+    def results(self, j: int = 0):
+        """Host copies of the selection, the output and the separate call's scores for replica j."""
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        d = self.reps[j]
+        nv = d["n_vis"] if self.nvis else None
+        self.one(j, stream)
+        self.ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv, out=self.sep.scores, stream=stream)
+        torch.cuda.synchronize()
+        return {"idx": self.step.idx.cpu().numpy(), "out": self.step.out.cpu().numpy(),
+                "scores": self.sep.scores.cpu().numpy()}
+
 
 def replicas_for(w) -> int:
     per = w.U * (w.N * 128 * 2 + w.K * 512 * 2)          # bytes a step streams from its inputs
     return max(2, math.ceil(2 * LLC_BYTES / max(per, 1)) + 1)
 
 
-def cpu_baseline(w, x, budget_s: float = 20.0):
-    """The oracle, as it stands, on the host cores: whole decode units of the same workload."""
+def cpu_baseline(w, x, gpu=None, budget_s: float = 20.0):
+    """The oracle, as it stands, on the host cores: whole decode units of the same workload.
+    With `gpu` (host copies of the GPU's selection, output and scores for the same inputs), also
+    how the GPU results agree with the oracle's on the units it ran."""
+    import numpy as np
+
     from oracle import oracle
 
     cores = len(os.sched_getaffinity(0))
@@ -186,11 +266,36 @@ def cpu_baseline(w, x, budget_s: float = 20.0):
     n = min(n, w.U * w.T)
     sel = list(range(n))
     t0 = time.perf_counter()
-    oracle.step(w, x, sel=sel, nthreads=min(cores, n))
+    ref = oracle.step(w, x, sel=sel, nthreads=min(cores, n))
     el = time.perf_counter() - t0
-    return {"value": n / el, "unit": "decode tokens/s/layer", "cores": min(cores, n), "kind": "oracle",
-            "sample": f"{n} of {w.U} layer-units of {w.name} (full indexer, top-k and attention per unit), "
-                      f"1 pass, {el:.1f} s on {min(cores, n)} threads; 1-thread unit time {per_unit:.2f} s"}
+    rec = {"value": n / el, "unit": "decode tokens/s/layer", "cores": min(cores, n), "kind": "oracle",
+           "sample": f"{n} of {w.U} layer-units of {w.name} (full indexer, top-k and attention per unit), "
+                     f"1 pass, {el:.1f} s on {min(cores, n)} threads; 1-thread unit time {per_unit:.2f} s"}
+    if gpu is not None:
+        g_idx = gpu["idx"].reshape(w.U * w.T, w.K)[:n]
+        g_out = gpu["out"].reshape(w.U * w.T, w.H, 512)[:n]
+        g_sc = gpu["scores"].reshape(w.U * w.T, w.N)[:n]
+        attn_err, score_err, outside, inside = 0.0, 0.0, 0, 0
+        for i in range(n):
+            o = ref["out"][i]
+            attn_err = max(attn_err, float(np.max(np.abs(g_out[i] - o)) / np.max(np.abs(o))))
+            s = ref["scores"][i]
+            vis = np.isfinite(s)
+            if vis.any():
+                score_err = max(score_err, float(np.max(np.abs(g_sc[i][vis] - s[vis])) / np.max(np.abs(s[vis]))))
+            r_set = set(int(j) for j in ref["idx"][i] if j >= 0)
+            g_set = set(int(j) for j in g_idx[i] if j >= 0)
+            kth = min((s[j] for j in r_set), default=0.0)
+            for j in r_set ^ g_set:
+                if abs(s[j] - kth) <= 1e-5 * abs(kth):
+                    inside += 1
+                else:
+                    outside += 1
+        rec["agreement"] = {"units": n, "max_normwise_attention_error": attn_err,
+                            "max_score_rel_error": score_err, "topk_diff_rows_inside_tie_band": inside,
+                            "topk_diff_rows_outside_tie_band": outside,
+                            "bounds": {"attention": 2e-3, "tie_band_rel": 1e-5}}
+    return rec
 
 
 def traffic_for(kernel_hash: str, units: int):
@@ -243,6 +348,10 @@ def main():
     b = Bench(w, x, reps)
     r = b.run(args.steps, args.warmup)
     log(f"[bench] {w.name}: {r}")
+    pct = b.percentiles(min(args.steps, 100))
+    gr = b.graph_run(args.steps)
+    log(f"[bench] {w.name}: per step {pct}, graph {gr}")
+    gpu_res = b.results(0) if not args.no_cpu else None
     units = w.U * w.T
     value = units / (r["ms_per_step"] / 1e3)
     sel_bytes = units * select_bytes_per_unit(w.N, w.K)
@@ -277,30 +386,18 @@ def main():
                  "kernel_us": {"indexer_topk": r["select_ms"] * 1e3, "mqa": r["mqa_ms"] * 1e3,
                                "indexer_alone": r["indexer_ms"] * 1e3, "topk_alone": r["topk_ms"] * 1e3},
                  "wall_ms_per_step": r["wall_ms_per_step"]},
+        "per_step": pct,
+        "hip_graph": {"ms_per_step": gr["ms_per_step"], "value": units / (gr["ms_per_step"] / 1e3),
+                      "replays_match_eager": gr["replays_match_eager"]},
     }
     del b
     torch.cuda.empty_cache()
 
     if not args.only_main:
-        # ---- decode at 16,384 rows (43 layers)
-        w2 = gen.CONFIGS["c2"]
-        x2 = gen.make_config(w2)
-        b2 = Bench(w2, x2, replicas_for(w2))
-        r2 = b2.run(args.steps, args.warmup)
-        log(f"[bench] {w2.name}: {r2}")
-        by2 = w2.U * decode_bytes_per_unit(w2.N, w2.H, w2.K, w2.W)
-        rec["decode_n16384"] = {
-            "workload": w2.name, "value": w2.U / (r2["ms_per_step"] / 1e3), "unit": "decode tokens/s/layer",
-            "ms_per_step": r2["ms_per_step"], "frac_hbm": by2 / (r2["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-            "indexer_topk_frac_hbm": w2.U * select_bytes_per_unit(w2.N, w2.K) / (r2["select_ms"] / 1e3) / 1e9
-            / HBM_PEAK_GBS,
-            "kernel_us": {"indexer_topk": r2["select_ms"] * 1e3, "mqa": r2["mqa_ms"] * 1e3,
-                          "indexer_alone": r2["indexer_ms"] * 1e3, "topk_alone": r2["topk_ms"] * 1e3},
-        }
-        del b2, x2
-        torch.cuda.empty_cache()
-        # ---- long context (8 sessions x 262,144 rows) and the Pro shape (128 heads, top-1024)
-        for key, name in (("c4", "decode_8sessions_n262144"), ("c5", "pro_decode_4sessions_n65536")):
+        # ---- decode at 16,384 and 32,768 rows (43 layers), long context (8 sessions x 262,144
+        # rows) and the Pro shape (128 heads, top-1024)
+        for key, name in (("c2", "decode_n16384"), ("c2_32k", "decode_n32768"), ("c4", "decode_8sessions_n262144"),
+                          ("c5", "pro_decode_4sessions_n65536")):
             w4 = gen.CONFIGS[key]
             x4 = gen.make_config(w4)
             b4 = Bench(w4, x4, replicas_for(w4))
@@ -346,7 +443,7 @@ def main():
         rec["copy_probe_bytes"] = n
 
     if not args.no_cpu:
-        rec["cpu_baseline"] = cpu_baseline(w, x)
+        rec["cpu_baseline"] = cpu_baseline(w, x, gpu_res)
     print(json.dumps(rec), flush=True)
 
 
