@@ -3,7 +3,8 @@
     python -m sparse_compressed_kv_amd.build
 
 Every HIP source under csrc/ is compiled for gfx950 only; packed-fp32 VALU
-ops are disabled (-packed-fp32-ops) for all device code.
+ops are disabled (-packed-fp32-ops) for all device code, and MFMA
+accumulators are kept in ordinary VGPRs (-amdgpu-mfma-vgpr-form).
 """
 from __future__ import annotations
 
@@ -23,6 +24,9 @@ ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: the indexer epilogues read every accumulator, and the
+    # accumulator-register form costs one v_accvgpr_read per value plus extra registers.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", os.path.join(ROOT, "include"),
 ]
 
