@@ -242,8 +242,10 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
     if (T >= kIndexerManyQueries) {
         const int n_qb = (T + kPQ - 1) / kPQ;
         const int64_t wgs = (int64_t)U * n_qb;
-        // about three workgroups per CU in all, never a split shorter than 4 tiles
-        int n_split = (int)((768 + wgs - 1) / wgs);
+        // Three workgroups fit on a CU (163 VGPRs); split the key range so that about two full
+        // rounds of them run (a sweep over 512..6,144 workgroups at 2,048 queries: 1,536 is
+        // fastest, 152 us against 163 us for 1,024), never a split shorter than 4 tiles.
+        int n_split = (int)((1536 + wgs - 1) / wgs);
         const int64_t max_split = (N + 4 * kPTile - 1) / (4 * kPTile);
         if (n_split > max_split) n_split = (int)max_split;
         if (n_split < 1) n_split = 1;
