@@ -60,6 +60,7 @@ typedef enum { DS4A_F32 = 0, DS4A_BF16 = 1, DS4A_F16 = 2 } ds4a_dtype;
 #define DS4A_MAX_HEADS 128        /* H : a multiple of 16 up to 128 (Flash 64, Pro 128) */
 #define DS4A_MAX_TOPK 2048        /* K : 1..2048 (Flash 512, Pro 1024)          */
 #define DS4A_MAX_WINDOW 1024      /* W : a multiple of 32 up to 1024 (n_swa = 128) */
+#define DS4A_MAX_DENSE_ROWS (1 << 20) /* N of ds4a_dense_mqa: 0..2^20 compressed rows  */
 
 /* A1 — indexer scores (section 3-3: the indexer's own thin query scores every
  * compressed row).  For unit u, query t and row j < n_vis[u][t]:
@@ -97,9 +98,10 @@ int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores,
  * rows that reach the main attention).  idx receives exactly the set that
  * ds4a_topk_select returns on the scores of ds4a_indexer_score for the same
  * arguments (the scores are computed by the same device code, bit for bit).
- * With T < 4 and at least 128 chunks of 4096 rows in the call, the scores never
- * reach memory: each chunk of a query is scored and its top-K selected on chip,
- * and only (score, row) candidates are kept in the workspace; otherwise the
+ * With T < 4 and at least 128 chunk workgroups in the call (chunks of 2,048 to
+ * 8,192 rows, sized per call so that the busiest CU carries the least), the scores
+ * never reach memory: each chunk of a query is scored and its top-K selected on
+ * chip, and only (score, row) candidates are kept in the workspace; otherwise the
  * scores are written to the workspace and selected from there.
  * Arguments as for ds4a_indexer_score and ds4a_topk_select.
  *   workspace: ds4a_workspace_bytes(2, U, T, N, K, 0, 0) bytes (0 -> NULL allowed)
@@ -138,6 +140,26 @@ int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int
                     float scale, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Dense attention for the layers that have no indexer (section 3-2 of the same
+ * page: ratio-128 layers fold 128 tokens into one row and are few enough to be
+ * read whole; ratio-0 layers, the first two of Flash, keep only the raw window).
+ * As ds4a_sparse_mqa, with the union
+ *   union   = raw rows raw_kv[u][t + r], r = 0..W-1, then comp_kv[u][j] for every
+ *             j < n_vis[u][t] (all N if n_vis is NULL), in row order
+ * and the same arithmetic (same device code, chosen at compile time).
+ *   N        : compressed rows per unit, 0..DS4A_MAX_DENSE_ROWS (0: raw window
+ *              only, comp_kv may then be NULL); W + N >= 1
+ *   n_vis    : int32 [U][T] or NULL; values are clamped to [0, N]
+ *   workspace: ds4a_workspace_bytes(3, U, T, N, 0, H, W) bytes (0 -> NULL allowed)
+ * Other arguments and errors as for ds4a_sparse_mqa; DS4A_E_UNSUPPORTED also when
+ * the call would need 2^31 or more workgroups.
+ */
+int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
+                   const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                   const void *raw_kv, const void *comp_kv, const int32_t *n_vis,
+                   float scale, float *out,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* A3 alone, for inspection: writes the rotated query as f32 [U][T][H][D], using
  * the same device code as ds4a_sparse_mqa's prologue (fp64 angle and rotation,
  * rounded once to f32).  Same argument rules as ds4a_sparse_mqa. */
@@ -145,8 +167,9 @@ int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtyp
                 const int64_t *q_pos, double rope_theta, float *q_out, void *stream);
 
 /* Workspace bytes for `which` = 0 (ds4a_topk_select; H and W ignored),
- * 1 (ds4a_sparse_mqa) or 2 (ds4a_indexer_topk; H and W ignored).  0 means no
- * workspace is needed (NULL is accepted), or that the arguments are invalid.
+ * 1 (ds4a_sparse_mqa), 2 (ds4a_indexer_topk; H and W ignored) or 3
+ * (ds4a_dense_mqa; K ignored, N may be 0).  0 means no workspace is needed
+ * (NULL is accepted), or that the arguments are invalid.
  * Host-only, never touches the GPU. */
 size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W);
 

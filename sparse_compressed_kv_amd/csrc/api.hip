@@ -87,6 +87,11 @@ int ds4a_version(void) { return DS4A_VERSION; }
 const char *ds4a_last_error(void) { return g_err; }
 
 size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W) {
+    if (which == 3) {                        // ds4a_dense_mqa: K ignored, N >= 0
+        if (U < 1 || T < 1 || (int64_t)U * T > (int64_t(1) << 24) || N < 0 || N > DS4A_MAX_DENSE_ROWS) return 0;
+        if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW || W + N < 1) return 0;
+        return ds4a::plan_mqa(U, T, H, W, (int)N).workspace_bytes;
+    }
     if (U < 1 || T < 1 || N < 1 || N > kMaxRows || K < 1 || K > DS4A_MAX_TOPK) return 0;
     if (which == 0) return ds4a::topk_workspace_bytes((int64_t)U * T, N, K);
     if (which == 2) return ds4a::indexer_topk_workspace_bytes(U, T, N, K);
@@ -184,8 +189,46 @@ int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int
     }
     return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
                                            static_cast<const uint16_t *>(raw_kv),
-                                           static_cast<const uint16_t *>(comp_kv), idx, scale, out, workspace,
-                                           static_cast<hipStream_t>(stream)));
+                                           static_cast<const uint16_t *>(comp_kv), idx, nullptr, scale, out,
+                                           workspace, static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,
+                   const int64_t *q_pos, double rope_theta, const void *raw_kv, const void *comp_kv,
+                   const int32_t *n_vis, float scale, float *out, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    const char *fn = "ds4a_dense_mqa";
+    if (U < 1 || T < 1) return fail(DS4A_E_SHAPE, "%s: U=%d and T=%d must be >= 1", fn, U, T);
+    if ((int64_t)U * T > (int64_t(1) << 24)) return fail(DS4A_E_SHAPE, "%s: U*T=%lld too large", fn, (long long)U * T);
+    if (N < 0) return fail(DS4A_E_SHAPE, "%s: N=%lld must be >= 0", fn, (long long)N);
+    if (N > DS4A_MAX_DENSE_ROWS)
+        return fail(DS4A_E_UNSUPPORTED, "%s: N=%lld (at most %d)", fn, (long long)N, DS4A_MAX_DENSE_ROWS);
+    // the shape rules of ds4a_sparse_mqa, with K standing for the N dense rows (>= 1 there)
+    if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, W, N > 0 ? N : 1, 1, q_dtype, rope_theta)) return rc;
+    if (W + N < 1) return fail(DS4A_E_SHAPE, "%s: W=%d and N=0: nothing to attend", fn, W);
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+        return fail(DS4A_E_SHAPE, "%s: scale must be finite", fn);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_pos);
+    if (W > 0) REQUIRE_PTR(raw_kv);
+    if (N > 0) REQUIRE_PTR(comp_kv);
+    OPTIONAL_PTR(n_vis);
+    REQUIRE_PTR(out);
+    const ds4a::MqaPlan plan = ds4a::plan_mqa(U, T, H, W, (int)N);
+    if ((int64_t)U * T * plan.n_chunks * plan.n_hg >= (int64_t(1) << 31))
+        return fail(DS4A_E_UNSUPPORTED, "%s: U*T=%lld queries over %lld rows is more than one launch holds", fn,
+                    (long long)U * T, (long long)N);
+    const size_t need = plan.workspace_bytes;
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, (int)N, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
+                                           static_cast<const uint16_t *>(raw_kv),
+                                           static_cast<const uint16_t *>(comp_kv), nullptr, n_vis, scale, out,
+                                           workspace, static_cast<hipStream_t>(stream)));
 }
 
 int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtype, const int64_t *q_pos,

@@ -42,9 +42,11 @@ struct MqaPlan {
     size_t workspace_bytes;
 };
 MqaPlan plan_mqa(int U, int T, int H, int W, int K);
+// idx == nullptr: dense attention, the union is the raw window plus compressed rows
+// 0 .. n_vis-1 (K must equal N; n_vis may be nullptr for all N).
 hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                       const int64_t *q_pos, double theta, const uint16_t *raw, const uint16_t *comp,
-                      const int32_t *idx, float scale, float *out, void *workspace,
+                      const int32_t *idx, const int32_t *n_vis, float scale, float *out, void *workspace,
                       hipStream_t stream);
 hipError_t launch_rope(int U, int T, int H, const void *q, int q_bf16, const int64_t *q_pos,
                        double theta, float *q_out, hipStream_t stream);

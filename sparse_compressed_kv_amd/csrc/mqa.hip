@@ -63,6 +63,7 @@ constexpr int kQtBytes = kHG * kRot * 4;                     // rotated query ta
 constexpr int kTileBufs = 3;                 // tile buffers in LDS: one barrier per tile
 constexpr int kLdsBytes = kTileBufs * kTileBytes + 2 * kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
 constexpr int kPadTiles = 3;                 // row-table padding for the look-ahead loads past a chunk's end
+constexpr int kMaxTilesPerChunk = 96;         // LDS: kLdsBytes + 128 B per tile of row table <= 160 KiB
 constexpr int kRowRegs = 2;            // row-table entries per thread loaded ahead of the first gathers
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[64], l[64], O[64][512]
 constexpr float kRescale = 8.f;               // softmax reference moves when a logit exceeds it by this
@@ -85,7 +86,8 @@ struct MqaArgs {
     const int64_t *pos;
     const uint16_t *raw;
     const uint16_t *comp;
-    const int32_t *idx;
+    const int32_t *idx;                      // sparse: [U][T][K]; dense: unused
+    const int32_t *n_vis;                    // dense: visible compressed rows per query, or NULL (all N)
     float scale;
     float *out;
     float *part;
@@ -195,8 +197,9 @@ __device__ __forceinline__ void pack_q_frags(const float (&v)[kKs][8], const flo
 }
 
 // LO_ALL: the query is f32, so every k-step carries a lo half; otherwise (bf16 query)
-// only the rotated tail does.
-template <bool LO_ALL>
+// only the rotated tail does.  DENSE: the union is the raw window plus compressed rows
+// 0 .. n_vis-1 in order (a.K = N; no index list), else the raw window plus idx's rows.
+template <bool LO_ALL, bool DENSE>
 __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -233,19 +236,23 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     // Union row rho of this chunk: a compressed row, -2 for a raw row, -1 for none (past the
     // chunk's end, a -1 or out-of-range index, past K).  idx is always read, at a clamped
     // position (idx_at), so a run of these loads issues back to back with no branch.
+    const int64_t j_lim = DENSE ? clamp_nvis(a.n_vis, q, a.N) : a.N;   // compressed rows that may enter
     auto idx_at = [&](int rho) __attribute__((always_inline)) -> int32_t {
         const int k = rho - a.W;
+        if (DENSE) return k;
         return idx_q[k < 0 ? 0 : (k < a.K ? k : a.K - 1)];
     };
     auto union_row = [&](int rho, int32_t j) __attribute__((always_inline)) -> int32_t {
         const int k = rho - a.W;
-        const int32_t comp = (k < a.K && j >= 0 && (int64_t)j < a.N) ? j : -1;
+        const int32_t comp = (k < a.K && j >= 0 && (int64_t)j < j_lim) ? j : -1;
         return rho >= tile1 * kTile ? -1 : (k < 0 ? -2 : comp);
     };
-    // A row that takes no part (-1) is read from compressed row 0 (N >= 1): it is finite,
-    // its logit is masked to -inf and its probability is 0, so no branch guards the load.
+    // A row that takes no part (-1) is read from compressed row 0, or from raw row 0 when there
+    // are no compressed rows (a raw-window-only call): it is finite, its logit is masked to
+    // -inf and its probability is 0, so no branch guards the load.
+    const uint16_t *none_row = a.N > 0 ? comp_u : raw_q;
     auto union_ptr = [&](int rho, int32_t v) __attribute__((always_inline)) -> const uint16_t * {
-        return v == -2 ? raw_q + (int64_t)rho * kD : comp_u + (int64_t)(v < 0 ? 0 : v) * kD;
+        return v == -2 ? raw_q + (int64_t)rho * kD : (v >= 0 ? comp_u + (int64_t)v * kD : none_row);
     };
     // Set-up loads first, then the first two tiles' row gathers, then the set-up's use of its
     // loads: vector loads complete in issue order, so a gather issued before the set-up's own
@@ -635,6 +642,7 @@ MqaPlan plan_mqa(int U, int T, int H, int W, int K) {
     if (want < 1) want = 1;
     if (want > p.n_tiles) want = p.n_tiles;
     p.tiles_per_chunk = (int)((p.n_tiles + want - 1) / want);
+    if (p.tiles_per_chunk > kMaxTilesPerChunk) p.tiles_per_chunk = kMaxTilesPerChunk;   // row table fits in LDS
     p.n_chunks = (p.n_tiles + p.tiles_per_chunk - 1) / p.tiles_per_chunk;
     p.workspace_bytes = p.n_chunks > 1 ? sizeof(float) * (size_t)items * (size_t)p.n_chunks * kRec : 0;
     return p;
@@ -642,32 +650,34 @@ MqaPlan plan_mqa(int U, int T, int H, int W, int K) {
 
 hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                       const int64_t *q_pos, double theta, const uint16_t *raw, const uint16_t *comp,
-                      const int32_t *idx, float scale, float *out, void *workspace,
+                      const int32_t *idx, const int32_t *n_vis, float scale, float *out, void *workspace,
                       hipStream_t stream)
 {
+    const bool dense = idx == nullptr;       // dense: K = N, rows 0 .. n_vis-1 follow the raw window
     const MqaPlan p = plan_mqa(U, T, H, W, K);
     const int lds = kLdsBytes + 4 * kTile * (p.tiles_per_chunk + kPadTiles);
-    static int attr_bytes[2] = {0, 0};
-    const void *fn = q_bf16 ? reinterpret_cast<const void *>(sparse_mqa_kernel<false>)
-                            : reinterpret_cast<const void *>(sparse_mqa_kernel<true>);
-    if (lds > attr_bytes[q_bf16 ? 1 : 0]) {
-        hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    using Fn = void (*)(MqaArgs);
+    const int variant = (q_bf16 ? 1 : 0) + (dense ? 2 : 0);
+    static const Fn kernels[4] = {sparse_mqa_kernel<true, false>, sparse_mqa_kernel<false, false>,
+                                  sparse_mqa_kernel<true, true>, sparse_mqa_kernel<false, true>};
+    static int attr_bytes[4] = {0, 0, 0, 0};
+    const Fn fn = kernels[variant];
+    if (lds > attr_bytes[variant]) {
+        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
         if (e != hipSuccess) return e;
-        attr_bytes[q_bf16 ? 1 : 0] = lds;
+        attr_bytes[variant] = lds;
     }
     MqaArgs a = {};
     a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_tiles = p.n_tiles;
     a.tiles_per_chunk = p.tiles_per_chunk; a.n_chunks = p.n_chunks;
     a.N = N;
     a.n_items = (int64_t)U * T * p.n_chunks;
-    a.q = q; a.q_bf16 = q_bf16; a.pos = q_pos; a.raw = raw; a.comp = comp; a.idx = idx;
+    a.q = q; a.q_bf16 = q_bf16; a.pos = q_pos; a.raw = raw; a.comp = comp; a.idx = idx; a.n_vis = n_vis;
     a.scale = scale; a.out = out; a.part = static_cast<float *>(workspace);
     a.log2_theta = log2(theta);
     const int64_t blocks = a.n_items * p.n_hg;
-    if (q_bf16)
-        hipLaunchKernelGGL(sparse_mqa_kernel<false>, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
-    else
-        hipLaunchKernelGGL(sparse_mqa_kernel<true>, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(kThreads), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_chunks == 1) return e;
     hipLaunchKernelGGL(mqa_merge_kernel, dim3((unsigned)((int64_t)U * T * p.n_hg * kMergeWgs)), dim3(256), 0, stream,

@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
     L.ds4a_indexer_topk.restype = i32
     L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
     L.ds4a_sparse_mqa.restype = i32
+    L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
+    L.ds4a_dense_mqa.restype = i32
     L.ds4a_rope_q.argtypes = [i32, i32, i32, i32, i32, P, i32, P, dbl, P, P]
     L.ds4a_rope_q.restype = i32
     _lib = L
@@ -201,6 +203,35 @@ def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 1000
         U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta),
         _ptr(raw_kv) if W > 0 else None, _ptr(comp_kv), _ptr(idx), float(scale), _ptr(out), _ptr(ws), nb,
         _stream(stream)))
+    return out
+
+
+def dense_mqa(q, q_pos, raw_kv, comp_kv, scale: float, theta: float = 10000.0, W: int = 128, n_vis=None,
+              out=None, workspace=None, stream=None):
+    """Dense attention (layers without an indexer).  q [U,T,H,512] f32|bf16, q_pos i64 [U,T],
+    raw_kv f16 [U,T+W-1,512] (or None when W = 0), comp_kv bf16 [U,N,512] (N may be 0, or None),
+    n_vis i32 [U,T] or None -> f32 [U,T,H,512]."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    U, T, H, D = q.shape
+    N = 0 if comp_kv is None else comp_kv.shape[1]
+    _need(q, "q", q.dtype)
+    qd = _q_dtype(q)
+    _need(q_pos, "q_pos", torch.int64, (U, T))
+    if W > 0:
+        _need(raw_kv, "raw_kv", torch.float16, (U, T + W - 1, D))
+    if N > 0:
+        _need(comp_kv, "comp_kv", torch.bfloat16, (U, N, D))
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    if out is None:
+        out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (U, T, H, D))
+    ws, nb = _workspace(workspace_bytes(3, U, T, N, 0, H, W), q.device, workspace)
+    _check("ds4a_dense_mqa", lib().ds4a_dense_mqa(
+        U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta),
+        _ptr(raw_kv) if W > 0 else None, _ptr(comp_kv) if N > 0 else None,
+        _ptr(n_vis) if n_vis is not None else None, float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
     return out
 
 

@@ -18,8 +18,8 @@ def L():
 
 def test_exports_every_declared_symbol(L):
     names = ops.declared_symbols()
-    assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_rope_q",
-            "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
+    assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_dense_mqa",
+            "ds4a_rope_q", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -104,6 +104,38 @@ def test_mqa_validation(L):
     assert _mqa(L, ws=None, ws_bytes=0) == -5
     assert _mqa(L, ws_bytes=need - 1) == -5
     assert _mqa(L, U=1 << 16, T=1 << 9) == -2     # U*T above 2^24 (keeps every grid below 2^31)
+
+
+def _dense(L, **kw):
+    a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, q=A, q_dtype=0, q_pos=A, theta=10000.0,
+             raw=A, comp=A, n_vis=None, scale=0.044, out=A, ws=A, ws_bytes=1 << 30)
+    a.update(kw)
+    return L.ds4a_dense_mqa(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["q"], a["q_dtype"],
+                            a["q_pos"], a["theta"], a["raw"], a["comp"], a["n_vis"], a["scale"], a["out"], a["ws"],
+                            a["ws_bytes"], S)
+
+
+def test_dense_mqa_validation(L):
+    assert _dense(L, U=0) == -2
+    assert _dense(L, N=-1) == -2
+    assert _dense(L, N=(1 << 20) + 1) == -3
+    assert _dense(L, W=0, N=0) == -2                 # nothing to attend
+    assert _dense(L, H=40) == -3
+    assert _dense(L, W=100) == -3
+    assert _dense(L, q_dtype=7) == -6
+    assert _dense(L, scale=float("inf")) == -2
+    assert _dense(L, q=None) == -1
+    assert _dense(L, comp=None) == -1                # N > 0 needs the rows
+    assert _dense(L, raw=None) == -1                 # W > 0 needs the window
+    assert _dense(L, n_vis=MIS) == -4
+    need = ops.workspace_bytes(3, 1, 1, 1000, 0, 64, 128)
+    assert need > 0                                  # one query: split over workgroups
+    assert _dense(L, ws=None, ws_bytes=0) == -5
+    assert _dense(L, N=0, comp=None, ws=None, ws_bytes=0) == -5   # raw only: comp may be NULL
+    assert ops.workspace_bytes(3, 1, 1, 0, 0, 64, 0) == 0          # nothing to attend
+    assert ops.workspace_bytes(3, 1, 1, -1, 0, 64, 128) == 0
+    assert ops.workspace_bytes(3, 300, 1, 0, 0, 64, 128) == 0      # enough queries: no split
+    assert ops.workspace_bytes(3, 1, 300, 4000, 0, 16, 32) > 0     # 127 tiles > 96 per chunk: split
 
 
 def test_rope_validation(L):

@@ -263,6 +263,61 @@ def test_mqa_matches_oracle_on_given_sets(H, qd, W, K):
             assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, e)
 
 
+DENSE_CASES = [
+    # (H, q dtype, W, N, U, T, n_vis): ratio-128 layers (all compressed rows, no indexer) and
+    # ratio-0 layers (raw window only), decode and prefill-like shapes
+    dict(H=64, qd="f32", W=128, N=2048, U=3, T=1, nv=None),
+    dict(H=64, qd="f32", W=128, N=0, U=2, T=1, nv=None),
+    dict(H=64, qd="bf16", W=128, N=700, U=1, T=6, nv=[[100, 300, 0, 699, 700, 50]]),
+    dict(H=128, qd="f32", W=128, N=1000, U=2, T=1, nv=None),
+    dict(H=32, qd="bf16", W=0, N=500, U=2, T=2, nv=[[500, 1], [250, 499]]),
+    dict(H=64, qd="f32", W=128, N=8192, U=2, T=1, nv=None),
+    dict(H=16, qd="bf16", W=32, N=4000, U=1, T=300, nv="causal"),
+]
+
+
+def _dense_nv(case):
+    nv = case["nv"]
+    if nv is None:
+        return None
+    if nv == "causal":
+        return (case["N"] // 2 + 7 * np.arange(case["T"])).clip(0, case["N"]).astype(np.int32)[None, :]
+    return np.array(nv, dtype=np.int32)
+
+
+@pytest.mark.parametrize("case", DENSE_CASES, ids=lambda c: f"H{c['H']}{c['qd']}W{c['W']}N{c['N']}U{c['U']}T{c['T']}")
+def test_dense_mqa_matches_oracle(case):
+    """ds4a_dense_mqa against the oracle's union softmax over raw rows + compressed rows [0, n_vis)."""
+    H, W, N, U, T = case["H"], case["W"], case["N"], case["U"], case["T"]
+    w, x = _mqa_case(H, case["qd"], W, max(N, 1), 1, seed=4, U=U, T=T)
+    nv = _dense_nv(case)
+    d = upload(x)
+    comp = d["comp"] if N > 0 else None
+    out = torch.full((U, T, H, 512), float("nan"), device="cuda")
+    ops.dense_mqa(d["q"], d["pos"], d["raw"] if W else None, comp, w.scale, W=W,
+                  n_vis=torch.from_numpy(nv).cuda() if nv is not None else None, out=out)
+    got = out.cpu().numpy()
+    checks = [(u, t) for u in range(U) for t in range(T)]
+    if len(checks) > 12:                      # many queries: a spread of them, ends included
+        checks = checks[:4] + checks[len(checks) // 2:len(checks) // 2 + 4] + checks[-4:]
+    for u, t in checks:
+        n = N if nv is None else int(nv[u, t])
+        ref = _oracle_out(w, x, u, t, np.arange(n, dtype=np.int32))
+        e = normwise_err(got[u, t], ref)
+        assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, e)
+
+
+def test_dense_equals_sparse_over_all_rows():
+    """The dense call is the sparse call with idx = 0..N-1: the same bits."""
+    H, W, N, U, T = 64, 128, 1500, 3, 2
+    w, x = _mqa_case(H, "f32", W, N, N, seed=6, U=U, T=T)
+    d = upload(x)
+    idx = torch.arange(N, dtype=torch.int32, device="cuda").expand(U, T, N).contiguous()
+    a = ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], idx, w.scale, W=W)
+    b = ops.dense_mqa(d["q"], d["pos"], d["raw"], d["comp"], w.scale, W=W)
+    assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("order,U,T", [("rising", 1, 1), ("falling", 2, 2)])
 def test_mqa_wide_logit_range(order, U, T):
     """Selected rows scaled so that logits climb (or fall) by tens across the union: the
