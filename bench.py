@@ -12,8 +12,9 @@ tokens/s/layer = layer-units per second.  The main line is also timed with the
 step captured as a HIP graph (each replay checked against the eager result),
 and per step (p10 / p50 / p90).  Also measured in the same run: the same
 decode at N = 16,384 and 32,768 rows, 8 sessions at N = 262,144, the Pro shape
-(4 sessions, 128 heads, top-1024, N = 65,536), and chunked prefill (2,048
-queries, N = 8,192).  The CPU baseline runs the oracle on the main line's
+(4 sessions, 128 heads, top-1024, N = 65,536), the attention of a whole Flash
+decode step (all 43 layers by their compression ratio, 262,144 tokens of
+context), and chunked prefill (2,048 queries, N = 8,192).  The CPU baseline runs the oracle on the main line's
 units and also reports how the GPU results agree with it.
 
 Inputs are synthetic (synth.inputs), uploaded to HBM before timing.  Several
@@ -298,6 +299,79 @@ def cpu_baseline(w, x, gpu=None, budget_s: float = 20.0):
     return rec
 
 
+def full_schedule(steps: int, warmup: int):
+    """Attention of one whole Flash decode step, all 43 layers, at 262,144 tokens of context,
+    with the layer schedule of "Reading the architecture of DwarfStar (ds4.c), part 1/8",
+    section 3-2: layers 0-1 keep only the raw window (ds4a_dense_mqa with N = 0), even layers
+    from 2 on are ratio 4 (65,536 rows: ds4a_indexer_topk + ds4a_sparse_mqa, top-512) and odd
+    layers from 3 on ratio 128 (2,048 rows, all of them: ds4a_dense_mqa)."""
+    import torch
+
+    from sparse_compressed_kv_amd import ops
+    from synth import inputs as gen
+
+    ctx = 262144
+    w4 = gen.Workload("flash_ratio4_layers_ctx262144", 6, U=21, T=1, N=ctx // 4, heavy_frac=0.01, pos_base=ctx - 1)
+    w128 = gen.Workload("flash_ratio128_layers_ctx262144", 7, U=20, T=1, N=ctx // 128, pos_base=ctx - 1)
+    w0 = gen.Workload("flash_ratio0_layers_ctx262144", 8, U=2, T=1, N=1, pos_base=ctx - 1)
+    r4 = [upload(gen.make_config(w4)) for _ in range(replicas_for(w4))]
+    x128 = gen.make_config(w128)
+    r128 = [upload(x128) for _ in range(2)]
+    x0 = gen.make_config(w0)
+    r0 = [upload(x0) for _ in range(2)]
+    st4 = ops.Step(w4.U, 1, w4.N, fused=True)
+    out128 = torch.empty((w128.U, 1, 64, 512), dtype=torch.float32, device="cuda")
+    ws128 = torch.empty(max(ops.workspace_bytes(3, w128.U, 1, w128.N, 0, 64, 128), 1), dtype=torch.uint8,
+                        device="cuda")
+    out0 = torch.empty((w0.U, 1, 64, 512), dtype=torch.float32, device="cuda")
+    ws0 = torch.empty(max(ops.workspace_bytes(3, w0.U, 1, 0, 0, 64, 128), 1), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    scale, theta = w4.scale, w4.theta
+
+    def g4(i):
+        d = r4[i % len(r4)]
+        st4.select(d, stream=stream)
+        ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st4.idx, scale, theta, W=128, out=st4.out,
+                       workspace=st4.ws_mqa, stream=stream)
+
+    def g128(i):
+        d = r128[i % len(r128)]
+        ops.dense_mqa(d["q"], d["pos"], d["raw"], d["comp"], scale, theta, W=128, out=out128, workspace=ws128,
+                      stream=stream)
+
+    def g0(i):
+        d = r0[i % len(r0)]
+        ops.dense_mqa(d["q"], d["pos"], d["raw"], None, scale, theta, W=128, out=out0, workspace=ws0, stream=stream)
+
+    def timed(fn, n):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(n):
+            fn(warmup + i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
+
+    def whole(i):
+        g0(i)
+        g4(i)
+        g128(i)
+
+    for i in range(warmup):
+        whole(i)
+    ms = timed(whole, steps)
+    parts = {"ratio0_us": 1e3 * timed(g0, steps), "ratio4_us": 1e3 * timed(g4, steps),
+             "ratio128_us": 1e3 * timed(g128, steps)}
+    by = (w4.U * decode_bytes_per_unit(w4.N, 64, 512, 128)
+          + w128.U * (w128.N * 1024 + 128 * 1024 + 64 * 512 * 4 * 2)
+          + w0.U * (128 * 1024 + 64 * 512 * 4 * 2))
+    return {"workload": "flash_43layers_ctx262144 (2 raw-only + 21 ratio-4 + 20 ratio-128 layers)",
+            "ms_per_step": ms, "value": 1e3 / ms, "unit": "decode tokens/s (all 43 layers' attention)",
+            "algorithmic_bytes": by, "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "parts_back_to_back": parts}
+
+
 def traffic_for(kernel_hash: str, units: int):
     """HBM bytes per ds4a_indexer_topk call from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters
     (both kernels of the call), scaled by the same counters' reading of a plain copy of known size;
@@ -414,6 +488,11 @@ def main():
             }
             del b4, x4
             torch.cuda.empty_cache()
+        # ---- a whole Flash decode step: the 43 layers' attention by their compression ratio
+        fs = full_schedule(args.steps, args.warmup)
+        log(f"[bench] {fs['workload']}: {fs}")
+        rec["full_schedule_ctx262144"] = fs
+        torch.cuda.empty_cache()
         # ---- chunked prefill: 2,048 queries, 8,192 rows
         w3 = gen.CONFIGS["c3"]
         x3 = gen.make_config(w3)
