@@ -6,7 +6,7 @@
  * for the top-k.  Threads run only across independent (unit, query) pairs.
  *
  * Source of the method: "Reading the architecture of DwarfStar (ds4.c),
- * part 1/8" (Qiita), sections 2, 3, 3-1 and 3-3 (cited per function below).
+ * part 1/8" (Qiita), sections 2, 3, 3-1, 3-2 and 3-3 (cited per function below).
  */
 #define _GNU_SOURCE
 #include "ds4o.h"
@@ -340,5 +340,152 @@ int ds4o_step(int U, int T, int64_t N, int H, int D, int n_rot, int W, int Hi, i
     for (int i = 0; i < started; i++)
         pthread_join(th[i], NULL);
     pthread_mutex_destroy(&j.lock);
+    return 0;
+}
+
+/* ------------------------------------------------------------ compressor */
+
+/* Round |x| to a multiple of 2^q_exp by rint (ties to even multiple) in double; exact while
+ * |x| / 2^q_exp stays below 2^53. */
+static double round_to_quantum(double a, int q_exp)
+{
+    return ldexp(rint(ldexp(a, -q_exp)), q_exp);
+}
+
+/* bfloat16: 8 significant bits, exponent range of binary32 (normals down to 2^-126,
+ * subnormal quantum 2^-133), largest finite (2 - 2^-7) * 2^127. */
+uint16_t ds4o_round_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);                                  /* a = f * 2^e, 0.5 <= f < 1 */
+    int binade = e - 1;                            /* 2^binade <= a < 2^(binade+1) */
+    if (binade < -126)
+        binade = -126;
+    double r = round_to_quantum(a, binade - 7);
+    if (r >= ldexp(2.0 - ldexp(1.0, -8), 127))     /* at or past the halfway point to 2^128 */
+        return (uint16_t)(sign | 0x7f80);
+    float f = (float)r;                            /* exact: 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+double ds4o_e4m3_to_f64(uint8_t c)
+{
+    int sign = (c >> 7) & 1;
+    int e = (c >> 3) & 0xf;
+    int m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);                  /* m/8 * 2^-6 */
+    else
+        v = ldexp((double)(8 + m), e - 10);        /* (1 + m/8) * 2^(e-7) */
+    return sign ? -v : v;
+}
+
+uint8_t ds4o_round_e4m3(double x)
+{
+    if (isnan(x))
+        return 0x7f;
+    uint8_t sign = signbit(x) ? 0x80 : 0;
+    double a = fabs(x);
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7e);             /* saturate: 1.75 * 2^8 */
+    if (a == 0.0)
+        return sign;
+    int e;
+    frexp(a, &e);
+    int binade = e - 1;
+    if (binade < -6)
+        binade = -6;                               /* subnormals share the quantum 2^-9 */
+    double r = round_to_quantum(a, binade - 3);
+    if (r >= 448.0)
+        return (uint8_t)(sign | 0x7e);
+    if (r == 0.0)
+        return sign;
+    frexp(r, &e);
+    binade = e - 1;
+    if (binade < -6)                               /* subnormal: r = m * 2^-9 */
+        return (uint8_t)(sign | (int)ldexp(r, 9));
+    int m = (int)ldexp(r, -binade + 3) - 8;        /* r = (8 + m) * 2^(binade-3) */
+    return (uint8_t)(sign | ((binade + 7) << 3) | m);
+}
+
+/* Section 3-2 of the article: at every ratio boundary the compressor pools its frontier of
+ * `ratio` (kv, score) rows into one row, channel by channel, with the scores as softmax
+ * logits (a row of weight e^(s - max) each, divided by their sum), then applies an RMS
+ * normalisation, the tail RoPE and an FP8 quantise-dequantise round trip, in that order.
+ * Readings for what the article leaves open: the norm is x / sqrt(mean(x^2) + eps) times a
+ * per-channel gain; the tail RoPE is the one the query gets (adjacent pairs of the last n_rot
+ * dims, angle pos * theta^(-2i/n_rot)) at the position the caller gives; the FP8 format is
+ * E4M3FN with one power-of-two scale per row, the smallest that brings max|y| to <= 448,
+ * values rounded to nearest (ties to even) and clipped; the row is then stored as bf16 (an
+ * E4M3 value times a power of two is exact in bf16). */
+int ds4o_compress_row(int width, int ratio, const float *state_kv, const float *state_score,
+                      const float *gain, double eps, int n_rot, int64_t pos, double theta, int fp8,
+                      double *y_pre, double *scale, uint16_t *out_bf16)
+{
+    if (width < 2 || ratio < 1 || n_rot < 0 || n_rot > width || (n_rot & 1))
+        return -1;
+    double *pooled = malloc(sizeof(double) * (size_t)width);
+    double *y = malloc(sizeof(double) * (size_t)width);
+    if (!pooled || !y) {
+        free(pooled);
+        free(y);
+        return -1;
+    }
+    /* softmax-weighted pooling over the frontier rows, per channel */
+    for (int j = 0; j < width; j++) {
+        double m = -INFINITY;
+        for (int r = 0; r < ratio; r++) {
+            double s = (double)state_score[(int64_t)r * width + j];
+            if (s > m)
+                m = s;
+        }
+        double num = 0.0, den = 0.0;
+        for (int r = 0; r < ratio; r++) {
+            double wgt = exp((double)state_score[(int64_t)r * width + j] - m);
+            den += wgt;
+            num += wgt * (double)state_kv[(int64_t)r * width + j];
+        }
+        pooled[j] = den > 0.0 ? num / den : 0.0;
+    }
+    /* RMS normalisation */
+    double ms = 0.0;
+    for (int j = 0; j < width; j++)
+        ms += pooled[j] * pooled[j];
+    ms /= (double)width;
+    double inv = 1.0 / sqrt(ms + eps);
+    for (int j = 0; j < width; j++)
+        pooled[j] = pooled[j] * inv * (double)gain[j];
+    /* tail RoPE, as for a query of one head */
+    ds4o_rope_q(1, width, n_rot, pos, theta, pooled, y);
+    if (y_pre)
+        memcpy(y_pre, y, sizeof(double) * (size_t)width);
+    double s = 1.0;
+    if (fp8) {
+        double amax = 0.0;
+        for (int j = 0; j < width; j++)
+            if (fabs(y[j]) > amax)
+                amax = fabs(y[j]);
+        if (amax > 0.0)
+            s = ldexp(1.0, (int)ceil(log2(amax / 448.0)));
+        for (int j = 0; j < width; j++)
+            y[j] = ds4o_e4m3_to_f64(ds4o_round_e4m3(y[j] / s)) * s;
+    }
+    if (scale)
+        *scale = s;
+    for (int j = 0; j < width; j++)
+        out_bf16[j] = ds4o_round_bf16(y[j]);
+    free(pooled);
+    free(y);
     return 0;
 }

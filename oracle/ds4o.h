@@ -11,6 +11,9 @@
  *     dims, RoPE on the last n_rot = 64 dims, 128-row raw window, indexer with
  *     64 heads x 128 dims and top-k 512 (Pro: 1024);
  *   - section 3-1: raw-window values are rounded to f16 when pushed;
+ *   - section 3-2: the compressor folds `ratio` recent tokens into one row by
+ *     a per-channel softmax-weighted pooling, then normalises, rotates the
+ *     tail and round-trips the row through FP8;
  *   - section 3-3: a thin indexer scores the compressed rows and only the
  *     top-k of them reach the main attention;
  *   - section 3 (overview): attention runs over the raw window plus the
@@ -81,6 +84,33 @@ int ds4o_step(int U, int T, int64_t N, int H, int D, int n_rot, int W, int Hi, i
               const uint16_t *qI, const float *w, const int32_t *n_vis, double scale,
               const int64_t *sel, int64_t n_sel, int nthreads,
               double *scores, int32_t *idx, double *out);
+
+/* ------------------------------------------------------------ compressor */
+
+/* Nearest bfloat16 of a double (round to nearest, ties to even), gradual underflow,
+ * overflow to infinity.  Returns the bit pattern. */
+uint16_t ds4o_round_bf16(double x);
+
+/* OCP FP8 E4M3FN: 1 sign, 4 exponent (bias 7), 3 fraction bits, no infinities,
+ * S.1111.111 is NaN, largest finite 448, subnormals m/8 * 2^-6. */
+double ds4o_e4m3_to_f64(uint8_t c);
+
+/* Nearest E4M3FN value of x, ties to the even code; magnitudes above 448 saturate to
+ * +-448, NaN gives 0x7f.  Returns the code. */
+uint8_t ds4o_round_e4m3(double x);
+
+/* One compressed row from the compressor's frontier (section 3-2 of the article):
+ *   pooled[j] = sum_r softmax_r(state_score[r][j]) * state_kv[r][j]   (r < ratio)
+ *   y         = pooled / sqrt(mean_j pooled[j]^2 + eps) * gain          (RMS norm)
+ *   y         = y with its last n_rot dims rotated at position pos     (tail RoPE)
+ *   y8        = FP8 round trip of y if fp8 (E4M3FN, one power-of-two scale per row)
+ *   out_bf16  = bf16(y8)
+ * state_kv, state_score: f32 [ratio][width]; gain: f32 [width].  y_pre (double [width],
+ * y before the FP8 step) and scale (the row's FP8 scale, 1 without FP8) may be NULL.
+ * Returns 0, or -1 on bad sizes. */
+int ds4o_compress_row(int width, int ratio, const float *state_kv, const float *state_score,
+                      const float *gain, double eps, int n_rot, int64_t pos, double theta, int fp8,
+                      double *y_pre, double *scale, uint16_t *out_bf16);
 
 #ifdef __cplusplus
 }

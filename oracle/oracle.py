@@ -54,6 +54,11 @@ def lib() -> ctypes.CDLL:
         L.ds4o_step.argtypes = [i32, i32, i64, i32, i32, i32, i32, i32, i32, i32,
                                 P, i32, P, dbl, P, P, P, P, P, P, dbl, P, i64, i32, P, P, P]
         L.ds4o_step.restype = i32
+        L.ds4o_round_bf16.argtypes, L.ds4o_round_bf16.restype = [dbl], ctypes.c_uint16
+        L.ds4o_e4m3_to_f64.argtypes, L.ds4o_e4m3_to_f64.restype = [ctypes.c_uint8], dbl
+        L.ds4o_round_e4m3.argtypes, L.ds4o_round_e4m3.restype = [dbl], ctypes.c_uint8
+        L.ds4o_compress_row.argtypes = [i32, i32, P, P, P, dbl, i32, i64, dbl, i32, P, P, P]
+        L.ds4o_compress_row.restype = i32
         _lib = L
     return _lib
 
@@ -171,3 +176,41 @@ def step(w, x: dict, sel=None, nthreads: int = 1, want=("scores", "idx", "out"))
     if out is not None:
         res["out"] = out
     return res
+
+
+def round_bf16(x) -> np.ndarray:
+    """Nearest bfloat16 of each float64 (ties to even) -> bit patterns."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    f = lib().ds4o_round_bf16
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint16).reshape(x.shape)
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    f = lib().ds4o_e4m3_to_f64
+    return np.array([f(int(v)) for v in c.ravel()], dtype=np.float64).reshape(c.shape)
+
+
+def round_e4m3(x) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    f = lib().ds4o_round_e4m3
+    return np.array([f(float(v)) for v in x.ravel()], dtype=np.uint8).reshape(x.shape)
+
+
+def compress_row(state_kv, state_score, gain, eps: float = 1e-6, n_rot: int = 64, pos: int = 0,
+                 theta: float = 10000.0, fp8: bool = True):
+    """One emitted row: state_kv, state_score f32 [ratio, width], gain f32 [width]
+    -> (bf16 bits [width], y before the FP8 step float64 [width], the row's FP8 scale)."""
+    kv = np.ascontiguousarray(state_kv, dtype=np.float32)
+    sc = np.ascontiguousarray(state_score, dtype=np.float32)
+    g = np.ascontiguousarray(gain, dtype=np.float32)
+    ratio, width = kv.shape
+    assert sc.shape == kv.shape and g.shape == (width,)
+    out = np.empty(width, dtype=np.uint16)
+    y = np.empty(width, dtype=np.float64)
+    scale = ctypes.c_double(0.0)
+    rc = lib().ds4o_compress_row(width, ratio, _p(kv), _p(sc), _p(g), float(eps), int(n_rot), int(pos),
+                                 float(theta), 1 if fp8 else 0, _p(y), ctypes.byref(scale), _p(out))
+    if rc != 0:
+        raise ValueError(f"ds4o_compress_row rejected its arguments (rc={rc})")
+    return out, y, scale.value

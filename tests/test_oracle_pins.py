@@ -338,3 +338,126 @@ def test_step_composes_the_parts_and_threads_agree(oracle_mod):
         assert np.array_equal(r1["out"][i], o)
     sub = oracle_mod.step(w, x, sel=[5, 1], nthreads=2)
     assert np.array_equal(sub["out"][0], r1["out"][5]) and np.array_equal(sub["idx"][1], r1["idx"][1])
+
+
+# ------------------------------------------------------------ compressor (section 3-2)
+
+def _e4m3_torch(codes):
+    t = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8).copy())
+    return t.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_e4m3_decode_matches_torch_all_codes(oracle_mod):
+    codes = np.arange(256, dtype=np.uint8)
+    ours, ref = oracle_mod.e4m3_to_f64(codes), _e4m3_torch(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan) and nan.sum() == 2          # S.1111.111 only
+    assert np.array_equal(ours[~nan], ref[~nan])
+    assert ours[0x7e] == 448.0 and ours[0x08] == 2.0 ** -6 and ours[0x01] == 2.0 ** -9
+
+
+def test_e4m3_rounding_matches_torch(oracle_mod):
+    rng = np.random.default_rng(21)
+    finite = _e4m3_torch(np.arange(256, dtype=np.uint8))
+    finite = np.unique(finite[np.isfinite(finite)])
+    mids = (finite[1:] + finite[:-1]) / 2                                  # every tie
+    x = np.concatenate([finite, mids, rng.uniform(-448, 448, 2000), rng.standard_normal(2000) * 1e-2,
+                        rng.standard_normal(500) * 1e-3])
+    x = x.astype(np.float32).astype(np.float64)                            # torch casts from f32
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = oracle_mod.round_e4m3(x)
+    same = (ours == ref) | ((ours & 0x7f) == 0) & ((ref & 0x7f) == 0)       # +-0 alike
+    assert same.all(), x[~same][:5]
+    assert (oracle_mod.round_e4m3(np.array([448.0, 449.0, 464.0, 1e6, -1e6])) == [0x7e, 0x7e, 0x7e, 0x7e, 0xfe]).all()
+
+
+def test_round_bf16_matches_torch(oracle_mod):
+    rng = np.random.default_rng(22)
+    x = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000), [0.0, -0.0, 1.00390625,
+                        1.005859375, -3.0e38, 1e-40]]).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle_mod.round_bf16(x.astype(np.float64)), ref)
+
+
+def _frontier(rng, ratio, width, spread=1.0):
+    kv = rng.standard_normal((ratio, width)).astype(np.float32)
+    sc = (rng.standard_normal((ratio, width)) * spread).astype(np.float32)
+    return kv, sc
+
+
+def test_compress_equal_scores_is_mean(oracle_mod):
+    """Equal scores: the softmax weights are uniform, so the pooled row is the plain mean."""
+    rng = np.random.default_rng(23)
+    kv, _ = _frontier(rng, 4, 512)
+    sc = np.full_like(kv, 0.37)
+    ones = np.ones(512, np.float32)
+    _, y, _ = oracle_mod.compress_row(kv, sc, ones, eps=0.0, n_rot=0, fp8=False)
+    m = kv.astype(np.float64).mean(axis=0)
+    np.testing.assert_allclose(y, m / np.sqrt(np.mean(m * m)), rtol=1e-12, atol=1e-14)
+
+
+def test_compress_dominant_score_picks_its_row(oracle_mod):
+    rng = np.random.default_rng(24)
+    kv, sc = _frontier(rng, 128, 128)
+    sc[77] += 60.0                                                          # e^-60 for the others
+    _, y, _ = oracle_mod.compress_row(kv, sc, np.ones(128, np.float32), eps=0.0, n_rot=0, fp8=False)
+    r = kv[77].astype(np.float64)
+    np.testing.assert_allclose(y, r / np.sqrt(np.mean(r * r)), rtol=1e-12)
+
+
+def test_compress_ratio_one_and_permutation(oracle_mod):
+    rng = np.random.default_rng(25)
+    kv, sc = _frontier(rng, 16, 512, spread=3.0)
+    g = rng.uniform(0.5, 2.0, 512).astype(np.float32)
+    a = oracle_mod.compress_row(kv, sc, g, n_rot=64, pos=777, fp8=True)
+    perm = rng.permutation(16)
+    b = oracle_mod.compress_row(kv[perm], sc[perm], g, n_rot=64, pos=777, fp8=True)
+    assert np.array_equal(a[0], b[0])                                       # frontier order is irrelevant
+    _, y1, _ = oracle_mod.compress_row(kv[:1], sc[:1], np.ones(512, np.float32), eps=0.0, n_rot=0, fp8=False)
+    r = kv[0].astype(np.float64)
+    np.testing.assert_allclose(y1, r / np.sqrt(np.mean(r * r)), rtol=1e-12)   # one row: itself
+
+
+def test_compress_rms_gain_and_scale_invariance(oracle_mod):
+    rng = np.random.default_rng(26)
+    kv, sc = _frontier(rng, 4, 512)
+    g = np.full(512, 2.0, np.float32)
+    _, y, _ = oracle_mod.compress_row(kv, sc, g, eps=0.0, n_rot=0, fp8=False)
+    assert abs(np.mean(y * y) - 4.0) < 1e-12                                # RMS of the output = gain
+    _, y2, _ = oracle_mod.compress_row(kv * np.float32(8.0), sc, g, eps=0.0, n_rot=0, fp8=False)
+    np.testing.assert_allclose(y2, y, rtol=1e-12)                           # scale of kv divides out
+    _, y3, _ = oracle_mod.compress_row(kv, sc, g, eps=1e-2, n_rot=0, fp8=False)
+    assert np.mean(y3 * y3) < np.mean(y * y)                                # eps only shrinks
+
+
+def test_compress_tail_rope_is_complex_rotation(oracle_mod):
+    rng = np.random.default_rng(27)
+    kv, sc = _frontier(rng, 4, 512)
+    g = np.ones(512, np.float32)
+    _, y0, _ = oracle_mod.compress_row(kv, sc, g, n_rot=64, pos=0, fp8=False)
+    _, yn, _ = oracle_mod.compress_row(kv, sc, g, n_rot=0, pos=0, fp8=False)
+    np.testing.assert_array_equal(y0, yn)                                   # position 0: no rotation
+    pos = 123457
+    _, yp, _ = oracle_mod.compress_row(kv, sc, g, n_rot=64, pos=pos, fp8=False)
+    np.testing.assert_array_equal(yp[:448], yn[:448])
+    z = yn[448::2] + 1j * yn[449::2]
+    ang = pos * 10000.0 ** (-2.0 * np.arange(32) / 64.0)
+    zr = z * np.exp(1j * ang)
+    np.testing.assert_allclose(yp[448::2], zr.real, atol=1e-12)
+    np.testing.assert_allclose(yp[449::2], zr.imag, atol=1e-12)
+
+
+def test_compress_fp8_round_trip_bounds(oracle_mod):
+    """The stored row is E4M3 values times one power of two, within half an E4M3 step of y."""
+    rng = np.random.default_rng(28)
+    for trial in range(20):
+        kv, sc = _frontier(rng, 4 if trial % 2 else 128, 512, spread=2.0)
+        g = rng.uniform(0.1, 3.0, 512).astype(np.float32)
+        out, y, s = oracle_mod.compress_row(kv, sc, g, n_rot=64, pos=trial * 1000, fp8=True)
+        v = bf16_f64(out)
+        assert s == 2.0 ** round(math.log2(s))
+        assert np.max(np.abs(y)) / s <= 448.0 and np.max(np.abs(y)) / s > 224.0
+        q = v / s
+        assert np.array_equal(_e4m3_torch(oracle_mod.round_e4m3(q)), q)     # every value is an E4M3 value
+        step = np.where(np.abs(y / s) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y / s), 1e-300))) - 3))
+        assert np.all(np.abs(q - y / s) <= step / 2 + 1e-12)
