@@ -61,6 +61,8 @@ typedef enum { DS4A_F32 = 0, DS4A_BF16 = 1, DS4A_F16 = 2 } ds4a_dtype;
 #define DS4A_MAX_TOPK 2048        /* K : 1..2048 (Flash 512, Pro 1024)          */
 #define DS4A_MAX_WINDOW 1024      /* W : a multiple of 32 up to 1024 (n_swa = 128) */
 #define DS4A_MAX_DENSE_ROWS (1 << 20) /* N of ds4a_dense_mqa: 0..2^20 compressed rows  */
+#define DS4A_MAX_COMPRESS_WIDTH 1024  /* width of ds4a_compress_rows (512 KV, 128 indexer)  */
+#define DS4A_MAX_COMPRESS_RATIO 1024  /* ratio of ds4a_compress_rows (4 or 128 in Flash)   */
 
 /* A1 — indexer scores (section 3-3: the indexer's own thin query scores every
  * compressed row).  For unit u, query t and row j < n_vis[u][t]:
@@ -159,6 +161,35 @@ int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
                    const void *raw_kv, const void *comp_kv, const int32_t *n_vis,
                    float scale, float *out,
                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* Compressor row emission (section 3-2: tokens older than the raw window are folded,
+ * `ratio` at a time, into one compressed row by a learned pooling; the indexer has its own
+ * compressor of the same form).  For each unit u (a layer or a session), from its frontier
+ * of `ratio` rows (each token's KV row and its score row, the score already carrying the
+ * positional bias):
+ *   pooled[j] = sum_r e^(s[r][j] - m[j]) kv[r][j] / sum_r e^(s[r][j] - m[j]),  m[j] = max_r s[r][j]
+ *   y         = pooled / sqrt(mean_j pooled[j]^2 + eps) * gain[u]             (RMS norm)
+ *   y         = y with its last n_rot dims rotated as the query's tail is rotated
+ *               (adjacent pairs, angle row_pos[u] * rope_theta^(-2i/n_rot))
+ *   y         = FP8 round trip of y when fp8 = 1
+ *   out[u * out_stride + j] = bf16(y[j])
+ * Readings of what the page leaves open: the norm's form (epsilon and a per-channel gain
+ * are inputs); the rotation's position (an input: row_pos); the FP8 format: OCP E4M3FN
+ * with one power-of-two scale per row, the smallest that brings max|y| to <= 448, values
+ * rounded to nearest (ties to even) and clipped, then scaled back (exact in bf16).
+ * Arithmetic is fp32 except the rotation angle (fp64, as for the query).
+ *   width    : even, 2..DS4A_MAX_COMPRESS_WIDTH (512 for KV rows, 128 for indexer keys)
+ *   ratio    : 1..DS4A_MAX_COMPRESS_RATIO       n_rot : even, 0..min(width, 512)
+ *   state_kv, state_score : f32 [U][ratio][width]     gain : f32 [U][width]
+ *   eps      : >= 0 (finite)                     row_pos : int64 [U]
+ *   fp8      : 0 or 1                            out : bf16 [U][out_stride], row u at u * out_stride
+ *   out_stride : elements between units' rows, >= width (e.g. N * width to append the row
+ *              to a [U][N][width] cache at row n: out = cache + n * width)
+ * Errors as for the other calls; no workspace.
+ */
+int ds4a_compress_rows(int U, int width, int ratio, const float *state_kv, const float *state_score,
+                       const float *gain, float eps, int n_rot, const int64_t *row_pos, double rope_theta,
+                       int fp8, void *out, int64_t out_stride, void *stream);
 
 /* A3 alone, for inspection: writes the rotated query as f32 [U][T][H][D], using
  * the same device code as ds4a_sparse_mqa's prologue (fp64 angle and rotation,

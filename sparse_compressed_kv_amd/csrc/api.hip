@@ -231,6 +231,30 @@ int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, cons
                                            workspace, static_cast<hipStream_t>(stream)));
 }
 
+int ds4a_compress_rows(int U, int width, int ratio, const float *state_kv, const float *state_score,
+                       const float *gain, float eps, int n_rot, const int64_t *row_pos, double rope_theta, int fp8,
+                       void *out, int64_t out_stride, void *stream) {
+    const char *fn = "ds4a_compress_rows";
+    if (U < 1 || U > (1 << 24)) return fail(DS4A_E_SHAPE, "%s: U=%d must be in [1, 2^24]", fn, U);
+    if (width < 2 || width % 2 || ratio < 1 || n_rot < 0 || n_rot % 2 || n_rot > width)
+        return fail(DS4A_E_SHAPE, "%s: width=%d ratio=%d n_rot=%d out of range", fn, width, ratio, n_rot);
+    if (width > DS4A_MAX_COMPRESS_WIDTH || ratio > DS4A_MAX_COMPRESS_RATIO || n_rot > 512)
+        return fail(DS4A_E_UNSUPPORTED, "%s: width=%d ratio=%d n_rot=%d (width <= %d, ratio <= %d, n_rot <= 512)",
+                    fn, width, ratio, n_rot, DS4A_MAX_COMPRESS_WIDTH, DS4A_MAX_COMPRESS_RATIO);
+    if (!(eps >= 0.f) || eps == INFINITY) return fail(DS4A_E_SHAPE, "%s: eps must be finite and >= 0", fn);
+    if (!(rope_theta > 0.0) || rope_theta != rope_theta) return fail(DS4A_E_SHAPE, "%s: rope_theta must be > 0", fn);
+    if (fp8 != 0 && fp8 != 1) return fail(DS4A_E_SHAPE, "%s: fp8 must be 0 or 1", fn);
+    if (out_stride < width) return fail(DS4A_E_SHAPE, "%s: out_stride=%lld < width", fn, (long long)out_stride);
+    REQUIRE_PTR(state_kv);
+    REQUIRE_PTR(state_score);
+    REQUIRE_PTR(gain);
+    REQUIRE_PTR(row_pos);
+    REQUIRE_PTR(out);
+    return hip_status(fn, ds4a::launch_compress(U, width, ratio, state_kv, state_score, gain, eps, n_rot, row_pos,
+                                                rope_theta, fp8, static_cast<uint16_t *>(out), out_stride,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtype, const int64_t *q_pos,
                 double rope_theta, float *q_out, void *stream) {
     const char *fn = "ds4a_rope_q";

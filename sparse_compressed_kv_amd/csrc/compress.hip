@@ -1,0 +1,136 @@
+// compress.hip — compressor row emission: the step that makes the compressed rows the
+// indexer and the attention read.
+//
+// "Reading the architecture of DwarfStar (ds4.c), part 1/8" (Qiita), section 3-2: tokens
+// older than the raw window are not dropped but folded, `ratio` at a time (4 or 128 by
+// layer), into one row.  Each token's KV and score rows (scores with a positional bias
+// added) go into a frontier of `ratio` rows; at the ratio boundary the frontier is pooled
+// channel by channel with the scores as softmax logits, and the pooled row is normalised
+// (RMS), its tail rotated (RoPE) and round-tripped through FP8.  The indexer keeps its
+// own, narrower compressor of the same form.
+//
+// One workgroup per emitted row (one unit: a layer or a session).  The pooling reads the
+// frontier once, lane-consecutive across channels; the RMS and the FP8 scale are block
+// reductions; the rotation reuses the query's fp64 angle code (rope.hpp).  Readings of what
+// the page leaves open (the norm's epsilon and gain, the rotation's position, the FP8
+// format and scale) are stated at ds4a_compress_rows in the header.
+#include "common.hpp"
+#include "launch.hpp"
+#include "rope.hpp"
+
+namespace ds4a {
+
+namespace {
+
+constexpr int kCThreads = 256;
+constexpr int kCMaxWidth = 1024;
+
+// max and sum over the workgroup (kCThreads threads); every thread gets the result.
+__device__ float block_sum(float v, float *red) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    v = wave_xor_sum(v, 1); v = wave_xor_sum(v, 2); v = wave_xor_sum(v, 4);
+    v = wave_xor_sum(v, 8); v = wave_xor_sum(v, 16); v = wave_xor_sum(v, 32);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float s = 0.f;
+    for (int i = 0; i < kCThreads / kWave; ++i) s += red[i];   // the same order in every thread
+    __syncthreads();
+    return s;
+}
+
+__device__ float block_max(float v, float *red) {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    v = wave_xor_max(v, 1); v = wave_xor_max(v, 2); v = wave_xor_max(v, 4);
+    v = wave_xor_max(v, 8); v = wave_xor_max(v, 16); v = wave_xor_max(v, 32);
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    float m = 0.f;
+    for (int i = 0; i < kCThreads / kWave; ++i) m = fmaxf(m, red[i]);
+    __syncthreads();
+    return m;
+}
+
+// Nearest OCP E4M3FN value of x (ties to even), clipped to +-448; x finite.  The quantum of
+// x's binade is a power of two, so x / quantum is exact and rintf rounds it to even.
+__device__ __forceinline__ float round_e4m3(float x) {
+    const float a = fabsf(x);
+    if (a >= 448.f) return copysignf(448.f, x);
+    int e = (int)((__float_as_uint(a) >> 23) & 0xff) - 127;   // binade of a (-127 for 0 / subnormal)
+    if (e < -6) e = -6;                                          // E4M3 subnormals: quantum 2^-9
+    const float r = ldexpf(rintf(ldexpf(a, 3 - e)), e - 3);
+    return copysignf(r, x);
+}
+
+// Power-of-two scale s, the smallest with amax / s <= 448 = 0.875 * 2^9 (amax > 0).
+__device__ __forceinline__ float e4m3_scale(float amax) {
+    int e;
+    const float f = frexpf(amax, &e);                            // amax = f * 2^e, f in [0.5, 1)
+    return ldexpf(1.f, f <= 0.875f ? e - 9 : e - 8);
+}
+
+__global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
+    int width, int ratio, const float *__restrict__ state_kv, const float *__restrict__ state_score,
+    const float *__restrict__ gain, float eps, int n_rot, const int64_t *__restrict__ row_pos, double log2_theta,
+    int fp8, uint16_t *__restrict__ out, int64_t out_stride)
+{
+    __shared__ float s_y[kCMaxWidth];
+    __shared__ float s_red[kCThreads / kWave];
+    const int64_t u = blockIdx.x;
+    const float *kv = state_kv + u * (int64_t)ratio * width;
+    const float *sc = state_score + u * (int64_t)ratio * width;
+
+    // per-channel softmax pooling over the frontier rows, then the sum of squares
+    float ss = 0.f;
+    for (int j = threadIdx.x; j < width; j += kCThreads) {
+        float m = -INFINITY;
+        for (int r = 0; r < ratio; ++r) m = fmaxf(m, sc[(int64_t)r * width + j]);
+        float num = 0.f, den = 0.f;
+        for (int r = 0; r < ratio; ++r) {
+            const float w = __expf(sc[(int64_t)r * width + j] - m);
+            den += w;
+            num += w * kv[(int64_t)r * width + j];
+        }
+        const float p = num / den;                               // den >= 1 (the max row)
+        s_y[j] = p;
+        ss += p * p;
+    }
+    ss = block_sum(ss, s_red);
+    const float inv = 1.f / sqrtf(ss / (float)width + eps);
+    for (int j = threadIdx.x; j < width; j += kCThreads) s_y[j] = s_y[j] * inv * gain[u * width + j];
+    __syncthreads();
+
+    // tail RoPE: thread i < n_rot/2 rotates the pair (width - n_rot + 2i, +1)
+    if (threadIdx.x < n_rot / 2) {
+        const int i = threadIdx.x, j0 = width - n_rot + 2 * i;
+        double cs, sn;
+        rope_angle(log2_theta, i, row_pos[u], cs, sn, n_rot);
+        rope_rotate(cs, sn, s_y[j0], s_y[j0 + 1]);
+    }
+    __syncthreads();
+
+    float s = 1.f;
+    if (fp8) {
+        float amax = 0.f;
+        for (int j = threadIdx.x; j < width; j += kCThreads) amax = fmaxf(amax, fabsf(s_y[j]));
+        amax = block_max(amax, s_red);
+        if (amax > 0.f) s = e4m3_scale(amax);
+    }
+    uint16_t *o = out + u * out_stride;
+    for (int j = threadIdx.x; j < width; j += kCThreads) {
+        const float y = fp8 ? round_e4m3(s_y[j] / s) * s : s_y[j];   // s a power of two: exact
+        o[j] = (uint16_t)f32_to_bf16_bits(y);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_compress(int U, int width, int ratio, const float *state_kv, const float *state_score,
+                           const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta, int fp8,
+                           uint16_t *out, int64_t out_stride, hipStream_t stream)
+{
+    hipLaunchKernelGGL(compress_rows_kernel, dim3((unsigned)U), dim3(kCThreads), 0, stream, width, ratio, state_kv,
+                       state_score, gain, eps, n_rot, row_pos, log2(theta), fp8, out, out_stride);
+    return hipGetLastError();
+}
+
+}  // namespace ds4a

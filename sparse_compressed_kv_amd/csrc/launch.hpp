@@ -48,6 +48,9 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
                       const int64_t *q_pos, double theta, const uint16_t *raw, const uint16_t *comp,
                       const int32_t *idx, const int32_t *n_vis, float scale, float *out, void *workspace,
                       hipStream_t stream);
+hipError_t launch_compress(int U, int width, int ratio, const float *state_kv, const float *state_score,
+                           const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta, int fp8,
+                           uint16_t *out, int64_t out_stride, hipStream_t stream);
 hipError_t launch_rope(int U, int T, int H, const void *q, int q_bf16, const int64_t *q_pos,
                        double theta, float *q_out, hipStream_t stream);
 

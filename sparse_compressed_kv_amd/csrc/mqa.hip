@@ -37,6 +37,7 @@
 // log-sum-exp.
 #include "common.hpp"
 #include "launch.hpp"
+#include "rope.hpp"
 
 #include <math.h>
 #include <type_traits>
@@ -93,31 +94,6 @@ struct MqaArgs {
     float *part;
     double log2_theta;                       // log2(rope_theta), computed on the host in fp64
 };
-
-// The angle of the adjacent pair i of the query tail, pos * theta^(-2i/n_rot), as (cos, sin)
-// in fp64.  The angle (up to ~1e6 rad) is first reduced by a two-part 2*pi in fp64, so that
-// sincos runs on |x| <= pi.
-__device__ __forceinline__ void rope_angle(double log2_theta, int i, int64_t pos, double &cs, double &sn) {
-    const double inv_freq = exp2(-(double)(2 * i) / (double)kRot * log2_theta);
-    const double ang = (double)pos * inv_freq;
-    const double k = rint(ang * 0.15915494309189535);          // 1 / (2 pi)
-    double red = fma(-k, 6.283185307179586, ang);              // 2 pi, high part
-    red = fma(-k, 2.4492935982947064e-16, red);                // 2 pi, low part
-    sincos(red, &sn, &cs);
-}
-
-// Rotate the pair (a, b) by the angle (cs, sn) in fp64 and round once to f32.
-__device__ __forceinline__ void rope_rotate(double cs, double sn, float &a, float &b) {
-    const double x = (double)a, y = (double)b;
-    a = (float)(x * cs - y * sn);
-    b = (float)(x * sn + y * cs);
-}
-
-__device__ __forceinline__ void rope_pair(double log2_theta, int i, int64_t pos, float &a, float &b) {
-    double cs, sn;
-    rope_angle(log2_theta, i, pos, cs, sn);
-    rope_rotate(cs, sn, a, b);
-}
 
 // Query dims [d, d+8) of head h of query q as f32, as stored (no rotation).
 __device__ __forceinline__ void load_q8_plain(const MqaArgs &a, int64_t q, int h, int d, float (&v)[8]) {

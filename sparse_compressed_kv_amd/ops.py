@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
     L.ds4a_sparse_mqa.restype = i32
     L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
     L.ds4a_dense_mqa.restype = i32
+    L.ds4a_compress_rows.argtypes = [i32, i32, i32, P, P, P, flt, i32, P, dbl, i32, P, i64, P]
+    L.ds4a_compress_rows.restype = i32
     L.ds4a_rope_q.argtypes = [i32, i32, i32, i32, i32, P, i32, P, dbl, P, P]
     L.ds4a_rope_q.restype = i32
     _lib = L
@@ -232,6 +234,27 @@ def dense_mqa(q, q_pos, raw_kv, comp_kv, scale: float, theta: float = 10000.0, W
         U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta),
         _ptr(raw_kv) if W > 0 else None, _ptr(comp_kv) if N > 0 else None,
         _ptr(n_vis) if n_vis is not None else None, float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    return out
+
+
+def compress_rows(state_kv, state_score, gain, row_pos, eps: float = 1e-6, n_rot: int = 64,
+                  theta: float = 10000.0, fp8: bool = True, out=None, stream=None):
+    """Compressor row emission.  state_kv, state_score f32 [U, ratio, width], gain f32 [U, width],
+    row_pos i64 [U] -> bf16 [U, width] (or into `out`, a bf16 tensor whose rows are
+    out[u] = the row of unit u, e.g. cache[:, n, :] of a [U, N, width] cache)."""
+    U, ratio, width = state_kv.shape
+    _need(state_kv, "state_kv", torch.float32, (U, ratio, width))
+    _need(state_score, "state_score", torch.float32, (U, ratio, width))
+    _need(gain, "gain", torch.float32, (U, width))
+    _need(row_pos, "row_pos", torch.int64, (U,))
+    if out is None:
+        out = torch.empty((U, width), dtype=torch.bfloat16, device=state_kv.device)
+    if out.dtype != torch.bfloat16 or out.shape != (U, width) or out.stride(1) != 1 or out.device.type != "cuda":
+        raise ValueError("out must be a bf16 [U, width] view with unit-stride rows on the GPU")
+    stride = out.stride(0) if U > 1 else width
+    _check("ds4a_compress_rows", lib().ds4a_compress_rows(
+        U, width, ratio, _ptr(state_kv), _ptr(state_score), _ptr(gain), float(eps), int(n_rot), _ptr(row_pos),
+        float(theta), 1 if fp8 else 0, _ptr(out), stride, _stream(stream)))
     return out
 
 

@@ -19,7 +19,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = ops.declared_symbols()
     assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_dense_mqa",
-            "ds4a_rope_q", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
+            "ds4a_compress_rows", "ds4a_rope_q", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -136,6 +136,32 @@ def test_dense_mqa_validation(L):
     assert ops.workspace_bytes(3, 1, 1, -1, 0, 64, 128) == 0
     assert ops.workspace_bytes(3, 300, 1, 0, 0, 64, 128) == 0      # enough queries: no split
     assert ops.workspace_bytes(3, 1, 300, 4000, 0, 16, 32) > 0     # 127 tiles > 96 per chunk: split
+
+
+def _compress(L, **kw):
+    a = dict(U=2, width=512, ratio=4, kv=A, sc=A, gain=A, eps=1e-6, n_rot=64, pos=A, theta=10000.0, fp8=1, out=None,
+             stride=512)
+    a.update(kw)
+    return L.ds4a_compress_rows(a["U"], a["width"], a["ratio"], a["kv"], a["sc"], a["gain"], a["eps"], a["n_rot"],
+                                a["pos"], a["theta"], a["fp8"], a["out"], a["stride"], S)
+
+
+def test_compress_rows_validation(L):
+    assert _compress(L, U=0) == -2
+    assert _compress(L, width=511) == -2
+    assert _compress(L, ratio=0) == -2
+    assert _compress(L, n_rot=63) == -2
+    assert _compress(L, n_rot=514) == -2            # more than width
+    assert _compress(L, width=2048, n_rot=64, stride=2048) == -3
+    assert _compress(L, ratio=2048) == -3
+    assert _compress(L, eps=-1.0) == -2
+    assert _compress(L, theta=0.0) == -2
+    assert _compress(L, fp8=2) == -2
+    assert _compress(L, stride=100) == -2
+    assert _compress(L, kv=None) == -1
+    assert _compress(L, pos=MIS) == -4
+    assert _compress(L) == -1                       # out is NULL: checked last, nothing enqueued
+    assert "out" in ops.last_error()
 
 
 def test_rope_validation(L):

@@ -6,6 +6,8 @@ scores, and against the fp64 oracle equal apart from rows whose scores lie withi
 error of 2e-3 per (unit, query).  The hi/lo bf16 operand design is also held to
 1e-4, far inside that bar, so that losing one of the split terms is caught.
 """
+import math
+
 import numpy as np
 import pytest
 import torch
@@ -316,6 +318,64 @@ def test_dense_equals_sparse_over_all_rows():
     a = ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], idx, w.scale, W=W)
     b = ops.dense_mqa(d["q"], d["pos"], d["raw"], d["comp"], w.scale, W=W)
     assert torch.equal(a, b)
+
+
+COMPRESS_CASES = [
+    # (U, width, ratio, n_rot, fp8): ratio-4 and ratio-128 KV rows, the indexer's 128-wide
+    # keys, no FP8, one-row frontiers, a width that is not a multiple of the workgroup
+    dict(U=43, width=512, ratio=4, n_rot=64, fp8=True),
+    dict(U=20, width=512, ratio=128, n_rot=64, fp8=True),
+    dict(U=21, width=128, ratio=4, n_rot=64, fp8=True),
+    dict(U=5, width=128, ratio=4, n_rot=0, fp8=True),
+    dict(U=3, width=512, ratio=4, n_rot=64, fp8=False),
+    dict(U=4, width=512, ratio=1, n_rot=64, fp8=True),
+    dict(U=2, width=1000, ratio=7, n_rot=512, fp8=True),
+]
+
+
+def _compress_inputs(case, seed):
+    rng = np.random.default_rng(seed)
+    U, r, wd = case["U"], case["ratio"], case["width"]
+    kv = rng.standard_normal((U, r, wd)).astype(np.float32)
+    sc = (rng.standard_normal((U, r, wd)) * 2.0).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, (U, wd)).astype(np.float32)
+    pos = (4 * rng.integers(1, 1 << 18, U)).astype(np.int64)
+    return kv, sc, gain, pos
+
+
+def _near_midpoint(x, a, b, rel=1e-5):
+    """x (exact) lies within rel of the midpoint of the two representable values a and b."""
+    return abs(x - (a + b) / 2) <= rel * max(abs(x), 1e-30)
+
+
+@pytest.mark.parametrize("case", COMPRESS_CASES, ids=lambda c: f"U{c['U']}w{c['width']}r{c['ratio']}rot{c['n_rot']}{'fp8' if c['fp8'] else ''}")
+def test_compress_rows_matches_oracle(case):
+    """Emitted rows against the oracle: identical bf16 rows, except that a value may take the
+    neighbouring code where the oracle's exact value lies on a rounding midpoint (fp32 here,
+    fp64 there)."""
+    kv, sc, gain, pos = _compress_inputs(case, 31)
+    U, wd = case["U"], case["width"]
+    N = 3
+    cache = torch.full((U, N, wd), 7.0, dtype=torch.bfloat16, device="cuda")   # rows 0 and 2 must stay 7
+    ops.compress_rows(torch.from_numpy(kv).cuda(), torch.from_numpy(sc).cuda(), torch.from_numpy(gain).cuda(),
+                      torch.from_numpy(pos).cuda(), eps=1e-6, n_rot=case["n_rot"], fp8=case["fp8"], out=cache[:, 1, :])
+    host = cache.cpu()
+    assert torch.all(host[:, 0] == 7.0) and torch.all(host[:, 2] == 7.0)
+    got = host[:, 1].view(torch.int16).numpy().view(np.uint16)
+    for u in range(U):
+        ref, y, s = orc.compress_row(kv[u], sc[u], gain[u], eps=1e-6, n_rot=case["n_rot"], pos=int(pos[u]),
+                                     fp8=case["fp8"])
+        g_v, r_v = bf16_f64(got[u]), bf16_f64(ref)
+        if case["fp8"]:
+            amax = np.max(np.abs(y)) / 448.0
+            if abs(amax / 2.0 ** round(math.log2(amax)) - 1.0) < 1e-6:
+                continue                                  # scale on a power of two: either is right
+        diff = np.nonzero(got[u] != ref)[0]
+        for j in diff:
+            x = y[j] / s if case["fp8"] else y[j]
+            a, b = (g_v[j] / s, r_v[j] / s) if case["fp8"] else (g_v[j], r_v[j])
+            assert _near_midpoint(x, a, b), (u, j, x, a, b)
+        assert len(diff) <= max(2, wd // 100), (u, len(diff))
 
 
 @pytest.mark.parametrize("order,U,T", [("rising", 1, 1), ("falling", 2, 2)])
