@@ -14,7 +14,8 @@ and per step (p10 / p50 / p90).  Also measured in the same run: the same
 decode at N = 16,384 and 32,768 rows, 8 sessions at N = 262,144, the Pro shape
 (4 sessions, 128 heads, top-1024, N = 65,536), the attention of a whole Flash
 decode step (all 43 layers by their compression ratio, 262,144 tokens of
-context), and chunked prefill (2,048 queries, N = 8,192).  The CPU baseline runs the oracle on the main line's
+context), compressor row emission for the 41 layers that compress, and
+chunked prefill (2,048 queries, N = 8,192).  The CPU baseline runs the oracle on the main line's
 units and also reports how the GPU results agree with it.
 
 Inputs are synthetic (synth.inputs), uploaded to HBM before timing.  Several
@@ -372,6 +373,49 @@ def full_schedule(steps: int, warmup: int):
             "algorithmic_bytes": by, "frac_hbm": by / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, "parts_back_to_back": parts}
 
 
+def compressor(steps: int):
+    """Compressor row emission for one decode token that closes a block in every layer that
+    compresses: 21 ratio-4 layers (a 512-wide KV row and a 128-wide indexer key each) and 20
+    ratio-128 layers (a 512-wide KV row), written into caches of 65,536 / 2,048 rows.  The
+    frontier inputs are synthetic."""
+    import torch
+
+    from sparse_compressed_kv_amd import ops
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    groups = [("ratio4_kv", 21, 4, 512, 65536), ("ratio4_index_keys", 21, 4, 128, 65536),
+              ("ratio128_kv", 20, 128, 512, 2048)]
+    calls = []
+    by = 0
+    for name, U, ratio, width, rows in groups:
+        kv = torch.randn(U, ratio, width, device="cuda", generator=g)
+        sc = torch.randn(U, ratio, width, device="cuda", generator=g) * 2
+        gain = torch.rand(U, width, device="cuda", generator=g) + 0.5
+        pos = torch.full((U,), 262143, dtype=torch.int64, device="cuda")
+        cache = torch.zeros(U, rows, width, dtype=torch.bfloat16, device="cuda")
+        out = cache[:, rows - 1, :]
+        calls.append(lambda kv=kv, sc=sc, gain=gain, pos=pos, out=out: ops.compress_rows(
+            kv, sc, gain, pos, eps=1e-6, n_rot=64, fp8=True, out=out))
+        by += U * (2 * ratio * width * 4 + width * 4 + width * 2 + 8)
+    for _ in range(5):
+        for c in calls:
+            c()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        for c in calls:
+            c()
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    return {"workload": "compressor_emit_41layers (21 x ratio-4 KV + index key, 20 x ratio-128 KV)",
+            "us_per_token": us, "launches": len(calls), "algorithmic_bytes": by,
+            "GB_per_s": by / (us / 1e6) / 1e9}
+
+
 def traffic_for(kernel_hash: str, units: int):
     """HBM bytes per ds4a_indexer_topk call from committed rocprofv3 FETCH_SIZE/WRITE_SIZE counters
     (both kernels of the call), scaled by the same counters' reading of a plain copy of known size;
@@ -493,6 +537,10 @@ def main():
         log(f"[bench] {fs['workload']}: {fs}")
         rec["full_schedule_ctx262144"] = fs
         torch.cuda.empty_cache()
+        # ---- compressor row emission for the layers that compress
+        cm = compressor(args.steps)
+        log(f"[bench] {cm['workload']}: {cm}")
+        rec["compressor_emit"] = cm
         # ---- chunked prefill: 2,048 queries, 8,192 rows
         w3 = gen.CONFIGS["c3"]
         x3 = gen.make_config(w3)

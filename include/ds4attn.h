@@ -178,7 +178,8 @@ int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
  * with one power-of-two scale per row, the smallest that brings max|y| to <= 448, values
  * rounded to nearest (ties to even) and clipped, then scaled back (exact in bf16).
  * Arithmetic is fp32 except the rotation angle (fp64, as for the query).
- *   width    : even, 2..DS4A_MAX_COMPRESS_WIDTH (512 for KV rows, 128 for indexer keys)
+ *   width    : a multiple of 4, 4..DS4A_MAX_COMPRESS_WIDTH (512 for KV rows, 128 for
+ *              indexer keys)
  *   ratio    : 1..DS4A_MAX_COMPRESS_RATIO       n_rot : even, 0..min(width, 512)
  *   state_kv, state_score : f32 [U][ratio][width]     gain : f32 [U][width]
  *   eps      : >= 0 (finite)                     row_pos : int64 [U]

@@ -236,7 +236,7 @@ int ds4a_compress_rows(int U, int width, int ratio, const float *state_kv, const
                        void *out, int64_t out_stride, void *stream) {
     const char *fn = "ds4a_compress_rows";
     if (U < 1 || U > (1 << 24)) return fail(DS4A_E_SHAPE, "%s: U=%d must be in [1, 2^24]", fn, U);
-    if (width < 2 || width % 2 || ratio < 1 || n_rot < 0 || n_rot % 2 || n_rot > width)
+    if (width < 4 || width % 4 || ratio < 1 || n_rot < 0 || n_rot % 2 || n_rot > width)
         return fail(DS4A_E_SHAPE, "%s: width=%d ratio=%d n_rot=%d out of range", fn, width, ratio, n_rot);
     if (width > DS4A_MAX_COMPRESS_WIDTH || ratio > DS4A_MAX_COMPRESS_RATIO || n_rot > 512)
         return fail(DS4A_E_UNSUPPORTED, "%s: width=%d ratio=%d n_rot=%d (width <= %d, ratio <= %d, n_rot <= 512)",

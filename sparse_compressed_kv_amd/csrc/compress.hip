@@ -9,9 +9,11 @@
 // (RMS), its tail rotated (RoPE) and round-tripped through FP8.  The indexer keeps its
 // own, narrower compressor of the same form.
 //
-// One workgroup per emitted row (one unit: a layer or a session).  The pooling reads the
-// frontier once, lane-consecutive across channels; the RMS and the FP8 scale are block
-// reductions; the rotation reuses the query's fp64 angle code (rope.hpp).  Readings of what
+// One workgroup of 1024 threads per emitted row (one unit: a layer or a session).  The
+// pooling reads the frontier once in 16-byte lane-consecutive loads, several rows in flight
+// per thread, as an online softmax per row group whose partials merge in LDS; the RMS and
+// the FP8 scale are block reductions; the rotation reuses the query's fp64 angle code
+// (rope.hpp).  Readings of what
 // the page leaves open (the norm's epsilon and gain, the rotation's position, the FP8
 // format and scale) are stated at ds4a_compress_rows in the header.
 #include "common.hpp"
@@ -22,8 +24,9 @@ namespace ds4a {
 
 namespace {
 
-constexpr int kCThreads = 256;
+constexpr int kCThreads = 1024;
 constexpr int kCMaxWidth = 1024;
+constexpr int kCUnroll = 4;                   // frontier rows in flight per thread
 
 // max and sum over the workgroup (kCThreads threads); every thread gets the result.
 __device__ float block_sum(float v, float *red) {
@@ -68,29 +71,71 @@ __device__ __forceinline__ float e4m3_scale(float amax) {
     return ldexpf(1.f, f <= 0.875f ? e - 9 : e - 8);
 }
 
+// Online softmax-weighted sum: fold (score s, value v) into (reference m, sum of weights den,
+// weighted sum num), weights relative to m.
+__device__ __forceinline__ void fold(float s, float v, float &m, float &den, float &num) {
+    const float mn = fmaxf(m, s);
+    const float a = __expf(m - mn), b = __expf(s - mn);          // a = 0 for the first row (m = -inf)
+    den = den * a + b;
+    num = num * a + b * v;
+    m = mn;
+}
+
+// One workgroup per unit.  Pooling: thread t takes 4 consecutive channels (column t % ncol,
+// one 16-byte load per frontier row and array) and every G-th frontier row from row t / ncol,
+// kCUnroll rows' loads in flight; the G partial (reference, weight sum, weighted sum) of a
+// channel are merged through LDS.
 __global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
     int width, int ratio, const float *__restrict__ state_kv, const float *__restrict__ state_score,
     const float *__restrict__ gain, float eps, int n_rot, const int64_t *__restrict__ row_pos, double log2_theta,
     int fp8, uint16_t *__restrict__ out, int64_t out_stride)
 {
     __shared__ float s_y[kCMaxWidth];
+    __shared__ f32x4 s_part[3][kCThreads];                       // (m, den, num) per thread, 4 channels each
     __shared__ float s_red[kCThreads / kWave];
     const int64_t u = blockIdx.x;
-    const float *kv = state_kv + u * (int64_t)ratio * width;
-    const float *sc = state_score + u * (int64_t)ratio * width;
+    const int ncol = width / 4;
+    const int G = min(kCThreads / ncol, ratio);                  // row groups
+    const int col = threadIdx.x % ncol, grp = threadIdx.x / ncol;
+    const f32x4 *kv = reinterpret_cast<const f32x4 *>(state_kv + u * (int64_t)ratio * width) + col;
+    const f32x4 *sc = reinterpret_cast<const f32x4 *>(state_score + u * (int64_t)ratio * width) + col;
 
-    // per-channel softmax pooling over the frontier rows, then the sum of squares
+    if (grp < G) {
+        float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, den[4] = {0.f, 0.f, 0.f, 0.f};
+        float num[4] = {0.f, 0.f, 0.f, 0.f};
+        for (int r0 = grp; r0 < ratio; r0 += kCUnroll * G) {
+            f32x4 a[kCUnroll], b[kCUnroll];
+#pragma unroll
+            for (int k = 0; k < kCUnroll; ++k) {
+                const int r = r0 + k * G < ratio ? r0 + k * G : r0;   // past the end: repeat r0, skipped below
+                a[k] = kv[(int64_t)r * ncol];
+                b[k] = sc[(int64_t)r * ncol];
+            }
+#pragma unroll
+            for (int k = 0; k < kCUnroll; ++k) {
+                if (r0 + k * G >= ratio) break;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) fold(b[k][e], a[k][e], m[e], den[e], num[e]);
+            }
+        }
+        s_part[0][threadIdx.x] = f32x4{m[0], m[1], m[2], m[3]};
+        s_part[1][threadIdx.x] = f32x4{den[0], den[1], den[2], den[3]};
+        s_part[2][threadIdx.x] = f32x4{num[0], num[1], num[2], num[3]};
+    }
+    __syncthreads();
+    // merge the row groups of each channel, then the sum of squares of the pooled row
     float ss = 0.f;
     for (int j = threadIdx.x; j < width; j += kCThreads) {
-        float m = -INFINITY;
-        for (int r = 0; r < ratio; ++r) m = fmaxf(m, sc[(int64_t)r * width + j]);
-        float num = 0.f, den = 0.f;
-        for (int r = 0; r < ratio; ++r) {
-            const float w = __expf(sc[(int64_t)r * width + j] - m);
-            den += w;
-            num += w * kv[(int64_t)r * width + j];
+        const int c = j / 4, e = j % 4;
+        float mm = -INFINITY;
+        for (int g = 0; g < G; ++g) mm = fmaxf(mm, s_part[0][g * ncol + c][e]);
+        float d = 0.f, n = 0.f;
+        for (int g = 0; g < G; ++g) {
+            const float w = __expf(s_part[0][g * ncol + c][e] - mm);
+            d += s_part[1][g * ncol + c][e] * w;
+            n += s_part[2][g * ncol + c][e] * w;
         }
-        const float p = num / den;                               // den >= 1 (the max row)
+        const float p = n / d;                                   // d >= 1 (the max row's weight)
         s_y[j] = p;
         ss += p * p;
     }

@@ -149,6 +149,7 @@ def _compress(L, **kw):
 def test_compress_rows_validation(L):
     assert _compress(L, U=0) == -2
     assert _compress(L, width=511) == -2
+    assert _compress(L, width=514) == -2             # a multiple of 4
     assert _compress(L, ratio=0) == -2
     assert _compress(L, n_rot=63) == -2
     assert _compress(L, n_rot=514) == -2            # more than width
