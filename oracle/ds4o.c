@@ -489,3 +489,27 @@ int ds4o_compress_row(int width, int ratio, const float *state_kv, const float *
     free(y);
     return 0;
 }
+
+void ds4o_indexer_score_fp8(int64_t N, int Hi, int Di, const uint16_t *qI, const float *w,
+                            const uint8_t *k8, const float *scale, int64_t n_vis, double *s)
+{
+    double *key = (double *)malloc(sizeof(double) * (size_t)Di);
+    for (int64_t j = 0; j < N; j++) {
+        if (j >= n_vis) {
+            s[j] = -INFINITY;
+            continue;
+        }
+        for (int d = 0; d < Di; d++)
+            key[d] = ds4o_e4m3_to_f64(k8[j * Di + d]) * (double)scale[j];
+        double total = 0.0;
+        for (int h = 0; h < Hi; h++) {
+            double dot = 0.0;
+            for (int d = 0; d < Di; d++)
+                dot += ds4o_bf16_to_f64(qI[(int64_t)h * Di + d]) * key[d];
+            double relu = dot > 0.0 ? dot : 0.0;
+            total += (double)w[h] * relu;
+        }
+        s[j] = total;
+    }
+    free(key);
+}

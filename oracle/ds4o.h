@@ -99,6 +99,15 @@ double ds4o_e4m3_to_f64(uint8_t c);
  * +-448, NaN gives 0x7f.  Returns the code. */
 uint8_t ds4o_round_e4m3(double x);
 
+/* Indexer scores of one query over FP8-stored keys: the key of row j is the E4M3FN value
+ * of each code times the row's scale (the compressor's round trip, "Reading the
+ * architecture of DwarfStar (ds4.c), part 4/8", section 3-2), then as ds4o_indexer_score:
+ *   s[j] = sum_h w[h] * max(0, sum_d qI[h][d] * e4m3(k8[j][d]) * scale[j])   for j < n_vis
+ *   s[j] = -infinity                                                        for j >= n_vis
+ * qI: bf16 [Hi][Di], w: f32 [Hi], k8: E4M3FN codes [N][Di], scale: f32 [N], s: double [N]. */
+void ds4o_indexer_score_fp8(int64_t N, int Hi, int Di, const uint16_t *qI, const float *w,
+                            const uint8_t *k8, const float *scale, int64_t n_vis, double *s);
+
 /* One compressed row from the compressor's frontier (section 3-2 of the article):
  *   pooled[j] = sum_r softmax_r(state_score[r][j]) * state_kv[r][j]   (r < ratio)
  *   y         = pooled / sqrt(mean_j pooled[j]^2 + eps) * gain          (RMS norm)

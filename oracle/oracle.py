@@ -57,6 +57,8 @@ def lib() -> ctypes.CDLL:
         L.ds4o_round_bf16.argtypes, L.ds4o_round_bf16.restype = [dbl], ctypes.c_uint16
         L.ds4o_e4m3_to_f64.argtypes, L.ds4o_e4m3_to_f64.restype = [ctypes.c_uint8], dbl
         L.ds4o_round_e4m3.argtypes, L.ds4o_round_e4m3.restype = [dbl], ctypes.c_uint8
+        L.ds4o_indexer_score_fp8.argtypes = [i64, i32, i32, P, P, P, P, i64, P]
+        L.ds4o_indexer_score_fp8.restype = None
         L.ds4o_compress_row.argtypes = [i32, i32, P, P, P, dbl, i32, i64, dbl, i32, P, P, P]
         L.ds4o_compress_row.restype = i32
         _lib = L
@@ -99,6 +101,22 @@ def indexer_score(qI, w, kI, n_vis: int | None = None) -> np.ndarray:
     assert kI.shape[1] == Di and w.shape == (Hi,)
     s = np.empty(N, dtype=np.float64)
     lib().ds4o_indexer_score(N, Hi, Di, _p(qI), _p(w), _p(kI), N if n_vis is None else int(n_vis), _p(s))
+    return s
+
+
+def indexer_score_fp8(qI, w, k8, scale, n_vis: int | None = None) -> np.ndarray:
+    """One query over FP8-stored keys.  qI bf16 bits [Hi, Di], w f32 [Hi], k8 E4M3FN codes
+    uint8 [N, Di], scale f32 [N] -> float64 [N]."""
+    qI = _u16(qI)
+    k8 = np.ascontiguousarray(k8, dtype=np.uint8)
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    scale = np.ascontiguousarray(scale, dtype=np.float32)
+    Hi, Di = qI.shape
+    N = k8.shape[0]
+    assert k8.shape[1] == Di and w.shape == (Hi,) and scale.shape == (N,)
+    s = np.empty(N, dtype=np.float64)
+    lib().ds4o_indexer_score_fp8(N, Hi, Di, _p(qI), _p(w), _p(k8), _p(scale), N if n_vis is None else int(n_vis),
+                                 _p(s))
     return s
 
 

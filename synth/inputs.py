@@ -9,12 +9,18 @@ so raw rows are generated already f16-rounded.
 
 Recipe (every tensor of every unit has its own stream):
     rng = numpy.random.Generator(PCG64(SeedSequence([0xD54A, cfg_id, seed, unit, tensor_id])))
-    tensor ids: q=0, raw=1, comp=2, idx_k=3, idx_q=4, idx_w=5, heavy=6
+    tensor ids: q=0, raw=1, comp=2, idx_k=3, idx_q=4, idx_w=5, heavy=6, idx_k8=7, idx_k_scale=8
 Normal values are drawn as float32 N(0,1) and rounded once, round-to-nearest-even,
 to the stored dtype (bf16 or f16); f32 tensors are stored as drawn.  Indexer
 head weights are float32 U(0,1).  "Heavy" rows: round(frac*N) distinct rows
 whose compressed row and indexer-key row are both multiplied by 4 (exact in
 bf16).
+
+FP8-stored indexer keys (the compressor's output format: OCP E4M3FN codes and one
+power-of-two scale per row) are drawn as codes directly: sign uniform, exponent
+field round(N(11, 1.5)) clipped to 0..15, fraction uniform 0..7, the NaN pattern
+S.1111.111 replaced by S.1111.110; row scales 2^e with e uniform in -8..-6 (about
+the N(0,1) magnitudes of the bf16 keys), heavy rows' scales times 4.
 
 This module draws and rounds numbers only; it contains none of the
 attention arithmetic.
@@ -28,7 +34,8 @@ import os
 
 import numpy as np
 
-TENSOR_IDS = {"q": 0, "raw": 1, "comp": 2, "idx_k": 3, "idx_q": 4, "idx_w": 5, "heavy": 6}
+TENSOR_IDS = {"q": 0, "raw": 1, "comp": 2, "idx_k": 3, "idx_q": 4, "idx_w": 5, "heavy": 6, "idx_k8": 7,
+              "idx_k_scale": 8}
 _CHUNK_ELEMS = 1 << 22
 
 
@@ -164,6 +171,39 @@ def make_indexer_unit(w: Workload, unit: int, seed: int = 0) -> dict[str, np.nda
     if heavy.size:
         idx_k[heavy] = bf16_bits_from_f32(bf16_bits_to_f32(idx_k[heavy]) * np.float32(4.0))
     return {"idx_k": idx_k, "idx_q": idx_q, "idx_w": idx_w, "heavy": heavy}
+
+
+def e4m3_codes(rng, shape) -> np.ndarray:
+    """Finite OCP E4M3FN codes (uint8) with the exponent spread described above."""
+    n = int(np.prod(shape))
+    e = np.clip(np.rint(rng.normal(11.0, 1.5, n)), 0, 15).astype(np.uint8)
+    m = rng.integers(0, 8, n, dtype=np.uint8)
+    sign = rng.integers(0, 2, n, dtype=np.uint8)
+    c = (sign << np.uint8(7)) | (e << np.uint8(3)) | m
+    c[(c & np.uint8(0x7F)) == np.uint8(0x7F)] -= np.uint8(1)
+    return c.reshape(shape)
+
+
+def make_indexer_fp8_unit(w: Workload, unit: int, seed: int = 0) -> dict[str, np.ndarray]:
+    """Indexer inputs of one unit with FP8-stored keys: idx_k8 uint8 [N, Di] codes, idx_k_scale
+    f32 [N] powers of two; idx_q, idx_w and the heavy rows as make_indexer_unit draws them."""
+    T, N, Hi, Di = w.T, w.N, w.Hi, w.Di
+    idx_q = bf16_bits_from_f32(_rng(w, seed, unit, "idx_q").standard_normal((T, Hi, Di), dtype=np.float32))
+    idx_w = _rng(w, seed, unit, "idx_w").random((T, Hi), dtype=np.float32)
+    k8 = e4m3_codes(_rng(w, seed, unit, "idx_k8"), (N, Di))
+    scale = np.ldexp(np.float32(1.0), _rng(w, seed, unit, "idx_k_scale").integers(-8, -5, N)).astype(np.float32)
+    heavy = np.sort(_rng(w, seed, unit, "heavy").choice(N, size=w.n_heavy(), replace=False)).astype(np.int64)
+    if heavy.size:
+        scale[heavy] *= np.float32(4.0)
+    return {"idx_k8": k8, "idx_k_scale": scale, "idx_q": idx_q, "idx_w": idx_w, "heavy": heavy}
+
+
+def make_indexer_fp8_config(w: Workload, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:
+    """make_indexer_fp8_unit for all U units, stacked."""
+    n = threads or min(16, os.cpu_count() or 1, w.U)
+    with concurrent.futures.ThreadPoolExecutor(max_workers=max(1, n)) as ex:
+        units = list(ex.map(lambda u: make_indexer_fp8_unit(w, u, seed), range(w.U)))
+    return {key: np.stack([x[key] for x in units]) for key in ("idx_k8", "idx_k_scale", "idx_q", "idx_w")}
 
 
 def make_config(w: Workload, seed: int = 0, threads: int | None = None) -> dict[str, np.ndarray]:

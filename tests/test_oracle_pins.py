@@ -371,6 +371,55 @@ def test_e4m3_rounding_matches_torch(oracle_mod):
     assert (oracle_mod.round_e4m3(np.array([448.0, 449.0, 464.0, 1e6, -1e6])) == [0x7e, 0x7e, 0x7e, 0x7e, 0xfe]).all()
 
 
+def _fp8_keys(rng, n, di=128):
+    """Codes over the whole finite range (zeros and subnormals included) and positive scales."""
+    k8 = gen.e4m3_codes(rng, (n, di))
+    k8[0, :16] = np.arange(16, dtype=np.uint8)                               # zero and subnormals
+    k8[1, :8] = np.array([0x80, 0x81, 0x87, 0x88, 0x7E, 0xFE, 0x00, 0x08], np.uint8)
+    return k8
+
+
+def test_indexer_fp8_pow2_scale_equals_bf16_keys(oracle_mod):
+    """Power-of-two scales: code value * scale is exact in bf16, so the FP8 score equals the bf16
+    indexer score on those keys, made here through torch's own E4M3 and bf16 types."""
+    rng = np.random.default_rng(24)
+    N = 40
+    k8 = _fp8_keys(rng, N)
+    scale = np.ldexp(np.float32(1.0), rng.integers(-12, 4, N)).astype(np.float32)
+    qI, w = rand_bf16(rng, (64, 128)), rng.random(64, dtype=np.float32)
+    kv = torch.from_numpy(k8.copy()).view(torch.float8_e4m3fn).to(torch.float32) * torch.from_numpy(scale)[:, None]
+    kb = kv.to(torch.bfloat16)
+    assert torch.equal(kb.to(torch.float32), kv)                               # exact
+    kI = kb.view(torch.int16).numpy().view(np.uint16)
+    got = oracle_mod.indexer_score_fp8(qI, w, k8, scale, n_vis=31)
+    ref = oracle_mod.indexer_score(qI, w, kI, n_vis=31)
+    assert np.array_equal(got, ref)
+    assert np.isneginf(ref[31:]).all() and (ref[:31] > 0).any()
+
+
+def test_indexer_fp8_one_hot_weight_and_scale_homogeneity(oracle_mod):
+    """One head: ReLU of the matmul with the torch-decoded keys times their scales; any positive
+    scale factors out of the score (the ReLU is positively homogeneous)."""
+    rng = np.random.default_rng(25)
+    N = 33
+    k8 = _fp8_keys(rng, N)
+    scale = rng.uniform(0.01, 3.0, N).astype(np.float32)
+    qI = rand_bf16(rng, (64, 128))
+    dec = torch.from_numpy(k8.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    for h in (0, 40):
+        w = np.zeros(64, np.float32)
+        w[h] = 1.0
+        ref = np.maximum((dec * scale.astype(np.float64)[:, None]) @ bf16_f64(qI)[h], 0.0)
+        np.testing.assert_allclose(oracle_mod.indexer_score_fp8(qI, w, k8, scale), ref, rtol=1e-13, atol=1e-13)
+        assert (ref == 0).any() and (ref > 0).any()
+    w = rng.random(64, dtype=np.float32)
+    ones = oracle_mod.indexer_score_fp8(qI, w, k8, np.ones(N, np.float32))
+    full = oracle_mod.indexer_score_fp8(qI, w, k8, scale)
+    np.testing.assert_allclose(full, ones * scale, rtol=1e-13, atol=0)
+    part = oracle_mod.indexer_score_fp8(qI, w, k8, scale, n_vis=5)
+    assert np.all(np.isneginf(part[5:])) and np.array_equal(part[:5], full[:5])
+
+
 def test_round_bf16_matches_torch(oracle_mod):
     rng = np.random.default_rng(22)
     x = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-30, 30, 3000), [0.0, -0.0, 1.00390625,
