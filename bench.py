@@ -52,22 +52,26 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def indexer_bytes_per_unit(N: int, T: int = 1) -> int:
+KEY_BYTES_BF16 = 128 * 2          # one indexer key row in bf16
+KEY_BYTES_FP8 = 128 + 4           # E4M3 codes plus the row's f32 scale
+
+
+def indexer_bytes_per_unit(N: int, T: int = 1, key_bytes: int = KEY_BYTES_BF16) -> int:
     """Algorithmic HBM bytes of the indexer for one unit: keys read once, the query block and
     head weights read, scores written."""
-    return N * 128 * 2 + T * (64 * 128 * 2 + 64 * 4) + T * N * 4
+    return N * key_bytes + T * (64 * 128 * 2 + 64 * 4) + T * N * 4
 
 
-def select_bytes_per_unit(N: int, K: int) -> int:
+def select_bytes_per_unit(N: int, K: int, key_bytes: int = KEY_BYTES_BF16) -> int:
     """Algorithmic HBM bytes of the fused A1 + A2 call for one decode unit: keys read once, the
     query block and head weights read, the K selected rows written."""
-    return N * 128 * 2 + 64 * 128 * 2 + 64 * 4 + K * 4
+    return N * key_bytes + 64 * 128 * 2 + 64 * 4 + K * 4
 
 
-def decode_bytes_per_unit(N: int, H: int, K: int, W: int = 128) -> int:
+def decode_bytes_per_unit(N: int, H: int, K: int, W: int = 128, key_bytes: int = KEY_BYTES_BF16) -> int:
     """Algorithmic HBM bytes of a whole decode step for one unit (keys, selected rows, raw rows,
     query, output, indexer query and weights)."""
-    return N * 128 * 2 + K * 512 * 2 + W * 512 * 2 + H * 512 * 4 * 2 + 64 * 128 * 2 + 64 * 4
+    return N * key_bytes + K * 512 * 2 + W * 512 * 2 + H * 512 * 4 * 2 + 64 * 128 * 2 + 64 * 4
 
 
 def prefill_flops(w) -> float:
@@ -104,15 +108,22 @@ def upload(x: dict) -> dict:
 
 class Bench:
     """Device-resident replicas of one workload, and timed steps over them.  A step is
-    ds4a_indexer_topk (A1 + A2) then ds4a_sparse_mqa (A3-A6)."""
+    ds4a_indexer_topk (A1 + A2) then ds4a_sparse_mqa (A3-A6); with `fp8_keys` (the indexer keys
+    as E4M3 codes and row scales, synth.make_indexer_fp8_config) the select is
+    ds4a_indexer_topk_fp8."""
 
-    def __init__(self, w, x, replicas: int):
+    def __init__(self, w, x, replicas: int, fp8_keys=None):
         import torch
 
         from sparse_compressed_kv_amd import ops
 
         self.torch, self.ops, self.w = torch, ops, w
         self.reps = [upload(x) for _ in range(replicas)]
+        self.fp8 = fp8_keys is not None
+        if self.fp8:
+            for d in self.reps:
+                d["k8"] = torch.from_numpy(fp8_keys["idx_k8"]).cuda()
+                d["sc"] = torch.from_numpy(fp8_keys["idx_k_scale"]).cuda()
         self.step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=True)
         self.sep = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=False)
         self.nvis = w.vis_base is not None
@@ -122,9 +133,17 @@ class Bench:
         w, st = self.w, self.step
         d = self.reps[i % len(self.reps)]
         nv = d["n_vis"] if self.nvis else None
-        st.select(d, n_vis=nv, stream=stream)
+        self.select(d, nv, stream)
         self.ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W, out=st.out,
                             workspace=st.ws_mqa, stream=stream)
+
+    def select(self, d, nv, stream):
+        st = self.step
+        if self.fp8:
+            self.ops.indexer_topk_fp8(d["idx_q"], d["idx_w"], d["k8"], d["sc"], self.w.K, n_vis=nv, out=st.idx,
+                                      workspace=st.ws_topk, stream=stream)
+        else:
+            st.select(d, n_vis=nv, stream=stream)
 
     def run(self, steps: int, warmup: int):
         torch, ops, w = self.torch, self.ops, self.w
@@ -154,11 +173,13 @@ class Bench:
         # (inputs rotated as in the step), HIP events at the two ends only.  The separate A1 and
         # A2 calls are timed too, for comparison with the fused call the step uses.
         calls = {
-            "select": lambda d, nv: st.select(d, n_vis=nv, stream=stream),
+            "select": lambda d, nv: self.select(d, nv, stream),
             "mqa": lambda d, nv: ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta,
                                                 W=w.W, out=st.out, workspace=st.ws_mqa, stream=stream),
-            "indexer": lambda d, nv: ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv,
-                                                       out=sep.scores, stream=stream),
+            "indexer": (lambda d, nv: ops.indexer_score_fp8(d["idx_q"], d["idx_w"], d["k8"], d["sc"], n_vis=nv,
+                                                            out=sep.scores, stream=stream)) if self.fp8 else
+                       (lambda d, nv: ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv,
+                                                        out=sep.scores, stream=stream)),
             "topk": lambda d, nv: ops.topk_select(sep.scores, w.K, n_vis=nv, out=sep.idx, workspace=sep.ws_topk,
                                                   stream=stream),
         }
@@ -532,6 +553,26 @@ def main():
             }
             del b4, x4
             torch.cuda.empty_cache()
+        # ---- the main workload with FP8-stored indexer keys (E4M3 codes + one scale per row)
+        x8 = gen.make_indexer_fp8_config(w)
+        b8 = Bench(w, x, reps, fp8_keys=x8)
+        del x8
+        r8 = b8.run(args.steps, args.warmup)
+        log(f"[bench] {w.name} fp8 keys: {r8}")
+        sel8 = units * select_bytes_per_unit(w.N, w.K, KEY_BYTES_FP8)
+        by8 = units * decode_bytes_per_unit(w.N, w.H, w.K, w.W, KEY_BYTES_FP8)
+        rec["decode_n65536_fp8_keys"] = {
+            "workload": w.name + "_fp8keys", "value": units / (r8["ms_per_step"] / 1e3),
+            "unit": "decode tokens/s/layer", "ms_per_step": r8["ms_per_step"],
+            "frac_hbm": by8 / (r8["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "indexer_topk_frac_hbm": sel8 / (r8["select_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "indexer_alone_frac_hbm": units * indexer_bytes_per_unit(w.N, 1, KEY_BYTES_FP8) / (r8["indexer_ms"] / 1e3)
+            / 1e9 / HBM_PEAK_GBS,
+            "kernel_us": {"indexer_topk": r8["select_ms"] * 1e3, "mqa": r8["mqa_ms"] * 1e3,
+                          "indexer_alone": r8["indexer_ms"] * 1e3, "topk_alone": r8["topk_ms"] * 1e3},
+        }
+        del b8
+        torch.cuda.empty_cache()
         # ---- a whole Flash decode step: the 43 layers' attention by their compression ratio
         fs = full_schedule(args.steps, args.warmup)
         log(f"[bench] {fs['workload']}: {fs}")

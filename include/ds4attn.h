@@ -113,6 +113,32 @@ int ds4a_indexer_topk(int U, int T, int64_t N, int Hi, int Di, int K,
                       const int32_t *n_vis, int32_t *idx,
                       void *workspace, size_t workspace_bytes, void *stream);
 
+/* A1 and A1 + A2 on FP8-stored indexer keys.  The compressor that emits the
+ * indexer's keys rounds each row to FP8 (section 3-2 of "Reading the architecture
+ * of DwarfStar (ds4.c), part 4/8"; format as at ds4a_compress_rows: OCP E4M3FN with
+ * one power-of-two scale per row), so keeping the codes and the scale instead of
+ * bf16 values loses nothing and halves the bytes the indexer streams per row
+ * (256 -> 128, plus 4 for the scale).  As ds4a_indexer_score / ds4a_indexer_topk
+ * with idx_k replaced by
+ *   idx_k8      : uint8 [U][N][128] E4M3FN codes (the NaN codes 0x7F, 0xFF not allowed)
+ *   idx_k_scale : f32 [U][N], finite and > 0
+ * where the key of row j is code value * idx_k_scale[u][j].  The score is taken as
+ *   s[j] = idx_k_scale[u][j] * sum_h w[h] * max(0, <qI[h], code values of row j>)
+ * (a positive factor passes through the ReLU); the code values are widened to bf16
+ * exactly and the products run on the same bf16 MFMAs as the bf16 entry points.
+ * With power-of-two scales (as the compressor emits them) every score is bit-identical
+ * to the bf16 entry point's score on keys code value * scale, so idx is identical too.
+ * Routing (fused or score + select) and workspace sizes are those of the bf16 calls:
+ *   workspace: ds4a_workspace_bytes(2, U, T, N, K, 0, 0) bytes (topk; 0 -> NULL allowed)
+ */
+int ds4a_indexer_score_fp8(int U, int T, int64_t N, int Hi, int Di,
+                           const void *idx_q, const float *idx_w, const uint8_t *idx_k8,
+                           const float *idx_k_scale, const int32_t *n_vis, float *scores, void *stream);
+int ds4a_indexer_topk_fp8(int U, int T, int64_t N, int Hi, int Di, int K,
+                          const void *idx_q, const float *idx_w, const uint8_t *idx_k8,
+                          const float *idx_k_scale, const int32_t *n_vis, int32_t *idx,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
 /* A3-A6 — sparse multi-query attention over the raw window plus the selected
  * rows (sections 2 and 3; the raw window keeps f16-rounded values, section 3-1).
  * For unit u, query t, head h:

@@ -37,6 +37,12 @@ bool misaligned(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) !
         if (misaligned(p)) return fail(DS4A_E_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
     } while (0)
 
+#define REQUIRE_PTR_AS(p, name)                                                     \
+    do {                                                                            \
+        if (!(p)) return fail(DS4A_E_NULL, "%s: %s is NULL", fn, name);             \
+        if (misaligned(p)) return fail(DS4A_E_ALIGN, "%s: %s is not 16-byte aligned", fn, name); \
+    } while (0)
+
 #define OPTIONAL_PTR(p)                                                             \
     do {                                                                            \
         if ((p) && misaligned(p)) return fail(DS4A_E_ALIGN, "%s: %s is not 16-byte aligned", fn, #p); \
@@ -102,21 +108,68 @@ size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, in
     return 0;
 }
 
-int ds4a_indexer_score(int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
-                       const void *idx_k, const int32_t *n_vis, float *scores, void *stream) {
-    const char *fn = "ds4a_indexer_score";
+namespace {
+
+// Key rows of the bf16 (fp8 false) or E4M3 entry points, checked in argument order.
+#define REQUIRE_KEYS(keys, fp8)                                                     \
+    do {                                                                            \
+        REQUIRE_PTR_AS((keys).k, (fp8) ? "idx_k8" : "idx_k");                       \
+        if (fp8) REQUIRE_PTR_AS((keys).scale, "idx_k_scale");                       \
+    } while (0)
+
+int indexer_score(const char *fn, int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
+                  ds4a::KeyRows idx_k, bool fp8, const int32_t *n_vis, float *scores, void *stream) {
     if (int rc = check_units(fn, U, T, N)) return rc;
     if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
         return fail(DS4A_E_UNSUPPORTED, "%s: Hi=%d Di=%d (only %d x %d)", fn, Hi, Di, DS4A_INDEXER_HEADS,
                     DS4A_INDEXER_DIM);
     REQUIRE_PTR(idx_q);
     REQUIRE_PTR(idx_w);
-    REQUIRE_PTR(idx_k);
+    REQUIRE_KEYS(idx_k, fp8);
     REQUIRE_PTR(scores);
     OPTIONAL_PTR(n_vis);
-    return hip_status(fn, ds4a::launch_indexer(U, T, N, static_cast<const uint16_t *>(idx_q), idx_w,
-                                               static_cast<const uint16_t *>(idx_k), n_vis, scores,
-                                               static_cast<hipStream_t>(stream)));
+    return hip_status(fn, ds4a::launch_indexer(U, T, N, static_cast<const uint16_t *>(idx_q), idx_w, idx_k, n_vis,
+                                               scores, static_cast<hipStream_t>(stream)));
+}
+
+int indexer_topk(const char *fn, int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q,
+                 const float *idx_w, ds4a::KeyRows idx_k, bool fp8, const int32_t *n_vis, int32_t *idx,
+                 void *workspace, size_t workspace_bytes, void *stream) {
+    if (int rc = check_units(fn, U, T, N)) return rc;
+    if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
+        return fail(DS4A_E_UNSUPPORTED, "%s: Hi=%d Di=%d (only %d x %d)", fn, Hi, Di, DS4A_INDEXER_HEADS,
+                    DS4A_INDEXER_DIM);
+    if (K < 1) return fail(DS4A_E_SHAPE, "%s: K=%d must be >= 1", fn, K);
+    if (K > DS4A_MAX_TOPK) return fail(DS4A_E_UNSUPPORTED, "%s: K=%d (at most %d)", fn, K, DS4A_MAX_TOPK);
+    REQUIRE_PTR(idx_q);
+    REQUIRE_PTR(idx_w);
+    REQUIRE_KEYS(idx_k, fp8);
+    REQUIRE_PTR(idx);
+    OPTIONAL_PTR(n_vis);
+    const size_t need = ds4a::indexer_topk_workspace_bytes(U, T, N, K);
+    if (need) {
+        if (!workspace || workspace_bytes < need)
+            return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    }
+    return hip_status(fn, ds4a::launch_indexer_topk(U, T, N, K, static_cast<const uint16_t *>(idx_q), idx_w, idx_k,
+                                                    n_vis, idx, workspace, static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int ds4a_indexer_score(int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
+                       const void *idx_k, const int32_t *n_vis, float *scores, void *stream) {
+    return indexer_score("ds4a_indexer_score", U, T, N, Hi, Di, idx_q, idx_w, ds4a::KeyRows{idx_k, nullptr}, false,
+                         n_vis, scores, stream);
+}
+
+int ds4a_indexer_score_fp8(int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
+                           const uint8_t *idx_k8, const float *idx_k_scale, const int32_t *n_vis, float *scores,
+                           void *stream) {
+    return indexer_score("ds4a_indexer_score_fp8", U, T, N, Hi, Di, idx_q, idx_w,
+                         ds4a::KeyRows{idx_k8, idx_k_scale}, true, n_vis, scores, stream);
 }
 
 int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores, const int32_t *n_vis, int32_t *idx,
@@ -142,28 +195,15 @@ int ds4a_topk_select(int U, int T, int64_t N, int K, const float *scores, const 
 int ds4a_indexer_topk(int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q, const float *idx_w,
                       const void *idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
                       size_t workspace_bytes, void *stream) {
-    const char *fn = "ds4a_indexer_topk";
-    if (int rc = check_units(fn, U, T, N)) return rc;
-    if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
-        return fail(DS4A_E_UNSUPPORTED, "%s: Hi=%d Di=%d (only %d x %d)", fn, Hi, Di, DS4A_INDEXER_HEADS,
-                    DS4A_INDEXER_DIM);
-    if (K < 1) return fail(DS4A_E_SHAPE, "%s: K=%d must be >= 1", fn, K);
-    if (K > DS4A_MAX_TOPK) return fail(DS4A_E_UNSUPPORTED, "%s: K=%d (at most %d)", fn, K, DS4A_MAX_TOPK);
-    REQUIRE_PTR(idx_q);
-    REQUIRE_PTR(idx_w);
-    REQUIRE_PTR(idx_k);
-    REQUIRE_PTR(idx);
-    OPTIONAL_PTR(n_vis);
-    const size_t need = ds4a::indexer_topk_workspace_bytes(U, T, N, K);
-    if (need) {
-        if (!workspace || workspace_bytes < need)
-            return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
-                        workspace ? workspace_bytes : (size_t)0);
-        if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
-    }
-    return hip_status(fn, ds4a::launch_indexer_topk(U, T, N, K, static_cast<const uint16_t *>(idx_q), idx_w,
-                                                    static_cast<const uint16_t *>(idx_k), n_vis, idx, workspace,
-                                                    static_cast<hipStream_t>(stream)));
+    return indexer_topk("ds4a_indexer_topk", U, T, N, Hi, Di, K, idx_q, idx_w, ds4a::KeyRows{idx_k, nullptr}, false,
+                        n_vis, idx, workspace, workspace_bytes, stream);
+}
+
+int ds4a_indexer_topk_fp8(int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q, const float *idx_w,
+                          const uint8_t *idx_k8, const float *idx_k_scale, const int32_t *n_vis, int32_t *idx,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return indexer_topk("ds4a_indexer_topk_fp8", U, T, N, Hi, Di, K, idx_q, idx_w,
+                        ds4a::KeyRows{idx_k8, idx_k_scale}, true, n_vis, idx, workspace, workspace_bytes, stream);
 }
 
 int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q, int q_dtype,

@@ -15,6 +15,7 @@ typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -52,6 +53,15 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float x) {
     uint32_t u = __float_as_uint(x);
     u += 0x7FFFu + ((u >> 16) & 1u);
     return u >> 16;
+}
+
+// 8 OCP E4M3FN codes (byte k = element k) -> the same 8 values as bf16 (exact: every E4M3
+// value is a bf16 value); v_cvt_scalef32_pk_bf16_fp8 with scale 1 converts two at a time.
+__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 v) {
+    return u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.x, 1.0f, true)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, false)),
+                 __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(v.y, 1.0f, true))};
 }
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) {

@@ -22,7 +22,9 @@ namespace ds4a {
 namespace {
 
 constexpr int kFWaves = kNT / kWave;
-constexpr int kFBpi = 2;                      // 16-row blocks in flight per wave
+// 16-row blocks in flight per wave, for both key formats (3 or 4 blocks of E4M3 rows measured
+// no faster on MI355X: their loads are limited by request rate, not by bytes in flight).
+constexpr int kFBpi = 2;
 // Device figures behind the chunk rule (MI355X): 256 CUs, each holding two chunk workgroups
 // at once (the row loop keeps the query in VGPRs, 125 per lane: 4 waves per SIMD).  Fixed,
 // so that workspace sizes do not depend on the device a call runs on.
@@ -30,10 +32,10 @@ constexpr int64_t kFCUs = 256;
 constexpr int64_t kFSlots = 2 * kFCUs;
 
 // A chunk of up to EPT * 512 rows (`rows` per chunk): each thread selects over EPT keys.
-template <int EPT>
+template <int EPT, bool FP8>
 __global__ __launch_bounds__(kNT) void indexer_select_kernel(
     int T, int64_t N, int K, int rows, int64_t chunks,
-    const uint16_t *__restrict__ qI, const float *__restrict__ w, const uint16_t *__restrict__ kI,
+    const uint16_t *__restrict__ qI, const float *__restrict__ w, KeyRows keys,
     const int32_t *__restrict__ n_vis, int32_t *__restrict__ out, uint32_t *__restrict__ out_keys)
 {
     __shared__ u32x4 sq[kHeads * kDim / 8];
@@ -53,15 +55,17 @@ __global__ __launch_bounds__(kNT) void indexer_select_kernel(
     const int n = rem <= 0 ? 0 : (rem < rows ? (int)rem : rows);     // visible rows of this chunk
 
     if (n > 0) {                                  // uniform across the workgroup
-        const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
-        u32x4 kb[kFBpi][4];
-        indexer_load_keys<kFBpi>(gk, indexer_first_row<kFBpi>(c0, wave), c0 + n, g, c, kb);
+        const KeyRows unit = {static_cast<const char *>(keys.k) + u * N * kKeyRowBytes<FP8>,
+                              FP8 ? keys.scale + u * N : nullptr};
+        const KeyStream<FP8> st = key_stream<FP8>(unit, c0, n);
+        KeyBlock<FP8> kb[kFBpi];
+        indexer_first_keys<kFBpi, FP8>(st, wave, g, c, kb);   // in flight during the query set-up
         bf16x8 aq[4][4];
         indexer_query_frags<kNT>(qI, q, sq, g, c, aq);
         float wh[4];
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
-        indexer_score_rows<kFWaves, kFBpi>(aq, wh, gk, c0, c0 + n, wave, g, c, s_sc, kb);
+        indexer_score_rows<kFWaves, kFBpi, FP8>(aq, wh, st, n, wave, g, c, s_sc, kb);
     }
     __syncthreads();
 
@@ -128,11 +132,12 @@ bool use_fused(int T, int64_t Q, int64_t N, int K) {
 
 template <int EPT>
 void launch_select(int64_t grid, int T, int64_t N, int K, int rows, int64_t chunks, const uint16_t *idx_q,
-                   const float *idx_w, const uint16_t *idx_k, const int32_t *n_vis, int32_t *ids, uint32_t *keys,
+                   const float *idx_w, KeyRows idx_k, const int32_t *n_vis, int32_t *ids, uint32_t *keys,
                    hipStream_t stream)
 {
-    hipLaunchKernelGGL(indexer_select_kernel<EPT>, dim3((unsigned)grid), dim3(kNT), 0, stream, T, N, K, rows, chunks,
-                       idx_q, idx_w, idx_k, n_vis, ids, keys);
+    const auto kernel = idx_k.scale ? indexer_select_kernel<EPT, true> : indexer_select_kernel<EPT, false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(kNT), 0, stream, T, N, K, rows, chunks, idx_q, idx_w, idx_k,
+                       n_vis, ids, keys);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -147,7 +152,7 @@ size_t indexer_topk_workspace_bytes(int U, int T, int64_t N, int K) {
 }
 
 hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *idx_q, const float *idx_w,
-                               const uint16_t *idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
+                               KeyRows idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
                                hipStream_t stream)
 {
     const int64_t Q = (int64_t)U * T;

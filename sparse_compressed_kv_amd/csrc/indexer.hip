@@ -21,10 +21,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / kWave;
 constexpr int64_t kRowsPerWg = 1024;                          // rows per workgroup (256 KiB of keys)
+// 16-row blocks in flight per wave, for both key formats (3 or 4 blocks of E4M3 rows measured
+// no faster on MI355X: their loads are limited by request rate, not by bytes in flight).
+constexpr int kBpi = 2;
 
+template <bool FP8>
 __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     int T, int64_t N, int64_t rows_per_wg, int64_t wg_per_query,
-    const uint16_t *__restrict__ qI, const float *__restrict__ w, const uint16_t *__restrict__ kI,
+    const uint16_t *__restrict__ qI, const float *__restrict__ w, KeyRows keys,
     const int32_t *__restrict__ n_vis, float *__restrict__ scores)
 {
     const int64_t q = (int64_t)blockIdx.x / wg_per_query;          // flattened (u, t)
@@ -47,15 +51,17 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 
     __shared__ u32x4 sq[kHeads * kDim / 8];
     __shared__ __align__(16) float s_sc[kRowsPerWg];
-    const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
-    u32x4 kb[2][4];
-    indexer_load_keys<2>(gk, indexer_first_row<2>(r0, wave), rv1, g, c, kb);   // in flight during the query set-up
+    const KeyRows unit = {static_cast<const char *>(keys.k) + u * N * kKeyRowBytes<FP8>,
+                          FP8 ? keys.scale + u * N : nullptr};
+    const KeyStream<FP8> st = key_stream<FP8>(unit, r0, (int)(rv1 - r0));
+    KeyBlock<FP8> kb[kBpi];
+    indexer_first_keys<kBpi, FP8>(st, wave, g, c, kb);   // in flight during the query set-up
     bf16x8 aq[4][4];
     indexer_query_frags<kThreads>(qI, q, sq, g, c, aq);
     float wh[4];
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
-    indexer_score_rows<kWaves, 2>(aq, wh, gk, r0, rv1, wave, g, c, s_sc, kb);
+    indexer_score_rows<kWaves, kBpi, FP8>(aq, wh, st, (int)(rv1 - r0), wave, g, c, s_sc, kb);
 
     __syncthreads();
     const bool row_aligned = ((q * N) & 3) == 0;      // scores of this query start 16-byte aligned
@@ -88,9 +94,10 @@ constexpr int kPRB = kPTile / 16;              // 16-row blocks per tile
 static_assert(kPThreads == 4 * kPTile && kPRB % 4 == 0, "staging and score-store mappings");
 static_assert(kPQ == kIndexerManyQueries, "the prefill kernel's query count per workgroup");
 
+template <bool FP8>
 __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
     int T, int64_t N, int n_qb, int n_split,
-    const uint16_t *__restrict__ qI, const float *__restrict__ w, const uint16_t *__restrict__ kI,
+    const uint16_t *__restrict__ qI, const float *__restrict__ w, KeyRows keys,
     const int32_t *__restrict__ n_vis, float *__restrict__ scores)
 {
     __shared__ __align__(16) unsigned char s_k[2 * kPTileBytes];
@@ -142,19 +149,28 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) wh[ht][r] = w[q * kHeads + 16 * ht + 4 * g + r];
 
-    // Tile staging: thread tid moves chunks 4(tid%4) .. +3 of tile row tid/4 (64 B).
-    const u32x4 *gk = reinterpret_cast<const u32x4 *>(kI + u * N * kDim);
+    // Tile staging: thread tid moves dims 32(tid%4) .. +31 of tile row tid/4, i.e. 16-byte
+    // chunks 4(tid%4) .. +3 of the bf16 row in LDS; E4M3 rows arrive as four 8-byte pieces and
+    // are widened to bf16 (exactly) on the way into LDS, their scale applied to the scores.
+    using Piece = typename std::conditional<FP8, u32x2, u32x4>::type;
+    const Piece *gk = static_cast<const Piece *>(keys.k) + u * N * kChunksPerRow;
+    const float *gsc = FP8 ? keys.scale + u * N : nullptr;
     const int sr = tid >> 2, sc0 = (tid & 3) * 4;
-    u32x4 st[4];
+    Piece st[4];
     auto load_tile = [&](int64_t tile) __attribute__((always_inline)) {
         const int64_t row = tile * kPTile + sr;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) st[k] = row < N ? gk[row * kChunksPerRow + sc0 + k] : u32x4{0u, 0u, 0u, 0u};
+        for (int k = 0; k < 4; ++k) st[k] = row < N ? gk[row * kChunksPerRow + sc0 + k] : Piece{};
     };
     auto store_tile = [&](int buf) __attribute__((always_inline)) {
         unsigned char *base = s_k + buf * kPTileBytes + sr * 256;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) *reinterpret_cast<u32x4 *>(base + (((sc0 + k) ^ (sr & 15)) << 4)) = st[k];
+        for (int k = 0; k < 4; ++k) {
+            u32x4 v;
+            if constexpr (FP8) v = e4m3x8_to_bf16x8(st[k]);
+            else v = st[k];
+            *reinterpret_cast<u32x4 *>(base + (((sc0 + k) ^ (sr & 15)) << 4)) = v;
+        }
     };
     // A-fragment read offsets: row 16rb + c, chunk (4s + g) ^ c (the row's low 4 bits are c).
     int a_off[4];
@@ -167,8 +183,17 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
     __syncthreads();
     for (int64_t tile = tile0; tile < tile1; ++tile) {
         const int buf = (int)((tile - tile0) & 1);
-        if (tile + 1 < tile1) load_tile(tile + 1);
         const int64_t trow0 = tile * kPTile;
+        // scales of the rows this lane stores (row 16rb + c of blocks rb = (kPRB/4) g + k)
+        float rsc[kPRB / 4];
+        if constexpr (FP8) {
+#pragma unroll
+            for (int k = 0; k < kPRB / 4; ++k) {
+                const int64_t row = trow0 + ((kPRB / 4) * g + k) * 16 + c;
+                rsc[k] = gsc[row < N ? row : N - 1];
+            }
+        }
+        if (tile + 1 < tile1) load_tile(tile + 1);
         if (active) {
             const unsigned char *tb = s_k + buf * kPTileBytes;
             // D[head 16ht + 4g + r][row 16rb + c] (A = query, B = keys): the head sum is mostly
@@ -209,6 +234,7 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
                 float v = part[0];
 #pragma unroll
                 for (int i = 1; i < kPRB; ++i) v = rb == i ? part[i] : v;
+                if constexpr (FP8) v *= rsc[k];
                 if (trow0 + rb * 16 + c >= nv) v = -INFINITY;
                 s_sc[wave][rb * 16 + c] = v;
             }
@@ -235,9 +261,9 @@ __global__ __launch_bounds__(kPThreads) void indexer_prefill_kernel(
 }  // namespace
 
 hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w,
-                          const uint16_t *idx_k, const int32_t *n_vis, float *scores,
-                          hipStream_t stream)
+                          KeyRows keys, const int32_t *n_vis, float *scores, hipStream_t stream)
 {
+    const bool fp8 = keys.scale != nullptr;
     const int64_t Q = (int64_t)U * T;
     if (T >= kIndexerManyQueries) {
         const int n_qb = (T + kPQ - 1) / kPQ;
@@ -249,8 +275,9 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
         const int64_t max_split = (N + 4 * kPTile - 1) / (4 * kPTile);
         if (n_split > max_split) n_split = (int)max_split;
         if (n_split < 1) n_split = 1;
-        hipLaunchKernelGGL(indexer_prefill_kernel, dim3((unsigned)(wgs * n_split)), dim3(kPThreads), 0, stream,
-                           T, N, n_qb, n_split, idx_q, idx_w, idx_k, n_vis, scores);
+        const auto kernel = fp8 ? indexer_prefill_kernel<true> : indexer_prefill_kernel<false>;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)(wgs * n_split)), dim3(kPThreads), 0, stream,
+                           T, N, n_qb, n_split, idx_q, idx_w, keys, n_vis, scores);
         return hipGetLastError();
     }
     // 1024-row chunks (256 KiB of keys per workgroup): fastest on MI355X among 256..8192-row chunks,
@@ -258,8 +285,9 @@ hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const 
     const int64_t rows = kRowsPerWg;
     const int64_t per_q = (N + rows - 1) / rows;
     const int64_t blocks = per_q * Q;
-    hipLaunchKernelGGL(indexer_score_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       T, N, rows, per_q, idx_q, idx_w, idx_k, n_vis, scores);
+    const auto kernel = fp8 ? indexer_score_kernel<true> : indexer_score_kernel<false>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, T, N, rows, per_q, idx_q, idx_w, keys,
+                       n_vis, scores);
     return hipGetLastError();
 }
 

@@ -12,7 +12,10 @@
 // lanes of a row.
 #pragma once
 
+#include <type_traits>
+
 #include "common.hpp"
+#include "launch.hpp"
 
 namespace ds4a {
 
@@ -48,56 +51,138 @@ __device__ __forceinline__ void indexer_query_frags(const uint16_t *__restrict__
         for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + ((4 * s + g) ^ c)]);
 }
 
-// Keys of the 16*BPI rows from `base` as MFMA A fragments: lane (g, c) takes the 16-byte
-// chunks 4s + g of row base + 16bi + c; rows at or past rv1 read as zero (no load).
-template <int BPI>
-__device__ __forceinline__ void indexer_load_keys(const u32x4 *__restrict__ gk, int64_t base, int64_t rv1, int g,
-                                                  int c, u32x4 (&kb)[BPI][4]) {
+// Per-lane key registers of one 16-row block: 4 k-steps of 8 values, as bf16 (16 bytes each)
+// or as E4M3 codes (8 bytes each, converted to bf16 just before the MFMAs) plus the scale of
+// row 4g + (c & 3) of the block, the row whose score the lane stores.
+template <bool FP8>
+struct KeyBlock {
+    u32x4 v[4];
+};
+template <>
+struct KeyBlock<true> {
+    u32x2 v[4];
+    float sc;
+};
+
+// The visible key rows [r0, r0 + n) of one unit as buffer resources: 32-bit offsets relative
+// to row r0 (n * row bytes < 2^32 for the chunk sizes used here), and reads past the last
+// visible row return zero without touching memory, so no row needs a bounds branch.
+template <bool FP8>
+struct KeyStream {
+    __amdgpu_buffer_rsrc_t k;
+    __amdgpu_buffer_rsrc_t sc;
+};
+
+template <bool FP8>
+constexpr int kKeyRowBytes = FP8 ? kDim : 2 * kDim;
+
+// ks: the unit's rows (row 0 at ks.k, scale 0 at ks.scale).
+template <bool FP8>
+__device__ __forceinline__ KeyStream<FP8> key_stream(const KeyRows &ks, int64_t r0, int n) {
+    constexpr int kRaw = 0x00020000;              // word 3 of a raw (stride 0) buffer resource
+    KeyStream<FP8> st;
+    const char *k = static_cast<const char *>(ks.k) + r0 * kKeyRowBytes<FP8>;
+    st.k = __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(k), (short)0, n * kKeyRowBytes<FP8>, kRaw);
+    if constexpr (FP8)
+        st.sc = __builtin_amdgcn_make_buffer_rsrc(const_cast<float *>(ks.scale + r0), (short)0, n * 4, kRaw);
+    return st;
+}
+
+// Keys of the 16-row block at local row `blk`: lane (g, c) takes dims 32s + 8g .. +7 (k-step s)
+// of row blk + c, i.e. 16-byte chunk (bf16) or 8-byte piece (E4M3) 4s + g of the row, so both
+// formats feed the same dims to the same MFMA slots; rows past the stream read as zero.
+template <bool FP8>
+__device__ __forceinline__ void indexer_load_block(const KeyStream<FP8> &st, int blk, int g, int c,
+                                                   KeyBlock<FP8> &kb) {
+    const int off = (blk + c) * kKeyRowBytes<FP8>;
 #pragma unroll
-    for (int bi = 0; bi < BPI; ++bi) {
-        const int64_t row = base + 16 * bi + c;
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            kb[bi][s] = row < rv1 ? gk[row * kChunksPerRow + 4 * s + g] : u32x4{0u, 0u, 0u, 0u};
+    for (int s = 0; s < 4; ++s) {
+        if constexpr (FP8) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b64(st.k, off + (4 * s + g) * 8, 0, 0);
+            kb.v[s] = u32x2{v[0], v[1]};
+        } else {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(st.k, off + (4 * s + g) * 16, 0, 0);
+            kb.v[s] = u32x4{v[0], v[1], v[2], v[3]};
+        }
     }
 }
 
-// First row of a wave's first iteration in indexer_score_rows.
-template <int BPI>
-__device__ __forceinline__ int64_t indexer_first_row(int64_t r0, int wave) { return r0 + 16 * BPI * wave; }
+template <bool FP8>
+__device__ __forceinline__ float indexer_load_scale(const KeyStream<FP8> &st, int blk, int g, int c) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(st.sc, (blk + 4 * g + (c & 3)) * 4, 0, 0));
+}
 
-// Scores of the visible rows [r0, rv1) of one query into s_out[row - r0] (LDS), by the
-// WAVES waves of the workgroup, BPI 16-row blocks per wave iteration; wh[ht] is the weight
-// of head 16ht + c.  kb holds the wave's first iteration of keys (indexer_load_keys at
-// indexer_first_row), so a caller can issue those loads before it sets up the query; the
-// next iteration's loads are issued as soon as the current blocks are used.  A row's score
-// does not depend on WAVES or BPI.
-template <int WAVES, int BPI>
+// The BPI blocks of a wave's first iteration in indexer_score_rows.
+template <int BPI, bool FP8>
+__device__ __forceinline__ void indexer_first_keys(const KeyStream<FP8> &st, int wave, int g, int c,
+                                                   KeyBlock<FP8> (&kb)[BPI]) {
+#pragma unroll
+    for (int bi = 0; bi < BPI; ++bi) {
+        const int blk = 16 * (BPI * wave + bi);
+        indexer_load_block<FP8>(st, blk, g, c, kb[bi]);
+        if constexpr (FP8) kb[bi].sc = indexer_load_scale<FP8>(st, blk, g, c);
+    }
+}
+
+// Scores of the n visible rows of a key stream into s_out[0 .. n) (LDS; the slots up to the next
+// multiple of 16 are written too), by the WAVES waves of the workgroup, BPI 16-row blocks per
+// wave iteration; wh[ht] is the weight of head 16ht + c.  kb holds the wave's first iteration
+// of keys (indexer_first_keys), so a caller can issue those loads before it sets up the
+// query.  A block's registers are refilled with the same block of the next iteration as soon
+// as its MFMAs are issued (its scale once the score is stored), so BPI blocks stay in flight
+// while the epilogues run; loads complete in issue order, the order the blocks are used in.
+// A row's score does not depend on WAVES or BPI.  E4M3 keys: the products use the code values
+// and the row's score is multiplied by its scale at the end (scale > 0 commutes with the
+// ReLU); with power-of-two scales the score is bit-identical to that of the bf16 keys
+// code * scale.
+template <int WAVES, int BPI, bool FP8>
 __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], const float (&wh)[4],
-                                                   const u32x4 *__restrict__ gk, int64_t r0, int64_t rv1,
-                                                   int wave, int g, int c, float *s_out, u32x4 (&kb)[BPI][4]) {
+                                                   const KeyStream<FP8> &st, int n, int wave, int g, int c,
+                                                   float *s_out, KeyBlock<FP8> (&kb)[BPI]) {
     constexpr int kRowsPerIter = 16 * BPI * WAVES;
-    for (int64_t base = indexer_first_row<BPI>(r0, wave); base < rv1; base += kRowsPerIter) {
+    // The head weights arrive before the loop: a wait for them inside it would also wait for
+    // every key load issued after them.
+    asm volatile("" : : "v"(wh[0]), "v"(wh[1]), "v"(wh[2]), "v"(wh[3]));
+    for (int base = 16 * BPI * wave; base < n; base += kRowsPerIter) {
 #pragma unroll
         for (int bi = 0; bi < BPI; ++bi) {
-            const int64_t blk = base + 16 * bi;
-            if (blk >= rv1) break;                    // uniform across the wave
+            // Every block is computed, also past n (its keys read as zero): a branch here would
+            // make the loop's waits cover the next block's loads as well.
+            const int blk = base + 16 * bi;
+            const bool live = blk < n;
+            u32x4 a[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                if constexpr (FP8) a[s] = e4m3x8_to_bf16x8(kb[bi].v[s]);
+                else a[s] = kb[bi].v[s];
+            }
             // D[row 4g + r][head 16ht + c] = <key row, query head> (A = keys, B = query).
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ht = 0; ht < 4; ++ht) {
                 f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(kb[bi][s]), aq[ht][s], d);
+                for (int s = 0; s < 4; ++s) d = mfma16(as_bf16x8(a[s]), aq[ht][s], d);
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * relu(d[r]);
             }
+            indexer_load_block<FP8>(st, blk + kRowsPerIter, g, c, kb[bi]);
             // Sum over the 16 heads of each row: the 16 lanes of a DPP row.
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
-            if (c == 0) *reinterpret_cast<f32x4 *>(s_out + (blk - r0) + 4 * g) = acc;
+            if constexpr (FP8) {
+                // lanes c < 4 of group g store row 4g + c, scaled
+                const int r = c & 3;
+                float v = acc[0];
+                v = r == 1 ? acc[1] : v;
+                v = r == 2 ? acc[2] : v;
+                v = r == 3 ? acc[3] : v;
+                if (live && c < 4) s_out[blk + 4 * g + r] = v * kb[bi].sc;
+                kb[bi].sc = indexer_load_scale<FP8>(st, blk + kRowsPerIter, g, c);
+            } else {
+                if (live && c == 0) *reinterpret_cast<f32x4 *>(s_out + blk + 4 * g) = acc;
+            }
         }
-        indexer_load_keys<BPI>(gk, base + kRowsPerIter, rv1, g, c, kb);
     }
 }
 

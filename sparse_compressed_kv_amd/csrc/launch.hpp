@@ -10,10 +10,16 @@ namespace ds4a {
 // Units with at least this many queries take the many-queries (prefill) indexer.
 constexpr int kIndexerManyQueries = 4;
 
+// Indexer key rows as stored: bf16 [U][N][128] (scale == nullptr), or OCP E4M3FN codes
+// [U][N][128] with one positive f32 scale per row [U][N] (the key is code value * scale).
+struct KeyRows {
+    const void *k;
+    const float *scale;
+};
+
 // A1: scores f32 [Q][N], Q = U*T.
-hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w,
-                          const uint16_t *idx_k, const int32_t *n_vis, float *scores,
-                          hipStream_t stream);
+hipError_t launch_indexer(int U, int T, int64_t N, const uint16_t *idx_q, const float *idx_w, KeyRows idx_k,
+                          const int32_t *n_vis, float *scores, hipStream_t stream);
 
 // A2
 size_t topk_workspace_bytes(int64_t Q, int64_t N, int K);
@@ -30,7 +36,7 @@ hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chu
 // scores kept in the workspace (many queries per unit).
 size_t indexer_topk_workspace_bytes(int U, int T, int64_t N, int K);
 hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *idx_q, const float *idx_w,
-                               const uint16_t *idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
+                               KeyRows idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
                                hipStream_t stream);
 
 // A3-A6

@@ -55,6 +55,10 @@ def lib() -> ctypes.CDLL:
     L.ds4a_topk_select.restype = i32
     L.ds4a_indexer_topk.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, P, sz, P]
     L.ds4a_indexer_topk.restype = i32
+    L.ds4a_indexer_score_fp8.argtypes = [i32, i32, i64, i32, i32, P, P, P, P, P, P, P]
+    L.ds4a_indexer_score_fp8.restype = i32
+    L.ds4a_indexer_topk_fp8.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
+    L.ds4a_indexer_topk_fp8.restype = i32
     L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
     L.ds4a_sparse_mqa.restype = i32
     L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
@@ -70,7 +74,7 @@ def lib() -> ctypes.CDLL:
 def declared_symbols() -> list[str]:
     """Function names the public header declares."""
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(ds4a_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ds4a_[a-z0-9_]+)\s*\(", text)))
 
 
 def last_error() -> str:
@@ -170,6 +174,53 @@ def indexer_topk(idx_q, idx_w, idx_k, K: int, n_vis=None, out=None, workspace=No
     ws, nb = _workspace(workspace_bytes(2, U, T, N, K), idx_q.device, workspace)
     _check("ds4a_indexer_topk", lib().ds4a_indexer_topk(U, T, N, Hi, Di, K, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k),
                                                         _ptr(n_vis), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    return out
+
+
+def _fp8_keys(idx_k8, idx_k_scale, U, Di):
+    """E4M3 key codes (uint8 or float8_e4m3fn) [U,N,Di] and their f32 row scales [U,N]."""
+    if not isinstance(idx_k8, torch.Tensor) or idx_k8.dim() != 3:
+        raise TypeError("idx_k8 must be a 3-d torch.Tensor")
+    if idx_k8.dtype == torch.float8_e4m3fn:
+        idx_k8 = idx_k8.view(torch.uint8)
+    N = idx_k8.shape[1]
+    _need(idx_k8, "idx_k8", torch.uint8, (U, N, Di))
+    _need(idx_k_scale, "idx_k_scale", torch.float32, (U, N))
+    return idx_k8, N
+
+
+def indexer_score_fp8(idx_q, idx_w, idx_k8, idx_k_scale, n_vis=None, out=None, stream=None):
+    """A1 on FP8-stored keys: codes [U,N,128] (E4M3FN), scales f32 [U,N] -> f32 [U,T,N]."""
+    _need(idx_q, "idx_q", torch.bfloat16)
+    U, T, Hi, Di = idx_q.shape
+    idx_k8, N = _fp8_keys(idx_k8, idx_k_scale, U, Di)
+    _need(idx_w, "idx_w", torch.float32, (U, T, Hi))
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    if out is None:
+        out = torch.empty((U, T, N), dtype=torch.float32, device=idx_q.device)
+    _need(out, "out", torch.float32, (U, T, N))
+    _check("ds4a_indexer_score_fp8",
+           lib().ds4a_indexer_score_fp8(U, T, N, Hi, Di, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k8), _ptr(idx_k_scale),
+                                        _ptr(n_vis), _ptr(out), _stream(stream)))
+    return out
+
+
+def indexer_topk_fp8(idx_q, idx_w, idx_k8, idx_k_scale, K: int, n_vis=None, out=None, workspace=None, stream=None):
+    """A1 + A2 on FP8-stored keys (as indexer_topk; same workspace size)."""
+    _need(idx_q, "idx_q", torch.bfloat16)
+    U, T, Hi, Di = idx_q.shape
+    idx_k8, N = _fp8_keys(idx_k8, idx_k_scale, U, Di)
+    _need(idx_w, "idx_w", torch.float32, (U, T, Hi))
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    if out is None:
+        out = torch.empty((U, T, K), dtype=torch.int32, device=idx_q.device)
+    _need(out, "out", torch.int32, (U, T, K))
+    ws, nb = _workspace(workspace_bytes(2, U, T, N, K), idx_q.device, workspace)
+    _check("ds4a_indexer_topk_fp8",
+           lib().ds4a_indexer_topk_fp8(U, T, N, Hi, Di, K, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k8), _ptr(idx_k_scale),
+                                       _ptr(n_vis), _ptr(out), _ptr(ws), nb, _stream(stream)))
     return out
 
 

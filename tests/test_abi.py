@@ -19,7 +19,7 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = ops.declared_symbols()
     assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_dense_mqa",
-            "ds4a_compress_rows", "ds4a_rope_q", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
+            "ds4a_compress_rows", "ds4a_rope_q", "ds4a_indexer_score_fp8", "ds4a_indexer_topk_fp8", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -73,6 +73,32 @@ def test_indexer_topk_validation(L):
     assert f(2, 1, 65536, 64, 128, 512, A, A, A, None, A, None, 0, S) == -5
     assert f(2, 1, 65536, 64, 128, 512, A, A, A, None, A, A, need - 1, S) == -5
     assert f(2, 1, 65536, 64, 128, 512, A, A, A, None, A, MIS, need, S) == -4
+
+
+def test_indexer_fp8_validation(L):
+    f = L.ds4a_indexer_score_fp8
+    assert f(0, 1, 10, 64, 128, A, A, A, A, None, A, S) == -2
+    assert f(1, 1, 10, 64, 64, A, A, A, A, None, A, S) == -3
+    assert f(1, 1, 10, 64, 128, A, A, None, A, None, A, S) == -1
+    assert "idx_k8" in ops.last_error()
+    assert f(1, 1, 10, 64, 128, A, A, A, None, None, A, S) == -1
+    assert "idx_k_scale" in ops.last_error()
+    assert f(1, 1, 10, 64, 128, A, A, MIS, A, None, A, S) == -4
+    assert f(1, 1, 10, 64, 128, A, A, A, MIS, None, A, S) == -4
+    assert "idx_k_scale" in ops.last_error()
+    assert f(1, 1, 10, 64, 128, A, A, A, A, None, None, S) == -1
+    g = L.ds4a_indexer_topk_fp8
+    assert g(1, 1, 10, 64, 128, 0, A, A, A, A, None, A, None, 0, S) == -2
+    assert g(1, 1, 10, 64, 128, 8, A, A, None, A, None, A, None, 0, S) == -1
+    assert "ds4a_indexer_topk_fp8" in ops.last_error() and "idx_k8" in ops.last_error()
+    assert g(1, 1, 10, 64, 128, 8, A, A, A, None, None, A, None, 0, S) == -1
+    assert g(1, 1, 10, 64, 128, 8, A, A, A, A, None, None, None, 0, S) == -1
+    need = ops.workspace_bytes(2, 2, 1, 65536, 512)
+    assert g(2, 1, 65536, 64, 128, 512, A, A, A, A, None, A, None, 0, S) == -5
+    assert g(2, 1, 65536, 64, 128, 512, A, A, A, A, None, A, MIS, need, S) == -4
+    # the bf16 entry point still names its own key argument
+    assert L.ds4a_indexer_topk(1, 1, 10, 64, 128, 8, A, A, None, None, A, None, 0, S) == -1
+    assert "idx_k " in ops.last_error() or ops.last_error().endswith("idx_k is NULL")
 
 
 def _mqa(L, **kw):

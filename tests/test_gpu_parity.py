@@ -223,6 +223,100 @@ def test_indexer_topk_all_tied():
     assert np.array_equal(got[:, 0], np.broadcast_to(np.arange(512, dtype=np.int32), (w.U, 512)))
 
 
+# ------------------------------------------------------- FP8-stored indexer keys
+
+def _fp8_inputs(U, T, N, seed, heavy=0.0):
+    w = gen.Workload("fp8", 107, U=U, T=T, N=N, H=16, K=64, heavy_frac=heavy)
+    x = gen.make_indexer_fp8_config(w, seed=seed)
+    x["idx_k8"][:, 0, :16] = np.arange(16, dtype=np.uint8)          # zero and subnormal codes
+    d = {
+        "iq": bits_to_torch(x["idx_q"], torch.bfloat16),
+        "iw": torch.from_numpy(x["idx_w"]).cuda(),
+        "k8": torch.from_numpy(x["idx_k8"]).cuda(),
+        "sc": torch.from_numpy(x["idx_k_scale"]).cuda(),
+    }
+    return x, d
+
+
+def _fp8_as_bf16(k8, sc):
+    """bf16 keys code value * scale, through torch's own types (exact: the scales are powers of 2)."""
+    kf = k8.view(torch.float8_e4m3fn).to(torch.float32) * sc[..., None]
+    kb = kf.to(torch.bfloat16)
+    assert torch.equal(kb.to(torch.float32), kf)
+    return kb
+
+
+FP8_SCORE_CASES = [c for c in INDEXER_CASES if c["N"] in (1, 700, 4097, 257, 2048)]
+
+
+@pytest.mark.parametrize("case", FP8_SCORE_CASES, ids=lambda c: f"U{c['U']}T{c['T']}N{c['N']}")
+def test_indexer_fp8_matches_oracle_and_bf16_bits(case):
+    """FP8 keys: scores within the fp32 bound of the oracle's fp64 scores on the decoded keys, and
+    bit-identical to the bf16 entry point's scores on keys code value * scale (both the one-query
+    score kernel and the many-queries kernel)."""
+    U, T, N = case["U"], case["T"], case["N"]
+    x, d = _fp8_inputs(U, T, N, seed=4, heavy=case.get("heavy", 0.0))
+    nv = _indexer_nv(case, U, T, N)
+    nvd = torch.from_numpy(nv).cuda()
+    got_t = ops.indexer_score_fp8(d["iq"], d["iw"], d["k8"], d["sc"], n_vis=nvd)
+    ref_t = ops.indexer_score(d["iq"], d["iw"], _fp8_as_bf16(d["k8"], d["sc"]), n_vis=nvd)
+    assert torch.equal(got_t.view(torch.int32), ref_t.view(torch.int32))
+    got = got_t.cpu().numpy()
+    dec = d["k8"].view(torch.float8_e4m3fn).to(torch.float64).cpu().numpy() * x["idx_k_scale"][..., None]
+    for u in range(U):
+        kabs = np.abs(dec[u])
+        for t in range(T):
+            v = int(nv[u, t])
+            ref = orc.indexer_score_fp8(x["idx_q"][u, t], x["idx_w"][u, t], x["idx_k8"][u], x["idx_k_scale"][u],
+                                        n_vis=v)
+            assert np.all(np.isneginf(got[u, t, v:]))
+            bound = (x["idx_w"][u, t].astype(np.float64)[:, None] *
+                     (np.abs(bf16_f64(x["idx_q"][u, t])) @ kabs.T)).sum(0)[:v]
+            err = np.abs(got[u, t, :v].astype(np.float64) - ref[:v])
+            assert np.all(err <= 2e-6 * bound + 1e-30), (u, t, float((err / np.maximum(bound, 1e-30)).max()))
+
+
+FP8_TOPK_CASES = [
+    dict(U=3, T=1, N=8193, K=512, nv=[[8193], [0], [300]], ept=None),        # scores through the workspace
+    dict(U=2, T=16, N=3000, K=512, nv="edges", ept=None),                    # many queries per unit
+    dict(U=100, T=3, N=2048, K=512, nv="edges", ept=4),
+    dict(U=200, T=1, N=8197, K=512, nv="edges", ept=12),
+    dict(U=43, T=1, N=65536, K=512, nv=None, heavy=0.01, ept=12),
+    dict(U=8, T=1, N=262144, K=512, nv="edges", ept=16),
+    dict(U=70, T=2, N=3000, K=64, nv="edges", ept=4),
+]
+
+
+@pytest.mark.parametrize("case", FP8_TOPK_CASES, ids=lambda c: f"U{c['U']}T{c['T']}N{c['N']}K{c['K']}")
+def test_indexer_topk_fp8_equals_bf16(case):
+    """ds4a_indexer_topk_fp8 selects exactly the rows ds4a_indexer_topk selects on keys code value *
+    scale, on every route (fused chunk sizes, scores through the workspace, many queries)."""
+    U, T, N, K = case["U"], case["T"], case["N"], case["K"]
+    assert routing.uses_fused(U, T, N, K) == (case["ept"] is not None)
+    if case["ept"] is not None:
+        assert routing.fused_shape(U * T, N, K)[0] == case["ept"]
+    x, d = _fp8_inputs(U, T, N, seed=5, heavy=case.get("heavy", 0.0))
+    del x
+    nvd = torch.from_numpy(_fused_nv(case, routing.fused_shape(U * T, N, K)[1])).cuda()
+    ref = ops.indexer_topk(d["iq"], d["iw"], _fp8_as_bf16(d["k8"], d["sc"]), K, n_vis=nvd)
+    got = torch.full_like(ref, -7)
+    ops.indexer_topk_fp8(d["iq"], d["iw"], d["k8"], d["sc"], K, n_vis=nvd, out=got)
+    assert torch.equal(got, ref)
+
+
+def test_indexer_topk_fp8_matches_oracle_sets():
+    """Decode shape through the fused kernel against the oracle's FP8 scores and top-k: equal
+    sets apart from rows within 1e-5 of the K-th score."""
+    U, T, N, K = 8, 1, 40000, 512
+    assert routing.uses_fused(U, T, N, K)
+    x, d = _fp8_inputs(U, T, N, seed=6, heavy=0.01)
+    got = ops.indexer_topk_fp8(d["iq"], d["iw"], d["k8"], d["sc"], K).cpu().numpy()
+    for u in range(U):
+        s = orc.indexer_score_fp8(x["idx_q"][u, 0], x["idx_w"][u, 0], x["idx_k8"][u], x["idx_k_scale"][u])
+        ok, nd = tie_band_ok(got[u, 0], orc.topk(s, K), s)
+        assert ok, (u, nd)
+
+
 # -------------------------------------------------------------- attention
 
 def _mqa_case(H, q_dtype, W, N, K, seed, U=2, T=2):
