@@ -513,3 +513,53 @@ void ds4o_indexer_score_fp8(int64_t N, int Hi, int Di, const uint16_t *qI, const
     }
     free(key);
 }
+
+int ds4o_compress_row_e4m3(int width, int ratio, const float *state_kv, const float *state_score,
+                           const float *gain, double eps, int n_rot, int64_t pos, double theta,
+                           uint8_t *codes, double *scale)
+{
+    double *y = malloc(sizeof(double) * (size_t)width);
+    uint16_t *tmp = malloc(sizeof(uint16_t) * (size_t)width);
+    double s = 1.0;
+    int rc = (y && tmp) ? ds4o_compress_row(width, ratio, state_kv, state_score, gain, eps, n_rot, pos,
+                                            theta, 1, y, &s, tmp)
+                        : -1;
+    if (rc == 0) {
+        for (int j = 0; j < width; j++)
+            codes[j] = ds4o_round_e4m3(y[j] / s);
+        if (scale)
+            *scale = s;
+    }
+    free(y);
+    free(tmp);
+    return rc;
+}
+
+/* ---------------------------------------------------------- cache upkeep */
+
+void ds4o_push_raw(int cap, int D, int T, const float *kv, uint16_t *raw, int32_t *n_raw)
+{
+    for (int t = 0; t < T; t++) {
+        const float *row = kv + (int64_t)t * D;
+        uint16_t *dst;
+        if (*n_raw < cap) {
+            dst = raw + (int64_t)(*n_raw) * D;
+            (*n_raw)++;
+        } else {
+            memmove(raw, raw + D, sizeof(uint16_t) * (size_t)(cap - 1) * (size_t)D);
+            dst = raw + (int64_t)(cap - 1) * D;
+        }
+        for (int d = 0; d < D; d++)
+            dst[d] = ds4o_round_f16(row[d]);
+    }
+}
+
+void ds4o_frontier_push(int width, int ratio, int64_t pos, const float *kv, const float *score,
+                        const float *ape, float *state_kv, float *state_score)
+{
+    const int64_t row = pos % ratio;
+    for (int j = 0; j < width; j++) {
+        state_kv[row * width + j] = kv[j];
+        state_score[row * width + j] = score[j] + ape[row * width + j];   /* f32 add */
+    }
+}

@@ -121,6 +121,27 @@ int ds4o_compress_row(int width, int ratio, const float *state_kv, const float *
                       const float *gain, double eps, int n_rot, int64_t pos, double theta, int fp8,
                       double *y_pre, double *scale, uint16_t *out_bf16);
 
+/* The E4M3FN codes of the row ds4o_compress_row emits with fp8 = 1 (the same steps; codes
+ * = round_e4m3(y[j] / scale), the form in which the row can be stored with its scale).
+ * codes: uint8 [width]; scale as above.  Returns 0, or -1 on bad sizes. */
+int ds4o_compress_row_e4m3(int width, int ratio, const float *state_kv, const float *state_score,
+                           const float *gain, double eps, int n_rot, int64_t pos, double theta,
+                           uint8_t *codes, double *scale);
+
+/* Raw sliding-window push ("Reading the architecture of DwarfStar (ds4.c), part 1/8",
+ * section 3-1): the T rows kv f32 [T][D] enter a window of cap rows (f16 bit patterns
+ * [cap][D] holding *n_raw rows) one after another.  While the window has room a row is
+ * stored at row *n_raw, every value rounded to f16, and *n_raw grows; once it is full, the
+ * rows slide down by one (row 0 leaves) and the new row is stored at row cap - 1. */
+void ds4o_push_raw(int cap, int D, int T, const float *kv, uint16_t *raw, int32_t *n_raw);
+
+/* One token entering the compressor's frontier (the same page, section 3-2, steps 2 and
+ * 3): its score row plus the positional bias ape[pos % ratio][*] (f32 adds), and its KV row,
+ * are written to frontier row pos % ratio.  kv, score: f32 [width]; ape: f32
+ * [ratio][width]; state_kv, state_score: f32 [ratio][width]. */
+void ds4o_frontier_push(int width, int ratio, int64_t pos, const float *kv, const float *score,
+                        const float *ape, float *state_kv, float *state_score);
+
 #ifdef __cplusplus
 }
 #endif

@@ -61,6 +61,12 @@ def lib() -> ctypes.CDLL:
         L.ds4o_indexer_score_fp8.restype = None
         L.ds4o_compress_row.argtypes = [i32, i32, P, P, P, dbl, i32, i64, dbl, i32, P, P, P]
         L.ds4o_compress_row.restype = i32
+        L.ds4o_compress_row_e4m3.argtypes = [i32, i32, P, P, P, dbl, i32, i64, dbl, P, P]
+        L.ds4o_compress_row_e4m3.restype = i32
+        L.ds4o_push_raw.argtypes = [i32, i32, i32, P, P, P]
+        L.ds4o_push_raw.restype = None
+        L.ds4o_frontier_push.argtypes = [i32, i32, i64, P, P, P, P, P]
+        L.ds4o_frontier_push.restype = None
         _lib = L
     return _lib
 
@@ -232,3 +238,45 @@ def compress_row(state_kv, state_score, gain, eps: float = 1e-6, n_rot: int = 64
     if rc != 0:
         raise ValueError(f"ds4o_compress_row rejected its arguments (rc={rc})")
     return out, y, scale.value
+
+
+def compress_row_e4m3(state_kv, state_score, gain, eps: float = 1e-6, n_rot: int = 64, pos: int = 0,
+                      theta: float = 10000.0):
+    """The FP8 row of compress_row as stored: (E4M3FN codes uint8 [width], the row's scale)."""
+    kv = np.ascontiguousarray(state_kv, dtype=np.float32)
+    sc = np.ascontiguousarray(state_score, dtype=np.float32)
+    g = np.ascontiguousarray(gain, dtype=np.float32)
+    ratio, width = kv.shape
+    codes = np.empty(width, dtype=np.uint8)
+    scale = ctypes.c_double(0.0)
+    rc = lib().ds4o_compress_row_e4m3(width, ratio, _p(kv), _p(sc), _p(g), float(eps), int(n_rot), int(pos),
+                                      float(theta), _p(codes), ctypes.byref(scale))
+    if rc != 0:
+        raise ValueError(f"ds4o_compress_row_e4m3 rejected its arguments (rc={rc})")
+    return codes, scale.value
+
+
+def push_raw(raw, n_raw: int, kv):
+    """Raw-window push of one unit: raw f16 bits [cap, D] holding n_raw rows, kv f32 [T, D]
+    -> (new window f16 bits [cap, D], new n_raw).  The inputs are not modified."""
+    w = np.array(raw, dtype=np.uint16, copy=True, order="C")
+    x = np.ascontiguousarray(kv, dtype=np.float32)
+    cap, D = w.shape
+    T = x.shape[0]
+    assert x.shape == (T, D)
+    n = ctypes.c_int32(int(n_raw))
+    lib().ds4o_push_raw(cap, D, T, _p(x), _p(w), ctypes.byref(n))
+    return w, n.value
+
+
+def frontier_push(state_kv, state_score, pos: int, kv, score, ape):
+    """One token into one unit's frontier -> (new state_kv, new state_score), f32 [ratio, width]."""
+    skv = np.array(state_kv, dtype=np.float32, copy=True, order="C")
+    ssc = np.array(state_score, dtype=np.float32, copy=True, order="C")
+    ratio, width = skv.shape
+    k = np.ascontiguousarray(kv, dtype=np.float32)
+    s = np.ascontiguousarray(score, dtype=np.float32)
+    a = np.ascontiguousarray(ape, dtype=np.float32)
+    assert k.shape == (width,) and s.shape == (width,) and a.shape == (ratio, width)
+    lib().ds4o_frontier_push(width, ratio, int(pos), _p(k), _p(s), _p(a), _p(skv), _p(ssc))
+    return skv, ssc

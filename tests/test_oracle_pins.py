@@ -510,3 +510,73 @@ def test_compress_fp8_round_trip_bounds(oracle_mod):
         assert np.array_equal(_e4m3_torch(oracle_mod.round_e4m3(q)), q)     # every value is an E4M3 value
         step = np.where(np.abs(y / s) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(y / s), 1e-300))) - 3))
         assert np.all(np.abs(q - y / s) <= step / 2 + 1e-12)
+
+
+# ------------------------------------------------------------ cache upkeep
+
+def test_compress_row_e4m3_codes_decode_to_the_emitted_row(oracle_mod):
+    """The stored form (codes, scale) decodes, through torch's E4M3 type, to exactly the bf16 row
+    the compressor emits with its FP8 round trip."""
+    rng = np.random.default_rng(26)
+    for width, ratio, n_rot in ((512, 4, 64), (128, 4, 64), (512, 128, 64), (40, 3, 0)):
+        kv, sc = _frontier(rng, ratio, width, spread=2.0)
+        gain = rng.uniform(0.5, 1.5, width).astype(np.float32)
+        out, _, s = oracle_mod.compress_row(kv, sc, gain, n_rot=n_rot, pos=1234, fp8=True)
+        codes, s2 = oracle_mod.compress_row_e4m3(kv, sc, gain, n_rot=n_rot, pos=1234)
+        assert s2 == s and math.log2(s) == round(math.log2(s))
+        assert not np.any((codes & 0x7F) == 0x7F)
+        assert np.array_equal(_e4m3_torch(codes) * s, bf16_f64(out))
+
+
+def _window_model(rows, cap, new_rows):
+    """The window as a list of rows: append each new row (f16-rounded by numpy), keep the last cap."""
+    out = [r for r in rows]
+    for r in new_rows:
+        with np.errstate(over="ignore"):                                 # f16 overflow -> inf, as intended
+            out.append(np.asarray(r, np.float32).astype(np.float16).view(np.uint16))
+        out = out[-cap:]
+    return out
+
+
+@pytest.mark.parametrize("cap,n0,T", [(4, 0, 3), (4, 2, 3), (4, 4, 1), (4, 1, 9), (8, 8, 8), (128, 127, 2),
+                                      (128, 0, 128), (128, 128, 300)])
+def test_push_raw_matches_window_model(oracle_mod, cap, n0, T):
+    rng = np.random.default_rng(cap * 1000 + n0 * 10 + T)
+    D = 16
+    raw = np.zeros((cap, D), np.uint16)
+    raw[:n0] = rng.integers(0, 0x7C00, (n0, D), dtype=np.uint16)       # finite f16 patterns
+    raw[n0:] = 0xBEEF                                                   # rows past n_raw: never read
+    kv = (rng.standard_normal((T, D)) * 10.0 ** rng.integers(-9, 6, (T, D))).astype(np.float32)
+    kv[0, :3] = [70000.0, -1e-8, 6.1e-5]                                # overflow, underflow, subnormal
+    got, n = oracle_mod.push_raw(raw, n0, kv)
+    ref = _window_model(list(raw[:n0]), cap, kv)
+    assert n == len(ref) == min(cap, n0 + T)
+    assert np.array_equal(got[:n], np.stack(ref))
+    assert np.all(got[n:] == 0xBEEF)
+    # T rows at once == one row at a time
+    w, m = raw, n0
+    for t in range(T):
+        w, m = oracle_mod.push_raw(w, m, kv[t:t + 1])
+    assert m == n and np.array_equal(w, got)
+
+
+def test_frontier_push_rows_and_bias(oracle_mod):
+    """Tokens at positions p0 .. p0+ratio-1 (p0 a multiple of ratio) fill rows 0 .. ratio-1 in
+    order; each push touches only its row; scores carry the bias row of their position (an f32
+    add, as numpy does it)."""
+    rng = np.random.default_rng(27)
+    ratio, width = 4, 24
+    ape = rng.standard_normal((ratio, width)).astype(np.float32)
+    skv = np.full((ratio, width), 9.0, np.float32)
+    ssc = np.full((ratio, width), 9.0, np.float32)
+    p0 = 4 * 1001
+    toks = [(rng.standard_normal(width).astype(np.float32), rng.standard_normal(width).astype(np.float32))
+            for _ in range(ratio)]
+    for i, (k, s) in enumerate(toks):
+        prev_kv, prev_sc = skv, ssc
+        skv, ssc = oracle_mod.frontier_push(skv, ssc, p0 + i, k, s, ape)
+        others = [r for r in range(ratio) if r != i]
+        assert np.array_equal(skv[others], prev_kv[others]) and np.array_equal(ssc[others], prev_sc[others])
+    for i, (k, s) in enumerate(toks):
+        assert np.array_equal(skv[i], k)
+        assert np.array_equal(ssc[i], s + ape[i])
