@@ -432,9 +432,121 @@ def compressor(steps: int):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
+    gus = graph_us(torch, lambda: [c() for c in calls], steps)
     return {"workload": "compressor_emit_41layers (21 x ratio-4 KV + index key, 20 x ratio-128 KV)",
-            "us_per_token": us, "launches": len(calls), "algorithmic_bytes": by,
-            "GB_per_s": by / (us / 1e6) / 1e9}
+            "us_per_token": us, "graph_us_per_token": gus, "launches": len(calls), "algorithmic_bytes": by,
+            "GB_per_s": by / (gus / 1e6) / 1e9}
+
+
+def graph_us(torch, fn, replays: int) -> float:
+    """Average GPU time of fn's launches, captured once as a HIP graph and replayed back to back
+    (no host launch overhead; fn must be safe to repeat)."""
+    fn()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    with torch.cuda.graph(g, stream=side):
+        fn()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        g.replay()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    cur = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    e0.record(cur)
+    for _ in range(replays):
+        g.replay()
+    e1.record(cur)
+    torch.cuda.synchronize()
+    del g
+    return e0.elapsed_time(e1) * 1e3 / replays
+
+
+def cache_upkeep(steps: int):
+    """Cache upkeep after one decode token of a whole Flash model (43 layers), device-side
+    counters throughout: the raw-window push of every layer (full 128-row windows, so each
+    push slides), the frontier push of the 41 compressing layers' compressors (21 ratio-4 KV,
+    21 indexer keys, 20 ratio-128 KV), and their append at a token that closes both a
+    ratio-4 and a ratio-128 group (index keys stored as E4M3 codes + scale, KV rows as bf16
+    after the FP8 round trip).  Inputs are synthetic."""
+    import torch
+
+    from sparse_compressed_kv_amd import ops
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    L, cap, D = 43, 128, 512
+    raw = (torch.randn(L, cap, D, device="cuda", generator=g)).to(torch.float16)
+    n_raw = torch.full((L,), cap, dtype=torch.int32, device="cuda")
+    kv_tok = torch.randn(L, 1, D, device="cuda", generator=g)
+    pos_val = 262143
+    groups = [("ratio4_kv", 21, 4, 512, 65536, False), ("ratio4_index_keys", 21, 4, 128, 65536, True),
+              ("ratio128_kv", 20, 128, 512, 2048, False)]
+    fronts, appends = [], []
+    by_front = by_app = 0
+    for name, U, ratio, width, rows, e4m3 in groups:
+        skv = torch.randn(U, ratio, width, device="cuda", generator=g)
+        ssc = torch.randn(U, ratio, width, device="cuda", generator=g) * 2
+        gain = torch.rand(U, width, device="cuda", generator=g) + 0.5
+        ape = torch.randn(ratio, width, device="cuda", generator=g)
+        kv = torch.randn(U, width, device="cuda", generator=g)
+        sc = torch.randn(U, width, device="cuda", generator=g)
+        pos = torch.full((U,), pos_val, dtype=torch.int64, device="cuda")
+        row_pos = pos // ratio
+        if e4m3:
+            comp = torch.zeros(U, rows, width, dtype=torch.uint8, device="cuda")
+            cs = torch.zeros(U, rows, dtype=torch.float32, device="cuda")
+        else:
+            comp = torch.zeros(U, rows, width, dtype=torch.bfloat16, device="cuda")
+            cs = None
+        # every timed call appends one row; the caches have room for all of them
+        n_comp = torch.zeros((U,), dtype=torch.int32, device="cuda")
+        fronts.append(lambda kv=kv, sc=sc, ape=ape, pos=pos, skv=skv, ssc=ssc: ops.frontier_push(
+            kv, sc, ape, pos, skv, ssc))
+        appends.append(lambda skv=skv, ssc=ssc, gain=gain, pos=pos, row_pos=row_pos, comp=comp, n=n_comp, cs=cs:
+                       ops.compress_append(skv, ssc, gain, pos, row_pos, comp, n, comp_scale=cs))
+        by_front += U * (2 * width * 4 + width * 4 + 2 * width * 4)
+        by_app += U * (2 * ratio * width * 4 + width * 4 + width * (1 if e4m3 else 2) + 16)
+
+    def push():                                    # the window stays full: every push slides
+        ops.push_raw(kv_tok, raw, n_raw)
+
+    def timed(fn, n):
+        for _ in range(5):
+            fn()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / n
+
+    def whole():
+        push()
+        for f in fronts:
+            f()
+        for a in appends:
+            a()
+
+    steps = min(steps, 300)                        # 3 x (steps + 10) appends fit the 2,048-row caches
+    by_push = L * ((cap - 1) * D * 2 * 2 + D * 4 + D * 2)
+    eager_us = timed(whole, steps)
+    # GPU time of each part and of the whole upkeep, as HIP graphs (the eager calls are bound
+    # by host launch overhead: seven short kernels)
+    push_us = graph_us(torch, push, steps)
+    front_us = graph_us(torch, lambda: [f() for f in fronts], steps)
+    append_us = graph_us(torch, lambda: [a() for a in appends], steps)
+    whole_us = graph_us(torch, whole, steps)
+    return {"workload": "cache_upkeep_43layers (raw push x 43, frontier push + append x 62)",
+            "us_per_token": whole_us, "timing": "HIP graph of the 7 launches, replayed back to back",
+            "eager_us_per_token": eager_us, "launches": 1 + 2 * len(groups),
+            "parts_us": {"push_raw": push_us, "frontier_push": front_us, "append": append_us},
+            "push_raw_bytes": by_push, "push_raw_GB_per_s": by_push / (push_us / 1e6) / 1e9,
+            "frontier_push_bytes": by_front, "append_bytes": by_app}
 
 
 def traffic_for(kernel_hash: str, units: int):
@@ -582,6 +694,10 @@ def main():
         cm = compressor(args.steps)
         log(f"[bench] {cm['workload']}: {cm}")
         rec["compressor_emit"] = cm
+        # ---- cache upkeep after a token: raw-window push, frontier push, compressed-row append
+        cu = cache_upkeep(args.steps)
+        log(f"[bench] {cu['workload']}: {cu}")
+        rec["cache_upkeep"] = cu
         # ---- chunked prefill: 2,048 queries, 8,192 rows
         w3 = gen.CONFIGS["c3"]
         x3 = gen.make_config(w3)

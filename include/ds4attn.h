@@ -218,6 +218,59 @@ int ds4a_compress_rows(int U, int width, int ratio, const float *state_kv, const
                        const float *gain, float eps, int n_rot, const int64_t *row_pos, double rope_theta,
                        int fp8, void *out, int64_t out_stride, void *stream);
 
+/* Formats of an emitted compressed row (ds4a_compress_append). */
+#define DS4A_ROW_BF16 0        /* bf16 values, no FP8 step                                 */
+#define DS4A_ROW_BF16_FP8RT 1  /* bf16 values after the FP8 round trip (as compress_rows fp8=1) */
+#define DS4A_ROW_E4M3 2        /* the FP8 row as stored: E4M3FN codes plus the row's f32 scale */
+
+/* Compressed-row append, the compressor's last step for one decode token per unit (section
+ * 3-2: at the ratio boundary one row is emitted into the unit's compressed cache).  Unit u
+ * emits only when its token closes a group, pos[u] mod ratio == ratio - 1 (the frontier then
+ * holds the group's `ratio` tokens); the row is that of ds4a_compress_rows (same device code)
+ * and goes to row n_comp[u] of the unit's cache, after which n_comp[u] is incremented.  A
+ * row past cap is not written but still counted, so n_comp[u] > cap after the call tells
+ * the caller the cache was full.  Other units are left untouched.
+ *   pos      : int64 [U] the token's position            row_pos : int64 [U] (RoPE position)
+ *   format   : DS4A_ROW_BF16, DS4A_ROW_BF16_FP8RT, DS4A_ROW_E4M3
+ *   comp     : bf16 [U][cap][width] (formats 0, 1) or uint8 [U][cap][width] codes (format 2)
+ *   comp_scale : f32 [U][cap] (format 2 only; the row's power-of-two scale, decoded value =
+ *              code value * scale)
+ *   n_comp   : int32 [U] device counters, read and written by the call
+ * Other arguments as for ds4a_compress_rows.  U * cap * width <= 2^40.
+ */
+int ds4a_compress_append(int U, int width, int ratio, const float *state_kv, const float *state_score,
+                         const float *gain, float eps, int n_rot, const int64_t *pos, const int64_t *row_pos,
+                         double rope_theta, int format, void *comp, float *comp_scale, int64_t cap,
+                         int32_t *n_comp, void *stream);
+
+/* Raw sliding-window push (section 3-1: the last n_swa = 128 tokens keep their KV rows, each
+ * value rounded to f16 when it enters; a full window slides down by one row per token).  For
+ * each unit u, the T rows kv[u][0..T-1] enter the window raw[u] in order, exactly as T single
+ * pushes: while the window holds fewer than cap rows the row is stored at row n_raw[u] and
+ * n_raw[u] grows; once full, the rows move down by one (row 0 leaves) and the new row is
+ * stored at row cap - 1.  Rows at or past n_raw[u] are never read.  n_raw values outside
+ * [0, cap] are clamped.
+ *   kv       : f32 [U][T][D]                 raw : f16 [U][cap][D] (read and written)
+ *   n_raw    : int32 [U] device counters      D  : a multiple of 8, 8..4096
+ *   cap      : 1..DS4A_MAX_WINDOW (128 in Flash and Pro)
+ * The window a decode query attends (raw_kv of ds4a_sparse_mqa with T = 1, W = cap) is raw[u]
+ * once it is full.
+ */
+int ds4a_push_raw(int U, int T, int D, int cap, const float *kv, void *raw, int32_t *n_raw, void *stream);
+
+/* A token entering the compressor's frontier (section 3-2: the score row gets the positional
+ * bias of the token's place in its group, and both rows are written to the frontier): for
+ * each unit u, with r = pos[u] mod ratio (taken in [0, ratio)),
+ *   state_kv[u][r][j]    = kv[u][j]
+ *   state_score[u][r][j] = score[u][j] + ape[r][j]     (f32 add)
+ *   kv, score : f32 [U][width]      ape : f32 [ratio][width]      pos : int64 [U]
+ *   state_kv, state_score : f32 [U][ratio][width]   width: a multiple of 4 up to
+ *   DS4A_MAX_COMPRESS_WIDTH; ratio: 1..DS4A_MAX_COMPRESS_RATIO
+ * Reading: the bias row is the one of the token's place pos mod ratio, the row it is written to.
+ */
+int ds4a_frontier_push(int U, int width, int ratio, const float *kv, const float *score, const float *ape,
+                       const int64_t *pos, float *state_kv, float *state_score, void *stream);
+
 /* A3 alone, for inspection: writes the rotated query as f32 [U][T][H][D], using
  * the same device code as ds4a_sparse_mqa's prologue (fp64 angle and rotation,
  * rounded once to f32).  Same argument rules as ds4a_sparse_mqa. */

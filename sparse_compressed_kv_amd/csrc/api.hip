@@ -290,9 +290,74 @@ int ds4a_compress_rows(int U, int width, int ratio, const float *state_kv, const
     REQUIRE_PTR(gain);
     REQUIRE_PTR(row_pos);
     REQUIRE_PTR(out);
+    const ds4a::RowDest dst = {fp8 ? DS4A_ROW_BF16_FP8RT : DS4A_ROW_BF16, out, nullptr, out_stride, 1, nullptr,
+                               nullptr};
     return hip_status(fn, ds4a::launch_compress(U, width, ratio, state_kv, state_score, gain, eps, n_rot, row_pos,
-                                                rope_theta, fp8, static_cast<uint16_t *>(out), out_stride,
+                                                rope_theta, dst, static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_compress_append(int U, int width, int ratio, const float *state_kv, const float *state_score,
+                         const float *gain, float eps, int n_rot, const int64_t *pos, const int64_t *row_pos,
+                         double rope_theta, int format, void *comp, float *comp_scale, int64_t cap, int32_t *n_comp,
+                         void *stream) {
+    const char *fn = "ds4a_compress_append";
+    if (U < 1 || U > (1 << 24)) return fail(DS4A_E_SHAPE, "%s: U=%d must be in [1, 2^24]", fn, U);
+    if (width < 4 || width % 4 || ratio < 1 || n_rot < 0 || n_rot % 2 || n_rot > width)
+        return fail(DS4A_E_SHAPE, "%s: width=%d ratio=%d n_rot=%d out of range", fn, width, ratio, n_rot);
+    if (width > DS4A_MAX_COMPRESS_WIDTH || ratio > DS4A_MAX_COMPRESS_RATIO || n_rot > 512)
+        return fail(DS4A_E_UNSUPPORTED, "%s: width=%d ratio=%d n_rot=%d (width <= %d, ratio <= %d, n_rot <= 512)",
+                    fn, width, ratio, n_rot, DS4A_MAX_COMPRESS_WIDTH, DS4A_MAX_COMPRESS_RATIO);
+    if (!(eps >= 0.f) || eps == INFINITY) return fail(DS4A_E_SHAPE, "%s: eps must be finite and >= 0", fn);
+    if (!(rope_theta > 0.0) || rope_theta != rope_theta) return fail(DS4A_E_SHAPE, "%s: rope_theta must be > 0", fn);
+    if (format != DS4A_ROW_BF16 && format != DS4A_ROW_BF16_FP8RT && format != DS4A_ROW_E4M3)
+        return fail(DS4A_E_DTYPE, "%s: format=%d (DS4A_ROW_BF16, DS4A_ROW_BF16_FP8RT or DS4A_ROW_E4M3)", fn, format);
+    if (cap < 1 || cap > kMaxRows || cap * (int64_t)width > kMaxElems / U)
+        return fail(DS4A_E_SHAPE, "%s: cap=%lld out of range (U * cap * width <= 2^40)", fn, (long long)cap);
+    REQUIRE_PTR(state_kv);
+    REQUIRE_PTR(state_score);
+    REQUIRE_PTR(gain);
+    REQUIRE_PTR(pos);
+    REQUIRE_PTR(row_pos);
+    REQUIRE_PTR(comp);
+    if (format == DS4A_ROW_E4M3) REQUIRE_PTR(comp_scale);
+    REQUIRE_PTR(n_comp);
+    const ds4a::RowDest dst = {format, comp, format == DS4A_ROW_E4M3 ? comp_scale : nullptr, cap * width, cap, pos,
+                               n_comp};
+    return hip_status(fn, ds4a::launch_compress(U, width, ratio, state_kv, state_score, gain, eps, n_rot, row_pos,
+                                                rope_theta, dst, static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_push_raw(int U, int T, int D, int cap, const float *kv, void *raw, int32_t *n_raw, void *stream) {
+    const char *fn = "ds4a_push_raw";
+    if (U < 1 || U > (1 << 24) || T < 1 || T > (1 << 24))
+        return fail(DS4A_E_SHAPE, "%s: U=%d T=%d must be in [1, 2^24]", fn, U, T);
+    if (D < 8 || D % 8 || cap < 1) return fail(DS4A_E_SHAPE, "%s: D=%d cap=%d out of range", fn, D, cap);
+    if (D > 4096 || cap > DS4A_MAX_WINDOW)
+        return fail(DS4A_E_UNSUPPORTED, "%s: D=%d cap=%d (D <= 4096, cap <= %d)", fn, D, cap, DS4A_MAX_WINDOW);
+    if ((int64_t)U * T * D > kMaxElems) return fail(DS4A_E_SHAPE, "%s: U*T*D too large", fn);
+    REQUIRE_PTR(kv);
+    REQUIRE_PTR(raw);
+    REQUIRE_PTR(n_raw);
+    return hip_status(fn, ds4a::launch_push_raw(U, T, D, cap, kv, static_cast<uint16_t *>(raw), n_raw,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+int ds4a_frontier_push(int U, int width, int ratio, const float *kv, const float *score, const float *ape,
+                       const int64_t *pos, float *state_kv, float *state_score, void *stream) {
+    const char *fn = "ds4a_frontier_push";
+    if (U < 1 || U > (1 << 24)) return fail(DS4A_E_SHAPE, "%s: U=%d must be in [1, 2^24]", fn, U);
+    if (width < 4 || width % 4 || ratio < 1) return fail(DS4A_E_SHAPE, "%s: width=%d ratio=%d out of range", fn, width, ratio);
+    if (width > DS4A_MAX_COMPRESS_WIDTH || ratio > DS4A_MAX_COMPRESS_RATIO)
+        return fail(DS4A_E_UNSUPPORTED, "%s: width=%d ratio=%d (width <= %d, ratio <= %d)", fn, width, ratio,
+                    DS4A_MAX_COMPRESS_WIDTH, DS4A_MAX_COMPRESS_RATIO);
+    REQUIRE_PTR(kv);
+    REQUIRE_PTR(score);
+    REQUIRE_PTR(ape);
+    REQUIRE_PTR(pos);
+    REQUIRE_PTR(state_kv);
+    REQUIRE_PTR(state_score);
+    return hip_status(fn, ds4a::launch_frontier_push(U, width, ratio, kv, score, ape, pos, state_kv, state_score,
+                                                     static_cast<hipStream_t>(stream)));
 }
 
 int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtype, const int64_t *q_pos,

@@ -71,6 +71,17 @@ __device__ __forceinline__ float e4m3_scale(float amax) {
     return ldexpf(1.f, f <= 0.875f ? e - 9 : e - 8);
 }
 
+// OCP E4M3FN code of an E4M3FN value r (|r| <= 448): sign, then the biased exponent and the
+// top 3 fraction bits of r's f32 pattern, or for |r| < 2^-6 the subnormal count |r| / 2^-9.
+__device__ __forceinline__ uint32_t e4m3_code(float r) {
+    const uint32_t b = __float_as_uint(r);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const float a = fabsf(r);
+    const uint32_t mag = a < 0.015625f ? (uint32_t)(a * 512.f)
+                                       : ((((b >> 23) & 0xffu) - 120u) << 3) | ((b >> 20) & 7u);
+    return sign | mag;
+}
+
 // Online softmax-weighted sum: fold (score s, value v) into (reference m, sum of weights den,
 // weighted sum num), weights relative to m.
 __device__ __forceinline__ void fold(float s, float v, float &m, float &den, float &num) {
@@ -84,16 +95,24 @@ __device__ __forceinline__ void fold(float s, float v, float &m, float &den, flo
 // One workgroup per unit.  Pooling: thread t takes 4 consecutive channels (column t % ncol,
 // one 16-byte load per frontier row and array) and every G-th frontier row from row t / ncol,
 // kCUnroll rows' loads in flight; the G partial (reference, weight sum, weighted sum) of a
-// channel are merged through LDS.
+// channel are merged through LDS.  `dst` says where the row goes (see RowDest in launch.hpp):
+// appends emit only for units whose token closes a group and write row n_rows[u] of the
+// unit's cache (when it is below cap), then count it.
 __global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
     int width, int ratio, const float *__restrict__ state_kv, const float *__restrict__ state_score,
     const float *__restrict__ gain, float eps, int n_rot, const int64_t *__restrict__ row_pos, double log2_theta,
-    int fp8, uint16_t *__restrict__ out, int64_t out_stride)
+    RowDest dst)
 {
     __shared__ float s_y[kCMaxWidth];
     __shared__ f32x4 s_part[3][kCThreads];                       // (m, den, num) per thread, 4 channels each
     __shared__ float s_red[kCThreads / kWave];
     const int64_t u = blockIdx.x;
+    if (dst.emit_pos) {                                          // uniform across the workgroup
+        int64_t ph = dst.emit_pos[u] % ratio;
+        if (ph < 0) ph += ratio;
+        if (ph != ratio - 1) return;
+    }
+    const int32_t row = dst.n_rows ? dst.n_rows[u] : 0;
     const int ncol = width / 4;
     const int G = min(kCThreads / ncol, ratio);                  // row groups
     const int col = threadIdx.x % ncol, grp = threadIdx.x / ncol;
@@ -153,6 +172,7 @@ __global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
     }
     __syncthreads();
 
+    const bool fp8 = dst.format != DS4A_ROW_BF16;
     float s = 1.f;
     if (fp8) {
         float amax = 0.f;
@@ -160,21 +180,34 @@ __global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
         amax = block_max(amax, s_red);
         if (amax > 0.f) s = e4m3_scale(amax);
     }
-    uint16_t *o = out + u * out_stride;
-    for (int j = threadIdx.x; j < width; j += kCThreads) {
-        const float y = fp8 ? round_e4m3(s_y[j] / s) * s : s_y[j];   // s a power of two: exact
-        o[j] = (uint16_t)f32_to_bf16_bits(y);
+    if (row >= 0 && row < dst.cap) {                             // uniform
+        const int64_t e0 = u * dst.unit_stride + (int64_t)row * width;
+        if (dst.format == DS4A_ROW_E4M3) {
+            uint8_t *o = static_cast<uint8_t *>(dst.out) + e0;
+            for (int j = threadIdx.x; j < width; j += kCThreads) o[j] = (uint8_t)e4m3_code(round_e4m3(s_y[j] / s));
+            if (threadIdx.x == 0) dst.scale[u * dst.cap + row] = s;
+        } else {
+            uint16_t *o = static_cast<uint16_t *>(dst.out) + e0;
+            for (int j = threadIdx.x; j < width; j += kCThreads) {
+                const float y = fp8 ? round_e4m3(s_y[j] / s) * s : s_y[j];   // s a power of two: exact
+                o[j] = (uint16_t)f32_to_bf16_bits(y);
+            }
+        }
+    }
+    if (dst.n_rows) {
+        __syncthreads();                                         // every thread has read n_rows[u]
+        if (threadIdx.x == 0) dst.n_rows[u] = row + 1;
     }
 }
 
 }  // namespace
 
 hipError_t launch_compress(int U, int width, int ratio, const float *state_kv, const float *state_score,
-                           const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta, int fp8,
-                           uint16_t *out, int64_t out_stride, hipStream_t stream)
+                           const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta,
+                           const RowDest &dst, hipStream_t stream)
 {
     hipLaunchKernelGGL(compress_rows_kernel, dim3((unsigned)U), dim3(kCThreads), 0, stream, width, ratio, state_kv,
-                       state_score, gain, eps, n_rot, row_pos, log2(theta), fp8, out, out_stride);
+                       state_score, gain, eps, n_rot, row_pos, log2(theta), dst);
     return hipGetLastError();
 }
 

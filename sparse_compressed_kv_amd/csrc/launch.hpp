@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "ds4attn.h"
+
 namespace ds4a {
 
 // Units with at least this many queries take the many-queries (prefill) indexer.
@@ -54,9 +56,30 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
                       const int64_t *q_pos, double theta, const uint16_t *raw, const uint16_t *comp,
                       const int32_t *idx, const int32_t *n_vis, float scale, float *out, void *workspace,
                       hipStream_t stream);
+// Where an emitted compressed row goes.  format (DS4A_ROW_* in the public header): bf16
+// values, bf16 values after the FP8 round trip, or E4M3 codes (uint8) plus the row's scale.
+// The row of unit u is row n_rows[u] (0 if n_rows is null) of a cache whose units are
+// unit_stride elements apart and hold cap rows of `width` elements; scales (E4M3) at
+// scale[u * cap + row].  With emit_pos, only units with emit_pos[u] mod ratio == ratio - 1
+// emit, and n_rows counts the rows emitted (also past cap, where nothing is written).
+struct RowDest {
+    int format;
+    void *out;
+    float *scale;
+    int64_t unit_stride;
+    int64_t cap;
+    const int64_t *emit_pos;
+    int32_t *n_rows;
+};
 hipError_t launch_compress(int U, int width, int ratio, const float *state_kv, const float *state_score,
-                           const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta, int fp8,
-                           uint16_t *out, int64_t out_stride, hipStream_t stream);
+                           const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta,
+                           const RowDest &dst, hipStream_t stream);
+// Cache upkeep: raw-window push (kv f32 [U][T][D] into f16 [U][cap][D], counts n_raw [U]) and
+// the compressor frontier push (row pos mod ratio of f32 [U][ratio][width]).
+hipError_t launch_push_raw(int U, int T, int D, int cap, const float *kv, uint16_t *raw, int32_t *n_raw,
+                           hipStream_t stream);
+hipError_t launch_frontier_push(int U, int width, int ratio, const float *kv, const float *score, const float *ape,
+                                const int64_t *pos, float *state_kv, float *state_score, hipStream_t stream);
 hipError_t launch_rope(int U, int T, int H, const void *q, int q_bf16, const int64_t *q_pos,
                        double theta, float *q_out, hipStream_t stream);
 

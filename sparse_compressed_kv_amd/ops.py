@@ -65,6 +65,12 @@ def lib() -> ctypes.CDLL:
     L.ds4a_dense_mqa.restype = i32
     L.ds4a_compress_rows.argtypes = [i32, i32, i32, P, P, P, flt, i32, P, dbl, i32, P, i64, P]
     L.ds4a_compress_rows.restype = i32
+    L.ds4a_compress_append.argtypes = [i32, i32, i32, P, P, P, flt, i32, P, P, dbl, i32, P, P, i64, P, P]
+    L.ds4a_compress_append.restype = i32
+    L.ds4a_push_raw.argtypes = [i32, i32, i32, i32, P, P, P, P]
+    L.ds4a_push_raw.restype = i32
+    L.ds4a_frontier_push.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
+    L.ds4a_frontier_push.restype = i32
     L.ds4a_rope_q.argtypes = [i32, i32, i32, i32, i32, P, i32, P, dbl, P, P]
     L.ds4a_rope_q.restype = i32
     _lib = L
@@ -307,6 +313,66 @@ def compress_rows(state_kv, state_score, gain, row_pos, eps: float = 1e-6, n_rot
         U, width, ratio, _ptr(state_kv), _ptr(state_score), _ptr(gain), float(eps), int(n_rot), _ptr(row_pos),
         float(theta), 1 if fp8 else 0, _ptr(out), stride, _stream(stream)))
     return out
+
+
+ROW_BF16, ROW_BF16_FP8RT, ROW_E4M3 = 0, 1, 2
+
+
+def compress_append(state_kv, state_score, gain, pos, row_pos, comp, n_comp, comp_scale=None, eps: float = 1e-6,
+                    n_rot: int = 64, theta: float = 10000.0, fp8: bool = True, stream=None):
+    """Compressed-row append: units whose token closes a group (pos mod ratio == ratio - 1) emit
+    a row into row n_comp[u] of their cache and count it.  comp: bf16 [U, cap, width] (rows
+    with or without the FP8 round trip, by `fp8`), or uint8 / float8_e4m3fn [U, cap, width]
+    codes with comp_scale f32 [U, cap] (the FP8 row as stored)."""
+    U, ratio, width = state_kv.shape
+    _need(state_kv, "state_kv", torch.float32, (U, ratio, width))
+    _need(state_score, "state_score", torch.float32, (U, ratio, width))
+    _need(gain, "gain", torch.float32, (U, width))
+    _need(pos, "pos", torch.int64, (U,))
+    _need(row_pos, "row_pos", torch.int64, (U,))
+    _need(n_comp, "n_comp", torch.int32, (U,))
+    if not isinstance(comp, torch.Tensor) or comp.dim() != 3:
+        raise TypeError("comp must be a 3-d torch.Tensor")
+    cap = comp.shape[1]
+    if comp.dtype == torch.bfloat16:
+        fmt = ROW_BF16_FP8RT if fp8 else ROW_BF16
+        _need(comp, "comp", torch.bfloat16, (U, cap, width))
+        if comp_scale is not None:
+            raise ValueError("comp_scale is for E4M3 caches only")
+    else:
+        if comp.dtype == torch.float8_e4m3fn:
+            comp = comp.view(torch.uint8)
+        fmt = ROW_E4M3
+        _need(comp, "comp", torch.uint8, (U, cap, width))
+        _need(comp_scale, "comp_scale", torch.float32, (U, cap))
+    _check("ds4a_compress_append", lib().ds4a_compress_append(
+        U, width, ratio, _ptr(state_kv), _ptr(state_score), _ptr(gain), float(eps), int(n_rot), _ptr(pos),
+        _ptr(row_pos), float(theta), fmt, _ptr(comp), _ptr(comp_scale), cap, _ptr(n_comp), _stream(stream)))
+
+
+def push_raw(kv, raw, n_raw, stream=None):
+    """Raw-window push: kv f32 [U, T, D] into raw f16 [U, cap, D] holding n_raw int32 [U] rows."""
+    U, T, D = kv.shape
+    cap = raw.shape[1]
+    _need(kv, "kv", torch.float32, (U, T, D))
+    _need(raw, "raw", torch.float16, (U, cap, D))
+    _need(n_raw, "n_raw", torch.int32, (U,))
+    _check("ds4a_push_raw", lib().ds4a_push_raw(U, T, D, cap, _ptr(kv), _ptr(raw), _ptr(n_raw), _stream(stream)))
+
+
+def frontier_push(kv, score, ape, pos, state_kv, state_score, stream=None):
+    """A token into the compressor frontier: row pos mod ratio of state_kv / state_score
+    f32 [U, ratio, width] takes kv [U, width] and score [U, width] + ape[pos mod ratio]."""
+    U, ratio, width = state_kv.shape
+    _need(kv, "kv", torch.float32, (U, width))
+    _need(score, "score", torch.float32, (U, width))
+    _need(ape, "ape", torch.float32, (ratio, width))
+    _need(pos, "pos", torch.int64, (U,))
+    _need(state_kv, "state_kv", torch.float32, (U, ratio, width))
+    _need(state_score, "state_score", torch.float32, (U, ratio, width))
+    _check("ds4a_frontier_push", lib().ds4a_frontier_push(U, width, ratio, _ptr(kv), _ptr(score), _ptr(ape),
+                                                          _ptr(pos), _ptr(state_kv), _ptr(state_score),
+                                                          _stream(stream)))
 
 
 def rope_q(q, q_pos, theta: float = 10000.0, out=None, stream=None):

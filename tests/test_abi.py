@@ -19,7 +19,8 @@ def L():
 def test_exports_every_declared_symbol(L):
     names = ops.declared_symbols()
     assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_dense_mqa",
-            "ds4a_compress_rows", "ds4a_rope_q", "ds4a_indexer_score_fp8", "ds4a_indexer_topk_fp8", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
+            "ds4a_compress_rows", "ds4a_rope_q", "ds4a_indexer_score_fp8", "ds4a_indexer_topk_fp8",
+            "ds4a_compress_append", "ds4a_push_raw", "ds4a_frontier_push", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -99,6 +100,43 @@ def test_indexer_fp8_validation(L):
     # the bf16 entry point still names its own key argument
     assert L.ds4a_indexer_topk(1, 1, 10, 64, 128, 8, A, A, None, None, A, None, 0, S) == -1
     assert "idx_k " in ops.last_error() or ops.last_error().endswith("idx_k is NULL")
+
+
+def test_cache_upkeep_validation(L):
+    p = L.ds4a_push_raw
+    assert p(0, 1, 512, 128, A, A, A, S) == -2
+    assert p(1, 0, 512, 128, A, A, A, S) == -2
+    assert p(1, 1, 500, 128, A, A, A, S) == -2
+    assert p(1, 1, 512, 0, A, A, A, S) == -2
+    assert p(1, 1, 512, 2048, A, A, A, S) == -3
+    assert p(1, 1, 8192, 128, A, A, A, S) == -3
+    assert p(1, 1, 512, 128, None, A, A, S) == -1
+    assert p(1, 1, 512, 128, A, A, None, S) == -1 and "n_raw" in ops.last_error()
+    assert p(1, 1, 512, 128, A, MIS, A, S) == -4
+    f = L.ds4a_frontier_push
+    assert f(1, 6, 4, A, A, A, A, A, A, S) == -2
+    assert f(1, 128, 0, A, A, A, A, A, A, S) == -2
+    assert f(1, 2048, 4, A, A, A, A, A, A, S) == -3
+    assert f(1, 128, 4, A, A, None, A, A, A, S) == -1 and "ape" in ops.last_error()
+    assert f(1, 128, 4, A, A, A, A, A, MIS, S) == -4
+    c = L.ds4a_compress_append
+
+    def ca(**kw):
+        a = dict(U=2, width=128, ratio=4, kv=A, sc=A, gain=A, eps=1e-6, n_rot=64, pos=A, row_pos=A, theta=1e4,
+                 fmt=2, comp=A, scale=A, cap=16, n=A)
+        a.update(kw)
+        return c(a["U"], a["width"], a["ratio"], a["kv"], a["sc"], a["gain"], a["eps"], a["n_rot"], a["pos"],
+                 a["row_pos"], a["theta"], a["fmt"], a["comp"], a["scale"], a["cap"], a["n"], S)
+
+    assert ca(fmt=3) == -6
+    assert ca(cap=0) == -2
+    assert ca(cap=1 << 40) == -2
+    assert ca(width=130) == -2
+    assert ca(ratio=2000) == -3
+    assert ca(scale=None) == -1 and "comp_scale" in ops.last_error()
+    assert ca(n=None) == -1 and "n_comp" in ops.last_error()
+    assert ca(pos=MIS) == -4
+    assert ca(eps=-1.0) == -2
 
 
 def _mqa(L, **kw):

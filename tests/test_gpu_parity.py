@@ -624,3 +624,173 @@ def test_e2e_ragged_prefill_small():
     x["n_vis"] = np.array([[0, 1, 300, 512, 777], [777, 600, 513, 2, 40]], dtype=np.int32)
     step = _run_step(w, upload(x))
     _check_e2e(w, x, step, sel=list(range(10)))
+
+
+# ------------------------------------------------------------ cache upkeep
+
+PUSH_CASES = [
+    dict(cap=128, D=512, T=1, n0=[0, 1, 64, 127, 128, 128]),
+    dict(cap=128, D=512, T=3, n0=[0, 126, 127, 128]),
+    dict(cap=128, D=512, T=128, n0=[0, 5, 128]),
+    dict(cap=128, D=512, T=300, n0=[0, 77, 128]),
+    dict(cap=4, D=64, T=9, n0=[0, 1, 3, 4, 7, -2]),
+    dict(cap=1024, D=512, T=2, n0=[1024, 1023]),
+]
+
+
+@pytest.mark.parametrize("case", PUSH_CASES, ids=lambda c: f"cap{c['cap']}D{c['D']}T{c['T']}")
+def test_push_raw_matches_oracle(case):
+    """Window rows and counts bit-exact against the oracle's push (f16 rounding: overflow,
+    underflow, subnormals, -0); rows past the new count untouched."""
+    cap, D, T, n0 = case["cap"], case["D"], case["T"], case["n0"]
+    U = len(n0)
+    rng = np.random.default_rng(cap + 7 * T + D)
+    raw = rng.integers(0, 0x7C00, (U, cap, D), dtype=np.uint16)
+    kv = (rng.standard_normal((U, T, D)) * 10.0 ** rng.integers(-9, 6, (U, T, D))).astype(np.float32)
+    kv[:, 0, :4] = [70000.0, -1e-8, 6.1e-5, -0.0]
+    raw_d = torch.from_numpy(raw.view(np.int16)).cuda().view(torch.float16)
+    n_d = torch.tensor(n0, dtype=torch.int32, device="cuda")
+    ops.push_raw(torch.from_numpy(kv).cuda(), raw_d, n_d)
+    got = raw_d.view(torch.int16).cpu().numpy().view(np.uint16)
+    got_n = n_d.cpu().numpy()
+    for u in range(U):
+        ref, n = orc.push_raw(raw[u], min(max(n0[u], 0), cap), kv[u])
+        assert got_n[u] == n, (u, got_n[u], n)
+        assert np.array_equal(got[u, :n], ref[:n]), u
+        assert np.array_equal(got[u, n:], raw[u, n:]), u
+
+
+@pytest.mark.parametrize("ratio,width", [(4, 512), (4, 128), (128, 512), (1, 8)])
+def test_frontier_push_matches_oracle(ratio, width):
+    rng = np.random.default_rng(ratio * width)
+    U = 6
+    skv = rng.standard_normal((U, ratio, width)).astype(np.float32)
+    ssc = rng.standard_normal((U, ratio, width)).astype(np.float32)
+    kv = rng.standard_normal((U, width)).astype(np.float32)
+    sc = rng.standard_normal((U, width)).astype(np.float32)
+    ape = rng.standard_normal((ratio, width)).astype(np.float32)
+    pos = np.array([0, ratio - 1, ratio, 12345, 2 ** 40 + 3, 7 * ratio + ratio // 2], dtype=np.int64)
+    d_kv, d_sc = torch.from_numpy(skv).cuda(), torch.from_numpy(ssc).cuda()
+    ops.frontier_push(torch.from_numpy(kv).cuda(), torch.from_numpy(sc).cuda(), torch.from_numpy(ape).cuda(),
+                      torch.from_numpy(pos).cuda(), d_kv, d_sc)
+    g_kv, g_sc = d_kv.cpu().numpy(), d_sc.cpu().numpy()
+    for u in range(U):
+        r_kv, r_sc = orc.frontier_push(skv[u], ssc[u], int(pos[u]), kv[u], sc[u], ape)
+        assert np.array_equal(g_kv[u], r_kv) and np.array_equal(g_sc[u].view(np.uint32), r_sc.view(np.uint32)), u
+
+
+def _codes_agree(got, ref, y, s, g_dec, r_dec):
+    """E4M3 codes equal (+-0 alike) except where the exact value lies on a rounding midpoint."""
+    same = (got == ref) | (((got & 0x7F) == 0) & ((ref & 0x7F) == 0))
+    for j in np.nonzero(~same)[0]:
+        assert _near_midpoint(y[j] / s, g_dec[j], r_dec[j]), (j, y[j] / s, g_dec[j], r_dec[j])
+    return int((~same).sum())
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "bf16_fp8rt", "e4m3"])
+def test_compress_append_matches_oracle(fmt):
+    """Only units whose token closes a group emit; the row lands at n_comp[u] (not written past
+    cap, still counted); bf16 rows as compress_rows, E4M3 codes and scales as the oracle's
+    stored form."""
+    rng = np.random.default_rng({"bf16": 1, "bf16_fp8rt": 2, "e4m3": 3}[fmt])
+    ratio, width, cap = 4, 128, 5
+    pos = np.array([3, 7, 4, 5, 6, 11, 1003, 1002, 15, 19], dtype=np.int64)
+    n0 = np.array([0, 4, 0, 1, 2, 5, 3, 3, 2, 1], dtype=np.int32)
+    U = len(pos)
+    kv = rng.standard_normal((U, ratio, width)).astype(np.float32)
+    sc = (rng.standard_normal((U, ratio, width)) * 2.0).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, (U, width)).astype(np.float32)
+    row_pos = (pos // ratio).astype(np.int64)
+    n_d = torch.from_numpy(n0.copy()).cuda()
+    if fmt == "e4m3":
+        comp = torch.full((U, cap, width), 0x55, dtype=torch.uint8, device="cuda")
+        scl = torch.full((U, cap), -1.0, dtype=torch.float32, device="cuda")
+    else:
+        comp = torch.full((U, cap, width), 7.0, dtype=torch.bfloat16, device="cuda")
+        scl = None
+    ops.compress_append(torch.from_numpy(kv).cuda(), torch.from_numpy(sc).cuda(), torch.from_numpy(gain).cuda(),
+                        torch.from_numpy(pos).cuda(), torch.from_numpy(row_pos).cuda(), comp, n_d, comp_scale=scl,
+                        fp8=(fmt != "bf16"))
+    got_n = n_d.cpu().numpy()
+    host = comp.cpu()
+    for u in range(U):
+        emits = pos[u] % ratio == ratio - 1
+        assert got_n[u] == n0[u] + (1 if emits else 0), u
+        rows = [r for r in range(cap) if not (emits and r == n0[u])]
+        if fmt == "e4m3":
+            assert torch.all(host[u, rows] == 0x55) and torch.all(scl[u, rows].cpu() == -1.0), u
+        else:
+            assert torch.all(host[u, rows] == 7.0), u
+        if not emits or n0[u] >= cap:
+            continue
+        r = int(n0[u])
+        if fmt == "e4m3":
+            codes, s = orc.compress_row_e4m3(kv[u], sc[u], gain[u], n_rot=64, pos=int(row_pos[u]))
+            _, y, _ = orc.compress_row(kv[u], sc[u], gain[u], n_rot=64, pos=int(row_pos[u]), fp8=True)
+            amax = np.max(np.abs(y)) / 448.0
+            if abs(amax / 2.0 ** round(math.log2(amax)) - 1.0) < 1e-6:
+                continue                                  # scale on a power of two: either is right
+            assert float(scl[u, r]) == s, u
+            got = host[u, r].numpy()
+            dec = lambda c: torch.from_numpy(c.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+            assert _codes_agree(got, codes, y, s, dec(got), dec(codes)) <= 2, u
+        else:
+            ref, y, s = orc.compress_row(kv[u], sc[u], gain[u], n_rot=64, pos=int(row_pos[u]), fp8=(fmt != "bf16"))
+            got = host[u, r].view(torch.int16).numpy().view(np.uint16)
+            diff = np.nonzero(got != ref)[0]
+            g_v, r_v = bf16_f64(got), bf16_f64(ref)
+            for j in diff:
+                x = y[j] / s if fmt != "bf16" else y[j]
+                a, b = (g_v[j] / s, r_v[j] / s) if fmt != "bf16" else (g_v[j], r_v[j])
+                assert _near_midpoint(x, a, b), (u, j)
+            assert len(diff) <= 2, u
+
+
+def test_decode_loop_cache_upkeep_matches_oracle():
+    """Twelve decode tokens through the device-side cache upkeep (frontier push, E4M3 index-key
+    append, raw-window push), counters kept on the GPU, against the oracle's loop."""
+    rng = np.random.default_rng(44)
+    U, ratio, width, cap, D, W = 3, 4, 128, 6, 64, 8
+    ape = rng.standard_normal((ratio, width)).astype(np.float32)
+    gain = rng.uniform(0.5, 1.5, (U, width)).astype(np.float32)
+    pos0 = np.array([0, 4 * 50, 4 * 77], dtype=np.int64)
+    d_skv = torch.zeros((U, ratio, width), dtype=torch.float32, device="cuda")
+    d_ssc = torch.zeros((U, ratio, width), dtype=torch.float32, device="cuda")
+    d_codes = torch.zeros((U, cap, width), dtype=torch.uint8, device="cuda")
+    d_scale = torch.zeros((U, cap), dtype=torch.float32, device="cuda")
+    d_ncomp = torch.zeros(U, dtype=torch.int32, device="cuda")
+    d_raw = torch.zeros((U, W, D), dtype=torch.float16, device="cuda")
+    d_nraw = torch.zeros(U, dtype=torch.int32, device="cuda")
+    o_skv = np.zeros((U, ratio, width), np.float32)
+    o_ssc = np.zeros((U, ratio, width), np.float32)
+    o_codes = np.zeros((U, cap, width), np.uint8)
+    o_scale = np.zeros((U, cap))
+    o_ncomp = [0] * U
+    o_raw = np.zeros((U, W, D), np.uint16)
+    o_nraw = [0] * U
+    for step in range(12):
+        pos = pos0 + step
+        kv = rng.standard_normal((U, width)).astype(np.float32)
+        sc = rng.standard_normal((U, width)).astype(np.float32)
+        rkv = rng.standard_normal((U, 1, D)).astype(np.float32)
+        d_pos = torch.from_numpy(pos).cuda()
+        ops.frontier_push(torch.from_numpy(kv).cuda(), torch.from_numpy(sc).cuda(), torch.from_numpy(ape).cuda(),
+                          d_pos, d_skv, d_ssc)
+        ops.compress_append(d_skv, d_ssc, torch.from_numpy(gain).cuda(), d_pos, d_pos // ratio, d_codes, d_ncomp,
+                            comp_scale=d_scale)
+        ops.push_raw(torch.from_numpy(rkv).cuda(), d_raw, d_nraw)
+        for u in range(U):
+            o_skv[u], o_ssc[u] = orc.frontier_push(o_skv[u], o_ssc[u], int(pos[u]), kv[u], sc[u], ape)
+            if pos[u] % ratio == ratio - 1:
+                c, s = orc.compress_row_e4m3(o_skv[u], o_ssc[u], gain[u], n_rot=64, pos=int(pos[u] // ratio))
+                o_codes[u, o_ncomp[u]], o_scale[u, o_ncomp[u]] = c, s
+                o_ncomp[u] += 1
+            o_raw[u], o_nraw[u] = orc.push_raw(o_raw[u], o_nraw[u], rkv[u])
+    assert d_ncomp.cpu().tolist() == o_ncomp == [3, 3, 3]
+    assert d_nraw.cpu().tolist() == o_nraw == [W] * U
+    assert np.array_equal(d_skv.cpu().numpy(), o_skv) and np.array_equal(d_ssc.cpu().numpy(), o_ssc)
+    assert np.array_equal(d_raw.view(torch.int16).cpu().numpy().view(np.uint16), o_raw)
+    assert np.array_equal(d_scale.cpu().numpy()[:, :3], o_scale[:, :3])
+    g = d_codes.cpu().numpy()
+    mism = ((g != o_codes) & ~(((g & 0x7F) == 0) & ((o_codes & 0x7F) == 0))).sum()
+    assert mism <= 3, mism                               # rounding-midpoint codes only
