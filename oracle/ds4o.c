@@ -180,9 +180,44 @@ void ds4o_rope_q(int H, int D, int n_rot, int64_t pos, double theta,
  * 512-vector per token, section 3-1); the union is the concatenation of the
  * raw rows and the selected rows, with no de-duplication; one softmax over
  * the whole union; no sink or bias terms.  Plain two-pass softmax. */
-int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
-                    const uint16_t *raw, const uint16_t *comp, const int32_t *idx,
-                    double scale, double *out)
+/* One softmax over the n_union rows (doubles, rows[r][d]) for each of the H heads; each row
+ * is key and value.  n_union >= 1. */
+static void attend_rows(int H, int D, int n_union, const double *rows, const double *q_rot, double scale,
+                        double *out)
+{
+    double *logit = (double *)malloc(sizeof(double) * (size_t)n_union);
+    for (int h = 0; h < H; h++) {
+        const double *qh = q_rot + (int64_t)h * D;
+        double m = -INFINITY;
+        for (int r = 0; r < n_union; r++) {
+            double dot = 0.0;
+            for (int d = 0; d < D; d++)
+                dot += qh[d] * rows[(int64_t)r * D + d];
+            logit[r] = scale * dot;
+            if (logit[r] > m)
+                m = logit[r];
+        }
+        double z = 0.0;
+        for (int r = 0; r < n_union; r++) {
+            logit[r] = exp(logit[r] - m);   /* now the unnormalised probability */
+            z += logit[r];
+        }
+        double *oh = out + (int64_t)h * D;
+        for (int d = 0; d < D; d++) {
+            double acc = 0.0;
+            for (int r = 0; r < n_union; r++)
+                acc += logit[r] * rows[(int64_t)r * D + d];
+            oh[d] = acc / z;
+        }
+    }
+    free(logit);
+}
+
+/* The union as doubles: the W raw rows, then compressed row idx[k] for each idx[k] >= 0,
+ * decoded from bf16 (comp8 == NULL) or from E4M3 codes times the row's scale. */
+static int union_mqa(int H, int D, int W, int K, const double *q_rot, const uint16_t *raw,
+                     const uint16_t *comp, const uint8_t *comp8, const float *comp_scale,
+                     const int32_t *idx, double scale, double *out)
 {
     int n_union = W;
     for (int k = 0; k < K; k++)
@@ -192,7 +227,6 @@ int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
         memset(out, 0, sizeof(double) * (size_t)H * (size_t)D);
         return 0;
     }
-    /* Materialise the union as doubles: rows[r][d]. */
     double *rows = (double *)malloc(sizeof(double) * (size_t)n_union * (size_t)D);
     int r = 0;
     for (int i = 0; i < W; i++, r++)
@@ -201,38 +235,29 @@ int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
     for (int k = 0; k < K; k++) {
         if (idx[k] < 0)
             continue;
+        const int64_t j = idx[k];
         for (int d = 0; d < D; d++)
-            rows[(int64_t)r * D + d] = ds4o_bf16_to_f64(comp[(int64_t)idx[k] * D + d]);
+            rows[(int64_t)r * D + d] = comp8 ? ds4o_e4m3_to_f64(comp8[j * D + d]) * (double)comp_scale[j]
+                                             : ds4o_bf16_to_f64(comp[j * D + d]);
         r++;
     }
-    double *logit = (double *)malloc(sizeof(double) * (size_t)n_union);
-    for (int h = 0; h < H; h++) {
-        const double *qh = q_rot + (int64_t)h * D;
-        double m = -INFINITY;
-        for (r = 0; r < n_union; r++) {
-            double dot = 0.0;
-            for (int d = 0; d < D; d++)
-                dot += qh[d] * rows[(int64_t)r * D + d];
-            logit[r] = scale * dot;
-            if (logit[r] > m)
-                m = logit[r];
-        }
-        double z = 0.0;
-        for (r = 0; r < n_union; r++) {
-            logit[r] = exp(logit[r] - m);   /* now the unnormalised probability */
-            z += logit[r];
-        }
-        double *oh = out + (int64_t)h * D;
-        for (int d = 0; d < D; d++) {
-            double acc = 0.0;
-            for (r = 0; r < n_union; r++)
-                acc += logit[r] * rows[(int64_t)r * D + d];
-            oh[d] = acc / z;
-        }
-    }
-    free(logit);
+    attend_rows(H, D, n_union, rows, q_rot, scale, out);
     free(rows);
     return n_union;
+}
+
+int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
+                    const uint16_t *raw, const uint16_t *comp, const int32_t *idx,
+                    double scale, double *out)
+{
+    return union_mqa(H, D, W, K, q_rot, raw, comp, NULL, NULL, idx, scale, out);
+}
+
+int ds4o_sparse_mqa_fp8(int H, int D, int W, int K, const double *q_rot,
+                        const uint16_t *raw, const uint8_t *comp8, const float *comp_scale,
+                        const int32_t *idx, double scale, double *out)
+{
+    return union_mqa(H, D, W, K, q_rot, raw, NULL, comp8, comp_scale, idx, scale, out);
 }
 
 /* ------------------------------------------------------------- whole step */

@@ -69,6 +69,13 @@ int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
                     const uint16_t *raw, const uint16_t *comp, const int32_t *idx,
                     double scale, double *out);
 
+/* As ds4o_sparse_mqa, with the compressed rows stored as FP8 (the compressor's round trip,
+ * "Reading the architecture of DwarfStar (ds4.c), part 4/8", section 3-2): row j is the
+ * E4M3FN value of each code times comp_scale[j].  comp8: uint8 [*][D]; comp_scale: f32 [*]. */
+int ds4o_sparse_mqa_fp8(int H, int D, int W, int K, const double *q_rot,
+                        const uint16_t *raw, const uint8_t *comp8, const float *comp_scale,
+                        const int32_t *idx, double scale, double *out);
+
 /* Whole step for U units x T queries (the layout of the GPU library's calls),
  * on nthreads host threads over independent (unit, query) pairs:
  *   q      : [U][T][H][D]  f32 (q_is_bf16 = 0) or bf16 bits (q_is_bf16 = 1)

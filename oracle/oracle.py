@@ -59,6 +59,8 @@ def lib() -> ctypes.CDLL:
         L.ds4o_round_e4m3.argtypes, L.ds4o_round_e4m3.restype = [dbl], ctypes.c_uint8
         L.ds4o_indexer_score_fp8.argtypes = [i64, i32, i32, P, P, P, P, i64, P]
         L.ds4o_indexer_score_fp8.restype = None
+        L.ds4o_sparse_mqa_fp8.argtypes = [i32, i32, i32, i32, P, P, P, P, P, dbl, P]
+        L.ds4o_sparse_mqa_fp8.restype = i32
         L.ds4o_compress_row.argtypes = [i32, i32, P, P, P, dbl, i32, i64, dbl, i32, P, P, P]
         L.ds4o_compress_row.restype = i32
         L.ds4o_compress_row_e4m3.argtypes = [i32, i32, P, P, P, dbl, i32, i64, dbl, P, P]
@@ -156,6 +158,26 @@ def sparse_mqa(q_rot, raw, comp, idx, scale: float) -> np.ndarray:
         comp = np.zeros((1, D), dtype=np.uint16)
     out = np.empty((H, D), dtype=np.float64)
     lib().ds4o_sparse_mqa(H, D, W, idx.shape[0], _p(q_rot), _p(raw), _p(comp), _p(idx), float(scale), _p(out))
+    return out
+
+
+def sparse_mqa_fp8(q_rot, raw, comp8, comp_scale, idx, scale: float) -> np.ndarray:
+    """One query over FP8-stored compressed rows: comp8 E4M3FN codes uint8 [N, D], comp_scale
+    f32 [N]; the rest as sparse_mqa."""
+    q_rot = np.ascontiguousarray(q_rot, dtype=np.float64)
+    raw = _u16(raw)
+    comp8 = np.ascontiguousarray(comp8, dtype=np.uint8)
+    cs = np.ascontiguousarray(comp_scale, dtype=np.float32)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    H, D = q_rot.shape
+    W = raw.shape[0] if raw.size else 0
+    if W == 0:
+        raw = np.zeros((1, D), dtype=np.uint16)
+    if comp8.size == 0:
+        comp8, cs = np.zeros((1, D), dtype=np.uint8), np.ones(1, dtype=np.float32)
+    out = np.empty((H, D), dtype=np.float64)
+    lib().ds4o_sparse_mqa_fp8(H, D, W, idx.shape[0], _p(q_rot), _p(raw), _p(comp8), _p(cs), _p(idx), float(scale),
+                              _p(out))
     return out
 
 

@@ -580,3 +580,28 @@ def test_frontier_push_rows_and_bias(oracle_mod):
     for i, (k, s) in enumerate(toks):
         assert np.array_equal(skv[i], k)
         assert np.array_equal(ssc[i], s + ape[i])
+
+
+@pytest.mark.parametrize("mult", [1.0, 1.5, 1.25])
+def test_attention_fp8_rows_equal_bf16_rows(oracle_mod, mult):
+    """Row scales of 1, 1.5 or 1.25 times a power of two: code value * scale has at most 6
+    significant bits, so it is exact in bf16; the FP8-row attention must then equal the bf16
+    attention on those rows (made through torch's own E4M3 and bf16 types)."""
+    rng = np.random.default_rng(int(mult * 100))
+    H, D, W, N, K = 4, 64, 3, 20, 9
+    q = rng.standard_normal((H, D)) * 0.2
+    raw = gen.f16_bits_from_f32(rng.standard_normal((W, D)).astype(np.float32))
+    k8 = gen.e4m3_codes(rng, (N, D))
+    scale = (mult * np.ldexp(1.0, rng.integers(-9, -4, N))).astype(np.float32)
+    kv = torch.from_numpy(k8.copy()).view(torch.float8_e4m3fn).to(torch.float64) * torch.from_numpy(scale).double()[:, None]
+    kb = kv.to(torch.bfloat16)
+    assert torch.equal(kb.to(torch.float64), kv)
+    comp = kb.view(torch.int16).numpy().view(np.uint16)
+    idx = np.array([3, 0, 19, -1, 3, 7, -1, 11, 2], dtype=np.int32)
+    got = oracle_mod.sparse_mqa_fp8(q, raw, k8, scale, idx, 0.3)
+    ref = oracle_mod.sparse_mqa(q, raw, comp, idx, 0.3)
+    assert np.array_equal(got, ref)
+    # and the rows' scales matter: doubling one selected row's scale changes the output
+    s2 = scale.copy()
+    s2[7] *= 2
+    assert not np.allclose(oracle_mod.sparse_mqa_fp8(q, raw, k8, s2, idx, 0.3), got)
