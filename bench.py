@@ -112,7 +112,7 @@ class Bench:
     as E4M3 codes and row scales, synth.make_indexer_fp8_config) the select is
     ds4a_indexer_topk_fp8."""
 
-    def __init__(self, w, x, replicas: int, fp8_keys=None):
+    def __init__(self, w, x, replicas: int, fp8_keys=None, fp8_rows: bool = False):
         import torch
 
         from sparse_compressed_kv_amd import ops
@@ -120,10 +120,15 @@ class Bench:
         self.torch, self.ops, self.w = torch, ops, w
         self.reps = [upload(x) for _ in range(replicas)]
         self.fp8 = fp8_keys is not None
+        self.fp8_rows = fp8_rows
         if self.fp8:
             for d in self.reps:
                 d["k8"] = torch.from_numpy(fp8_keys["idx_k8"]).cuda()
                 d["sc"] = torch.from_numpy(fp8_keys["idx_k_scale"]).cuda()
+        if fp8_rows:
+            for i, d in enumerate(self.reps):
+                d["comp8"], d["comp_s"] = fp8_rows_on_device(torch, w, seed=100 + i)
+                del d["comp"]
         self.step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=True)
         self.sep = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=False)
         self.nvis = w.vis_base is not None
@@ -134,8 +139,16 @@ class Bench:
         d = self.reps[i % len(self.reps)]
         nv = d["n_vis"] if self.nvis else None
         self.select(d, nv, stream)
-        self.ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W, out=st.out,
-                            workspace=st.ws_mqa, stream=stream)
+        self.attend(d, stream)
+
+    def attend(self, d, stream):
+        w, st = self.w, self.step
+        if self.fp8_rows:
+            self.ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp8"], st.idx, w.scale, w.theta, W=w.W,
+                                out=st.out, workspace=st.ws_mqa, stream=stream, comp_scale=d["comp_s"])
+        else:
+            self.ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta, W=w.W,
+                                out=st.out, workspace=st.ws_mqa, stream=stream)
 
     def select(self, d, nv, stream):
         st = self.step
@@ -174,8 +187,7 @@ class Bench:
         # A2 calls are timed too, for comparison with the fused call the step uses.
         calls = {
             "select": lambda d, nv: self.select(d, nv, stream),
-            "mqa": lambda d, nv: ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st.idx, w.scale, w.theta,
-                                                W=w.W, out=st.out, workspace=st.ws_mqa, stream=stream),
+            "mqa": lambda d, nv: self.attend(d, stream),
             "indexer": (lambda d, nv: ops.indexer_score_fp8(d["idx_q"], d["idx_w"], d["k8"], d["sc"], n_vis=nv,
                                                             out=sep.scores, stream=stream)) if self.fp8 else
                        (lambda d, nv: ops.indexer_score(d["idx_q"], d["idx_w"], d["idx_k"], n_vis=nv,
@@ -265,6 +277,23 @@ class Bench:
         torch.cuda.synchronize()
         return {"idx": self.step.idx.cpu().numpy(), "out": self.step.out.cpu().numpy(),
                 "scores": self.sep.scores.cpu().numpy()}
+
+
+def fp8_rows_on_device(torch, w, seed: int):
+    """Compressed rows as stored in FP8 (E4M3 codes [U][N][512] + f32 row scales [U][N]) for the
+    timing runs, drawn on the GPU with a seeded torch generator: sign uniform, exponent field
+    round(N(11, 1.5)) clipped to 0..15, fraction uniform, the NaN pattern moved to S.1111.110;
+    scales 2^e, e uniform in -8..-6 (the recipe of synth.inputs.e4m3_codes)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    shape = (w.U, w.N, 512)
+    e = (torch.randn(shape, device="cuda", generator=g) * 1.5 + 11.0).round().clamp(0, 15).to(torch.uint8)
+    m = torch.randint(0, 8, shape, device="cuda", generator=g, dtype=torch.uint8)
+    sg = torch.randint(0, 2, shape, device="cuda", generator=g, dtype=torch.uint8)
+    codes = (sg << 7) | (e << 3) | m
+    codes = torch.where((codes & 0x7F) == 0x7F, codes - 1, codes)
+    ex = torch.randint(-8, -5, (w.U, w.N), device="cuda", generator=g).to(torch.float32)
+    return codes.contiguous(), torch.exp2(ex).contiguous()
 
 
 def replicas_for(w) -> int:
@@ -684,6 +713,21 @@ def main():
                           "indexer_alone": r8["indexer_ms"] * 1e3, "topk_alone": r8["topk_ms"] * 1e3},
         }
         del b8
+        torch.cuda.empty_cache()
+        # ---- the same with the compressed rows the attention reads stored in FP8 too
+        x8 = gen.make_indexer_fp8_config(w)
+        b9 = Bench(w, x, reps, fp8_keys=x8, fp8_rows=True)
+        del x8
+        r9 = b9.run(args.steps, args.warmup)
+        log(f"[bench] {w.name} fp8 keys + fp8 rows: {r9}")
+        by9 = units * (decode_bytes_per_unit(w.N, w.H, w.K, w.W, KEY_BYTES_FP8) - w.K * 512 * 2 + w.K * (512 + 4))
+        rec["decode_n65536_fp8_keys_rows"] = {
+            "workload": w.name + "_fp8keys_fp8rows", "value": units / (r9["ms_per_step"] / 1e3),
+            "unit": "decode tokens/s/layer", "ms_per_step": r9["ms_per_step"],
+            "frac_hbm": by9 / (r9["ms_per_step"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+            "kernel_us": {"indexer_topk": r9["select_ms"] * 1e3, "mqa": r9["mqa_ms"] * 1e3},
+        }
+        del b9
         torch.cuda.empty_cache()
         # ---- a whole Flash decode step: the 43 layers' attention by their compression ratio
         fs = full_schedule(args.steps, args.warmup)

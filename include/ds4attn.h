@@ -188,6 +188,29 @@ int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
                    float scale, float *out,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/* A3-A6 and the dense attention over compressed rows stored as FP8 (the compressor's output
+ * format, section 3-2 of "Reading the architecture of DwarfStar (ds4.c), part 4/8"; the
+ * stored form of DS4A_ROW_E4M3 rows from ds4a_compress_append).  As ds4a_sparse_mqa /
+ * ds4a_dense_mqa with comp_kv replaced by
+ *   comp_kv8   : uint8 [U][N][512] E4M3FN codes (NaN codes not allowed)
+ *   comp_scale : f32 [U][N], finite and > 0
+ * where compressed row j is code value * comp_scale[u][j] (raw rows stay f16).  Codes widen to
+ * bf16 exactly on the way into LDS and use the same bf16 MFMAs as the bf16 entry points; a
+ * row's scale multiplies its logit and, for the weighted sum, its probability (fp32).  With
+ * power-of-two scales the output is bit-identical to the bf16 entry point's on rows
+ * code value * scale.  Workspace sizes are those of the bf16 calls (which = 1 and 3).
+ */
+int ds4a_sparse_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K,
+                        const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                        const void *raw_kv, const uint8_t *comp_kv8, const float *comp_scale,
+                        const int32_t *idx, float scale, float *out,
+                        void *workspace, size_t workspace_bytes, void *stream);
+int ds4a_dense_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N,
+                       const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                       const void *raw_kv, const uint8_t *comp_kv8, const float *comp_scale,
+                       const int32_t *n_vis, float scale, float *out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
 /* Compressor row emission (section 3-2: tokens older than the raw window are folded,
  * `ratio` at a time, into one compressed row by a learned pooling; the indexer has its own
  * compressor of the same form).  For each unit u (a layer or a session), from its frontier

@@ -35,6 +35,11 @@
 // barriers per tile (logit halves, buffer turnover).  When the union is split over several workgroups each
 // writes (max, sum, unnormalised O) and a merge kernel combines them by
 // log-sum-exp.
+// Compressed rows stored as FP8 (E4M3 codes, 512 bytes, plus one f32 scale per row; the
+// compressor's output format) are widened to bf16 while they are staged, exactly, and their
+// scale is kept in the row's LDS padding: it multiplies the row's logit and, for the PV
+// product, its probability.  With power-of-two scales the output is bit-identical to that of
+// the bf16 rows code * scale.
 #include "common.hpp"
 #include "launch.hpp"
 #include "rope.hpp"
@@ -86,7 +91,8 @@ struct MqaArgs {
     int q_bf16;
     const int64_t *pos;
     const uint16_t *raw;
-    const uint16_t *comp;
+    const void *comp;                        // bf16 rows [U][N][512], or E4M3 codes [U][N][512]
+    const float *comp_scale;                 // E4M3 rows: f32 [U][N]
     const int32_t *idx;                      // sparse: [U][T][K]; dense: unused
     const int32_t *n_vis;                    // dense: visible compressed rows per query, or NULL (all N)
     float scale;
@@ -175,7 +181,8 @@ __device__ __forceinline__ void pack_q_frags(const float (&v)[kKs][8], const flo
 // LO_ALL: the query is f32, so every k-step carries a lo half; otherwise (bf16 query)
 // only the rotated tail does.  DENSE: the union is the raw window plus compressed rows
 // 0 .. n_vis-1 in order (a.K = N; no index list), else the raw window plus idx's rows.
-template <bool LO_ALL, bool DENSE>
+// E8: compressed rows are E4M3 codes with row scales (N >= 1), else bf16.
+template <bool LO_ALL, bool DENSE, bool E8>
 __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -206,7 +213,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const int tile_raw = a.W / kTile;                      // tiles [0, tile_raw) are raw rows
 
     const uint16_t *raw_q = a.raw + (u * (int64_t)(a.T + a.W - 1) + t) * kD;
-    const uint16_t *comp_u = a.comp + u * a.N * kD;
+    constexpr int kCompRowBytes = E8 ? kD : 2 * kD;
+    const unsigned char *comp_u = static_cast<const unsigned char *>(a.comp) + u * a.N * kCompRowBytes;
+    const float *cscale_u = E8 ? a.comp_scale + u * a.N : nullptr;
     const int32_t *idx_q = a.idx + q * (int64_t)a.K;
 
     // Union row rho of this chunk: a compressed row, -2 for a raw row, -1 for none (past the
@@ -225,10 +234,26 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     };
     // A row that takes no part (-1) is read from compressed row 0, or from raw row 0 when there
     // are no compressed rows (a raw-window-only call): it is finite, its logit is masked to
-    // -inf and its probability is 0, so no branch guards the load.
-    const uint16_t *none_row = a.N > 0 ? comp_u : raw_q;
-    auto union_ptr = [&](int rho, int32_t v) __attribute__((always_inline)) -> const uint16_t * {
-        return v == -2 ? raw_q + (int64_t)rho * kD : (v >= 0 ? comp_u + (int64_t)v * kD : none_row);
+    // -inf and its probability is 0, so no branch guards the load.  With E4M3 rows a tile's
+    // format decides the load's width, so a none row of a raw tile is raw row 0 (raw tiles
+    // exist only when W > 0) and one of a compressed tile is compressed row 0 (N >= 1).
+    const unsigned char *raw_b = reinterpret_cast<const unsigned char *>(raw_q);
+    const unsigned char *none_row = (E8 ? false : a.N == 0) ? raw_b : comp_u;
+    const unsigned char *none_raw = E8 ? raw_b : none_row;
+    auto union_ptr = [&](int rho, int32_t v, bool raw_tile) __attribute__((always_inline)) -> const unsigned char * {
+        return v == -2 ? raw_b + (int64_t)rho * (2 * kD)
+                       : (v >= 0 ? comp_u + (int64_t)v * kCompRowBytes : (raw_tile ? none_raw : none_row));
+    };
+    // One staged row: lane = 16-byte chunk of a bf16 / f16 row; an E4M3 row arrives as 8 bytes
+    // per lane (x, y) plus its scale (z, every lane loads the same word), widened at the store.
+    auto load_row = [&](int rho, int32_t v, bool raw_tile) __attribute__((always_inline)) -> u32x4 {
+        const unsigned char *p = union_ptr(rho, v, raw_tile);
+        if (E8 && !raw_tile) {
+            const u32x2 x = reinterpret_cast<const u32x2 *>(p)[lane];
+            const float sc = cscale_u[v >= 0 ? v : 0];
+            return u32x4{x[0], x[1], __float_as_uint(sc), 0u};
+        }
+        return reinterpret_cast<const u32x4 *>(p)[lane];
     };
     // Set-up loads first, then the first two tiles' row gathers, then the set-up's use of its
     // loads: vector loads complete in issue order, so a gather issued before the set-up's own
@@ -286,8 +311,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int r0 = tile0 * kTile + wave_u + kWaves * i, r1 = r0 + kTile;
-            st0[i] = reinterpret_cast<const u32x4 *>(union_ptr(r0, union_row(r0, j0[i])))[lane];
-            st1[i] = reinterpret_cast<const u32x4 *>(union_ptr(r1, union_row(r1, j1[i])))[lane];
+            st0[i] = load_row(r0, union_row(r0, j0[i]), tile0 < tile_raw);
+            st1[i] = load_row(r1, union_row(r1, j1[i]), tile0 + 1 < tile_raw);
         }
     }
     // (stored at the same clamped position, with no branch, so that the compiler does not move
@@ -316,10 +341,11 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     __syncthreads();
 
     auto load_tile = [&](int tt, u32x4 (&st)[kStage]) __attribute__((always_inline)) {
+        const bool raw_tile = tt < tile_raw;                 // uniform
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int rho = tt * kTile + wave + kWaves * i;
-            st[i] = reinterpret_cast<const u32x4 *>(union_ptr(rho, s_row[rho - rho0]))[lane];
+            st[i] = load_row(rho, s_row[rho - rho0], raw_tile);
         }
     };
     // Every LDS address below is a per-lane base plus a compile-time offset: the swizzle bit
@@ -331,11 +357,22 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     const int qk_base = c * kRowStride + (((kDH * dh) >> 3) + (g ^ ((c >> 2) & 1))) * 16;
     const int pv_base = (4 * g + (c >> 2)) * kRowStride + (((kDH * dh) >> 3) + (((c >> 1) & 1) ^ (g & 1))) * 16 +
                         (c & 1) * 8;
-    auto store_tile = [&](int buf, const u32x4 (&st)[kStage]) __attribute__((always_inline)) {
+    // E4M3 rows: the widened row, and the scale at byte kD * 2 of the LDS row (its padding).
+    auto store_tile = [&](int buf, const u32x4 (&st)[kStage], bool raw_tile) __attribute__((always_inline)) {
         unsigned char *base = tiles + buf * kTileBytes + st_base;
+        if (E8 && !raw_tile) {
 #pragma unroll
-        for (int i = 0; i < kStage; ++i)
-            *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = st[i];
+            for (int i = 0; i < kStage; ++i) {
+                *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = e4m3x8_to_bf16x8(u32x2{st[i][0], st[i][1]});
+                if (lane == 0)
+                    *reinterpret_cast<uint32_t *>(tiles + buf * kTileBytes + (wave + kWaves * i) * kRowStride + 2 * kD) =
+                        st[i][2];
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kStage; ++i)
+                *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = st[i];
+        }
     };
     const float *tail = s_qt + (kHW * ht + c) * kRot;
     u32x4 qhi[kKs], qlo[kKs];
@@ -350,7 +387,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         if (tile0 < tmid) pack_q_frags<true>(qv, tail, d0, g, qhi, qlo);
         else pack_q_frags<false>(qv, tail, d0, g, qhi, qlo);
     }
-    store_tile(0, st0);
+    store_tile(0, st0, tile0 < tile_raw);
     load_tile(tile0 + 2, st0);
     // Waves w and w + 4 share a SIMD.  Between two barriers both would otherwise run the
     // same phases in lock-step (softmax on the VALU while the matrix core idles, then both
@@ -369,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         __attribute__((always_inline)) {
         constexpr bool F16 = decltype(f16_tag)::value;
         constexpr int kXb = decltype(xb_tag)::value;
-        store_tile(bnext, sv);
+        store_tile(bnext, sv, tt + 1 < tile_raw);
         load_tile(tt + 3, sv);
         const unsigned char *tb = tiles + bcur * kTileBytes;
         f32x4 *xc = xch + kXb * (kXchBytes / 16);
@@ -409,14 +446,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
                 acc[rt] = xc[((2 * ht) * 2 + rt) * kWave + lane] + xc[((2 * ht + 1) * 2 + rt) * kWave + lane];
 
             // ---- mask, online softmax (head c; rows 16rt + 4g + r)
-            float p[2][4];
+            float p[2][4], rsc[2][4] = {{1.f, 1.f, 1.f, 1.f}, {1.f, 1.f, 1.f, 1.f}};
             float tmax = -INFINITY;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int rho = tt * kTile + 16 * rt + 4 * g + r;
-                    p[rt][r] = s_row[rho - rho0] != -1 ? a.scale * acc[rt][r] : -INFINITY;
+                    float l = a.scale * acc[rt][r];
+                    if (E8 && !F16) {                   // E4M3 rows: the row's scale (LDS padding)
+                        rsc[rt][r] = *reinterpret_cast<const float *>(tb + (16 * rt + 4 * g + r) * kRowStride + 2 * kD);
+                        l *= rsc[rt][r];
+                    }
+                    p[rt][r] = s_row[rho - rho0] != -1 ? l : -INFINITY;
                     tmax = fmaxf(tmax, p[rt][r]);
                 }
             tmax = wave_xor_max(tmax, 16);
@@ -461,7 +503,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
                 }
             } else {
                 bf16x8 phi, plo;
-                pack_hi_lo8(pv, phi, plo);
+                if (E8) {                               // value rows carry their scale too
+                    const float pvs[8] = {p[0][0] * rsc[0][0], p[0][1] * rsc[0][1], p[0][2] * rsc[0][2],
+                                          p[0][3] * rsc[0][3], p[1][0] * rsc[1][0], p[1][1] * rsc[1][1],
+                                          p[1][2] * rsc[1][2], p[1][3] * rsc[1][3]};
+                    pack_hi_lo8(pvs, phi, plo);
+                } else {
+                    pack_hi_lo8(pv, phi, plo);
+                }
 #pragma unroll
                 for (int b = 0; b < kDB; ++b) {
                     const s16x4 v1 = lds_read_tr16(tb + pv_base + 32 * b);
@@ -625,18 +674,23 @@ MqaPlan plan_mqa(int U, int T, int H, int W, int K) {
 }
 
 hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
-                      const int64_t *q_pos, double theta, const uint16_t *raw, const uint16_t *comp,
-                      const int32_t *idx, const int32_t *n_vis, float scale, float *out, void *workspace,
-                      hipStream_t stream)
+                      const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                      const float *comp_scale, const int32_t *idx, const int32_t *n_vis, float scale, float *out,
+                      void *workspace, hipStream_t stream)
 {
     const bool dense = idx == nullptr;       // dense: K = N, rows 0 .. n_vis-1 follow the raw window
+    // E4M3 rows need at least one compressed row (the none rows of compressed tiles read row
+    // 0); with N = 0 there is no compressed row to read, so the format does not matter.
+    const bool e8 = comp_scale != nullptr && N > 0;
     const MqaPlan p = plan_mqa(U, T, H, W, K);
     const int lds = kLdsBytes + 4 * kTile * (p.tiles_per_chunk + kPadTiles);
     using Fn = void (*)(MqaArgs);
-    const int variant = (q_bf16 ? 1 : 0) + (dense ? 2 : 0);
-    static const Fn kernels[4] = {sparse_mqa_kernel<true, false>, sparse_mqa_kernel<false, false>,
-                                  sparse_mqa_kernel<true, true>, sparse_mqa_kernel<false, true>};
-    static int attr_bytes[4] = {0, 0, 0, 0};
+    const int variant = (q_bf16 ? 1 : 0) + (dense ? 2 : 0) + (e8 ? 4 : 0);
+    static const Fn kernels[8] = {sparse_mqa_kernel<true, false, false>, sparse_mqa_kernel<false, false, false>,
+                                  sparse_mqa_kernel<true, true, false>,  sparse_mqa_kernel<false, true, false>,
+                                  sparse_mqa_kernel<true, false, true>,  sparse_mqa_kernel<false, false, true>,
+                                  sparse_mqa_kernel<true, true, true>,   sparse_mqa_kernel<false, true, true>};
+    static int attr_bytes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     const Fn fn = kernels[variant];
     if (lds > attr_bytes[variant]) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
@@ -650,6 +704,7 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
     a.N = N;
     a.n_items = (int64_t)U * T * p.n_chunks;
     a.q = q; a.q_bf16 = q_bf16; a.pos = q_pos; a.raw = raw; a.comp = comp; a.idx = idx; a.n_vis = n_vis;
+    a.comp_scale = e8 ? comp_scale : nullptr;
     a.scale = scale; a.out = out; a.part = static_cast<float *>(workspace);
     a.log2_theta = log2(theta);
     const int64_t blocks = a.n_items * p.n_hg;

@@ -63,6 +63,11 @@ def lib() -> ctypes.CDLL:
     L.ds4a_sparse_mqa.restype = i32
     L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
     L.ds4a_dense_mqa.restype = i32
+    L.ds4a_sparse_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt, P, P,
+                                      sz, P]
+    L.ds4a_sparse_mqa_fp8.restype = i32
+    L.ds4a_dense_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, P, flt, P, P, sz, P]
+    L.ds4a_dense_mqa_fp8.restype = i32
     L.ds4a_compress_rows.argtypes = [i32, i32, i32, P, P, P, flt, i32, P, dbl, i32, P, i64, P]
     L.ds4a_compress_rows.restype = i32
     L.ds4a_compress_append.argtypes = [i32, i32, i32, P, P, P, flt, i32, P, P, dbl, i32, P, P, i64, P, P]
@@ -238,10 +243,23 @@ def _q_dtype(q):
     raise TypeError(f"q must be float32 or bfloat16 (got {q.dtype})")
 
 
+def _comp_rows(comp_kv, comp_scale, U, N, D):
+    """bf16 rows, or E4M3 codes (uint8 / float8_e4m3fn) with f32 row scales -> (rows, fp8)."""
+    if comp_scale is None:
+        _need(comp_kv, "comp_kv", torch.bfloat16, (U, N, D))
+        return comp_kv, False
+    if comp_kv.dtype == torch.float8_e4m3fn:
+        comp_kv = comp_kv.view(torch.uint8)
+    _need(comp_kv, "comp_kv8", torch.uint8, (U, N, D))
+    _need(comp_scale, "comp_scale", torch.float32, (U, N))
+    return comp_kv, True
+
+
 def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 10000.0, W: int = 128,
-               out=None, workspace=None, stream=None):
+               out=None, workspace=None, stream=None, comp_scale=None):
     """A3-A6.  q [U,T,H,512] f32|bf16, q_pos i64 [U,T], raw_kv f16 [U,T+W-1,512],
-    comp_kv bf16 [U,N,512], idx i32 [U,T,K] -> f32 [U,T,H,512]."""
+    comp_kv bf16 [U,N,512] (or E4M3 codes [U,N,512] with comp_scale f32 [U,N]),
+    idx i32 [U,T,K] -> f32 [U,T,H,512]."""
     if not isinstance(q, torch.Tensor):
         raise TypeError("q must be a torch.Tensor")
     U, T, H, D = q.shape
@@ -252,24 +270,29 @@ def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 1000
     _need(q_pos, "q_pos", torch.int64, (U, T))
     if W > 0:
         _need(raw_kv, "raw_kv", torch.float16, (U, T + W - 1, D))
-    _need(comp_kv, "comp_kv", torch.bfloat16, (U, N, D))
+    comp_kv, fp8 = _comp_rows(comp_kv, comp_scale, U, N, D)
     _need(idx, "idx", torch.int32, (U, T, K))
     if out is None:
         out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (U, T, H, D))
     ws, nb = _workspace(workspace_bytes(1, U, T, N, K, H, W), q.device, workspace)
-    _check("ds4a_sparse_mqa", lib().ds4a_sparse_mqa(
-        U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta),
-        _ptr(raw_kv) if W > 0 else None, _ptr(comp_kv), _ptr(idx), float(scale), _ptr(out), _ptr(ws), nb,
-        _stream(stream)))
+    raw = _ptr(raw_kv) if W > 0 else None
+    if fp8:
+        _check("ds4a_sparse_mqa_fp8", lib().ds4a_sparse_mqa_fp8(
+            U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, _ptr(comp_kv), _ptr(comp_scale),
+            _ptr(idx), float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    else:
+        _check("ds4a_sparse_mqa", lib().ds4a_sparse_mqa(
+            U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, _ptr(comp_kv), _ptr(idx),
+            float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
     return out
 
 
 def dense_mqa(q, q_pos, raw_kv, comp_kv, scale: float, theta: float = 10000.0, W: int = 128, n_vis=None,
-              out=None, workspace=None, stream=None):
+              out=None, workspace=None, stream=None, comp_scale=None):
     """Dense attention (layers without an indexer).  q [U,T,H,512] f32|bf16, q_pos i64 [U,T],
-    raw_kv f16 [U,T+W-1,512] (or None when W = 0), comp_kv bf16 [U,N,512] (N may be 0, or None),
-    n_vis i32 [U,T] or None -> f32 [U,T,H,512]."""
+    raw_kv f16 [U,T+W-1,512] (or None when W = 0), comp_kv bf16 [U,N,512] (N may be 0, or None;
+    or E4M3 codes with comp_scale f32 [U,N]), n_vis i32 [U,T] or None -> f32 [U,T,H,512]."""
     if not isinstance(q, torch.Tensor):
         raise TypeError("q must be a torch.Tensor")
     U, T, H, D = q.shape
@@ -279,18 +302,26 @@ def dense_mqa(q, q_pos, raw_kv, comp_kv, scale: float, theta: float = 10000.0, W
     _need(q_pos, "q_pos", torch.int64, (U, T))
     if W > 0:
         _need(raw_kv, "raw_kv", torch.float16, (U, T + W - 1, D))
+    fp8 = comp_scale is not None
     if N > 0:
-        _need(comp_kv, "comp_kv", torch.bfloat16, (U, N, D))
+        comp_kv, fp8 = _comp_rows(comp_kv, comp_scale, U, N, D)
     if n_vis is not None:
         _need(n_vis, "n_vis", torch.int32, (U, T))
     if out is None:
         out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
     _need(out, "out", torch.float32, (U, T, H, D))
     ws, nb = _workspace(workspace_bytes(3, U, T, N, 0, H, W), q.device, workspace)
-    _check("ds4a_dense_mqa", lib().ds4a_dense_mqa(
-        U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta),
-        _ptr(raw_kv) if W > 0 else None, _ptr(comp_kv) if N > 0 else None,
-        _ptr(n_vis) if n_vis is not None else None, float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    raw = _ptr(raw_kv) if W > 0 else None
+    comp = _ptr(comp_kv) if N > 0 else None
+    nv = _ptr(n_vis) if n_vis is not None else None
+    if fp8:
+        _check("ds4a_dense_mqa_fp8", lib().ds4a_dense_mqa_fp8(
+            U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta), raw, comp,
+            _ptr(comp_scale) if N > 0 else None, nv, float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    else:
+        _check("ds4a_dense_mqa", lib().ds4a_dense_mqa(
+            U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta), raw, comp, nv, float(scale), _ptr(out),
+            _ptr(ws), nb, _stream(stream)))
     return out
 
 

@@ -20,7 +20,8 @@ def test_exports_every_declared_symbol(L):
     names = ops.declared_symbols()
     assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_dense_mqa",
             "ds4a_compress_rows", "ds4a_rope_q", "ds4a_indexer_score_fp8", "ds4a_indexer_topk_fp8",
-            "ds4a_compress_append", "ds4a_push_raw", "ds4a_frontier_push", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
+            "ds4a_compress_append", "ds4a_push_raw", "ds4a_frontier_push", "ds4a_sparse_mqa_fp8",
+            "ds4a_dense_mqa_fp8", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -168,6 +169,37 @@ def test_mqa_validation(L):
     assert _mqa(L, ws=None, ws_bytes=0) == -5
     assert _mqa(L, ws_bytes=need - 1) == -5
     assert _mqa(L, U=1 << 16, T=1 << 9) == -2     # U*T above 2^24 (keeps every grid below 2^31)
+
+
+def test_mqa_fp8_validation(L):
+    def sp(**kw):
+        a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, K=512, q=A, q_dtype=0, q_pos=A, theta=10000.0,
+                 raw=A, comp=A, cs=A, idx=A, scale=0.044, out=A, ws=None, ws_bytes=0)
+        a.update(kw)
+        return L.ds4a_sparse_mqa_fp8(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["K"], a["q"],
+                                     a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["comp"], a["cs"], a["idx"],
+                                     a["scale"], a["out"], a["ws"], a["ws_bytes"], S)
+
+    assert sp(D=256) == -3
+    assert sp(comp=None) == -1 and "comp_kv8" in ops.last_error()
+    assert sp(cs=None) == -1 and "comp_scale" in ops.last_error()
+    assert sp(cs=MIS) == -4
+    assert sp(idx=None) == -1
+    assert sp() == -5                      # one query: the union is split, a workspace is needed
+
+    def de(**kw):
+        a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, q=A, q_dtype=0, q_pos=A, theta=10000.0,
+                 raw=A, comp=A, cs=A, n_vis=None, scale=0.044, out=A, ws=None, ws_bytes=0)
+        a.update(kw)
+        return L.ds4a_dense_mqa_fp8(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["q"], a["q_dtype"],
+                                    a["q_pos"], a["theta"], a["raw"], a["comp"], a["cs"], a["n_vis"], a["scale"],
+                                    a["out"], a["ws"], a["ws_bytes"], S)
+
+    assert de(cs=None) == -1 and "ds4a_dense_mqa_fp8" in ops.last_error()
+    assert de(N=-1) == -2
+    assert de() == -5
+    # the bf16 entry point still names its own argument
+    assert _mqa(L, comp=None) == -1 and "comp_kv " in ops.last_error() + " "
 
 
 def _dense(L, **kw):

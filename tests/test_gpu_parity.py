@@ -794,3 +794,80 @@ def test_decode_loop_cache_upkeep_matches_oracle():
     g = d_codes.cpu().numpy()
     mism = ((g != o_codes) & ~(((g & 0x7F) == 0) & ((o_codes & 0x7F) == 0))).sum()
     assert mism <= 3, mism                               # rounding-midpoint codes only
+
+
+# ------------------------------------------------ FP8-stored compressed rows (attention)
+
+def _fp8_comp(U, N, seed, pow2=True):
+    rng = np.random.default_rng(seed)
+    codes = gen.e4m3_codes(rng, (U, N, 512))
+    if pow2:
+        sc = np.ldexp(np.float32(1.0), rng.integers(-8, -5, (U, N))).astype(np.float32)
+    else:
+        sc = (rng.uniform(0.5, 2.0, (U, N)) * 2.0 ** -7).astype(np.float32)
+    c8 = torch.from_numpy(codes).cuda()
+    s8 = torch.from_numpy(sc).cuda()
+    return codes, sc, c8, s8
+
+
+def _given_sets(U, T, N, K, seed):
+    rng = np.random.default_rng(seed)
+    idx = np.stack([np.stack([np.sort(rng.choice(N, K, replace=False)) for _ in range(T)]) for _ in range(U)])
+    idx = idx.astype(np.int32)
+    idx[0, 0, 3] = -1
+    idx[0, 0, 5] = idx[0, 0, 6]
+    idx[-1, -1, -1] = N + 5
+    return idx
+
+
+@pytest.mark.parametrize("H,qd,W,K", [(64, "f32", 128, 512), (64, "bf16", 128, 512), (128, "f32", 128, 1024),
+                                      (32, "bf16", 0, 96), (16, "f32", 32, 40)])
+def test_mqa_fp8_rows_bit_identical_to_bf16(H, qd, W, K):
+    """E4M3 rows with power-of-two scales give the bf16 entry point's output on rows
+    code value * scale, bit for bit (sparse)."""
+    N = 3000
+    w, x = _mqa_case(H, qd, W, N, K, seed=5)
+    d = upload(x)
+    codes, sc, c8, s8 = _fp8_comp(w.U, N, seed=H + K)
+    kb = (c8.view(torch.float8_e4m3fn).to(torch.float32) * s8[..., None]).to(torch.bfloat16)
+    idx = torch.from_numpy(_given_sets(w.U, w.T, N, K, 11)).cuda()
+    ref = ops.sparse_mqa(d["q"], d["pos"], d["raw"], kb, idx, w.scale, W=W)
+    got = ops.sparse_mqa(d["q"], d["pos"], d["raw"], c8, idx, w.scale, W=W, comp_scale=s8)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("H,qd,W,N,T", [(64, "f32", 128, 2048, 1), (64, "bf16", 0, 500, 2), (32, "f32", 32, 0, 2),
+                                        (16, "bf16", 32, 4000, 3)])
+def test_dense_mqa_fp8_rows_bit_identical_to_bf16(H, qd, W, N, T):
+    w = gen.Workload("dfp8", 108, U=2, T=T, N=max(N, 1), H=H, K=1, W=W, q_dtype=qd, pos_base=777)
+    x = gen.make_config(w, seed=6)
+    d = upload(x)
+    codes, sc, c8, s8 = _fp8_comp(2, N, seed=N + H)
+    kb = (c8.view(torch.float8_e4m3fn).to(torch.float32) * s8[..., None]).to(torch.bfloat16)
+    nv = torch.tensor([[N] * T, [max(0, N // 2 - 1)] * T], dtype=torch.int32, device="cuda")
+    raw = d["raw"] if W > 0 else None
+    ref = ops.dense_mqa(d["q"], d["pos"], raw, kb, w.scale, W=W, n_vis=nv)
+    got = ops.dense_mqa(d["q"], d["pos"], raw, c8, w.scale, W=W, n_vis=nv, comp_scale=s8)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+
+
+@pytest.mark.parametrize("H,qd,W,K", [(64, "f32", 128, 512), (128, "bf16", 128, 1024)])
+def test_mqa_fp8_rows_match_oracle(H, qd, W, K):
+    """Arbitrary positive row scales against the oracle's FP8-row attention."""
+    N = 3000
+    w, x = _mqa_case(H, qd, W, N, K, seed=7)
+    d = upload(x)
+    codes, sc, c8, s8 = _fp8_comp(w.U, N, seed=3 * K, pow2=False)
+    idx = _given_sets(w.U, w.T, N, K, 12)
+    got = ops.sparse_mqa(d["q"], d["pos"], d["raw"], c8, torch.from_numpy(idx).cuda(), w.scale, W=W,
+                         comp_scale=s8).cpu().numpy()
+    for u in range(w.U):
+        for t in range(w.T):
+            ix = idx[u, t].copy()
+            ix[(ix < 0) | (ix >= N)] = -1
+            q = x["q"][u, t]
+            q64 = bf16_f64(q) if q.dtype == np.uint16 else q.astype(np.float64)
+            qr = orc.rope_q(q64, int(x["pos"][u, t]))
+            ref = orc.sparse_mqa_fp8(qr, x["raw"][u, t:t + W], codes[u], sc[u], ix, w.scale)
+            e = normwise_err(got[u, t], ref)
+            assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, e)
