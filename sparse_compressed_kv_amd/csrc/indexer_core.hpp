@@ -5,8 +5,7 @@
 //     s[j] = sum_h w[h] * max(0, <qI[h], kI[j]>)
 // The query's 64x128 bf16 block sits in VGPRs as MFMA B fragments; key rows stream from
 // HBM straight into A-operand registers.  Each wave takes 16*BPI consecutive rows per
-// iteration: BPI 16-row blocks, all loads issued before any is used, each row read as
-// 4 x 64-byte contiguous segments.  Per 16-row block: 4 head tiles x 4 k-steps = 16
+// iteration: BPI 16-row blocks in flight, the dims of a row in the k-step order of kdim.  Per 16-row block: 4 head tiles x 4 k-steps = 16
 // v_mfma_f32_16x16x32_bf16 with the keys as A, so D holds 4 rows x 1 head per lane; the fp32
 // ReLU + weighted head sum is 16 in-lane FMAs plus a 4-step DPP butterfly across the 16
 // lanes of a row.
@@ -33,7 +32,15 @@ __device__ __forceinline__ float relu(float x) {
     return __int_as_float(b > 0 ? b : 0);
 }
 
-// Query block of query q as B fragments aq[ht][s] = qI[16ht + c][32s + 8g .. +7], through an
+// The 128 dims of a key or query row, in the order the MFMA k-steps take them: k-step s of
+// lane group g holds dims kdim(s, g) .. +7, kdim(s, g) = 64(s >> 1) + 16g + 8(s & 1).  So a
+// lane's k-steps 0 and 1 (and 2 and 3) are 16 adjacent dims: one 16-byte load of E4M3 codes,
+// with the 4 lane groups of a row reading 64 adjacent bytes (a bf16 row is read as 16-byte
+// chunks, 2 per 32 adjacent bytes).  Any fixed order gives the same sum up to fp32 rounding;
+// using one order for both key formats keeps them bit-identical.
+__device__ __forceinline__ constexpr int kdim(int s, int g) { return 64 * (s >> 1) + 16 * g + 8 * (s & 1); }
+
+// Query block of query q as B fragments aq[ht][s] = qI[16ht + c][kdim(s, g) .. +7], through an
 // LDS copy whose 16-byte chunk k of head h sits at h*16 + (k ^ (h & 15)), so the 16 lanes
 // reading 16 heads at one k hit distinct banks.  Every thread of the workgroup calls it.
 template <int THREADS>
@@ -48,7 +55,7 @@ __device__ __forceinline__ void indexer_query_frags(const uint16_t *__restrict__
 #pragma unroll
     for (int ht = 0; ht < 4; ++ht)
 #pragma unroll
-        for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + ((4 * s + g) ^ c)]);
+        for (int s = 0; s < 4; ++s) aq[ht][s] = as_bf16x8(sq[(16 * ht + c) * kChunksPerRow + ((kdim(s, g) / 8) ^ c)]);
 }
 
 // Per-lane key registers of one 16-row block: 4 k-steps of 8 values, as bf16 (16 bytes each)
@@ -88,20 +95,25 @@ __device__ __forceinline__ KeyStream<FP8> key_stream(const KeyRows &ks, int64_t 
     return st;
 }
 
-// Keys of the 16-row block at local row `blk`: lane (g, c) takes dims 32s + 8g .. +7 (k-step s)
-// of row blk + c, i.e. 16-byte chunk (bf16) or 8-byte piece (E4M3) 4s + g of the row, so both
-// formats feed the same dims to the same MFMA slots; rows past the stream read as zero.
+// Keys of the 16-row block at local row `blk`: lane (g, c) takes dims kdim(s, g) .. +7 of row
+// blk + c for k-step s, so both formats feed the same dims to the same MFMA slots: two 16-byte
+// loads of 16 codes (k-steps 0-1 and 2-3) for E4M3 rows, four of 8 bf16 values for bf16 rows.
+// Rows past the stream read as zero.
 template <bool FP8>
 __device__ __forceinline__ void indexer_load_block(const KeyStream<FP8> &st, int blk, int g, int c,
                                                    KeyBlock<FP8> &kb) {
     const int off = (blk + c) * kKeyRowBytes<FP8>;
+    if constexpr (FP8) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        if constexpr (FP8) {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b64(st.k, off + (4 * s + g) * 8, 0, 0);
-            kb.v[s] = u32x2{v[0], v[1]};
-        } else {
-            const auto v = __builtin_amdgcn_raw_buffer_load_b128(st.k, off + (4 * s + g) * 16, 0, 0);
+        for (int j = 0; j < 2; ++j) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(st.k, off + kdim(2 * j, g), 0, 0);
+            kb.v[2 * j] = u32x2{v[0], v[1]};
+            kb.v[2 * j + 1] = u32x2{v[2], v[3]};
+        }
+    } else {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            const auto v = __builtin_amdgcn_raw_buffer_load_b128(st.k, off + 2 * kdim(s, g), 0, 0);
             kb.v[s] = u32x4{v[0], v[1], v[2], v[3]};
         }
     }
