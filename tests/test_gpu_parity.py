@@ -871,3 +871,35 @@ def test_mqa_fp8_rows_match_oracle(H, qd, W, K):
             ref = orc.sparse_mqa_fp8(qr, x["raw"][u, t:t + W], codes[u], sc[u], ix, w.scale)
             e = normwise_err(got[u, t], ref)
             assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, e)
+
+
+def test_e2e_fp8_caches_decode():
+    """A decode step over FP8 caches end to end (E4M3 indexer keys and compressed rows with
+    power-of-two row scales, as ds4a_compress_append stores them): ds4a_indexer_topk_fp8 then
+    ds4a_sparse_mqa_fp8 against the oracle's FP8 scores, top-k and FP8-row attention, with
+    12,000 of 20,000 rows visible and heavy rows."""
+    w = gen.Workload("e2e_fp8", 109, U=6, T=1, N=20000, H=64, K=512, heavy_frac=0.01, vis_base=12000)
+    x = gen.make_config(w, seed=8)
+    x8 = gen.make_indexer_fp8_config(w, seed=8)
+    codes, sc, c8, s8 = _fp8_comp(w.U, w.N, seed=19)
+    d = upload(x)
+    nv = d["n_vis"]
+    idx = ops.indexer_topk_fp8(d["idx_q"], d["idx_w"], torch.from_numpy(x8["idx_k8"]).cuda(),
+                               torch.from_numpy(x8["idx_k_scale"]).cuda(), w.K, n_vis=nv)
+    out = ops.sparse_mqa(d["q"], d["pos"], d["raw"], c8, idx, w.scale, w.theta, W=w.W, comp_scale=s8)
+    idx_h, out_h = idx.cpu().numpy(), out.cpu().numpy()
+    compared = 0
+    for u in range(w.U):
+        v = int(x["n_vis"][u, 0])
+        s = orc.indexer_score_fp8(x8["idx_q"][u, 0], x8["idx_w"][u, 0], x8["idx_k8"][u], x8["idx_k_scale"][u], n_vis=v)
+        ok, ndiff = tie_band_ok(idx_h[u, 0], orc.topk(s, w.K, n_vis=v), s)
+        assert ok, (u, ndiff)
+        ix = idx_h[u, 0].copy()
+        q = x["q"][u, 0]
+        q64 = bf16_f64(q) if q.dtype == np.uint16 else q.astype(np.float64)
+        qr = orc.rope_q(q64, int(x["pos"][u, 0]))
+        ref = orc.sparse_mqa_fp8(qr, x["raw"][u, 0:w.W], codes[u], sc[u], ix, w.scale)
+        e = normwise_err(out_h[u, 0], ref)
+        assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, e)
+        compared += 1
+    assert compared == w.U
