@@ -26,7 +26,7 @@ namespace {
 
 constexpr int kCThreads = 1024;
 constexpr int kCMaxWidth = 1024;
-constexpr int kCUnroll = 4;                   // frontier rows in flight per thread
+constexpr int kCUnroll = 8;                   // frontier rows in flight per thread (long frontiers)
 
 // max and sum over the workgroup (kCThreads threads); every thread gets the result.
 __device__ float block_sum(float v, float *red) {
@@ -94,10 +94,12 @@ __device__ __forceinline__ void fold(float s, float v, float &m, float &den, flo
 
 // One workgroup per unit.  Pooling: thread t takes 4 consecutive channels (column t % ncol,
 // one 16-byte load per frontier row and array) and every G-th frontier row from row t / ncol,
-// kCUnroll rows' loads in flight; the G partial (reference, weight sum, weighted sum) of a
+// UNROLL rows' loads in flight (1 when a thread has a single row, kCUnroll otherwise); the G
+// partial (reference, weight sum, weighted sum) of a
 // channel are merged through LDS.  `dst` says where the row goes (see RowDest in launch.hpp):
 // appends emit only for units whose token closes a group and write row n_rows[u] of the
 // unit's cache (when it is below cap), then count it.
+template <int UNROLL>
 __global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
     int width, int ratio, const float *__restrict__ state_kv, const float *__restrict__ state_score,
     const float *__restrict__ gain, float eps, int n_rot, const int64_t *__restrict__ row_pos, double log2_theta,
@@ -122,19 +124,22 @@ __global__ __launch_bounds__(kCThreads) void compress_rows_kernel(
     if (grp < G) {
         float m[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, den[4] = {0.f, 0.f, 0.f, 0.f};
         float num[4] = {0.f, 0.f, 0.f, 0.f};
-        for (int r0 = grp; r0 < ratio; r0 += kCUnroll * G) {
-            f32x4 a[kCUnroll], b[kCUnroll];
+        for (int r0 = grp; r0 < ratio; r0 += UNROLL * G) {
+            f32x4 a[UNROLL], b[UNROLL];
 #pragma unroll
-            for (int k = 0; k < kCUnroll; ++k) {
-                const int r = r0 + k * G < ratio ? r0 + k * G : r0;   // past the end: repeat r0, skipped below
+            for (int k = 0; k < UNROLL; ++k) {
+                const int r = r0 + k * G < ratio ? r0 + k * G : r0;   // past the end: repeat r0, masked below
                 a[k] = kv[(int64_t)r * ncol];
                 b[k] = sc[(int64_t)r * ncol];
             }
+            // Rows past the end fold as score -inf, an exact no-op (weight 0, the others times 1;
+            // row r0 is always real, so the reference is finite by then).  No branch: one would
+            // let the compiler issue each row's loads only when the row is folded.
 #pragma unroll
-            for (int k = 0; k < kCUnroll; ++k) {
-                if (r0 + k * G >= ratio) break;
+            for (int k = 0; k < UNROLL; ++k) {
+                const bool ok = r0 + k * G < ratio;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) fold(b[k][e], a[k][e], m[e], den[e], num[e]);
+                for (int e = 0; e < 4; ++e) fold(ok ? b[k][e] : -INFINITY, ok ? a[k][e] : 0.f, m[e], den[e], num[e]);
             }
         }
         s_part[0][threadIdx.x] = f32x4{m[0], m[1], m[2], m[3]};
@@ -206,8 +211,10 @@ hipError_t launch_compress(int U, int width, int ratio, const float *state_kv, c
                            const float *gain, float eps, int n_rot, const int64_t *row_pos, double theta,
                            const RowDest &dst, hipStream_t stream)
 {
-    hipLaunchKernelGGL(compress_rows_kernel, dim3((unsigned)U), dim3(kCThreads), 0, stream, width, ratio, state_kv,
-                       state_score, gain, eps, n_rot, row_pos, log2(theta), dst);
+    const int G = kCThreads / (width / 4) < ratio ? kCThreads / (width / 4) : ratio;
+    const auto kernel = ratio <= G ? compress_rows_kernel<1> : compress_rows_kernel<kCUnroll>;
+    hipLaunchKernelGGL(kernel, dim3((unsigned)U), dim3(kCThreads), 0, stream, width, ratio, state_kv, state_score,
+                       gain, eps, n_rot, row_pos, log2(theta), dst);
     return hipGetLastError();
 }
 

@@ -30,11 +30,11 @@
 // as an f16 pair for them and re-split as a bf16 pair for the compressed tiles.
 // LDS rows are 1056 bytes apart and their 16-byte chunks are XOR-swizzled by
 // row bit 2, which keeps both the row reads of QK and the transposed reads of
-// PV free of bank conflicts.  Loads run two tiles ahead through two register
-// stages (1 KiB of one row per wave instruction) into two LDS buffers; two
-// barriers per tile (logit halves, buffer turnover).  When the union is split over several workgroups each
-// writes (max, sum, unnormalised O) and a merge kernel combines them by
-// log-sum-exp.
+// PV free of bank conflicts.  Loads run three tiles ahead: two register stages
+// (one row per wave instruction) feed three LDS tile buffers, so one barrier per
+// tile (after the exchange of logit halves) also covers the buffer turnover.
+// When the union is split over several workgroups each writes (max, sum,
+// unnormalised O) and a merge kernel combines them by log-sum-exp.
 // Compressed rows stored as FP8 (E4M3 codes, 512 bytes, plus one f32 scale per row; the
 // compressor's output format) are widened to bf16 while they are staged, exactly, and their
 // scale is kept in the row's LDS padding: it multiplies the row's logit and, for the PV
