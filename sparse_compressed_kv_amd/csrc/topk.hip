@@ -30,6 +30,8 @@
 #include "launch.hpp"
 #include "select.hpp"
 
+#include <type_traits>
+
 namespace ds4a {
 
 namespace {
@@ -155,9 +157,21 @@ hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chu
         int32_t *ti = ids_a; ids_a = ids_b; ids_b = ti;
     }
     if (stride > kMergeMax) return hipErrorInvalidValue;
-    if (stride <= kLevelChunk)            // 16 candidates per thread suffice
-        hipLaunchKernelGGL(topk_cand_kernel<16>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride,
-                           kLevelChunk, (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
+    // The last level: one workgroup per query, with as few candidates per thread as the list
+    // needs (each select pass walks every thread's EPT keys).
+    const auto last = [&](auto ept_tag) {
+        constexpr int kEpt = decltype(ept_tag)::value;
+        hipLaunchKernelGGL(topk_cand_kernel<kEpt>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride,
+                           kEpt * kNT, (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
+    };
+    if (stride <= 4 * kNT)
+        last(std::integral_constant<int, 4>{});
+    else if (stride <= 8 * kNT)
+        last(std::integral_constant<int, 8>{});
+    else if (stride <= 12 * kNT)
+        last(std::integral_constant<int, 12>{});
+    else if (stride <= kLevelChunk)
+        last(std::integral_constant<int, 16>{});
     else
         hipLaunchKernelGGL(topk_cand_kernel<24>, dim3((unsigned)Q), dim3(kNT), 0, stream, N, K, lv, stride, kMergeMax,
                            (int64_t)1, keys_a, ids_a, n_vis, idx, (uint32_t *)nullptr);
