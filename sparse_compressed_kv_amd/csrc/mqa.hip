@@ -79,11 +79,6 @@ __device__ __forceinline__ int chunk_off(int r, int c) {
     return r * kRowStride + ((c ^ ((r >> 2) & 1)) << 4);
 }
 
-// Byte offset of element d (0..511) of tile row r.
-__device__ __forceinline__ int elem_off(int r, int d) {
-    return chunk_off(r, d >> 3) + ((d & 7) << 1);
-}
-
 struct MqaArgs {
     int T, H, W, K, n_hg, n_tiles, tiles_per_chunk, n_chunks;
     int64_t N, n_items;
