@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define DS4A_VERSION 1
+#define DS4A_VERSION 2
 
 typedef enum {
     DS4A_OK = 0,
@@ -145,7 +145,7 @@ int ds4a_indexer_topk_fp8(int U, int T, int64_t N, int Hi, int Di, int K,
  *   q'      = q[u][t][h] with dims D-n_rot+2i, D-n_rot+2i+1 rotated by the angle
  *             q_pos[u][t] * rope_theta^(-2i/n_rot)   (A3; stored rows are already
  *             rotated, so only the query is rotated here)
- *   union   = raw rows raw_kv[u][t + r], r = 0..W-1, then comp_kv[u][idx[u][t][k]]
+ *   union   = raw rows raw_kv[u][t + r], r = 0..W_t-1, then comp_kv[u][idx[u][t][k]]
  *             for every idx entry in [0, N) (no de-duplication)
  *   l_r     = scale * <q', row_r>                  (A4; each row is key and value)
  *   out     = sum_r softmax(l)_r * row_r           (A5, A6: one softmax over the union)
@@ -158,21 +158,24 @@ int ds4a_indexer_topk_fp8(int U, int T, int64_t N, int Hi, int Di, int K,
  *   q        : [U][T][H][D], q_dtype DS4A_F32 or DS4A_BF16 (pre-RoPE)
  *   q_pos    : int64 [U][T] absolute positions          rope_theta : > 0 (10000 in the tests)
  *   raw_kv   : f16 [U][T+W-1][D]   (query t uses rows t..t+W-1)
+ *   raw_vis  : int32 [U][T] or NULL: W_t = raw_vis[u][t] clamped to [0, W] raw rows take
+ *              part (a window that is not yet full at the start of a session: the first
+ *              rows of the window, as ds4a_push_raw fills it); NULL: W_t = W
  *   comp_kv  : bf16 [U][N][D]      idx : int32 [U][T][K] (from ds4a_topk_select)
  *   out      : f32 [U][T][H][D] (output)
  *   workspace: ds4a_workspace_bytes(1, U, T, N, K, H, W) bytes (0 -> NULL allowed)
  */
 int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K,
                     const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
-                    const void *raw_kv, const void *comp_kv, const int32_t *idx,
-                    float scale, float *out,
+                    const void *raw_kv, const int32_t *raw_vis, const void *comp_kv,
+                    const int32_t *idx, float scale, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
 /* Dense attention for the layers that have no indexer (section 3-2 of the same
  * page: ratio-128 layers fold 128 tokens into one row and are few enough to be
  * read whole; ratio-0 layers, the first two of Flash, keep only the raw window).
  * As ds4a_sparse_mqa, with the union
- *   union   = raw rows raw_kv[u][t + r], r = 0..W-1, then comp_kv[u][j] for every
+ *   union   = raw rows raw_kv[u][t + r], r = 0..W_t-1, then comp_kv[u][j] for every
  *             j < n_vis[u][t] (all N if n_vis is NULL), in row order
  * and the same arithmetic (same device code, chosen at compile time).
  *   N        : compressed rows per unit, 0..DS4A_MAX_DENSE_ROWS (0: raw window
@@ -184,8 +187,8 @@ int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int
  */
 int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
                    const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
-                   const void *raw_kv, const void *comp_kv, const int32_t *n_vis,
-                   float scale, float *out,
+                   const void *raw_kv, const int32_t *raw_vis, const void *comp_kv,
+                   const int32_t *n_vis, float scale, float *out,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* A3-A6 and the dense attention over compressed rows stored as FP8 (the compressor's output
@@ -202,13 +205,13 @@ int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
  */
 int ds4a_sparse_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K,
                         const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
-                        const void *raw_kv, const uint8_t *comp_kv8, const float *comp_scale,
-                        const int32_t *idx, float scale, float *out,
+                        const void *raw_kv, const int32_t *raw_vis, const uint8_t *comp_kv8,
+                        const float *comp_scale, const int32_t *idx, float scale, float *out,
                         void *workspace, size_t workspace_bytes, void *stream);
 int ds4a_dense_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N,
                        const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
-                       const void *raw_kv, const uint8_t *comp_kv8, const float *comp_scale,
-                       const int32_t *n_vis, float scale, float *out,
+                       const void *raw_kv, const int32_t *raw_vis, const uint8_t *comp_kv8,
+                       const float *comp_scale, const int32_t *n_vis, float scale, float *out,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /* Compressor row emission (section 3-2: tokens older than the raw window are folded,

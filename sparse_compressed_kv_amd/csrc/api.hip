@@ -217,15 +217,16 @@ namespace {
     } while (0)
 
 int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q,
-               int q_dtype, const int64_t *q_pos, double rope_theta, const void *raw_kv, const void *comp_kv,
-               const float *comp_scale, bool fp8, const int32_t *idx, float scale, float *out, void *workspace,
-               size_t workspace_bytes, void *stream) {
+               int q_dtype, const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+               const void *comp_kv, const float *comp_scale, bool fp8, const int32_t *idx, float scale, float *out,
+               void *workspace, size_t workspace_bytes, void *stream) {
     if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, W, N, K, q_dtype, rope_theta)) return rc;
     if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
         return fail(DS4A_E_SHAPE, "%s: scale must be finite", fn);
     REQUIRE_PTR(q);
     REQUIRE_PTR(q_pos);
     if (W > 0) REQUIRE_PTR(raw_kv);
+    OPTIONAL_PTR(raw_vis);
     REQUIRE_COMP(comp_kv, comp_scale, fp8);
     REQUIRE_PTR(idx);
     REQUIRE_PTR(out);
@@ -238,13 +239,14 @@ int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int
     }
     return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
                                            static_cast<const uint16_t *>(raw_kv), comp_kv, fp8 ? comp_scale : nullptr,
-                                           idx, nullptr, scale, out, workspace, static_cast<hipStream_t>(stream)));
+                                           idx, nullptr, raw_vis, scale, out, workspace,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,
-              const int64_t *q_pos, double rope_theta, const void *raw_kv, const void *comp_kv,
-              const float *comp_scale, bool fp8, const int32_t *n_vis, float scale, float *out, void *workspace,
-              size_t workspace_bytes, void *stream) {
+              const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+              const void *comp_kv, const float *comp_scale, bool fp8, const int32_t *n_vis, float scale, float *out,
+              void *workspace, size_t workspace_bytes, void *stream) {
     if (U < 1 || T < 1) return fail(DS4A_E_SHAPE, "%s: U=%d and T=%d must be >= 1", fn, U, T);
     if ((int64_t)U * T > (int64_t(1) << 24)) return fail(DS4A_E_SHAPE, "%s: U*T=%lld too large", fn, (long long)U * T);
     if (N < 0) return fail(DS4A_E_SHAPE, "%s: N=%lld must be >= 0", fn, (long long)N);
@@ -258,6 +260,7 @@ int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int6
     REQUIRE_PTR(q);
     REQUIRE_PTR(q_pos);
     if (W > 0) REQUIRE_PTR(raw_kv);
+    OPTIONAL_PTR(raw_vis);
     if (N > 0) REQUIRE_COMP(comp_kv, comp_scale, fp8);
     OPTIONAL_PTR(n_vis);
     REQUIRE_PTR(out);
@@ -274,41 +277,42 @@ int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int6
     }
     return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, (int)N, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
                                            static_cast<const uint16_t *>(raw_kv), comp_kv, fp8 ? comp_scale : nullptr,
-                                           nullptr, n_vis, scale, out, workspace, static_cast<hipStream_t>(stream)));
+                                           nullptr, n_vis, raw_vis, scale, out, workspace,
+                                           static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
 
 int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q, int q_dtype,
-                    const int64_t *q_pos, double rope_theta, const void *raw_kv, const void *comp_kv,
-                    const int32_t *idx, float scale, float *out, void *workspace, size_t workspace_bytes,
-                    void *stream) {
-    return sparse_mqa("ds4a_sparse_mqa", U, T, H, D, n_rot, W, N, K, q, q_dtype, q_pos, rope_theta, raw_kv, comp_kv,
-                      nullptr, false, idx, scale, out, workspace, workspace_bytes, stream);
+                    const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+                    const void *comp_kv, const int32_t *idx, float scale, float *out, void *workspace,
+                    size_t workspace_bytes, void *stream) {
+    return sparse_mqa("ds4a_sparse_mqa", U, T, H, D, n_rot, W, N, K, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis,
+                      comp_kv, nullptr, false, idx, scale, out, workspace, workspace_bytes, stream);
 }
 
 int ds4a_sparse_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q,
                         int q_dtype, const int64_t *q_pos, double rope_theta, const void *raw_kv,
-                        const uint8_t *comp_kv8, const float *comp_scale, const int32_t *idx, float scale,
-                        float *out, void *workspace, size_t workspace_bytes, void *stream) {
+                        const int32_t *raw_vis, const uint8_t *comp_kv8, const float *comp_scale, const int32_t *idx,
+                        float scale, float *out, void *workspace, size_t workspace_bytes, void *stream) {
     return sparse_mqa("ds4a_sparse_mqa_fp8", U, T, H, D, n_rot, W, N, K, q, q_dtype, q_pos, rope_theta, raw_kv,
-                      comp_kv8, comp_scale, true, idx, scale, out, workspace, workspace_bytes, stream);
+                      raw_vis, comp_kv8, comp_scale, true, idx, scale, out, workspace, workspace_bytes, stream);
 }
 
 int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,
-                   const int64_t *q_pos, double rope_theta, const void *raw_kv, const void *comp_kv,
-                   const int32_t *n_vis, float scale, float *out, void *workspace, size_t workspace_bytes,
-                   void *stream) {
-    return dense_mqa("ds4a_dense_mqa", U, T, H, D, n_rot, W, N, q, q_dtype, q_pos, rope_theta, raw_kv, comp_kv,
-                     nullptr, false, n_vis, scale, out, workspace, workspace_bytes, stream);
+                   const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+                   const void *comp_kv, const int32_t *n_vis, float scale, float *out, void *workspace,
+                   size_t workspace_bytes, void *stream) {
+    return dense_mqa("ds4a_dense_mqa", U, T, H, D, n_rot, W, N, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis,
+                     comp_kv, nullptr, false, n_vis, scale, out, workspace, workspace_bytes, stream);
 }
 
 int ds4a_dense_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,
-                       const int64_t *q_pos, double rope_theta, const void *raw_kv, const uint8_t *comp_kv8,
-                       const float *comp_scale, const int32_t *n_vis, float scale, float *out, void *workspace,
-                       size_t workspace_bytes, void *stream) {
-    return dense_mqa("ds4a_dense_mqa_fp8", U, T, H, D, n_rot, W, N, q, q_dtype, q_pos, rope_theta, raw_kv, comp_kv8,
-                     comp_scale, true, n_vis, scale, out, workspace, workspace_bytes, stream);
+                       const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+                       const uint8_t *comp_kv8, const float *comp_scale, const int32_t *n_vis, float scale,
+                       float *out, void *workspace, size_t workspace_bytes, void *stream) {
+    return dense_mqa("ds4a_dense_mqa_fp8", U, T, H, D, n_rot, W, N, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis,
+                     comp_kv8, comp_scale, true, n_vis, scale, out, workspace, workspace_bytes, stream);
 }
 
 int ds4a_compress_rows(int U, int width, int ratio, const float *state_kv, const float *state_score,

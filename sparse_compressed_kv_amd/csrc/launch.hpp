@@ -53,11 +53,12 @@ MqaPlan plan_mqa(int U, int T, int H, int W, int K);
 // idx == nullptr: dense attention, the union is the raw window plus compressed rows
 // 0 .. n_vis-1 (K must equal N; n_vis may be nullptr for all N).
 // comp: bf16 rows [U][N][512] (comp_scale == nullptr) or E4M3 codes [U][N][512] with f32 row
-// scales [U][N].
+// scales [U][N].  raw_vis: int32 [U][T] raw rows of each query's window that take part (rows
+// r < raw_vis, clamped to [0, W]), or nullptr for all W.
 hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                       const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
-                      const float *comp_scale, const int32_t *idx, const int32_t *n_vis, float scale, float *out,
-                      void *workspace, hipStream_t stream);
+                      const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                      float scale, float *out, void *workspace, hipStream_t stream);
 // Where an emitted compressed row goes.  format (DS4A_ROW_* in the public header): bf16
 // values, bf16 values after the FP8 round trip, or E4M3 codes (uint8) plus the row's scale.
 // The row of unit u is row n_rows[u] (0 if n_rows is null) of a cache whose units are

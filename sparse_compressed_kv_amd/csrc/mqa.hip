@@ -90,6 +90,7 @@ struct MqaArgs {
     const float *comp_scale;                 // E4M3 rows: f32 [U][N]
     const int32_t *idx;                      // sparse: [U][T][K]; dense: unused
     const int32_t *n_vis;                    // dense: visible compressed rows per query, or NULL (all N)
+    const int32_t *raw_vis;                  // raw rows of each query's window that take part, or NULL (all W)
     float scale;
     float *out;
     float *part;
@@ -222,10 +223,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         if (DENSE) return k;
         return idx_q[k < 0 ? 0 : (k < a.K ? k : a.K - 1)];
     };
+    // raw rows r < raw_lim of the window take part (a window that is not yet full)
+    const int raw_lim = a.raw_vis ? (int)clamp_nvis(a.raw_vis, q, a.W) : a.W;
     auto union_row = [&](int rho, int32_t j) __attribute__((always_inline)) -> int32_t {
         const int k = rho - a.W;
         const int32_t comp = (k < a.K && j >= 0 && (int64_t)j < j_lim) ? j : -1;
-        return rho >= tile1 * kTile ? -1 : (k < 0 ? -2 : comp);
+        return rho >= tile1 * kTile ? -1 : (k < 0 ? (rho < raw_lim ? -2 : -1) : comp);
     };
     // A row that takes no part (-1) is read from compressed row 0, or from raw row 0 when there
     // are no compressed rows (a raw-window-only call): it is finite, its logit is masked to
@@ -670,8 +673,8 @@ MqaPlan plan_mqa(int U, int T, int H, int W, int K) {
 
 hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                       const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
-                      const float *comp_scale, const int32_t *idx, const int32_t *n_vis, float scale, float *out,
-                      void *workspace, hipStream_t stream)
+                      const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                      float scale, float *out, void *workspace, hipStream_t stream)
 {
     const bool dense = idx == nullptr;       // dense: K = N, rows 0 .. n_vis-1 follow the raw window
     // E4M3 rows need at least one compressed row (the none rows of compressed tiles read row
@@ -700,6 +703,7 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
     a.n_items = (int64_t)U * T * p.n_chunks;
     a.q = q; a.q_bf16 = q_bf16; a.pos = q_pos; a.raw = raw; a.comp = comp; a.idx = idx; a.n_vis = n_vis;
     a.comp_scale = e8 ? comp_scale : nullptr;
+    a.raw_vis = W > 0 ? raw_vis : nullptr;
     a.scale = scale; a.out = out; a.part = static_cast<float *>(workspace);
     a.log2_theta = log2(theta);
     const int64_t blocks = a.n_items * p.n_hg;

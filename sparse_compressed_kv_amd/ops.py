@@ -59,14 +59,16 @@ def lib() -> ctypes.CDLL:
     L.ds4a_indexer_score_fp8.restype = i32
     L.ds4a_indexer_topk_fp8.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, P, P, sz, P]
     L.ds4a_indexer_topk_fp8.restype = i32
-    L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
+    L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt, P, P, sz,
+                                  P]
     L.ds4a_sparse_mqa.restype = i32
-    L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, flt, P, P, sz, P]
+    L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, P, flt, P, P, sz, P]
     L.ds4a_dense_mqa.restype = i32
-    L.ds4a_sparse_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt, P, P,
-                                      sz, P]
+    L.ds4a_sparse_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, P, flt, P,
+                                      P, sz, P]
     L.ds4a_sparse_mqa_fp8.restype = i32
-    L.ds4a_dense_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, P, flt, P, P, sz, P]
+    L.ds4a_dense_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, P, P, flt, P, P, sz,
+                                     P]
     L.ds4a_dense_mqa_fp8.restype = i32
     L.ds4a_compress_rows.argtypes = [i32, i32, i32, P, P, P, flt, i32, P, dbl, i32, P, i64, P]
     L.ds4a_compress_rows.restype = i32
@@ -255,11 +257,17 @@ def _comp_rows(comp_kv, comp_scale, U, N, D):
     return comp_kv, True
 
 
+def _raw_vis(raw_vis, U, T, W):
+    if raw_vis is None or W == 0:
+        return None
+    return _need(raw_vis, "raw_vis", torch.int32, (U, T))
+
+
 def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 10000.0, W: int = 128,
-               out=None, workspace=None, stream=None, comp_scale=None):
+               out=None, workspace=None, stream=None, comp_scale=None, raw_vis=None):
     """A3-A6.  q [U,T,H,512] f32|bf16, q_pos i64 [U,T], raw_kv f16 [U,T+W-1,512],
     comp_kv bf16 [U,N,512] (or E4M3 codes [U,N,512] with comp_scale f32 [U,N]),
-    idx i32 [U,T,K] -> f32 [U,T,H,512]."""
+    idx i32 [U,T,K], raw_vis i32 [U,T] (raw rows taking part) or None -> f32 [U,T,H,512]."""
     if not isinstance(q, torch.Tensor):
         raise TypeError("q must be a torch.Tensor")
     U, T, H, D = q.shape
@@ -277,19 +285,20 @@ def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 1000
     _need(out, "out", torch.float32, (U, T, H, D))
     ws, nb = _workspace(workspace_bytes(1, U, T, N, K, H, W), q.device, workspace)
     raw = _ptr(raw_kv) if W > 0 else None
+    rv = _ptr(_raw_vis(raw_vis, U, T, W))
     if fp8:
         _check("ds4a_sparse_mqa_fp8", lib().ds4a_sparse_mqa_fp8(
-            U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, _ptr(comp_kv), _ptr(comp_scale),
-            _ptr(idx), float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+            U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, _ptr(comp_kv),
+            _ptr(comp_scale), _ptr(idx), float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
     else:
         _check("ds4a_sparse_mqa", lib().ds4a_sparse_mqa(
-            U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, _ptr(comp_kv), _ptr(idx),
+            U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, _ptr(comp_kv), _ptr(idx),
             float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
     return out
 
 
 def dense_mqa(q, q_pos, raw_kv, comp_kv, scale: float, theta: float = 10000.0, W: int = 128, n_vis=None,
-              out=None, workspace=None, stream=None, comp_scale=None):
+              out=None, workspace=None, stream=None, comp_scale=None, raw_vis=None):
     """Dense attention (layers without an indexer).  q [U,T,H,512] f32|bf16, q_pos i64 [U,T],
     raw_kv f16 [U,T+W-1,512] (or None when W = 0), comp_kv bf16 [U,N,512] (N may be 0, or None;
     or E4M3 codes with comp_scale f32 [U,N]), n_vis i32 [U,T] or None -> f32 [U,T,H,512]."""
@@ -312,16 +321,17 @@ def dense_mqa(q, q_pos, raw_kv, comp_kv, scale: float, theta: float = 10000.0, W
     _need(out, "out", torch.float32, (U, T, H, D))
     ws, nb = _workspace(workspace_bytes(3, U, T, N, 0, H, W), q.device, workspace)
     raw = _ptr(raw_kv) if W > 0 else None
+    rv = _ptr(_raw_vis(raw_vis, U, T, W))
     comp = _ptr(comp_kv) if N > 0 else None
     nv = _ptr(n_vis) if n_vis is not None else None
     if fp8:
         _check("ds4a_dense_mqa_fp8", lib().ds4a_dense_mqa_fp8(
-            U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta), raw, comp,
+            U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, comp,
             _ptr(comp_scale) if N > 0 else None, nv, float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
     else:
         _check("ds4a_dense_mqa", lib().ds4a_dense_mqa(
-            U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta), raw, comp, nv, float(scale), _ptr(out),
-            _ptr(ws), nb, _stream(stream)))
+            U, T, H, D, 64, W, N, _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, comp, nv, float(scale),
+            _ptr(out), _ptr(ws), nb, _stream(stream)))
     return out
 
 

@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol(L):
 
 
 def test_version(L):
-    assert L.ds4a_version() == 1
+    assert L.ds4a_version() == 2
 
 
 def test_indexer_validation(L):
@@ -142,11 +142,11 @@ def test_cache_upkeep_validation(L):
 
 def _mqa(L, **kw):
     a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, K=512, q=A, q_dtype=0, q_pos=A, theta=10000.0,
-             raw=A, comp=A, idx=A, scale=0.044, out=A, ws=A, ws_bytes=1 << 30)
+             raw=A, raw_vis=None, comp=A, idx=A, scale=0.044, out=A, ws=A, ws_bytes=1 << 30)
     a.update(kw)
     return L.ds4a_sparse_mqa(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["K"], a["q"],
-                             a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["comp"], a["idx"], a["scale"],
-                             a["out"], a["ws"], a["ws_bytes"], S)
+                             a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["raw_vis"], a["comp"], a["idx"],
+                             a["scale"], a["out"], a["ws"], a["ws_bytes"], S)
 
 
 def test_mqa_validation(L):
@@ -163,6 +163,7 @@ def test_mqa_validation(L):
     assert _mqa(L, scale=float("nan")) == -2
     assert _mqa(L, q=None) == -1
     assert _mqa(L, comp=MIS) == -4
+    assert _mqa(L, raw_vis=MIS) == -4 and "raw_vis" in ops.last_error()
     assert _mqa(L, U=0) == -2
     need = ops.workspace_bytes(1, 1, 1, 1000, 512, 64, 128)
     assert need > 0                       # one query: the union is split over workgroups
@@ -174,26 +175,27 @@ def test_mqa_validation(L):
 def test_mqa_fp8_validation(L):
     def sp(**kw):
         a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, K=512, q=A, q_dtype=0, q_pos=A, theta=10000.0,
-                 raw=A, comp=A, cs=A, idx=A, scale=0.044, out=A, ws=None, ws_bytes=0)
+                 raw=A, raw_vis=None, comp=A, cs=A, idx=A, scale=0.044, out=A, ws=None, ws_bytes=0)
         a.update(kw)
         return L.ds4a_sparse_mqa_fp8(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["K"], a["q"],
-                                     a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["comp"], a["cs"], a["idx"],
-                                     a["scale"], a["out"], a["ws"], a["ws_bytes"], S)
+                                     a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["raw_vis"], a["comp"],
+                                     a["cs"], a["idx"], a["scale"], a["out"], a["ws"], a["ws_bytes"], S)
 
     assert sp(D=256) == -3
     assert sp(comp=None) == -1 and "comp_kv8" in ops.last_error()
     assert sp(cs=None) == -1 and "comp_scale" in ops.last_error()
     assert sp(cs=MIS) == -4
+    assert sp(raw_vis=MIS) == -4 and "raw_vis" in ops.last_error()
     assert sp(idx=None) == -1
     assert sp() == -5                      # one query: the union is split, a workspace is needed
 
     def de(**kw):
         a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, q=A, q_dtype=0, q_pos=A, theta=10000.0,
-                 raw=A, comp=A, cs=A, n_vis=None, scale=0.044, out=A, ws=None, ws_bytes=0)
+                 raw=A, raw_vis=None, comp=A, cs=A, n_vis=None, scale=0.044, out=A, ws=None, ws_bytes=0)
         a.update(kw)
         return L.ds4a_dense_mqa_fp8(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["q"], a["q_dtype"],
-                                    a["q_pos"], a["theta"], a["raw"], a["comp"], a["cs"], a["n_vis"], a["scale"],
-                                    a["out"], a["ws"], a["ws_bytes"], S)
+                                    a["q_pos"], a["theta"], a["raw"], a["raw_vis"], a["comp"], a["cs"], a["n_vis"],
+                                    a["scale"], a["out"], a["ws"], a["ws_bytes"], S)
 
     assert de(cs=None) == -1 and "ds4a_dense_mqa_fp8" in ops.last_error()
     assert de(N=-1) == -2
@@ -204,11 +206,11 @@ def test_mqa_fp8_validation(L):
 
 def _dense(L, **kw):
     a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, q=A, q_dtype=0, q_pos=A, theta=10000.0,
-             raw=A, comp=A, n_vis=None, scale=0.044, out=A, ws=A, ws_bytes=1 << 30)
+             raw=A, raw_vis=None, comp=A, n_vis=None, scale=0.044, out=A, ws=A, ws_bytes=1 << 30)
     a.update(kw)
     return L.ds4a_dense_mqa(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["q"], a["q_dtype"],
-                            a["q_pos"], a["theta"], a["raw"], a["comp"], a["n_vis"], a["scale"], a["out"], a["ws"],
-                            a["ws_bytes"], S)
+                            a["q_pos"], a["theta"], a["raw"], a["raw_vis"], a["comp"], a["n_vis"], a["scale"],
+                            a["out"], a["ws"], a["ws_bytes"], S)
 
 
 def test_dense_mqa_validation(L):
@@ -224,6 +226,7 @@ def test_dense_mqa_validation(L):
     assert _dense(L, comp=None) == -1                # N > 0 needs the rows
     assert _dense(L, raw=None) == -1                 # W > 0 needs the window
     assert _dense(L, n_vis=MIS) == -4
+    assert _dense(L, raw_vis=MIS) == -4 and "raw_vis" in ops.last_error()
     need = ops.workspace_bytes(3, 1, 1, 1000, 0, 64, 128)
     assert need > 0                                  # one query: split over workgroups
     assert _dense(L, ws=None, ws_bytes=0) == -5

@@ -512,6 +512,95 @@ def test_mqa_empty_union_is_zero():
     assert torch.count_nonzero(out).item() == 0
 
 
+# A window that is not yet full: raw_vis[u][t] raw rows take part (clamped to [0, W]); values
+# below 0, 0, 1, a tile's width and its neighbours, W - 1, W and above W.
+RAW_VIS = [[0, 1, 17, -5], [127, 128, 200, 64]]
+
+
+def _raw_ref(w, x, u, t, v, ix, codes=None, sc=None):
+    v = min(max(v, 0), w.W)
+    q = x["q"][u, t]
+    q64 = bf16_f64(q) if q.dtype == np.uint16 else q.astype(np.float64)
+    qr = orc.rope_q(q64, int(x["pos"][u, t]))
+    raw = x["raw"][u, t:t + v]
+    if codes is None:
+        return orc.sparse_mqa(qr, raw, x["comp"][u], ix, w.scale)
+    return orc.sparse_mqa_fp8(qr, raw, codes[u], sc[u], ix, w.scale)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16rows", "e4m3rows"])
+@pytest.mark.parametrize("qd", ["f32", "bf16"])
+def test_mqa_raw_vis_matches_oracle(qd, fp8):
+    """ds4a_sparse_mqa(_fp8) with raw_vis: only the first raw_vis rows of each query's window
+    enter the union, against the oracle on those rows."""
+    N, K = 3000, 512
+    w, x = _mqa_case(64, qd, 128, N, K, seed=13, U=2, T=4)
+    d = upload(x)
+    idx = _given_sets(w.U, w.T, N, K, 14)
+    idx[1, 2, :] = -1                      # raw rows only (every one of the window: 200 clamps to W)
+    rv = torch.tensor(RAW_VIS, dtype=torch.int32, device="cuda")
+    codes = sc = None
+    comp, cs = d["comp"], None
+    if fp8:
+        codes, sc, comp, cs = _fp8_comp(w.U, N, seed=15, pow2=False)
+    got = ops.sparse_mqa(d["q"], d["pos"], d["raw"], comp, torch.from_numpy(idx).cuda(), w.scale, W=w.W,
+                         comp_scale=cs, raw_vis=rv).cpu().numpy()
+    for u in range(w.U):
+        for t in range(w.T):
+            ix = idx[u, t].copy()
+            ix[(ix < 0) | (ix >= N)] = -1
+            ref = _raw_ref(w, x, u, t, RAW_VIS[u][t], ix, codes, sc)
+            e = normwise_err(got[u, t], ref)
+            assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, RAW_VIS[u][t], e)
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16rows", "e4m3rows"])
+def test_dense_mqa_raw_vis_matches_oracle(fp8):
+    """ds4a_dense_mqa(_fp8) with raw_vis and n_vis together (a session's first tokens: part of
+    the window and few compressed rows)."""
+    N = 700
+    w, x = _mqa_case(64, "bf16", 128, N, 1, seed=16, U=2, T=4)
+    d = upload(x)
+    nv = np.array([[0, 5, 700, 0], [699, 1, 350, 700]], dtype=np.int32)
+    rv = torch.tensor(RAW_VIS, dtype=torch.int32, device="cuda")
+    codes = sc = None
+    comp, cs = d["comp"], None
+    if fp8:
+        codes, sc, comp, cs = _fp8_comp(w.U, N, seed=17, pow2=False)
+    out = torch.full((w.U, w.T, 64, 512), float("nan"), device="cuda")
+    ops.dense_mqa(d["q"], d["pos"], d["raw"], comp, w.scale, W=w.W, n_vis=torch.from_numpy(nv).cuda(),
+                  comp_scale=cs, raw_vis=rv, out=out)
+    got = out.cpu().numpy()
+    for u in range(w.U):
+        for t in range(w.T):
+            v = RAW_VIS[u][t]
+            ref = _raw_ref(w, x, u, t, v, np.arange(nv[u, t], dtype=np.int32), codes, sc)
+            if min(max(v, 0), w.W) == 0 and nv[u, t] == 0:
+                assert not got[u, t].any(), (u, t)          # empty union: zeros
+                continue
+            e = normwise_err(got[u, t], ref)
+            assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, t, v, e)
+
+
+def test_raw_vis_full_window_is_null_and_fp8_bits_hold():
+    """raw_vis = W everywhere gives the NULL call's bits; with power-of-two row scales the FP8
+    entry point still gives the bf16 entry point's bits under a partial raw_vis."""
+    N, K = 2000, 512
+    w, x = _mqa_case(64, "f32", 128, N, K, seed=18, U=2, T=4)
+    d = upload(x)
+    idx = torch.from_numpy(_given_sets(w.U, w.T, N, K, 19)).cuda()
+    full = torch.full((w.U, w.T), w.W, dtype=torch.int32, device="cuda")
+    a = ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], idx, w.scale, W=w.W)
+    b = ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], idx, w.scale, W=w.W, raw_vis=full)
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    codes, sc, c8, s8 = _fp8_comp(w.U, N, seed=20)
+    kb = (c8.view(torch.float8_e4m3fn).to(torch.float32) * s8[..., None]).to(torch.bfloat16)
+    rv = torch.tensor(RAW_VIS, dtype=torch.int32, device="cuda")
+    ref = ops.sparse_mqa(d["q"], d["pos"], d["raw"], kb, idx, w.scale, W=w.W, raw_vis=rv)
+    got = ops.sparse_mqa(d["q"], d["pos"], d["raw"], c8, idx, w.scale, W=w.W, comp_scale=s8, raw_vis=rv)
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+
+
 # -------------------------------------------------------------- end to end
 
 def _run_step(w, d, nv=True, fused=False):
@@ -794,6 +883,35 @@ def test_decode_loop_cache_upkeep_matches_oracle():
     g = d_codes.cpu().numpy()
     mism = ((g != o_codes) & ~(((g & 0x7F) == 0) & ((o_codes & 0x7F) == 0))).sum()
     assert mism <= 3, mism                               # rounding-midpoint codes only
+
+
+def test_session_start_push_then_attend_with_raw_vis():
+    """A prompt's rows pushed into an empty window and into a nearly full one, then a decode
+    query over that window with raw_vis = the window's row count (the counter ds4a_push_raw
+    keeps, read by the attention call on the device), against the oracle's push and attention."""
+    N, K, W, T_new = 1000, 512, 128, 40
+    w, x = _mqa_case(64, "f32", W, N, K, seed=21, U=2, T=1)
+    d = upload(x)
+    rng = np.random.default_rng(22)
+    n0 = np.array([0, 100], dtype=np.int32)
+    raw0 = x["raw"].copy()                               # [U][W][512] f16 bits, rows past n0 stale
+    rkv = (rng.standard_normal((w.U, T_new, 512)) * 0.5).astype(np.float32)
+    d_raw = bits_to_torch(raw0, torch.float16)
+    d_n = torch.from_numpy(n0.copy()).cuda()
+    ops.push_raw(torch.from_numpy(rkv).cuda(), d_raw, d_n)
+    idx = _given_sets(w.U, 1, N, K, 23)
+    got = ops.sparse_mqa(d["q"], d["pos"], d_raw, d["comp"], torch.from_numpy(idx).cuda(), w.scale, W=W,
+                         raw_vis=d_n.view(w.U, 1)).cpu().numpy()
+    for u in range(w.U):
+        o_raw, o_n = orc.push_raw(raw0[u], int(n0[u]), rkv[u])
+        assert o_n == int(d_n[u].item()) == [40, 128][u]
+        ix = idx[u, 0].copy()
+        ix[(ix < 0) | (ix >= N)] = -1
+        q = x["q"][u, 0].astype(np.float64)
+        qr = orc.rope_q(q, int(x["pos"][u, 0]))
+        ref = orc.sparse_mqa(qr, o_raw[:o_n], x["comp"][u], ix, w.scale)
+        e = normwise_err(got[u, 0], ref)
+        assert e <= CONTRACT_ERR and e <= DESIGN_ERR, (u, e)
 
 
 # ------------------------------------------------ FP8-stored compressed rows (attention)
