@@ -458,8 +458,9 @@ class Step:
             topk_select(self.scores, self.K, n_vis=n_vis, out=self.idx, workspace=self.ws_topk, stream=stream)
         return self.idx
 
-    def __call__(self, x: dict, n_vis=None, scale=1.0 / 512 ** 0.5, theta=10000.0, stream=None):
+    def __call__(self, x: dict, n_vis=None, scale=1.0 / 512 ** 0.5, theta=10000.0, stream=None, raw_vis=None):
+        """raw_vis: int32 [U, T] raw-window rows that take part (a window not yet full), or None."""
         self.select(x, n_vis=n_vis, stream=stream)
         sparse_mqa(x["q"], x["pos"], x["raw"], x["comp"], self.idx, scale, theta, W=self.W, out=self.out,
-                   workspace=self.ws_mqa, stream=stream)
+                   workspace=self.ws_mqa, stream=stream, raw_vis=raw_vis)
         return self.out

@@ -885,6 +885,22 @@ def test_decode_loop_cache_upkeep_matches_oracle():
     assert mism <= 3, mism                               # rounding-midpoint codes only
 
 
+def test_step_raw_vis_passes_through():
+    """ops.Step with raw_vis = W everywhere gives the bits of the call without it; a partial
+    raw_vis changes the output (the argument reaches the attention call)."""
+    w = gen.Workload("stepvis", 110, U=2, T=1, N=3000, H=64, K=512, heavy_frac=0.01)
+    x = gen.make_config(w, seed=1)
+    d = upload(x)
+    step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=True)
+    a = step(d, scale=w.scale).clone()
+    full = torch.full((w.U, w.T), w.W, dtype=torch.int32, device="cuda")
+    b = step(d, scale=w.scale, raw_vis=full).clone()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
+    part = torch.tensor([[5], [w.W]], dtype=torch.int32, device="cuda")
+    c = step(d, scale=w.scale, raw_vis=part)
+    assert not torch.equal(c[0], a[0]) and torch.equal(c[1].view(torch.int32), a[1].view(torch.int32))
+
+
 def test_session_start_push_then_attend_with_raw_vis():
     """A prompt's rows pushed into an empty window and into a nearly full one, then a decode
     query over that window with raw_vis = the window's row count (the counter ds4a_push_raw
