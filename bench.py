@@ -789,7 +789,20 @@ def main():
             "kernel_us": {"indexer_topk": r3["select_ms"] * 1e3, "mqa": r3["mqa_ms"] * 1e3,
                           "indexer_alone": r3["indexer_ms"] * 1e3, "topk_alone": r3["topk_ms"] * 1e3},
         }
-        del b3, x3
+        del b3
+        # ---- the same prefill over E4M3 indexer keys and E4M3 attention rows (half the gathered
+        # bytes); flops as above
+        b38 = Bench(w3, x3, 2, fp8_keys=gen.make_indexer_fp8_config(w3), fp8_rows=True)
+        r38 = b38.run(steps3, max(2, args.warmup // 10))
+        log(f"[bench] {w3.name} fp8 keys + fp8 rows: {r38}")
+        tf8 = fl / (r38["ms_per_step"] / 1e3) / 1e12
+        rec["prefill_fp8_keys_rows"] = {
+            "workload": w3.name + "_fp8keys_fp8rows", "value": w3.T / (r38["ms_per_step"] / 1e3),
+            "unit": "query-tok/s", "steps": steps3, "ms_per_step": r38["ms_per_step"],
+            "frac_mfma": tf8 / MFMA_BF16_PEAK_TFLOPS,
+            "kernel_us": {"indexer_topk": r38["select_ms"] * 1e3, "mqa": r38["mqa_ms"] * 1e3},
+        }
+        del b38, x3
 
     if args.copy_probe > 0:
         n = args.copy_probe

@@ -338,8 +338,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     }
     __syncthreads();
 
-    auto load_tile = [&](int tt, u32x4 (&st)[kStage]) __attribute__((always_inline)) {
-        const bool raw_tile = tt < tile_raw;                 // uniform
+    auto load_tile = [&](int tt, u32x4 (&st)[kStage], bool raw_tile) __attribute__((always_inline)) {
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int rho = tt * kTile + wave + kWaves * i;
@@ -386,7 +385,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         else pack_q_frags<false>(qv, tail, d0, g, qhi, qlo);
     }
     store_tile(0, st0, tile0 < tile_raw);
-    load_tile(tile0 + 2, st0);
+    load_tile(tile0 + 2, st0, tile0 + 2 < tile_raw);
     // Waves w and w + 4 share a SIMD.  Between two barriers both would otherwise run the
     // same phases in lock-step (softmax on the VALU while the matrix core idles, then both
     // queue their MFMAs); a higher issue priority for waves 0-3 lets them run ahead, so one
@@ -404,8 +403,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         __attribute__((always_inline)) {
         constexpr bool F16 = decltype(f16_tag)::value;
         constexpr int kXb = decltype(xb_tag)::value;
-        store_tile(bnext, sv, tt + 1 < tile_raw);
-        load_tile(tt + 3, sv);
+        // Raw tiles come first in the union: after a compressed tile every tile is compressed,
+        // so in compressed steps the format of the tiles staged ahead is known at compile time.
+        store_tile(bnext, sv, F16 && tt + 1 < tile_raw);
+        load_tile(tt + 3, sv, F16 && tt + 3 < tile_raw);
         const unsigned char *tb = tiles + bcur * kTileBytes;
         f32x4 *xc = xch + kXb * (kXchBytes / 16);
 
