@@ -243,15 +243,25 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
                        : (v >= 0 ? comp_u + (int64_t)v * kCompRowBytes : (raw_tile ? none_raw : none_row));
     };
     // One staged row: lane = 16-byte chunk of a bf16 / f16 row; an E4M3 row arrives as 8 bytes
-    // per lane (x, y) plus its scale (z, every lane loads the same word), widened at the store.
+    // per lane (x, y), widened at the store.
     auto load_row = [&](int rho, int32_t v, bool raw_tile) __attribute__((always_inline)) -> u32x4 {
         const unsigned char *p = union_ptr(rho, v, raw_tile);
         if (E8 && !raw_tile) {
             const u32x2 x = reinterpret_cast<const u32x2 *>(p)[lane];
-            const float sc = cscale_u[v >= 0 ? v : 0];
-            return u32x4{x[0], x[1], __float_as_uint(sc), 0u};
+            return u32x4{x[0], x[1], 0u, 0u};
         }
         return reinterpret_cast<const u32x4 *>(p)[lane];
+    };
+    // E4M3 rows: the scales of a wave's kStage rows of a tile in one load, lane l holding that of
+    // row l % kStage (in z of the first staged row); v = the rows' union entries.
+    static_assert(kStage == 4, "one scale per lane group of four");
+    auto load_scales = [&](const int32_t (&v)[kStage], bool raw_tile, u32x4 (&st)[kStage])
+        __attribute__((always_inline)) {
+        if (E8 && !raw_tile) {
+            const int k = lane & (kStage - 1);
+            const int32_t vl = k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
+            st[0][2] = __float_as_uint(cscale_u[vl >= 0 ? vl : 0]);
+        }
     };
     // Set-up loads first, then the first two tiles' row gathers, then the set-up's use of its
     // loads: vector loads complete in issue order, so a gather issued before the set-up's own
@@ -306,12 +316,17 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         // The position arrives with these reads, not after the gathers (the compiler would
         // otherwise issue its load at its first use, behind them).
         asm volatile("" : : "s"(pos));
+        int32_t v0[kStage], v1[kStage];
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int r0 = tile0 * kTile + wave_u + kWaves * i, r1 = r0 + kTile;
-            st0[i] = load_row(r0, union_row(r0, j0[i]), tile0 < tile_raw);
-            st1[i] = load_row(r1, union_row(r1, j1[i]), tile0 + 1 < tile_raw);
+            v0[i] = union_row(r0, j0[i]);
+            v1[i] = union_row(r1, j1[i]);
+            st0[i] = load_row(r0, v0[i], tile0 < tile_raw);
+            st1[i] = load_row(r1, v1[i], tile0 + 1 < tile_raw);
         }
+        load_scales(v0, tile0 < tile_raw, st0);
+        load_scales(v1, tile0 + 1 < tile_raw, st1);
     }
     // (stored at the same clamped position, with no branch, so that the compiler does not move
     // the load down here, behind the gathers)
@@ -339,11 +354,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
     __syncthreads();
 
     auto load_tile = [&](int tt, u32x4 (&st)[kStage], bool raw_tile) __attribute__((always_inline)) {
+        int32_t v[kStage];
 #pragma unroll
         for (int i = 0; i < kStage; ++i) {
             const int rho = tt * kTile + wave + kWaves * i;
-            st[i] = load_row(rho, s_row[rho - rho0], raw_tile);
+            v[i] = s_row[rho - rho0];
+            st[i] = load_row(rho, v[i], raw_tile);
         }
+        load_scales(v, raw_tile, st);
     };
     // Every LDS address below is a per-lane base plus a compile-time offset: the swizzle bit
     // of the rows a lane touches does not depend on the unrolled index.
@@ -359,12 +377,11 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         unsigned char *base = tiles + buf * kTileBytes + st_base;
         if (E8 && !raw_tile) {
 #pragma unroll
-            for (int i = 0; i < kStage; ++i) {
+            for (int i = 0; i < kStage; ++i)
                 *reinterpret_cast<u32x4 *>(base + i * kWaves * kRowStride) = e4m3x8_to_bf16x8(u32x2{st[i][0], st[i][1]});
-                if (lane == 0)
-                    *reinterpret_cast<uint32_t *>(tiles + buf * kTileBytes + (wave + kWaves * i) * kRowStride + 2 * kD) =
-                        st[i][2];
-            }
+            if (lane < kStage)                     // lane l: the scale of row wave + 8l
+                *reinterpret_cast<uint32_t *>(tiles + buf * kTileBytes + (wave + kWaves * lane) * kRowStride + 2 * kD) =
+                    st[0][2];
         } else {
 #pragma unroll
             for (int i = 0; i < kStage; ++i)
