@@ -318,6 +318,18 @@ def replicas_for(w) -> int:
     return max(2, math.ceil(2 * LLC_BYTES / max(per, 1)) + 1)
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (empty if it cannot be read)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return ""
+
+
 def cpu_baseline(w, x, gpu=None, budget_s: float = 20.0):
     """The oracle, as it stands, on the host cores: whole decode units of the same workload.
     With `gpu` (host copies of the GPU's selection, output and scores for the same inputs), also
@@ -339,7 +351,8 @@ def cpu_baseline(w, x, gpu=None, budget_s: float = 20.0):
     el = time.perf_counter() - t0
     rec = {"value": n / el, "unit": "decode tokens/s/layer", "cores": min(cores, n), "kind": "oracle",
            "sample": f"{n} of {w.U} layer-units of {w.name} (full indexer, top-k and attention per unit), "
-                     f"1 pass, {el:.1f} s on {min(cores, n)} threads; 1-thread unit time {per_unit:.2f} s"}
+                     f"1 pass, {el:.1f} s on {min(cores, n)} threads; 1-thread unit time {per_unit:.2f} s",
+           "one_thread_units_per_s": 1.0 / per_unit, "cpu_model": cpu_model()}
     if gpu is not None:
         g_idx = gpu["idx"].reshape(w.U * w.T, w.K)[:n]
         g_out = gpu["out"].reshape(w.U * w.T, w.H, 512)[:n]
