@@ -659,7 +659,7 @@ def main():
     torch.cuda.set_device(0)
 
     # ---- main line: decode, 43 layers x 65,536 rows
-    w = gen.CONFIGS["c2_64k"]
+    w = gen.CONFIGS["decode_43layers_n65536"]
     t0 = time.perf_counter()
     x = gen.make_config(w)
     log(f"[bench] generated {w.name} in {time.perf_counter() - t0:.1f}s")
@@ -717,8 +717,9 @@ def main():
     if not args.only_main:
         # ---- decode at 16,384 and 32,768 rows (43 layers), long context (8 sessions x 262,144
         # rows) and the Pro shape (128 heads, top-1024)
-        for key, name in (("c2", "decode_n16384"), ("c2_32k", "decode_n32768"), ("c4", "decode_8sessions_n262144"),
-                          ("c5", "pro_decode_4sessions_n65536")):
+        for key, name in (("decode_43layers_n16384", "decode_n16384"), ("decode_43layers_n32768", "decode_n32768"),
+                          ("decode_8sessions_n262144", "decode_8sessions_n262144"),
+                          ("pro_decode_4sessions_n65536", "pro_decode_4sessions_n65536")):
             w4 = gen.CONFIGS[key]
             x4 = gen.make_config(w4)
             b4 = Bench(w4, x4, replicas_for(w4))
@@ -786,7 +787,7 @@ def main():
         log(f"[bench] {cu['workload']}: {cu}")
         rec["cache_upkeep"] = cu
         # ---- chunked prefill: 2,048 queries, 8,192 rows
-        w3 = gen.CONFIGS["c3"]
+        w3 = gen.CONFIGS["prefill_2048q_n8192"]
         x3 = gen.make_config(w3)
         b3 = Bench(w3, x3, 2)
         steps3 = max(5, args.steps // 10)

@@ -109,14 +109,14 @@ class Workload:
 
 # The five workloads of the benchmark plan, plus the 32K- and 64K-row decode points.
 CONFIGS: dict[str, Workload] = {
-    "c1": Workload("decode_1layer_n2048", 1, U=1, T=1, N=2048, pos_base=8191),
-    "c2": Workload("decode_43layers_n16384", 2, U=43, T=1, N=16384, heavy_frac=0.01),
-    "c2_32k": Workload("decode_43layers_n32768", 2, U=43, T=1, N=32768, heavy_frac=0.01),
-    "c2_64k": Workload("decode_43layers_n65536", 2, U=43, T=1, N=65536, heavy_frac=0.01),
-    "c3": Workload("prefill_2048q_n8192", 3, U=1, T=2048, N=8192, q_dtype="bf16",
+    "decode_1layer_n2048": Workload("decode_1layer_n2048", 1, U=1, T=1, N=2048, pos_base=8191),
+    "decode_43layers_n16384": Workload("decode_43layers_n16384", 2, U=43, T=1, N=16384, heavy_frac=0.01),
+    "decode_43layers_n32768": Workload("decode_43layers_n32768", 2, U=43, T=1, N=32768, heavy_frac=0.01),
+    "decode_43layers_n65536": Workload("decode_43layers_n65536", 2, U=43, T=1, N=65536, heavy_frac=0.01),
+    "prefill_2048q_n8192": Workload("prefill_2048q_n8192", 3, U=1, T=2048, N=8192, q_dtype="bf16",
                    vis_base=4096, pos_base=4096),
-    "c4": Workload("decode_8sessions_n262144", 4, U=8, T=1, N=262144),
-    "c5": Workload("pro_decode_4sessions_n65536", 5, U=4, T=1, N=65536, H=128, K=1024,
+    "decode_8sessions_n262144": Workload("decode_8sessions_n262144", 4, U=8, T=1, N=262144),
+    "pro_decode_4sessions_n65536": Workload("pro_decode_4sessions_n65536", 5, U=4, T=1, N=65536, H=128, K=1024,
                    heavy_frac=0.005),
 }
 

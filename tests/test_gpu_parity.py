@@ -643,15 +643,15 @@ def _check_e2e(w, x, step, sel, nthreads=8):
     return worst
 
 
-def test_e2e_c1_decode_1layer():
-    w = gen.CONFIGS["c1"]
+def test_e2e_decode_1layer_n2048():
+    w = gen.CONFIGS["decode_1layer_n2048"]
     x = gen.make_config(w)
     step = _run_step(w, upload(x))
     _check_e2e(w, x, step, sel=[0])
 
 
-def test_e2e_c2_decode_43layers_full_size_sampled():
-    w = gen.CONFIGS["c2"]
+def test_e2e_decode_43layers_n16384_full_size_sampled():
+    w = gen.CONFIGS["decode_43layers_n16384"]
     x = gen.make_config(w)
     d = upload(x)
     step = _run_step(w, d)
@@ -666,30 +666,30 @@ def test_e2e_c2_decode_43layers_full_size_sampled():
     assert torch.equal(fs.idx, i1) and torch.equal(fs.out, o1)
 
 
-def test_e2e_c2_64k_decode_fused():
+def test_e2e_decode_43layers_n65536_fused():
     """The bench's main workload through the fused path, checked against the oracle."""
-    w = gen.CONFIGS["c2_64k"]
+    w = gen.CONFIGS["decode_43layers_n65536"]
     x = gen.make_config(w)
     step = _run_step(w, upload(x), fused=True)
     _check_e2e(w, x, step, sel=[0, 42])
 
 
-def test_e2e_c3_prefill_full_size_sampled():
-    w = gen.CONFIGS["c3"]
+def test_e2e_prefill_2048q_n8192_full_size_sampled():
+    w = gen.CONFIGS["prefill_2048q_n8192"]
     x = gen.make_config(w)
     step = _run_step(w, upload(x))
     _check_e2e(w, x, step, sel=[0, 1, 77, 1023, 1500, 2047])
 
 
-def test_e2e_c4_long_context_full_size_sampled():
-    w = gen.CONFIGS["c4"]
+def test_e2e_decode_8sessions_n262144_full_size_sampled():
+    w = gen.CONFIGS["decode_8sessions_n262144"]
     x = gen.make_config(w)
     step = _run_step(w, upload(x), nv=False)
     _check_e2e(w, x, step, sel=[0, 7])
 
 
-def test_e2e_c5_pro_full_size_sampled():
-    w = gen.CONFIGS["c5"]
+def test_e2e_pro_decode_4sessions_n65536_full_size_sampled():
+    w = gen.CONFIGS["pro_decode_4sessions_n65536"]
     x = gen.make_config(w)
     step = _run_step(w, upload(x), nv=False)
     _check_e2e(w, x, step, sel=[1, 3])
