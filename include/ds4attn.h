@@ -115,7 +115,7 @@ int ds4a_indexer_topk(int U, int T, int64_t N, int Hi, int Di, int K,
 
 /* A1 and A1 + A2 on FP8-stored indexer keys.  The compressor that emits the
  * indexer's keys rounds each row to FP8 (section 3-2 of "Reading the architecture
- * of DwarfStar (ds4.c), part 4/8"; format as at ds4a_compress_rows: OCP E4M3FN with
+ * of DwarfStar (ds4.c), part 1/8"; format as at ds4a_compress_rows: OCP E4M3FN with
  * one power-of-two scale per row), so keeping the codes and the scale instead of
  * bf16 values loses nothing and halves the bytes the indexer streams per row
  * (256 -> 128, plus 4 for the scale).  As ds4a_indexer_score / ds4a_indexer_topk
@@ -192,7 +192,7 @@ int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N,
                    void *workspace, size_t workspace_bytes, void *stream);
 
 /* A3-A6 and the dense attention over compressed rows stored as FP8 (the compressor's output
- * format, section 3-2 of "Reading the architecture of DwarfStar (ds4.c), part 4/8"; the
+ * format, section 3-2 of "Reading the architecture of DwarfStar (ds4.c), part 1/8"; the
  * stored form of DS4A_ROW_E4M3 rows from ds4a_compress_append).  As ds4a_sparse_mqa /
  * ds4a_dense_mqa with comp_kv replaced by
  *   comp_kv8   : uint8 [U][N][512] E4M3FN codes (NaN codes not allowed)

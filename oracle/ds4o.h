@@ -70,7 +70,7 @@ int ds4o_sparse_mqa(int H, int D, int W, int K, const double *q_rot,
                     double scale, double *out);
 
 /* As ds4o_sparse_mqa, with the compressed rows stored as FP8 (the compressor's round trip,
- * "Reading the architecture of DwarfStar (ds4.c), part 4/8", section 3-2): row j is the
+ * "Reading the architecture of DwarfStar (ds4.c), part 1/8", section 3-2): row j is the
  * E4M3FN value of each code times comp_scale[j].  comp8: uint8 [*][D]; comp_scale: f32 [*]. */
 int ds4o_sparse_mqa_fp8(int H, int D, int W, int K, const double *q_rot,
                         const uint16_t *raw, const uint8_t *comp8, const float *comp_scale,
@@ -108,7 +108,7 @@ uint8_t ds4o_round_e4m3(double x);
 
 /* Indexer scores of one query over FP8-stored keys: the key of row j is the E4M3FN value
  * of each code times the row's scale (the compressor's round trip, "Reading the
- * architecture of DwarfStar (ds4.c), part 4/8", section 3-2), then as ds4o_indexer_score:
+ * architecture of DwarfStar (ds4.c), part 1/8", section 3-2), then as ds4o_indexer_score:
  *   s[j] = sum_h w[h] * max(0, sum_d qI[h][d] * e4m3(k8[j][d]) * scale[j])   for j < n_vis
  *   s[j] = -infinity                                                        for j >= n_vis
  * qI: bf16 [Hi][Di], w: f32 [Hi], k8: E4M3FN codes [N][Di], scale: f32 [N], s: double [N]. */
@@ -136,10 +136,11 @@ int ds4o_compress_row_e4m3(int width, int ratio, const float *state_kv, const fl
                            uint8_t *codes, double *scale);
 
 /* Raw sliding-window push ("Reading the architecture of DwarfStar (ds4.c), part 1/8",
- * section 3-1): the T rows kv f32 [T][D] enter a window of cap rows (f16 bit patterns
- * [cap][D] holding *n_raw rows) one after another.  While the window has room a row is
- * stored at row *n_raw, every value rounded to f16, and *n_raw grows; once it is full, the
- * rows slide down by one (row 0 leaves) and the new row is stored at row cap - 1. */
+ * section 3-1): the window keeps the most recent tokens, each value rounded to f16.  After
+ * T rows kv f32 [T][D] arrive in a window of cap rows (f16 bit patterns [cap][D] holding
+ * *n_raw rows, oldest first), it holds the last min(cap, *n_raw + T) rows of the sequence
+ * "current rows, then the new rows", oldest first, and *n_raw is that count; rows past it
+ * are untouched. */
 void ds4o_push_raw(int cap, int D, int T, const float *kv, uint16_t *raw, int32_t *n_raw);
 
 /* One token entering the compressor's frontier (the same page, section 3-2, steps 2 and

@@ -1,4 +1,6 @@
-"""The workloads use the attention shape constants the pages print (tests/golden/shape_constants.txt)."""
+"""The workloads use the attention shape constants of tests/golden/shape_constants.txt: the
+Flash column as the method page prints it, the Pro column partly printed there (heads,
+top-k) and otherwise taken from the Pro-sized decode workload, each value labelled."""
 import os
 
 from synth.inputs import CONFIGS
@@ -15,6 +17,15 @@ def load_golden():
     return table
 
 
+def load_pro_sources():
+    src = {}
+    for line in open(GOLDEN):
+        line = line.split("#", 1)[0].split()
+        if line:
+            src[line[0]] = line[3]
+    return src
+
+
 def test_workload_shapes_match_printed_constants():
     g = load_golden()
     for key, w in CONFIGS.items():
@@ -27,6 +38,14 @@ def test_workload_shapes_match_printed_constants():
         assert w.Di == g["n_indexer_head_dim"][col]
         assert w.K == g["n_indexer_top_k"][col]
     assert g["n_head_kv"] == (1, 1)
+
+
+def test_pro_column_provenance_is_labelled():
+    """Only the Pro head count and indexer top-k are printed by the page (section 2 of part
+    1/8); every other Pro value is labelled as the workload's."""
+    src = load_pro_sources()
+    assert set(src.values()) <= {"page", "workload"}
+    assert {k for k, v in src.items() if v == "page"} == {"n_head", "n_indexer_top_k"}
 
 
 def test_indexer_only_inputs_equal_full_inputs():
