@@ -467,21 +467,22 @@ int ds4o_compress_row(int width, int ratio, const float *state_kv, const float *
         free(y);
         return -1;
     }
-    /* softmax-weighted pooling over the frontier rows, per channel */
+    /* softmax-weighted pooling over the frontier rows, per channel: the weight of frontier
+     * row r is exp(s_r - LSE), LSE = log(sum_r exp(s_r)) taken about the largest score so
+     * that no exponential overflows; the weights sum to one (scores are finite). */
     for (int j = 0; j < width; j++) {
-        double m = -INFINITY;
-        for (int r = 0; r < ratio; r++) {
-            double s = (double)state_score[(int64_t)r * width + j];
-            if (s > m)
-                m = s;
-        }
-        double num = 0.0, den = 0.0;
-        for (int r = 0; r < ratio; r++) {
-            double wgt = exp((double)state_score[(int64_t)r * width + j] - m);
-            den += wgt;
-            num += wgt * (double)state_kv[(int64_t)r * width + j];
-        }
-        pooled[j] = den > 0.0 ? num / den : 0.0;
+        const float *sc = state_score + j, *kv = state_kv + j;
+        double top = (double)sc[0];
+        for (int r = 1; r < ratio; r++)
+            top = fmax(top, (double)sc[(int64_t)r * width]);
+        double mass = 0.0;
+        for (int r = 0; r < ratio; r++)
+            mass += exp((double)sc[(int64_t)r * width] - top);
+        const double lse = top + log(mass);
+        double mean = 0.0;
+        for (int r = 0; r < ratio; r++)
+            mean += exp((double)sc[(int64_t)r * width] - lse) * (double)kv[(int64_t)r * width];
+        pooled[j] = mean;
     }
     /* RMS normalisation */
     double ms = 0.0;
@@ -564,19 +565,22 @@ int ds4o_compress_row_e4m3(int width, int ratio, const float *state_kv, const fl
 
 void ds4o_push_raw(int cap, int D, int T, const float *kv, uint16_t *raw, int32_t *n_raw)
 {
-    for (int t = 0; t < T; t++) {
-        const float *row = kv + (int64_t)t * D;
-        uint16_t *dst;
-        if (*n_raw < cap) {
-            dst = raw + (int64_t)(*n_raw) * D;
-            (*n_raw)++;
-        } else {
-            memmove(raw, raw + D, sizeof(uint16_t) * (size_t)(cap - 1) * (size_t)D);
-            dst = raw + (int64_t)(cap - 1) * D;
-        }
+    /* The window after the push holds the last min(cap, n + T) rows of the sequence
+     * (its n current rows, then the T new rows rounded to f16): one computed slide. */
+    const int64_t n = *n_raw, total = n + T;
+    const int64_t keep = total < cap ? total : cap;
+    const int64_t first = total - keep;             /* sequence index of the window's row 0 */
+    uint16_t *win = malloc(sizeof(uint16_t) * (size_t)(keep > 0 ? keep : 1) * (size_t)D);
+    if (!win)
+        return;
+    for (int64_t i = 0; i < keep; i++) {
+        const int64_t s = first + i;
         for (int d = 0; d < D; d++)
-            dst[d] = ds4o_round_f16(row[d]);
+            win[i * D + d] = s < n ? raw[s * D + d] : ds4o_round_f16(kv[(s - n) * D + d]);
     }
+    memcpy(raw, win, sizeof(uint16_t) * (size_t)keep * (size_t)D);
+    free(win);
+    *n_raw = (int32_t)keep;
 }
 
 void ds4o_frontier_push(int width, int ratio, int64_t pos, const float *kv, const float *score,
