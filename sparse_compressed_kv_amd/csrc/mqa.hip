@@ -45,6 +45,7 @@
 #include "rope.hpp"
 
 #include <math.h>
+#include <mutex>
 #include <type_traits>
 
 namespace ds4a {
@@ -70,9 +71,15 @@ constexpr int kTileBufs = 3;                 // tile buffers in LDS: one barrier
 constexpr int kLdsBytes = kTileBufs * kTileBytes + 2 * kXchBytes + kQtBytes;   // + 4 bytes per union row (row table)
 constexpr int kPadTiles = 3;                 // row-table padding for the look-ahead loads past a chunk's end
 constexpr int kMaxTilesPerChunk = 96;         // LDS: kLdsBytes + 128 B per tile of row table <= 160 KiB
+constexpr int kMaxLdsBytes = kLdsBytes + 4 * kTile * (kMaxTilesPerChunk + kPadTiles);
+static_assert(kMaxLdsBytes <= 160 * 1024, "the largest chunk's LDS fits a CU");
 constexpr int kRowRegs = 2;            // row-table entries per thread loaded ahead of the first gathers
 constexpr int kRec = 2 * kHG + kHG * kD;      // partial record: m[64], l[64], O[64][512]
 constexpr float kRescale = 8.f;               // softmax reference moves when a logit exceeds it by this
+
+// The row that a union entry taking no part is read from: 1 KiB of zeros (a bf16 or f16 row,
+// or an E4M3 row of codes 0).
+__device__ __align__(16) const unsigned char g_zero_row[2 * kD] = {};
 
 // Byte offset of 16-byte chunk c (0..63) of tile row r, XOR-swizzled by row bit 2.
 __device__ __forceinline__ int chunk_off(int r, int c) {
@@ -230,17 +237,15 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         const int32_t comp = (k < a.K && j >= 0 && (int64_t)j < j_lim) ? j : -1;
         return rho >= tile1 * kTile ? -1 : (k < 0 ? (rho < raw_lim ? -2 : -1) : comp);
     };
-    // A row that takes no part (-1) is read from compressed row 0, or from raw row 0 when there
-    // are no compressed rows (a raw-window-only call): it is finite, its logit is masked to
-    // -inf and its probability is 0, so no branch guards the load.  With E4M3 rows a tile's
-    // format decides the load's width, so a none row of a raw tile is raw row 0 (raw tiles
-    // exist only when W > 0) and one of a compressed tile is compressed row 0 (N >= 1).
+    // A row that takes no part (-1) is read from a row of zeros in device memory (a pointer
+    // select, so no branch guards the load): its logit is masked to -inf, its probability is 0
+    // and its values are 0, so nothing the caller's buffers hold outside the union (an
+    // unwritten raw row past raw_vis, compressed row 0 before the first one is emitted) can
+    // reach the output, not even a NaN or an infinity through 0 * x.
     const unsigned char *raw_b = reinterpret_cast<const unsigned char *>(raw_q);
-    const unsigned char *none_row = (E8 ? false : a.N == 0) ? raw_b : comp_u;
-    const unsigned char *none_raw = E8 ? raw_b : none_row;
-    auto union_ptr = [&](int rho, int32_t v, bool raw_tile) __attribute__((always_inline)) -> const unsigned char * {
+    auto union_ptr = [&](int rho, int32_t v, bool) __attribute__((always_inline)) -> const unsigned char * {
         return v == -2 ? raw_b + (int64_t)rho * (2 * kD)
-                       : (v >= 0 ? comp_u + (int64_t)v * kCompRowBytes : (raw_tile ? none_raw : none_row));
+                       : (v >= 0 ? comp_u + (int64_t)v * kCompRowBytes : g_zero_row);
     };
     // One staged row: lane = 16-byte chunk of a bf16 / f16 row; an E4M3 row arrives as 8 bytes
     // per lane (x, y), widened at the store.
@@ -260,7 +265,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mqa_kernel(MqaArgs a)
         if (E8 && !raw_tile) {
             const int k = lane & (kStage - 1);
             const int32_t vl = k == 0 ? v[0] : (k == 1 ? v[1] : (k == 2 ? v[2] : v[3]));
-            st[0][2] = __float_as_uint(cscale_u[vl >= 0 ? vl : 0]);
+            st[0][2] = vl >= 0 ? __float_as_uint(cscale_u[vl]) : 0x3F800000u;   // none rows: scale 1
         }
     };
     // Set-up loads first, then the first two tiles' row gathers, then the set-up's use of its
@@ -706,14 +711,16 @@ hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *
                                   sparse_mqa_kernel<true, true, false>,  sparse_mqa_kernel<false, true, false>,
                                   sparse_mqa_kernel<true, false, true>,  sparse_mqa_kernel<false, false, true>,
                                   sparse_mqa_kernel<true, true, true>,   sparse_mqa_kernel<false, true, true>};
-    static int attr_bytes[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // Each variant's dynamic LDS limit is raised once, to the largest size any plan asks
+    // for, so concurrent calls from several host threads never race on it.
+    static std::once_flag attr_once[8];
+    static hipError_t attr_err[8];
     const Fn fn = kernels[variant];
-    if (lds > attr_bytes[variant]) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-        if (e != hipSuccess) return e;
-        attr_bytes[variant] = lds;
-    }
+    std::call_once(attr_once[variant], [&] {
+        attr_err[variant] = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize, kMaxLdsBytes);
+    });
+    if (attr_err[variant] != hipSuccess) return attr_err[variant];
     MqaArgs a = {};
     a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_tiles = p.n_tiles;
     a.tiles_per_chunk = p.tiles_per_chunk; a.n_chunks = p.n_chunks;
