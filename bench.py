@@ -402,10 +402,10 @@ def full_schedule(steps: int, warmup: int):
     r0 = [upload(x0) for _ in range(2)]
     st4 = ops.Step(w4.U, 1, w4.N, fused=True)
     out128 = torch.empty((w128.U, 1, 64, 512), dtype=torch.float32, device="cuda")
-    ws128 = torch.empty(max(ops.workspace_bytes(3, w128.U, 1, w128.N, 0, 64, 128), 1), dtype=torch.uint8,
+    ws128 = torch.zeros(max(ops.workspace_bytes(3, w128.U, 1, w128.N, 0, 64, 128), 1), dtype=torch.uint8,
                         device="cuda")
     out0 = torch.empty((w0.U, 1, 64, 512), dtype=torch.float32, device="cuda")
-    ws0 = torch.empty(max(ops.workspace_bytes(3, w0.U, 1, 0, 0, 64, 128), 1), dtype=torch.uint8, device="cuda")
+    ws0 = torch.zeros(max(ops.workspace_bytes(3, w0.U, 1, 0, 0, 64, 128), 1), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     scale, theta = w4.scale, w4.theta
 

@@ -61,6 +61,8 @@ typedef enum { DS4A_F32 = 0, DS4A_BF16 = 1, DS4A_F16 = 2 } ds4a_dtype;
 #define DS4A_MAX_TOPK 2048        /* K : 1..2048 (Flash 512, Pro 1024)          */
 #define DS4A_MAX_WINDOW 1024      /* W : a multiple of 32 up to 1024 (n_swa = 128) */
 #define DS4A_MAX_DENSE_ROWS (1 << 20) /* N of ds4a_dense_mqa: 0..2^20 compressed rows  */
+#define DS4A_MAX_ATTN_ROWS ((1 << 22) - 1) /* N of ds4a_sparse_mqa(_fp8): rows a unit's cache may hold
+                                            (4 GiB of bf16 rows, addressed with 32-bit offsets) */
 #define DS4A_MAX_COMPRESS_WIDTH 1024  /* width of ds4a_compress_rows (512 KV, 128 indexer)  */
 #define DS4A_MAX_COMPRESS_RATIO 1024  /* ratio of ds4a_compress_rows (4 or 128 in Flash)   */
 
@@ -161,9 +163,14 @@ int ds4a_indexer_topk_fp8(int U, int T, int64_t N, int Hi, int Di, int K,
  *   raw_vis  : int32 [U][T] or NULL: W_t = raw_vis[u][t] clamped to [0, W] raw rows take
  *              part (a window that is not yet full at the start of a session: the first
  *              rows of the window, as ds4a_push_raw fills it); NULL: W_t = W
- *   comp_kv  : bf16 [U][N][D]      idx : int32 [U][T][K] (from ds4a_topk_select)
+ *   comp_kv  : bf16 [U][N][D], 1 <= N <= DS4A_MAX_ATTN_ROWS
+ *   idx      : int32 [U][T][K] (from ds4a_topk_select)
  *   out      : f32 [U][T][H][D] (output)
- *   workspace: ds4a_workspace_bytes(1, U, T, N, K, H, W) bytes (0 -> NULL allowed)
+ *   workspace: ds4a_workspace_bytes(1, U, T, N, K, H, W) bytes (0 -> NULL allowed).  When
+ *              the union of each query is split over several workgroups (few queries per
+ *              call), the workspace begins with arrival counters: they must be zero before
+ *              a workspace's first use (allocate it zero-filled), and every call leaves
+ *              them zero again.  Calls that share a workspace must be ordered on one stream.
  */
 int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K,
                     const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,

@@ -96,14 +96,14 @@ size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, in
     if (which == 3) {                        // ds4a_dense_mqa: K ignored, N >= 0
         if (U < 1 || T < 1 || (int64_t)U * T > (int64_t(1) << 24) || N < 0 || N > DS4A_MAX_DENSE_ROWS) return 0;
         if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW || W + N < 1) return 0;
-        return ds4a::plan_mqa(U, T, H, W, (int)N).workspace_bytes;
+        return ds4a::plan_attn(U, T, H, W, (int)N).workspace_bytes;
     }
     if (U < 1 || T < 1 || N < 1 || N > kMaxRows || K < 1 || K > DS4A_MAX_TOPK) return 0;
     if (which == 0) return ds4a::topk_workspace_bytes((int64_t)U * T, N, K);
     if (which == 2) return ds4a::indexer_topk_workspace_bytes(U, T, N, K);
     if (which == 1) {
         if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW) return 0;
-        return ds4a::plan_mqa(U, T, H, W, K).workspace_bytes;
+        return ds4a::plan_attn(U, T, H, W, K).workspace_bytes;
     }
     return 0;
 }
@@ -223,6 +223,8 @@ int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int
     if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, W, N, K, q_dtype, rope_theta)) return rc;
     if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
         return fail(DS4A_E_SHAPE, "%s: scale must be finite", fn);
+    if (N > DS4A_MAX_ATTN_ROWS)
+        return fail(DS4A_E_UNSUPPORTED, "%s: N=%lld (at most %d rows per unit)", fn, (long long)N, DS4A_MAX_ATTN_ROWS);
     REQUIRE_PTR(q);
     REQUIRE_PTR(q_pos);
     if (W > 0) REQUIRE_PTR(raw_kv);
@@ -230,14 +232,14 @@ int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int
     REQUIRE_COMP(comp_kv, comp_scale, fp8);
     REQUIRE_PTR(idx);
     REQUIRE_PTR(out);
-    const size_t need = ds4a::plan_mqa(U, T, H, W, K).workspace_bytes;
+    const size_t need = ds4a::plan_attn(U, T, H, W, K).workspace_bytes;
     if (need) {
         if (!workspace || workspace_bytes < need)
             return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                         workspace ? workspace_bytes : (size_t)0);
         if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
     }
-    return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
+    return hip_status(fn, ds4a::launch_attn(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
                                            static_cast<const uint16_t *>(raw_kv), comp_kv, fp8 ? comp_scale : nullptr,
                                            idx, nullptr, raw_vis, scale, out, workspace,
                                            static_cast<hipStream_t>(stream)));
@@ -264,8 +266,8 @@ int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int6
     if (N > 0) REQUIRE_COMP(comp_kv, comp_scale, fp8);
     OPTIONAL_PTR(n_vis);
     REQUIRE_PTR(out);
-    const ds4a::MqaPlan plan = ds4a::plan_mqa(U, T, H, W, (int)N);
-    if ((int64_t)U * T * plan.n_chunks * plan.n_hg >= (int64_t(1) << 31))
+    const ds4a::AttnPlan plan = ds4a::plan_attn(U, T, H, W, (int)N);
+    if (plan.blocks >= (int64_t(1) << 31))
         return fail(DS4A_E_UNSUPPORTED, "%s: U*T=%lld queries over %lld rows is more than one launch holds", fn,
                     (long long)U * T, (long long)N);
     const size_t need = plan.workspace_bytes;
@@ -275,7 +277,7 @@ int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int6
                         workspace ? workspace_bytes : (size_t)0);
         if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
     }
-    return hip_status(fn, ds4a::launch_mqa(U, T, H, W, N, (int)N, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
+    return hip_status(fn, ds4a::launch_attn(U, T, H, W, N, (int)N, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
                                            static_cast<const uint16_t *>(raw_kv), comp_kv, fp8 ? comp_scale : nullptr,
                                            nullptr, n_vis, raw_vis, scale, out, workspace,
                                            static_cast<hipStream_t>(stream)));

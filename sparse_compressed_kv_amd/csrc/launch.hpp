@@ -42,23 +42,38 @@ hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *i
                                hipStream_t stream);
 
 // A3-A6
-struct MqaPlan {
-    int n_hg;              // head groups of 16
-    int n_tiles;           // union tiles of 32 rows
-    int tiles_per_chunk;
+// A3-A6.  Two kernels: attn.hip, workgroups of (query, 64-head group, union chunk), for many
+// queries; attn_dq.hip, workgroups of (query, 16-head group, union chunk) with the dims split
+// over the waves, for few.  comp: bf16 rows [U][N][512] (comp_scale == nullptr) or E4M3 codes
+// [U][N][512] with f32 row scales [U][N].  raw_vis: int32 [U][T] raw rows of each query's
+// window that take part (rows r < raw_vis, clamped to [0, W]), or nullptr for all W.  A split
+// union keeps per-(query, 16-head group) arrival counters at the start of the workspace, zero
+// before the first call and returned to zero by every call, then the records.
+struct AttnPlan {
+    bool dq = false;       // the 16-head kernel
+    int n_hg;              // head groups (of 64, or of 16 for the 16-head kernel)
+    int n_steps;           // union steps of 32 rows
+    int steps_per_chunk;
     int n_chunks;
+    size_t count_bytes;    // counters (0 when the union is not split)
     size_t workspace_bytes;
+    int64_t blocks;        // grid size (padded to whole rounds of the 8 XCDs)
 };
-MqaPlan plan_mqa(int U, int T, int H, int W, int K);
-// idx == nullptr: dense attention, the union is the raw window plus compressed rows
-// 0 .. n_vis-1 (K must equal N; n_vis may be nullptr for all N).
-// comp: bf16 rows [U][N][512] (comp_scale == nullptr) or E4M3 codes [U][N][512] with f32 row
-// scales [U][N].  raw_vis: int32 [U][T] raw rows of each query's window that take part (rows
-// r < raw_vis, clamped to [0, W]), or nullptr for all W.
-hipError_t launch_mqa(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
-                      const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
-                      const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
-                      float scale, float *out, void *workspace, hipStream_t stream);
+AttnPlan plan_attn(int U, int T, int H, int W, int K);        // chooses the kernel
+AttnPlan plan_attn_wide(int U, int T, int H, int W, int K);
+AttnPlan plan_attn_dq(int U, int T, int H, int W, int K);
+hipError_t launch_attn_wide(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
+                            const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                            const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                            float scale, float *out, void *workspace, hipStream_t stream);
+hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
+                          const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                          const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                          float scale, float *out, void *workspace, hipStream_t stream);
+hipError_t launch_attn(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
+                       const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                       const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                       float scale, float *out, void *workspace, hipStream_t stream);
 // Where an emitted compressed row goes.  format (DS4A_ROW_* in the public header): bf16
 // values, bf16 values after the FP8 round trip, or E4M3 codes (uint8) plus the row's scale.
 // The row of unit u is row n_rows[u] (0 if n_rows is null) of a cache whose units are

@@ -130,10 +130,12 @@ def workspace_bytes(which: int, U: int, T: int, N: int, K: int, H: int = 0, W: i
 
 
 def _workspace(nbytes: int, device, ws):
+    """A workspace of at least nbytes: the caller's, or a new zero-filled one (the attention
+    keeps counters at its start that must be zero before its first use; calls leave them zero)."""
     if nbytes == 0:
         return None, 0
     if ws is None:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=device)
     if ws.numel() * ws.element_size() < nbytes:
         raise ValueError(f"workspace needs {nbytes} bytes")
     return ws, ws.numel() * ws.element_size()
@@ -445,8 +447,8 @@ class Step:
         self.out = torch.empty((U, T, H, 512), dtype=torch.float32, device=dev)
         nb0 = workspace_bytes(2 if fused else 0, U, T, N, K)
         nb1 = workspace_bytes(1, U, T, N, K, H, W)
-        self.ws_topk = torch.empty(max(nb0, 1), dtype=torch.uint8, device=dev)
-        self.ws_mqa = torch.empty(max(nb1, 1), dtype=torch.uint8, device=dev)
+        self.ws_topk = torch.zeros(max(nb0, 1), dtype=torch.uint8, device=dev)
+        self.ws_mqa = torch.zeros(max(nb1, 1), dtype=torch.uint8, device=dev)   # counters start at zero
 
     def select(self, x: dict, n_vis=None, stream=None):
         """A1 + A2 into self.idx."""

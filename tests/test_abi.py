@@ -230,11 +230,15 @@ def test_dense_mqa_validation(L):
     need = ops.workspace_bytes(3, 1, 1, 1000, 0, 64, 128)
     assert need > 0                                  # one query: split over workgroups
     assert _dense(L, ws=None, ws_bytes=0) == -5
-    assert _dense(L, N=0, comp=None, ws=None, ws_bytes=0) == -5   # raw only: comp may be NULL
+    assert _mqa(L, N=(1 << 22)) == -3                # 32-bit row offsets: at most 2^22 - 1 rows
+    # one query, raw window only (8 steps of 16 rows): split over 2 workgroups
+    assert ops.workspace_bytes(3, 1, 1, 0, 0, 64, 128) > 0
+    assert ops.workspace_bytes(3, 4, 1, 3000, 0, 128, 128) > 0     # 4 Pro queries: split
     assert ops.workspace_bytes(3, 1, 1, 0, 0, 64, 0) == 0          # nothing to attend
     assert ops.workspace_bytes(3, 1, 1, -1, 0, 64, 128) == 0
     assert ops.workspace_bytes(3, 300, 1, 0, 0, 64, 128) == 0      # enough queries: no split
-    assert ops.workspace_bytes(3, 1, 300, 4000, 0, 16, 32) > 0     # 127 tiles > 96 per chunk: split
+    assert ops.workspace_bytes(3, 1, 300, 3000, 0, 16, 32) == 0    # 190 steps: one chunk
+    assert ops.workspace_bytes(3, 1, 300, 3100, 0, 16, 32) > 0     # 196 steps > 192 per chunk: split
 
 
 def _compress(L, **kw):
