@@ -178,6 +178,26 @@ int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int
                     const int32_t *idx, float scale, float *out,
                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* ds4a_sparse_mqa for callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same call with no workspace argument.
+ * Where a split union needs counters and records, they live in the library's own scratch,
+ * a static device array of DS4A_SCRATCH_BYTES per GPU (the first DS4A_SCRATCH_COUNT_BYTES
+ * hold the counters: zero when the library loads, left zero by every call), held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no library allocation); its first
+ * call on a device looks the array's address up once.  A call whose split needs more
+ * counters or records than the scratch holds returns DS4A_E_WORKSPACE (decode, Pro decode
+ * and long-context session shapes fit many times over).  Every call on one GPU shares that
+ * GPU's scratch: calls that may overlap on one GPU (different streams, or host threads
+ * without ordering) race; order them on one stream.  Arguments, results and other errors as
+ * for ds4a_sparse_mqa.
+ */
+#define DS4A_SCRATCH_BYTES (16u << 20)
+#define DS4A_SCRATCH_COUNT_BYTES (64u << 10)
+int ds4a_sparse_mqa_noalloc(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K,
+                            const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                            const void *raw_kv, const int32_t *raw_vis, const void *comp_kv,
+                            const int32_t *idx, float scale, float *out, void *stream);
+
 /* Dense attention for the layers that have no indexer (section 3-2 of the same
  * page: ratio-128 layers fold 128 tokens into one row and are few enough to be
  * read whole; ratio-0 layers, the first two of Flash, keep only the raw window).

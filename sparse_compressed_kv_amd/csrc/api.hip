@@ -12,6 +12,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 namespace {
 
 thread_local char g_err[512];
@@ -117,7 +119,7 @@ namespace {
         if (fp8) REQUIRE_PTR_AS((keys).scale, "idx_k_scale");                       \
     } while (0)
 
-int indexer_score(const char *fn, int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
+static int indexer_score(const char *fn, int U, int T, int64_t N, int Hi, int Di, const void *idx_q, const float *idx_w,
                   ds4a::KeyRows idx_k, bool fp8, const int32_t *n_vis, float *scores, void *stream) {
     if (int rc = check_units(fn, U, T, N)) return rc;
     if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
@@ -132,7 +134,7 @@ int indexer_score(const char *fn, int U, int T, int64_t N, int Hi, int Di, const
                                                scores, static_cast<hipStream_t>(stream)));
 }
 
-int indexer_topk(const char *fn, int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q,
+static int indexer_topk(const char *fn, int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q,
                  const float *idx_w, ds4a::KeyRows idx_k, bool fp8, const int32_t *n_vis, int32_t *idx,
                  void *workspace, size_t workspace_bytes, void *stream) {
     if (int rc = check_units(fn, U, T, N)) return rc;
@@ -216,10 +218,36 @@ namespace {
         if (fp8) REQUIRE_PTR_AS(comp_scale, "comp_scale");                          \
     } while (0)
 
-int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q,
+// The allocation-free attention's scratch: counters at the start (zero when the code object
+// loads, left zero by every call), records after them.  Each device holds its own copy; host
+// code uses the device address looked up per device, never the symbol itself.
+static __device__ __align__(256) unsigned char scratch[DS4A_SCRATCH_BYTES];
+
+// scratch's address on the current device (looked up once per device).
+static hipError_t scratch_on_device(unsigned char **out) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static unsigned char *addr[kMaxDevices];
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<unsigned char *>(p);
+    }
+    *out = addr[dev];
+    return hipSuccess;
+}
+
+// noalloc: the workspace is the library's scratch (workspace and workspace_bytes unused).
+static int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q,
                int q_dtype, const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
                const void *comp_kv, const float *comp_scale, bool fp8, const int32_t *idx, float scale, float *out,
-               void *workspace, size_t workspace_bytes, void *stream) {
+               void *workspace, size_t workspace_bytes, void *stream, bool noalloc = false) {
     if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, W, N, K, q_dtype, rope_theta)) return rc;
     if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
         return fail(DS4A_E_SHAPE, "%s: scale must be finite", fn);
@@ -232,7 +260,24 @@ int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int
     REQUIRE_COMP(comp_kv, comp_scale, fp8);
     REQUIRE_PTR(idx);
     REQUIRE_PTR(out);
-    const size_t need = ds4a::plan_attn(U, T, H, W, K).workspace_bytes;
+    const ds4a::AttnPlan plan = ds4a::plan_attn(U, T, H, W, K);
+    if (noalloc) {
+        const size_t records = plan.workspace_bytes - plan.count_bytes;
+        if (plan.count_bytes > DS4A_SCRATCH_COUNT_BYTES || records > DS4A_SCRATCH_BYTES - DS4A_SCRATCH_COUNT_BYTES)
+            return fail(DS4A_E_WORKSPACE,
+                        "%s: this call needs %zu bytes of counters and %zu of records; the library's scratch "
+                        "holds %u and %u", fn, plan.count_bytes, records, (unsigned)DS4A_SCRATCH_COUNT_BYTES,
+                        (unsigned)(DS4A_SCRATCH_BYTES - DS4A_SCRATCH_COUNT_BYTES));
+        unsigned char *base = nullptr;
+        if (hipError_t e = scratch_on_device(&base); e != hipSuccess) return hip_status(fn, e);
+        return hip_status(fn, ds4a::launch_attn_parts(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta,
+                                                      static_cast<const uint16_t *>(raw_kv), comp_kv,
+                                                      fp8 ? comp_scale : nullptr, idx, nullptr, raw_vis, scale, out,
+                                                      reinterpret_cast<uint32_t *>(base),
+                                                      reinterpret_cast<float *>(base + DS4A_SCRATCH_COUNT_BYTES),
+                                                      static_cast<hipStream_t>(stream)));
+    }
+    const size_t need = plan.workspace_bytes;
     if (need) {
         if (!workspace || workspace_bytes < need)
             return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
@@ -245,7 +290,7 @@ int sparse_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int
                                            static_cast<hipStream_t>(stream)));
 }
 
-int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,
+static int dense_mqa(const char *fn, int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,
               const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
               const void *comp_kv, const float *comp_scale, bool fp8, const int32_t *n_vis, float scale, float *out,
               void *workspace, size_t workspace_bytes, void *stream) {
@@ -291,6 +336,14 @@ int ds4a_sparse_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, int
                     size_t workspace_bytes, void *stream) {
     return sparse_mqa("ds4a_sparse_mqa", U, T, H, D, n_rot, W, N, K, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis,
                       comp_kv, nullptr, false, idx, scale, out, workspace, workspace_bytes, stream);
+}
+
+int ds4a_sparse_mqa_noalloc(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q,
+                            int q_dtype, const int64_t *q_pos, double rope_theta, const void *raw_kv,
+                            const int32_t *raw_vis, const void *comp_kv, const int32_t *idx, float scale, float *out,
+                            void *stream) {
+    return sparse_mqa("ds4a_sparse_mqa_noalloc", U, T, H, D, n_rot, W, N, K, q, q_dtype, q_pos, rope_theta, raw_kv,
+                      raw_vis, comp_kv, nullptr, false, idx, scale, out, nullptr, 0, stream, true);
 }
 
 int ds4a_sparse_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N, int K, const void *q,

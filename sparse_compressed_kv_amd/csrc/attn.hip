@@ -632,17 +632,32 @@ hipError_t launch_attn(int U, int T, int H, int W, int64_t N, int K, const void 
                        float scale, float *out, void *workspace, hipStream_t stream)
 {
     const AttnPlan p = plan_attn(U, T, H, W, K);
+    uint32_t *count = static_cast<uint32_t *>(workspace);
+    float *part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.count_bytes);
     if (p.dq)
         return launch_attn_dq(p, U, T, H, W, N, K, q, q_bf16, q_pos, theta, raw, comp, comp_scale, idx, n_vis,
-                              raw_vis, scale, out, workspace, stream);
+                              raw_vis, scale, out, count, part, stream);
     return launch_attn_wide(p, U, T, H, W, N, K, q, q_bf16, q_pos, theta, raw, comp, comp_scale, idx, n_vis,
-                            raw_vis, scale, out, workspace, stream);
+                            raw_vis, scale, out, count, part, stream);
+}
+
+hipError_t launch_attn_parts(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
+                             const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                             const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                             float scale, float *out, uint32_t *count, float *part, hipStream_t stream)
+{
+    const AttnPlan p = plan_attn(U, T, H, W, K);
+    if (p.dq)
+        return launch_attn_dq(p, U, T, H, W, N, K, q, q_bf16, q_pos, theta, raw, comp, comp_scale, idx, n_vis,
+                              raw_vis, scale, out, count, part, stream);
+    return launch_attn_wide(p, U, T, H, W, N, K, q, q_bf16, q_pos, theta, raw, comp, comp_scale, idx, n_vis,
+                            raw_vis, scale, out, count, part, stream);
 }
 
 hipError_t launch_attn_wide(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                             const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                             const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
-                            float scale, float *out, void *workspace, hipStream_t stream)
+                            float scale, float *out, uint32_t *count, float *part, hipStream_t stream)
 {
     const bool dense = idx == nullptr;
     const bool e8 = comp_scale != nullptr && N > 0;
@@ -673,8 +688,8 @@ hipError_t launch_attn_wide(const AttnPlan &p, int U, int T, int H, int W, int64
     a.comp_scale = e8 ? comp_scale : nullptr;
     a.raw_vis = W > 0 ? raw_vis : nullptr;
     a.scale = scale; a.out = out;
-    a.count = static_cast<uint32_t *>(workspace);
-    a.part = reinterpret_cast<float *>(static_cast<char *>(workspace) + p.count_bytes);
+    a.count = count;
+    a.part = part;
     a.log2_theta = log2(theta);
     hipLaunchKernelGGL(fn, dim3((unsigned)p.blocks), dim3(kAT), lds, stream, a);
     return hipGetLastError();

@@ -65,11 +65,17 @@ AttnPlan plan_attn_dq(int U, int T, int H, int W, int K);
 hipError_t launch_attn_wide(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                             const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                             const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
-                            float scale, float *out, void *workspace, hipStream_t stream);
+                            float scale, float *out, uint32_t *count, float *part, hipStream_t stream);
 hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                           const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                           const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
-                          float scale, float *out, void *workspace, hipStream_t stream);
+                          float scale, float *out, uint32_t *count, float *part, hipStream_t stream);
+// As launch_attn with the counters and the records given apart (count: plan.count_bytes,
+// zero before the call and left zero; part: plan.workspace_bytes - plan.count_bytes).
+hipError_t launch_attn_parts(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
+                             const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                             const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
+                             float scale, float *out, uint32_t *count, float *part, hipStream_t stream);
 hipError_t launch_attn(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,
                        const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                        const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,

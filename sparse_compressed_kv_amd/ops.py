@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
     L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt, P, P, sz,
                                   P]
     L.ds4a_sparse_mqa.restype = i32
+    L.ds4a_sparse_mqa_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt,
+                                          P, P]
+    L.ds4a_sparse_mqa_noalloc.restype = i32
     L.ds4a_dense_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, P, i32, P, dbl, P, P, P, P, flt, P, P, sz, P]
     L.ds4a_dense_mqa.restype = i32
     L.ds4a_sparse_mqa_fp8.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, P, flt, P,
@@ -296,6 +299,33 @@ def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 1000
         _check("ds4a_sparse_mqa", lib().ds4a_sparse_mqa(
             U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, _ptr(comp_kv), _ptr(idx),
             float(scale), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    return out
+
+
+def sparse_mqa_noalloc(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 10000.0, W: int = 128,
+                       out=None, stream=None, raw_vis=None):
+    """sparse_mqa without a workspace: split unions use the library's own device scratch
+    (ds4a_sparse_mqa_noalloc; bf16 rows).  Calls that may overlap on one GPU race on it."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    U, T, H, D = q.shape
+    N = comp_kv.shape[1]
+    K = idx.shape[2]
+    _need(q, "q", q.dtype)
+    qd = _q_dtype(q)
+    _need(q_pos, "q_pos", torch.int64, (U, T))
+    if W > 0:
+        _need(raw_kv, "raw_kv", torch.float16, (U, T + W - 1, D))
+    _need(comp_kv, "comp_kv", torch.bfloat16, (U, N, D))
+    _need(idx, "idx", torch.int32, (U, T, K))
+    if out is None:
+        out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (U, T, H, D))
+    raw = _ptr(raw_kv) if W > 0 else None
+    rv = _ptr(_raw_vis(raw_vis, U, T, W))
+    _check("ds4a_sparse_mqa_noalloc", lib().ds4a_sparse_mqa_noalloc(
+        U, T, H, D, 64, W, N, K, _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, _ptr(comp_kv), _ptr(idx),
+        float(scale), _ptr(out), _stream(stream)))
     return out
 
 

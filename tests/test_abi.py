@@ -172,6 +172,27 @@ def test_mqa_validation(L):
     assert _mqa(L, U=1 << 16, T=1 << 9) == -2     # U*T above 2^24 (keeps every grid below 2^31)
 
 
+def test_mqa_noalloc_validation(L):
+    """The allocation-free attention validates as ds4a_sparse_mqa and refuses, before touching
+    the GPU, a split whose records would not fit the library's scratch."""
+    def na(**kw):
+        a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, K=512, q=A, q_dtype=0, q_pos=A, theta=10000.0,
+                 raw=A, raw_vis=None, comp=A, idx=A, scale=0.044, out=A)
+        a.update(kw)
+        return L.ds4a_sparse_mqa_noalloc(a["U"], a["T"], a["H"], a["D"], a["n_rot"], a["W"], a["N"], a["K"], a["q"],
+                                         a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["raw_vis"], a["comp"],
+                                         a["idx"], a["scale"], a["out"], S)
+
+    assert na(D=256) == -3
+    assert na(K=0) == -2
+    assert na(q=None) == -1 and "ds4a_sparse_mqa_noalloc" in ops.last_error()
+    assert na(comp=MIS) == -4
+    # 32 queries x 128 heads over a 3072-row union: two chunks of 16.8 MB of records
+    need = ops.workspace_bytes(1, 32, 1, 4096, 2048, 128, 1024)
+    assert need > (16 << 20)
+    assert na(U=32, H=128, W=1024, N=4096, K=2048) == -5 and "scratch" in ops.last_error()
+
+
 def test_mqa_fp8_validation(L):
     def sp(**kw):
         a = dict(U=1, T=1, H=64, D=512, n_rot=64, W=128, N=1000, K=512, q=A, q_dtype=0, q_pos=A, theta=10000.0,
