@@ -631,6 +631,53 @@ def traffic_for(kernel_hash: str, units: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def attention_record(w, units: int, mqa_ms: float) -> dict:
+    """The decode attention (A3-A6) alone: per unit, W + K rows of 1 KiB gathered, the f32 query
+    read and the f32 output written (64 heads x 512 dims each)."""
+    per_unit = (w.W + w.K) * 1024 + 2 * w.H * 512 * 4
+    gbs = units * per_unit / (mqa_ms / 1e3) / 1e9
+    return {"kernel": "attn_dq_kernel (ds4a_sparse_mqa: one workgroup per query and 16 heads)",
+            "algorithmic_bytes": units * per_unit, "bytes_per_unit": per_unit, "avg_launch_us": mqa_ms * 1e3,
+            "GB_per_s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS}
+
+
+def measured_ceilings(torch, ops) -> dict:
+    """HBM read stream over 4 GiB (larger than every cache) and the bf16 MFMA loop, each timed
+    with HIP events over repeated launches after warm-up launches."""
+    stream = torch.cuda.current_stream()
+
+    def timed(fn, reps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3 / reps
+
+    nbytes, grid_r = 4 << 30, 8192
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    sink_r = torch.empty(grid_r * 256, dtype=torch.int32, device="cuda")
+    t_r = timed(lambda: ops.ceiling_read(buf, grid_r, sink=sink_r), 10)
+    del buf, sink_r
+    iters, grid_m = 2000, 2048
+    sink_m = torch.empty(grid_m * 256, dtype=torch.float32, device="cuda")
+    flops = ops.ceiling_mfma(iters, grid_m, sink=sink_m)
+    t_m = timed(lambda: ops.ceiling_mfma(iters, grid_m, sink=sink_m), 10)
+    torch.cuda.empty_cache()
+    return {
+        "hbm_read": {"GB_per_s": nbytes / t_r / 1e9, "frac_of_spec": nbytes / t_r / 1e9 / HBM_PEAK_GBS,
+                     "bytes": nbytes, "grid": grid_r, "us": t_r * 1e6,
+                     "kernel": "ceiling_read_kernel (16 B non-temporal loads, grid-stride, 4 in flight)"},
+        "mfma_bf16": {"TFLOP_per_s": flops / t_m / 1e12, "frac_of_spec": flops / t_m / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                      "flops": flops, "grid": grid_m, "us": t_m * 1e6,
+                      "kernel": "ceiling_mfma_kernel (v_mfma_f32_16x16x32_bf16, 8 chains per wave, 8 waves per SIMD)"},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -706,6 +753,7 @@ def main():
                  "kernel_us": {"indexer_topk": r["select_ms"] * 1e3, "mqa": r["mqa_ms"] * 1e3,
                                "indexer_alone": r["indexer_ms"] * 1e3, "topk_alone": r["topk_ms"] * 1e3},
                  "wall_ms_per_step": r["wall_ms_per_step"]},
+        "attention": attention_record(w, units, r["mqa_ms"]),
         "per_step": pct,
         "warm": {"ms_per_step": warm_ms, "value": units / (warm_ms / 1e3), "input_replicas": 1},
         "hip_graph": {"ms_per_step": gr["ms_per_step"], "value": units / (gr["ms_per_step"] / 1e3),
@@ -817,6 +865,21 @@ def main():
             "kernel_us": {"indexer_topk": r38["select_ms"] * 1e3, "mqa": r38["mqa_ms"] * 1e3},
         }
         del b38, x3
+
+    # ---- measured ceilings (outside every timed region above): a plain HBM read stream and a
+    # plain bf16 matrix-core loop, each kernel's fraction is also given against these
+    rec["ceilings"] = measured_ceilings(torch, ops)
+    hbm_c = rec["ceilings"]["hbm_read"]["GB_per_s"]
+    mfma_c = rec["ceilings"]["mfma_bf16"]["TFLOP_per_s"]
+    rec["roofline"]["ceiling"] = hbm_c
+    rec["roofline"]["frac_of_ceiling"] = rec["roofline"]["achieved"] / hbm_c
+    rec["indexer_alone"]["frac_of_ceiling"] = rec["indexer_alone"]["achieved"] / hbm_c
+    rec["step"]["frac_of_hbm_ceiling"] = rec["step"]["GB_per_s"] / hbm_c
+    if "attention" in rec:
+        rec["attention"]["frac_of_ceiling"] = rec["attention"]["GB_per_s"] / hbm_c
+    if "prefill" in rec:
+        rec["prefill"]["roofline"]["ceiling"] = mfma_c
+        rec["prefill"]["roofline"]["frac_of_ceiling"] = rec["prefill"]["roofline"]["achieved"] / mfma_c
 
     if args.copy_probe > 0:
         n = args.copy_probe

@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(HERE, "libds4attn.so")
-SOURCES = ["api.hip", "indexer.hip", "topk.hip", "fused.hip", "rope_q.hip", "attn.hip", "attn_dq.hip", "compress.hip", "cache.hip"]
+SOURCES = ["api.hip", "indexer.hip", "topk.hip", "fused.hip", "rope_q.hip", "attn.hip", "attn_dq.hip", "compress.hip", "cache.hip", "ceiling.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = [

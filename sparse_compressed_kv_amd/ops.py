@@ -7,6 +7,7 @@ eager fallback: if the library is missing, or no GPU is present, calls raise.
 from __future__ import annotations
 
 import ctypes
+import glob
 import os
 import re
 
@@ -81,6 +82,10 @@ def lib() -> ctypes.CDLL:
     L.ds4a_push_raw.restype = i32
     L.ds4a_frontier_push.argtypes = [i32, i32, i32, P, P, P, P, P, P, P]
     L.ds4a_frontier_push.restype = i32
+    L.ds4a_ceiling_read.argtypes = [P, i64, i32, P, P]
+    L.ds4a_ceiling_read.restype = i32
+    L.ds4a_ceiling_mfma.argtypes = [i64, i32, P, ctypes.POINTER(ctypes.c_double), P]
+    L.ds4a_ceiling_mfma.restype = i32
     L.ds4a_rope_q.argtypes = [i32, i32, i32, i32, i32, P, i32, P, dbl, P, P]
     L.ds4a_rope_q.restype = i32
     _lib = L
@@ -88,9 +93,11 @@ def lib() -> ctypes.CDLL:
 
 
 def declared_symbols() -> list[str]:
-    """Function names the public header declares."""
-    text = open(HEADER).read()
-    return sorted(set(re.findall(r"\b(ds4a_[a-z0-9_]+)\s*\(", text)))
+    """Function names the public headers (include/*.h) declare."""
+    names = set()
+    for h in sorted(glob.glob(os.path.join(os.path.dirname(HEADER), "*.h"))):
+        names |= set(re.findall(r"\b(ds4a_[a-z0-9_]+)\s*\(", open(h).read()))
+    return sorted(names)
 
 
 def last_error() -> str:
@@ -496,3 +503,24 @@ class Step:
         sparse_mqa(x["q"], x["pos"], x["raw"], x["comp"], self.idx, scale, theta, W=self.W, out=self.out,
                    workspace=self.ws_mqa, stream=stream, raw_vis=raw_vis)
         return self.out
+
+
+def ceiling_read(src, grid: int = 8192, sink=None, stream=None):
+    """Launch the HBM read-stream ceiling kernel over the bytes of src (a CUDA tensor)."""
+    if sink is None:
+        sink = torch.empty(grid * 256, dtype=torch.int32, device=src.device)
+    rc = lib().ds4a_ceiling_read(_ptr(src), src.numel() * src.element_size(), grid, _ptr(sink), _stream(stream))
+    if rc != 0:
+        raise Ds4aError("ds4a_ceiling_read", rc, "bad argument" if rc == -1 else "launch failed")
+    return sink
+
+
+def ceiling_mfma(iters: int, grid: int = 2048, sink=None, stream=None) -> float:
+    """Launch the bf16 matrix-core ceiling kernel; returns the launch's dense flop count."""
+    if sink is None:
+        sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    fl = ctypes.c_double(0.0)
+    rc = lib().ds4a_ceiling_mfma(int(iters), grid, _ptr(sink), ctypes.byref(fl), _stream(stream))
+    if rc != 0:
+        raise Ds4aError("ds4a_ceiling_mfma", rc, "bad argument" if rc == -1 else "launch failed")
+    return fl.value

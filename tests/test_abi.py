@@ -26,6 +26,21 @@ def test_exports_every_declared_symbol(L):
         assert hasattr(L, n), n
 
 
+def test_ceiling_validation(L):
+    """The measured-ceiling kernels refuse bad arguments before launching anything."""
+    import ctypes as ct
+    sink = A
+    assert L.ds4a_ceiling_read(None, 1 << 20, 64, sink, S) == -1
+    assert L.ds4a_ceiling_read(MIS, 1 << 20, 64, sink, S) == -1
+    assert L.ds4a_ceiling_read(A, (1 << 20) + 4, 64, sink, S) == -1
+    assert L.ds4a_ceiling_read(A, 1 << 20, 0, sink, S) == -1
+    assert L.ds4a_ceiling_read(A, 1 << 20, 64, None, S) == -1
+    fl = ct.c_double(0.0)
+    assert L.ds4a_ceiling_mfma(0, 64, sink, ct.byref(fl), S) == -1
+    assert L.ds4a_ceiling_mfma(10, 0, sink, ct.byref(fl), S) == -1
+    assert L.ds4a_ceiling_mfma(10, 64, None, ct.byref(fl), S) == -1
+
+
 def test_version(L):
     assert L.ds4a_version() == 2
 
