@@ -22,7 +22,8 @@ Inputs are synthetic (synth.inputs), uploaded to HBM before timing.  Several
 replicas of each input set are rotated step by step so that no step finds its
 inputs in the 256 MB last-level cache.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--copy-probe BYTES]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--only-main | --prefill-only]
+                    [--copy-probe BYTES]
 """
 from __future__ import annotations
 
@@ -685,6 +686,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--only-main", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--prefill-only", action="store_true",
+                    help="time only the prefill workload (for counter runs); prints its record alone")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="after timing, run one device copy of this many bytes (counter calibration)")
     args = ap.parse_args()
@@ -704,6 +707,14 @@ def main():
 
     ops.lib()
     torch.cuda.set_device(0)
+
+    if args.prefill_only:
+        w3 = gen.CONFIGS["prefill_2048q_n8192"]
+        b3 = Bench(w3, gen.make_config(w3), 2)
+        r3 = b3.run(args.steps, args.warmup)
+        print(json.dumps({"workload": w3.name, "ms_per_step": r3["ms_per_step"],
+                          "kernel_us": {"indexer_topk": r3["select_ms"] * 1e3, "mqa": r3["mqa_ms"] * 1e3}}), flush=True)
+        return
 
     # ---- main line: decode, 43 layers x 65,536 rows
     w = gen.CONFIGS["decode_43layers_n65536"]

@@ -48,8 +48,9 @@ namespace {
 constexpr int kQKs = kKs / kAW;               // QK k-steps per wave (4)
 constexpr int kQDB = kDB / kAW;               // PV dim blocks per wave (8)
 constexpr int kDqNB = 4;                      // ring slots
-constexpr int kXchOff = kDqNB * kBuf;         // partial logits: [parity][wave][lane][8] f32
+constexpr int kXchOff = kDqNB * kBuf;         // partial logits: [parity][half][wave][lane][4] f32
 constexpr int kXchBuf = kAW * kWave * 8 * 4;  // 8 KiB per parity
+constexpr int kXchPlane = kAW * kWave * 4;     // floats of one half step's plane
 constexpr int kDqScaleOff = kXchOff + 2 * kXchBuf;
 template <bool E8> constexpr int kDqAngOff = kDqScaleOff + (E8 ? kDqNB * kAW * kScaleWave : 0);  // [32] (cos, sin) fp64
 template <bool E8> constexpr int kDqMaskOff = kDqAngOff<E8> + 32 * 16;      // sparse: row validity per step
@@ -254,9 +255,10 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
             p0[i] = acc[0][0][i] + acc[0][1][i];
             p1[i] = acc[1][0][i] + acc[1][1][i];
         }
-        float *dst = s_xch + (j & 1) * (kXchBuf / 4) + (wave * kWave + lane) * 8;
+        // one plane per half step, 16 contiguous bytes per lane (no bank conflicts)
+        float *dst = s_xch + (j & 1) * (kXchBuf / 4) + (wave * kWave + lane) * 4;
         *reinterpret_cast<f32x4 *>(dst) = p0;
-        *reinterpret_cast<f32x4 *>(dst + 4) = p1;
+        *reinterpret_cast<f32x4 *>(dst + kXchPlane) = p1;
     };
     // One step: the softmax of step j from the four waves' partial logits (added in the same
     // order in every wave), interleaved with QK of step jq (when QK), then PV of step j with, as
@@ -276,13 +278,13 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
         const uint32_t mask = step_mask(j);
-        const float *src = s_xch + (j & 1) * (kXchBuf / 4) + lane * 8;
+        const float *src = s_xch + (j & 1) * (kXchBuf / 4) + lane * 4;
         f32x4 s0 = *reinterpret_cast<const f32x4 *>(src);
-        f32x4 s1 = *reinterpret_cast<const f32x4 *>(src + 4);
+        f32x4 s1 = *reinterpret_cast<const f32x4 *>(src + kXchPlane);
 #pragma unroll
         for (int w = 1; w < kAW; ++w) {
-            s0 += *reinterpret_cast<const f32x4 *>(src + w * kWave * 8);
-            s1 += *reinterpret_cast<const f32x4 *>(src + w * kWave * 8 + 4);
+            s0 += *reinterpret_cast<const f32x4 *>(src + w * kWave * 4);
+            s1 += *reinterpret_cast<const f32x4 *>(src + w * kWave * 4 + kXchPlane);
         }
         // QK of step jq (independent of the softmax)
         if (QK) {
