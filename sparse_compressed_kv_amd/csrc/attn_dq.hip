@@ -20,9 +20,14 @@
 //     online softmax;
 //   - PV: O^T[128 dims x 16 heads] += V^T P^T, 8 dim blocks x (hi, lo) of P, with the V^T
 //     fragments (two ds_read_b64_tr_b16 per block) read one step ahead into registers.
-// The rows go through the same LDS ring as in attn.hip (buffer_load ... lds straight from
-// memory, zeros for rows that take no part), 4 slots, loads issued 3 steps ahead: a step's
-// slot is free once its QK and V^T reads are done, one step before its PV.  Per step, in one
+// The rows go through an LDS ring of the same geometry as in attn.hip (buffer_load ... lds
+// straight from memory, zeros for rows that take no part), 4 slots, loads issued 3 steps ahead:
+// a step's slot is free once its QK and V^T reads are done, one step before its PV.  Two more
+// waves issue those loads (16 rows of each step each) and widen E4M3 rows to bf16 in place:
+// a load into LDS holds its wave at issue until the CU's address unit takes it (64 bytes per
+// clock, so 512 clocks for a step's 32 KiB), which the four computing waves then never wait
+// for.  Waves meet at one barrier per step; the producers wait for a step's loads before it.
+// Per step, in one
 // stretch of code, the softmax of step j (VALU) runs beside QK of step j+1 (matrix core), then
 // PV of step j, reading step j+1's V^T fragments as step j's are consumed; the partial logits
 // of j+1 are published and one barrier ends the step.
@@ -45,6 +50,11 @@ namespace ds4a {
 
 namespace {
 
+constexpr int kDqP = 2;                       // producer waves
+constexpr int kDqT = kAT + kDqP * kWave;      // threads per workgroup: 4 computing + 2 producer waves
+constexpr int kPR = kSR / kDqP;               // rows each producer loads per step (16): half step p
+constexpr int kDqCodeOff = kHalfBuf - kPR * kCodeRow;   // E4M3 codes of a half step: its last 8 KiB
+constexpr int kPCodeBatch = kPR / 2 + 2;      // E4M3 step: loads per producer (codes, 2 x scales)
 constexpr int kQKs = kKs / kAW;               // QK k-steps per wave (4)
 constexpr int kQDB = kDB / kAW;               // PV dim blocks per wave (8)
 constexpr int kDqNB = 4;                      // ring slots
@@ -61,8 +71,90 @@ static_assert(kDqMaxLds<false> <= 160 * 1024 && kDqMaxLds<true> <= 160 * 1024, "
 static_assert(kDqMaxChunkSteps * kSR % kAT == 0, "row table fill");
 constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[wave][block][lane][4]
 
+// Row loads of the union's 32-row steps for producer wave p: rows 16p..16p+15 of each step
+// (half step p), step j in ring slot j % kDqNB.  Raw steps: rows of the query's window, 1 KiB
+// each, one instruction per row; rows at or past raw_vis lie past the window resource and read
+// as zeros.  Compressed steps: bf16 rows from their entries (row index, or -1: past the
+// resource, zeros); E4M3 rows as codes, two rows per instruction, into the last 8 KiB of the
+// half step, plus the rows' scales as the computing waves read them (per 8-row quarter, lane l
+// holding row l % 8).  Steps past the chunk are compressed steps of -1 entries.  Row data:
+// row r of the step at r * kRowStride, its 16-byte chunk k at position k ^ ((r >> 2) & 1).
+template <bool DENSE, bool E8>
+struct DqProducer {
+    unsigned char *ring;
+    uint32_t ring_a, scale_a;                // LDS addresses of the ring and of the E4M3 row scales
+    const int32_t *s_row;                    // sparse: compressed row of each union row of the chunk
+    __amdgpu_buffer_rsrc_t raw_rs, comp_rs, scale_rs;
+    int step0, n, n_raw, rho0, W, p, lane;
+    int64_t j_lim;                           // dense: visible compressed rows
+
+    __device__ __forceinline__ void entries(int j, i32x4 (&e)[4]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = i32x4{-1, -1, -1, -1};
+        if (j >= n || j < n_raw) return;
+        const int rho = (step0 + j) * kSR + p * kPR;
+        if (!DENSE) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i)       // same address in every lane
+                e[i] = *reinterpret_cast<const i32x4 *>(s_row + (rho - rho0) + 4 * i);
+            return;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int64_t x = (int64_t)rho + 4 * i + r - W;
+                e[i][r] = x < j_lim ? (int32_t)x : -1;
+            }
+    }
+    __device__ __forceinline__ void issue(int j, const i32x4 (&e)[4]) const {
+        const int slot = j % kDqNB;
+        const uint32_t hb = ring_a + (uint32_t)(slot * kBuf + p * kHalfBuf);
+        if (j < n_raw) {
+            const int R0 = (step0 + j) * kSR + p * kPR;
+            const uint32_t dst = hb;
+#pragma unroll
+            for (int r = 0; r < kPR; ++r)
+                dma16(dst + r * kRowStride, ((uint32_t)(R0 + r) << 10) + ((uint32_t)(lane ^ ((r >> 2) & 1)) << 4), raw_rs);
+        } else if (!E8) {
+            const uint32_t dst = hb;
+#pragma unroll
+            for (int r = 0; r < kPR; ++r)
+                dma16(dst + r * kRowStride, ((uint32_t)e[r >> 2][r & 3] << 10) + ((uint32_t)(lane ^ ((r >> 2) & 1)) << 4),
+                      comp_rs);
+        } else {
+            const uint32_t dst = hb + kDqCodeOff;
+#pragma unroll
+            for (int i = 0; i < kPR / 2; ++i) {
+                const int32_t ent = lane < 32 ? e[i >> 1][2 * (i & 1)] : e[i >> 1][2 * (i & 1) + 1];
+                dma16(dst + i * 2 * kCodeRow, ((uint32_t)ent << 9) + ((uint32_t)(lane & 31) << 4), comp_rs);
+            }
+            const int l8 = lane & 7;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int32_t es = l8 < 4 ? e[2 * h][l8 & 3] : e[2 * h + 1][l8 & 3];
+                dma4(scale_a + (uint32_t)((slot * kAW + 2 * p + h) * kScaleWave), (uint32_t)es << 2, scale_rs);
+            }
+        }
+    }
+    // E4M3 compressed step j, in place: this wave's 16 code rows, then the same rows as bf16.
+    // The codes lie in the half step's last 8 KiB, so the bf16 rows overwrite only codes this
+    // wave has already read.
+    __device__ __forceinline__ void widen(int j) const {
+        unsigned char *hb = ring + (j % kDqNB) * kBuf + p * kHalfBuf;
+        u32x2 x[kPR];
+#pragma unroll
+        for (int r = 0; r < kPR; ++r) x[r] = *reinterpret_cast<const u32x2 *>(hb + kDqCodeOff + r * kCodeRow + 8 * lane);
+        wait_lds();
+#pragma unroll
+        for (int r = 0; r < kPR; ++r)
+            *reinterpret_cast<u32x4 *>(hb + r * kRowStride + ((lane ^ ((r >> 2) & 1)) << 4)) = e4m3x8_to_bf16x8(x[r]);
+        wait_lds();
+    }
+};
+
 template <bool QF32, bool DENSE, bool E8>
-__global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
+__global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
 {
     constexpr int NB = kDqNB;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -87,7 +179,7 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
     const uint32_t u32 = q32 / (uint32_t)a.T;
     const int64_t q = q32, u = u32, t = q32 - u32 * (uint32_t)a.T;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // dim quarter
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // dim quarter, or producer kAW + p
     const int g = lane >> 4, c = lane & 15;
     const int h0 = hg * kWH;
 
@@ -105,22 +197,58 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
     const int raw_lim = a.raw_vis ? (int)clamp_nvis(a.raw_vis, q, a.W) : a.W;
     const int64_t j_lim = DENSE ? clamp_nvis(a.n_vis, q, a.N) : a.N;
 
-    StepLoader<DENSE, E8, NB> ld;
-    ld.ring = ring;
-    ld.s_scale = s_scale;
-    ld.s_row = s_row;
-    ld.raw_rs = rsrc(raw_q, (uint32_t)raw_lim * (2 * kD));
-    ld.comp_rs = rsrc(comp_u, (uint32_t)((uint64_t)a.N * kCompRowBytes));
-    ld.scale_rs = rsrc(cscale_u, E8 ? (uint32_t)a.N * 4u : 0u);
-    ld.step0 = step0; ld.n = n; ld.n_raw = n_raw; ld.rho0 = rho0; ld.W = a.W;
-    ld.wave = wave; ld.lane = lane; ld.j_lim = j_lim;
-
-    // ---- set-up: raw steps' loads first (they need no index), then index entries, query and
-    // row table, then the first compressed steps' loads.
+    if (wave >= kAW) {
+        // ---- producer wave: raw steps' loads at once (they need no index), the first
+        // compressed steps' after the row table, then per step: wait for step k+2's loads
+        // (widen it if E4M3), the barrier, and step k+5's loads into the slot of step k+1.
+        DqProducer<DENSE, E8> ld;
+        ld.ring = ring;
+        ld.ring_a = lds_addr(ring);
+        ld.scale_a = lds_addr(s_scale);
+        ld.s_row = s_row;
+        ld.raw_rs = rsrc(raw_q, (uint32_t)raw_lim * (2 * kD));
+        ld.comp_rs = rsrc(comp_u, (uint32_t)((uint64_t)a.N * kCompRowBytes));
+        ld.scale_rs = rsrc(cscale_u, E8 ? (uint32_t)a.N * 4u : 0u);
+        ld.step0 = step0; ld.n = n; ld.n_raw = n_raw; ld.rho0 = rho0; ld.W = a.W;
+        ld.p = wave - kAW; ld.lane = lane; ld.j_lim = j_lim;
+        // Only step 0 goes out before the row table's barrier: the loads of a cold start are
+        // slow to issue, and the computing waves would wait for them at that barrier.
+        i32x4 ent[4];
+        ld.entries(-1, ent);                  // no entries (raw steps)
+        if (n_raw > 0) ld.issue(0, ent);
+        __syncthreads();                      // row table
 #pragma unroll
-    for (int j = 0; j < NB - 1; ++j)
-        if (j < n_raw) ld.issue_raw(j);
+        for (int j = 0; j < NB - 1; ++j)
+            if (j > 0 || n_raw == 0) {
+                ld.entries(j, ent);
+                ld.issue(j, ent);
+            }
+        ld.entries(NB - 1, ent);
+        for (int k = -2; k <= n - 2; ++k) {
+            // loads issued after step k+2's: steps k+3 and k+4
+            if (!E8) {
+                wait_vm<2 * kPR>();
+            } else {
+                const int later_raw = min(max(n_raw - (k + 3), 0), 2);
+                if (later_raw == 0) wait_vm<2 * kPCodeBatch>();
+                else if (later_raw == 1) wait_vm<kPCodeBatch + kPR>();
+                else wait_vm<2 * kPR>();
+                if (k + 2 >= n_raw && k + 2 < n) ld.widen(k + 2);
+            }
+            __syncthreads();
+            ld.issue(k + NB + 1, ent);
+            ld.entries(k + NB + 2, ent);
+        }
+        wait_vm<0>();                         // no load may land in LDS after the workgroup ends
+        if (a.n_chunks > 1) {                 // the barriers of the record exchange
+            __syncthreads();
+            __syncthreads();
+        }
+        return;
+    }
 
+    // ---- computing waves: set-up (index entries, query, row table), then the steps.
+    const int64_t pos = a.pos[q];             // first: the rotation angles need only it
     constexpr int kPer = kDqMaxChunkSteps * kSR / kAT;        // index entries per thread (6)
     int32_t v_idx[kPer];
     if (!DENSE) {
@@ -150,7 +278,6 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
     }
-    const int64_t pos = a.pos[q];
     if (!DENSE) {
         // row table (local union row -> compressed row or -1) and per-step validity masks
 #pragma unroll
@@ -167,19 +294,9 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
     }
-    __syncthreads();                          // row table
-#pragma unroll
-    for (int j = 0; j < NB - 1; ++j)
-        if (j >= n_raw) {
-            i32x4 e0, e1;
-            ld.entries(j, e0, e1);
-            ld.issue_comp(j, e0, e1);
-        }
-    i32x4 ent_a, ent_b;                       // entries of the next step to issue (NB - 1)
-    ld.entries(NB - 1, ent_a, ent_b);
-
     // The rotated tail (dims 448..511) is wave 3's k-steps 2 and 3: pair 16(s-2) + 4g + e/2,
     // rotated in fp64 and rounded once to f32 (rope.hpp, as the compressor rotates its rows).
+    // Before the barrier, so that it overlaps the producers' first loads.
     if (wave == kAW - 1) {
         if (lane < kRot / 2) {
             double cs, sn;
@@ -195,6 +312,8 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
                 rope_rotate(s_ang[2 * pr], s_ang[2 * pr + 1], qv[s][e], qv[s][e + 1]);
             }
     }
+    __syncthreads();                          // row table
+
     // Query fragments: f16 pair while the steps are raw, bf16 pair after (a bf16 query's
     // unrotated dims have lo = 0).
     u32x4 qh[kQKs], ql[kQKs];
@@ -353,25 +472,13 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
 #pragma unroll
         for (int i = 0; i < kQDB; ++i) va[i] = tr_frag(tn + pv_base, b0 + i);
     };
-    // Step k+2 may be used: this wave's loads of it have landed (E4M3 compressed: the workgroup
-    // widens it), and the barrier publishes everyone's and the partial logits written before
-    // it.  Step k+1's QK and V^T reads are done by then, so its slot takes step k + NB + 1.
+    // Barrier k: step k+2 may be used (the producers have waited for its loads, and widened it
+    // if E4M3), the partial logits written before it are published, and this wave's QK and V^T
+    // reads of step k+1 are done, so the producers refill its slot with step k + NB + 1.
     auto advance = [&](int k) __attribute__((always_inline)) {
-        // loads issued after step k+2's: steps k+3 and k+4
-        if (!E8) {
-            wait_vm<2 * kRW>();
-        } else {
-            const int later_raw = min(max(n_raw - (k + 3), 0), 2);
-            if (later_raw == 0) wait_vm<2 * kCodeBatch>();
-            else if (later_raw == 1) wait_vm<kCodeBatch + kRW>();
-            else wait_vm<2 * kRW>();
-        }
+        (void)k;
         wait_lds();
-        if (E8 && k + 2 >= n_raw && k + 2 < n) ld.widen(k + 2);
         __syncthreads();
-        const int jn = k + NB + 1;
-        ld.issue(jn, ent_a, ent_b);
-        ld.entries(jn + 1, ent_a, ent_b);
     };
 
     // ---- the pipeline.  Barrier -2: step 0's rows.  Then QK and V^T of step 0, its partial
@@ -404,7 +511,6 @@ __global__ __launch_bounds__(kAT, 1) void attn_dq_kernel(AttnArgs a)
     for (int e = 0; e < 8; ++e) rs_cur[e] = rs_next[e];
     if (j < n_raw) step(F16T{}, F16T{}, std::false_type{}, j, j);
     else step(BF16T{}, BF16T{}, std::false_type{}, j, j);
-    wait_vm<0>();                             // no load may land in LDS after the workgroup ends
 
     l_run = sum_g(l_run);                     // the same in every wave
     if (a.n_chunks == 1) {
@@ -534,7 +640,7 @@ hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t
     a.count = count;
     a.part = part;
     a.log2_theta = log2(theta);
-    hipLaunchKernelGGL(fn, dim3((unsigned)p.blocks), dim3(kAT), lds, stream, a);
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.blocks), dim3(kDqT), lds, stream, a);
     return hipGetLastError();
 }
 
