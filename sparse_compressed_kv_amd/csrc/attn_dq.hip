@@ -55,21 +55,49 @@ constexpr int kDqT = kAT + kDqP * kWave;      // threads per workgroup: 4 comput
 constexpr int kPR = kSR / kDqP;               // rows each producer loads per step (16): half step p
 constexpr int kDqCodeOff = kHalfBuf - kPR * kCodeRow;   // E4M3 codes of a half step: its last 8 KiB
 constexpr int kPCodeBatch = kPR / 2 + 2;      // E4M3 step: loads per producer (codes, 2 x scales)
-constexpr int kQKs = kKs / kAW;               // QK k-steps per wave (4)
-constexpr int kQDB = kDB / kAW;               // PV dim blocks per wave (8)
+constexpr int kHKs = kKs / 2;                 // QK k-steps per wave: its half of the dims (8)
+constexpr int kQKs = kKs / kAW;               // k-steps of a quarter of the dims (4)
+constexpr int kHDB = kDB / 2;                 // PV dim blocks per wave (16)
+constexpr int kQDB = kDB / kAW;               // dim blocks each wave keeps after the merge (8)
 constexpr int kDqNB = 4;                      // ring slots
-constexpr int kXchOff = kDqNB * kBuf;         // partial logits: [parity][half][wave][lane][4] f32
-constexpr int kXchBuf = kAW * kWave * 8 * 4;  // 8 KiB per parity
-constexpr int kXchPlane = kAW * kWave * 4;     // floats of one half step's plane
+constexpr int kXchOff = kDqNB * kBuf;         // partial logits: [parity][wave][lane][4] f32
+constexpr int kXchBuf = kAW * kWave * 4 * 4;  // 4 KiB per parity
 constexpr int kDqScaleOff = kXchOff + 2 * kXchBuf;
 template <bool E8> constexpr int kDqAngOff = kDqScaleOff + (E8 ? kDqNB * kAW * kScaleWave : 0);  // [32] (cos, sin) fp64
-template <bool E8> constexpr int kDqMaskOff = kDqAngOff<E8> + 32 * 16;      // sparse: row validity per step
+template <bool E8> constexpr int kDqMlOff = kDqAngOff<E8> + 32 * 16;        // merge: m[wave][16], l[wave][16]
+template <bool E8> constexpr int kDqMaskOff = kDqMlOff<E8> + 2 * kAW * kWH * 4;   // sparse: row validity per step
 constexpr int kDqMaxChunkSteps = 48;          // longer unions are split
 template <bool E8> constexpr int kDqRowTabOff = kDqMaskOff<E8> + 4 * kDqMaxChunkSteps;
 template <bool E8> constexpr int kDqMaxLds = kDqRowTabOff<E8> + 4 * kSR * kDqMaxChunkSteps;
 static_assert(kDqMaxLds<false> <= 160 * 1024 && kDqMaxLds<true> <= 160 * 1024, "LDS of one workgroup");
 static_assert(kDqMaxChunkSteps * kSR % kAT == 0, "row table fill");
-constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[wave][block][lane][4]
+constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[quarter][block][lane][4]
+static_assert(kAW * kQDB * kWave * 16 <= kDqNB * kBuf, "row-half merge fits in the ring");
+static_assert(kAW * kQKs * 2 * kWave * 16 <= kBuf, "query quarters fit in one ring slot");
+constexpr float kLazy = 8.f;                  // reference slack (log2 units): P stays below 2^8
+
+// 4 floats -> hi + lo pair of the MFMA operand type, as the B operand of a folded PV step:
+// k = 8g + e takes hi of value e (e < 4) and lo of value e - 4 (e >= 4).
+template <bool F16>
+__device__ __forceinline__ u32x4 split4_fold(const float (&x)[4]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const f32x2 v = {x[2 * i], x[2 * i + 1]};
+        if (F16) {
+            const f16x2 h = __builtin_convertvector(v, f16x2);
+            const f16x2 l = __builtin_convertvector(v - __builtin_convertvector(h, f32x2), f16x2);
+            r[i] = __builtin_bit_cast(uint32_t, h);
+            r[2 + i] = __builtin_bit_cast(uint32_t, l);
+        } else {
+            const bf16x2 h = __builtin_convertvector(v, bf16x2);
+            const bf16x2 l = __builtin_convertvector(v - __builtin_convertvector(h, f32x2), bf16x2);
+            r[i] = __builtin_bit_cast(uint32_t, h);
+            r[2 + i] = __builtin_bit_cast(uint32_t, l);
+        }
+    }
+    return r;
+}
 
 // Row loads of the union's 32-row steps for producer wave p: rows 16p..16p+15 of each step
 // (half step p), step j in ring slot j % kDqNB.  Raw steps: rows of the query's window, 1 KiB
@@ -77,7 +105,7 @@ constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[wave][b
 // as zeros.  Compressed steps: bf16 rows from their entries (row index, or -1: past the
 // resource, zeros); E4M3 rows as codes, two rows per instruction, into the last 8 KiB of the
 // half step, plus the rows' scales as the computing waves read them (per 8-row quarter, lane l
-// holding row l % 8).  Steps past the chunk are compressed steps of -1 entries.  Row data:
+// holding row l % 8).  Row data:
 // row r of the step at r * kRowStride, its 16-byte chunk k at position k ^ ((r >> 2) & 1).
 template <bool DENSE, bool E8>
 struct DqProducer {
@@ -161,7 +189,9 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     unsigned char *ring = smem;
     float *s_xch = reinterpret_cast<float *>(smem + kXchOff);
     unsigned char *s_scale = smem + kDqScaleOff;
-    double *s_ang = reinterpret_cast<double *>(smem + kDqAngOff<E8>);
+    double *s_ang_all = reinterpret_cast<double *>(smem + kDqAngOff<E8>);
+    float *s_m = reinterpret_cast<float *>(smem + kDqMlOff<E8>);
+    float *s_l = s_m + kAW * kWH;
     uint32_t *s_mask = reinterpret_cast<uint32_t *>(smem + kDqMaskOff<E8>);
     int32_t *s_row = reinterpret_cast<int32_t *>(smem + kDqRowTabOff<E8>);
 
@@ -179,7 +209,8 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     const uint32_t u32 = q32 / (uint32_t)a.T;
     const int64_t q = q32, u = u32, t = q32 - u32 * (uint32_t)a.T;
     const int tid = threadIdx.x, lane = tid & (kWave - 1);
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // dim quarter, or producer kAW + p
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);   // (row half, dim half), or producer kAW + p
+    const int rh = wave >> 1, dh = wave & 1;  // computing wave: rows 16 rh.. of each step, dims 256 dh..
     const int g = lane >> 4, c = lane & 15;
     const int h0 = hg * kWH;
 
@@ -219,28 +250,33 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         __syncthreads();                      // row table
 #pragma unroll
         for (int j = 0; j < NB - 1; ++j)
-            if (j > 0 || n_raw == 0) {
+            if ((j > 0 || n_raw == 0) && j < n) {
                 ld.entries(j, ent);
                 ld.issue(j, ent);
             }
         ld.entries(NB - 1, ent);
+        // loads of step j: none past the chunk
+        auto batch = [&](int j) __attribute__((always_inline)) -> int {
+            return j >= n ? 0 : (E8 && j >= n_raw ? kPCodeBatch : kPR);
+        };
         for (int k = -2; k <= n - 2; ++k) {
-            // loads issued after step k+2's: steps k+3 and k+4
-            if (!E8) {
-                wait_vm<2 * kPR>();
-            } else {
-                const int later_raw = min(max(n_raw - (k + 3), 0), 2);
-                if (later_raw == 0) wait_vm<2 * kPCodeBatch>();
-                else if (later_raw == 1) wait_vm<kPCodeBatch + kPR>();
-                else wait_vm<2 * kPR>();
-                if (k + 2 >= n_raw && k + 2 < n) ld.widen(k + 2);
-            }
+            // wait for step k+2's loads: only steps k+3's and k+4's may still be in flight
+            const int later = batch(k + 3) + batch(k + 4);
+            if (later >= 2 * kPR) wait_vm<2 * kPR>();
+            else if (E8 && later >= kPR + kPCodeBatch) wait_vm<kPR + kPCodeBatch>();
+            else if (E8 && later >= 2 * kPCodeBatch) wait_vm<2 * kPCodeBatch>();
+            else if (later >= kPR) wait_vm<kPR>();
+            else if (E8 && later >= kPCodeBatch) wait_vm<kPCodeBatch>();
+            else wait_vm<0>();
+            if (E8 && k + 2 >= n_raw && k + 2 < n) ld.widen(k + 2);
             __syncthreads();
-            ld.issue(k + NB + 1, ent);
+            if (k + NB + 1 < n) ld.issue(k + NB + 1, ent);
             ld.entries(k + NB + 2, ent);
         }
-        wait_vm<0>();                         // no load may land in LDS after the workgroup ends
-        if (a.n_chunks > 1) {                 // the barriers of the record exchange
+        wait_vm<0>();                         // every load has landed before the ring is reused
+        __syncthreads();                      // the barriers of the row-half merge
+        __syncthreads();
+        if (a.n_chunks > 1) {                 // ... and of the record exchange
             __syncthreads();
             __syncthreads();
         }
@@ -259,9 +295,11 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             v_idx[r] = (i < n * kSR && k >= 0 && k < a.K) ? idx_q[k] : -1;
         }
     }
-    // This wave's quarter of the query: k-steps 4w + s (s < 4), dims 32(4w + s) + 8g + e.
+    // This wave loads a quarter of the query, qq = 2 dh + rh: k-steps 4 qq + i (i < 4), dims
+    // 32(4 qq + i) + 8g + e; the wave of the other row half brings the rest of its dim half.
+    const int qq = 2 * dh + rh;
     float qv[kQKs][8];
-    const int64_t q_off = (q * a.H + h0 + c) * (int64_t)kD + 8 * g + 32 * kQKs * wave;
+    const int64_t q_off = (q * a.H + h0 + c) * (int64_t)kD + 8 * g + 32 * kQKs * qq;
 #pragma unroll
     for (int s = 0; s < kQKs; ++s) {
         if (QF32) {
@@ -294,10 +332,10 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
     }
-    // The rotated tail (dims 448..511) is wave 3's k-steps 2 and 3: pair 16(s-2) + 4g + e/2,
+    // The rotated tail (dims 448..511) is quarter 3's k-steps 2 and 3: pair 16(s - 2) + 4g + e/2,
     // rotated in fp64 and rounded once to f32 (rope.hpp, as the compressor rotates its rows).
-    // Before the barrier, so that it overlaps the producers' first loads.
-    if (wave == kAW - 1) {
+    if (qq == kAW - 1) {
+        double *s_ang = s_ang_all;
         if (lane < kRot / 2) {
             double cs, sn;
             rope_angle(a.log2_theta, lane, pos, cs, sn);
@@ -312,21 +350,41 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
                 rope_rotate(s_ang[2 * pr], s_ang[2 * pr + 1], qv[s][e], qv[s][e + 1]);
             }
     }
-    __syncthreads();                          // row table
-
     // Query fragments: f16 pair while the steps are raw, bf16 pair after (a bf16 query's
-    // unrotated dims have lo = 0).
-    u32x4 qh[kQKs], ql[kQKs];
+    // unrotated dims have lo = 0).  Each wave publishes its quarter's pairs in ring slot 3, which
+    // takes rows only after the barrier of step -2, and reads its partner's after the next one.
+    u32x4 qh_m[kQKs], ql_m[kQKs];
 #pragma unroll
     for (int s = 0; s < kQKs; ++s) {
-        if (n_raw > 0) split8<true>(qv[s], qh[s], ql[s]);
-        else split8<false>(qv[s], qh[s], ql[s]);
+        if (n_raw > 0) split8<true>(qv[s], qh_m[s], ql_m[s]);
+        else split8<false>(qv[s], qh_m[s], ql_m[s]);
     }
+    u32x4 *xq = reinterpret_cast<u32x4 *>(ring + (NB - 1) * kBuf);      // [wave][k-step][hi, lo][lane]
+#pragma unroll
+    for (int s = 0; s < kQKs; ++s) {
+        xq[((wave * kQKs + s) * 2) * kWave + lane] = qh_m[s];
+        xq[((wave * kQKs + s) * 2 + 1) * kWave + lane] = ql_m[s];
+    }
+    __syncthreads();                          // row table, query quarters
+    u32x4 qh[kHKs], ql[kHKs];
+    auto assemble = [&](auto half) __attribute__((always_inline)) {
+        constexpr int R = decltype(half)::value;          // this wave's row half
+        const int partner = wave ^ 2;
+#pragma unroll
+        for (int s = 0; s < kQKs; ++s) {
+            qh[R * kQKs + s] = qh_m[s];
+            ql[R * kQKs + s] = ql_m[s];
+            qh[(1 - R) * kQKs + s] = xq[((partner * kQKs + s) * 2) * kWave + lane];
+            ql[(1 - R) * kQKs + s] = xq[((partner * kQKs + s) * 2 + 1) * kWave + lane];
+        }
+    };
+    if (rh == 0) assemble(std::integral_constant<int, 0>{});
+    else assemble(std::integral_constant<int, 1>{});
     // At the switch to compressed steps: the f16 pair holds q to ~22 bits, so the bf16 pair
     // made from hi + lo is as good as one made from q (about 16 bits).
     auto to_bf16_pair = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int s = 0; s < kQKs; ++s) {
+        for (int s = 0; s < kHKs; ++s) {
             const f16x8 h = as_f16x8(qh[s]), l = as_f16x8(ql[s]);
             float x[8];
 #pragma unroll
@@ -336,15 +394,16 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     };
 
     const float scale2 = a.scale * kLog2e;
-    const int qk_base = qk_base_of(g, c), pv_base = pv_base_of(g, c);
-    const int sg0 = wave * kQKs, b0 = wave * kQDB;          // this wave's first k-step, dim block
-    float m_run = -INFINITY, l_run = 0.f;
-    f32x4 o[kQDB];
+    // this wave's row half of a step, and its first k-step and dim block
+    const int qk_base = qk_base_of(g, c) + rh * kHalfBuf, pv_base = pv_base_of(g, c) + rh * kHalfBuf;
+    const int sg0 = dh * kHKs, bd0 = dh * kHDB;
+    float m_ref = -INFINITY, l_run = 0.f;     // lazy reference and sum of head c over this row half
+    f32x4 o[kHDB];                            // O^T of dims 256 dh + 16 i + 4g + (0..3), head c
 #pragma unroll
-    for (int b = 0; b < kQDB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
-    u32x4 va[kQDB];                           // V^T fragments of the step whose PV is next
-    f32x4 acc[2][2];                          // partial logits [half][k-step parity]
-    float rs_cur[8], rs_next[8];              // E4M3 row scales of the current and the next step
+    for (int b = 0; b < kHDB; ++b) o[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x2 va[kHDB];                           // V^T fragments of the step whose PV is next
+    f32x4 acc[2];                             // partial logits [k-step parity]
+    float rs_cur[4], rs_next[4];              // E4M3 row scales of the current and the next step
 
     auto step_mask = [&](int j) __attribute__((always_inline)) -> uint32_t {
         if (!DENSE) return s_mask[j];
@@ -353,124 +412,98 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         const int64_t cnt = lim - rho;
         return cnt >= kSR ? 0xFFFFFFFFu : (cnt <= 0 ? 0u : (1u << (uint32_t)cnt) - 1u);
     };
-    // Row scales of step j (rows 4g+e, 16+4g+e) into rs_next, read while its slot holds them.
+    // Row scales of step j (rows 16 rh + 4g + e) into rs_next, read while its slot holds them.
     auto read_scales = [&](auto f16_tag, int j) __attribute__((always_inline)) {
         constexpr bool F16 = decltype(f16_tag)::value;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rs_next[e] = 1.f;
+        for (int e = 0; e < 4; ++e) rs_next[e] = 1.f;
         if (E8 && !F16) {
-            const unsigned char *sb = s_scale + (j % NB) * kAW * kScaleWave + 16 * (g & 1);
-            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(sb + (g >> 1) * kScaleWave);
-            const f32x4 s1 = *reinterpret_cast<const f32x4 *>(sb + (2 + (g >> 1)) * kScaleWave);
+            const f32x4 s0 = *reinterpret_cast<const f32x4 *>(s_scale + ((j % NB) * kAW + 2 * rh + (g >> 1)) * kScaleWave +
+                                                              16 * (g & 1));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) { rs_next[e] = s0[e]; rs_next[4 + e] = s1[e]; }
+            for (int e = 0; e < 4; ++e) rs_next[e] = s0[e];
         }
     };
     // Partial logits of step j (this wave's dims) to the exchange buffer of j's parity.
     auto publish = [&](int j) __attribute__((always_inline)) {
-        f32x4 p0, p1;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p0[i] = acc[0][0][i] + acc[0][1][i];
-            p1[i] = acc[1][0][i] + acc[1][1][i];
-        }
-        // one plane per half step, 16 contiguous bytes per lane (no bank conflicts)
-        float *dst = s_xch + (j & 1) * (kXchBuf / 4) + (wave * kWave + lane) * 4;
-        *reinterpret_cast<f32x4 *>(dst) = p0;
-        *reinterpret_cast<f32x4 *>(dst + kXchPlane) = p1;
+        *reinterpret_cast<f32x4 *>(s_xch + (j & 1) * (kXchBuf / 4) + (wave * kWave + lane) * 4) = acc[0] + acc[1];
     };
-    // One step: the softmax of step j from the four waves' partial logits (added in the same
-    // order in every wave), interleaved with QK of step jq (when QK), then PV of step j with, as
-    // each V^T fragment is consumed, step jq's fragment read in its place.  P^T is a hi + lo
-    // pair, k = 8g + e (e < 4: rows 4g + e of the first half; e >= 4: of the second).
+    // One step: the softmax of step j over this wave's row half, from the two dim halves'
+    // partial logits (added in dim order, so both waves of the row half hold the same logits and
+    // take the same decisions), interleaved with QK of step jq (when QK), then PV of step j with,
+    // as each V^T fragment is consumed, step jq's fragment read in its place.  P^T is a hi + lo
+    // pair folded into k = 8g + e: hi of row 4g + e for e < 4, lo of the same row for e >= 4.
     auto step = [&](auto fp, auto fq, auto has_qk, int j, int jq) __attribute__((always_inline)) {
         constexpr bool FP = decltype(fp)::value, FQ = decltype(fq)::value;
         constexpr bool QK = decltype(has_qk)::value;
         const unsigned char *tn = ring + (jq % NB) * kBuf;
         // loads first: QK operands of step jq, the partial logits of step j
-        u32x4 x[kQKs][2];
+        u32x4 x[kHKs];
         if (QK) {
 #pragma unroll
-            for (int s = 0; s < kQKs; ++s) {
-                x[s][0] = *reinterpret_cast<const u32x4 *>(tn + qk_base + 64 * (sg0 + s));
-                x[s][1] = *reinterpret_cast<const u32x4 *>(tn + kHalfBuf + qk_base + 64 * (sg0 + s));
-            }
+            for (int s = 0; s < kHKs; ++s) x[s] = *reinterpret_cast<const u32x4 *>(tn + qk_base + 64 * (sg0 + s));
         }
-        const uint32_t mask = step_mask(j);
-        const float *src = s_xch + (j & 1) * (kXchBuf / 4) + lane * 4;
-        f32x4 s0 = *reinterpret_cast<const f32x4 *>(src);
-        f32x4 s1 = *reinterpret_cast<const f32x4 *>(src + kXchPlane);
-#pragma unroll
-        for (int w = 1; w < kAW; ++w) {
-            s0 += *reinterpret_cast<const f32x4 *>(src + w * kWave * 4);
-            s1 += *reinterpret_cast<const f32x4 *>(src + w * kWave * 4 + kXchPlane);
-        }
+        const uint32_t mask = step_mask(j) >> (16 * rh);
+        const float *src = s_xch + (j & 1) * (kXchBuf / 4) + ((2 * rh) * kWave + lane) * 4;
+        const f32x4 sl = *reinterpret_cast<const f32x4 *>(src) + *reinterpret_cast<const f32x4 *>(src + kWave * 4);
         // QK of step jq (independent of the softmax)
         if (QK) {
+            acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[1] = acc[0];
 #pragma unroll
-            for (int h = 0; h < 2; ++h)
-#pragma unroll
-                for (int p = 0; p < 2; ++p) acc[h][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < kQKs; ++s)
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    acc[h][s & 1] = mma<FQ>(x[s][h], qh[s], acc[h][s & 1]);
-                    acc[h][s & 1] = mma<FQ>(x[s][h], ql[s], acc[h][s & 1]);
-                }
+            for (int s = 0; s < kHKs; ++s) {
+                acc[s & 1] = mma<FQ>(x[s], qh[s], acc[s & 1]);
+                acc[s & 1] = mma<FQ>(x[s], ql[s], acc[s & 1]);
+            }
         }
-        // softmax of step j
-        float lg[8];
+        // softmax of step j against the lazy reference
+        float lg[4];
         float tmax = -INFINITY;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float l = (e < 4 ? s0[e] : s1[e - 4]) * scale2 * rs_cur[e];
-            lg[e] = (mask >> (16 * (e >> 2) + 4 * g + (e & 3))) & 1u ? l : -INFINITY;
+        for (int e = 0; e < 4; ++e) {
+            const float l = sl[e] * scale2 * rs_cur[e];
+            lg[e] = (mask >> (4 * g + e)) & 1u ? l : -INFINITY;
             tmax = fmaxf(tmax, lg[e]);
         }
-        tmax = max_g(tmax);
-        const float m_new = fmaxf(m_run, tmax);
-        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);   // 0 from -inf
-        l_run *= alpha;
+        tmax = max_g(tmax);                   // head c over the row half's 16 rows
+        if (__builtin_amdgcn_ballot_w64(tmax > m_ref + kLazy) != 0) {
+            const float m_new = fmaxf(m_ref, tmax);
+            const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_ref - m_new);   // 0 from -inf
+            l_run *= alpha;
 #pragma unroll
-        for (int b = 0; b < kQDB; ++b) o[b] *= alpha;
-        m_run = m_new;
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        float pv[8];
+            for (int b = 0; b < kHDB; ++b) o[b] *= alpha;
+            m_ref = m_new;
+        }
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        float pv[4];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
+        for (int e = 0; e < 4; ++e) {
             const float p = __builtin_amdgcn_exp2f(lg[e] - m_use);
             l_run += p;
             pv[e] = p * rs_cur[e];
         }
-        u32x4 ph, pl;
-        split8<FP>(pv, ph, pl);
+        const u32x4 pp = split4_fold<FP>(pv);
         // PV of step j; V^T of step jq in place
 #pragma unroll
-        for (int i = 0; i < kQDB; ++i) {
-            o[i] = mma<FP>(va[i], ph, o[i]);
-            o[i] = mma<FP>(va[i], pl, o[i]);
-            if (QK) va[i] = tr_frag(tn + pv_base, b0 + i);
+        for (int i = 0; i < kHDB; ++i) {
+            o[i] = mma<FP>(u32x4{va[i][0], va[i][1], va[i][0], va[i][1]}, pp, o[i]);
+            if (QK) va[i] = __builtin_bit_cast(u32x2, lds_read_tr16(tn + pv_base + 32 * (bd0 + i)));
         }
     };
     // QK and V^T of step 0 alone.
     auto first = [&](auto fq) __attribute__((always_inline)) {
         constexpr bool FQ = decltype(fq)::value;
         const unsigned char *tn = ring;
+        acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[1] = acc[0];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
+        for (int s = 0; s < kHKs; ++s) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(tn + qk_base + 64 * (sg0 + s));
+            acc[s & 1] = mma<FQ>(x, qh[s], acc[s & 1]);
+            acc[s & 1] = mma<FQ>(x, ql[s], acc[s & 1]);
+        }
 #pragma unroll
-            for (int p = 0; p < 2; ++p) acc[h][p] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < kQKs; ++s)
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const u32x4 x = *reinterpret_cast<const u32x4 *>(tn + h * kHalfBuf + qk_base + 64 * (sg0 + s));
-                acc[h][s & 1] = mma<FQ>(x, qh[s], acc[h][s & 1]);
-                acc[h][s & 1] = mma<FQ>(x, ql[s], acc[h][s & 1]);
-            }
-#pragma unroll
-        for (int i = 0; i < kQDB; ++i) va[i] = tr_frag(tn + pv_base, b0 + i);
+        for (int i = 0; i < kHDB; ++i) va[i] = __builtin_bit_cast(u32x2, lds_read_tr16(tn + pv_base + 32 * (bd0 + i)));
     };
     // Barrier k: step k+2 may be used (the producers have waited for its loads, and widened it
     // if E4M3), the partial logits written before it are published, and this wave's QK and V^T
@@ -494,7 +527,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         constexpr bool FJ = decltype(fj)::value, FN = decltype(fn)::value;
         if (FJ && !FN) to_bf16_pair();
 #pragma unroll
-        for (int e = 0; e < 8; ++e) rs_cur[e] = rs_next[e];
+        for (int e = 0; e < 4; ++e) rs_cur[e] = rs_next[e];
         step(fj, fn, std::true_type{}, j, j + 1);
         read_scales(fn, j + 1);
         publish(j + 1);
@@ -508,16 +541,51 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     }
     for (; j + 1 < n; ++j) body(BF16T{}, BF16T{}, j);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) rs_cur[e] = rs_next[e];
+    for (int e = 0; e < 4; ++e) rs_cur[e] = rs_next[e];
     if (j < n_raw) step(F16T{}, F16T{}, std::false_type{}, j, j);
     else step(BF16T{}, BF16T{}, std::false_type{}, j, j);
 
-    l_run = sum_g(l_run);                     // the same in every wave
+    // ---- the two row halves merged: wave (rh, dh) keeps dims 256 dh + 128 rh .. + 127 (quarter
+    // 2 dh + rh) and takes the other row half's (m, l, O) for them through LDS.
+    l_run = sum_g(l_run);                     // head c over this row half
+    wait_lds();
+    __syncthreads();                          // the producers' loads have landed; the ring is free
+    if (g == 0) {
+        s_m[wave * kWH + c] = m_ref;
+        s_l[wave * kWH + c] = l_run;
+    }
+    float *xo = reinterpret_cast<float *>(ring);                     // [wave][block][lane][4]
+    if (rh == 0) {
+#pragma unroll
+        for (int i = 0; i < kQDB; ++i) *reinterpret_cast<f32x4 *>(xo + ((wave * kQDB + i) * kWave + lane) * 4) = o[kQDB + i];
+    } else {
+#pragma unroll
+        for (int i = 0; i < kQDB; ++i) *reinterpret_cast<f32x4 *>(xo + ((wave * kQDB + i) * kWave + lane) * 4) = o[i];
+    }
+    wait_lds();
+    __syncthreads();
+    const int partner = wave ^ 2;             // same dim half, other row half
+    const float mo = s_m[partner * kWH + c], lo_ = s_l[partner * kWH + c];
+    const float m_run = fmaxf(m_ref, mo);
+    const float f_own = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_run);
+    const float f_oth = mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mo - m_run);
+    const float l_tot = l_run * f_own + lo_ * f_oth;
+    f32x4 om[kQDB];
+    auto merge_half = [&](auto half) __attribute__((always_inline)) {
+        constexpr int H0 = decltype(half)::value * kQDB;
+#pragma unroll
+        for (int i = 0; i < kQDB; ++i)
+            om[i] = o[H0 + i] * f_own + *reinterpret_cast<const f32x4 *>(xo + ((partner * kQDB + i) * kWave + lane) * 4) * f_oth;
+    };
+    if (rh == 0) merge_half(std::integral_constant<int, 0>{});
+    else merge_half(std::integral_constant<int, 1>{});
+    const int b0 = (2 * dh + rh) * kQDB;      // this wave's quarter, as dim blocks
+
     if (a.n_chunks == 1) {
-        const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+        const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float *orow = a.out + (q * a.H + h0 + c) * (int64_t)kD + 16 * b0 + 4 * g;
 #pragma unroll
-        for (int b = 0; b < kQDB; ++b) *reinterpret_cast<f32x4 *>(orow + 16 * b) = o[b] * inv;
+        for (int b = 0; b < kQDB; ++b) *reinterpret_cast<f32x4 *>(orow + 16 * b) = om[b] * inv;
         return;
     }
     // ---- split union: the workgroup's record, then the last workgroup of the (query, head
@@ -528,14 +596,14 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     const int64_t grp = q * a.n_hg + hg;
     const __amdgpu_buffer_rsrc_t rec_rs = rsrc(a.part + grp * nc * (int64_t)kDqRec, (uint32_t)(nc * kDqRec * 4));
     const uint32_t rec0 = (uint32_t)(chunk * kDqRec * 4);
-    const uint32_t o_off = 4 * (2 * kWH + (wave * kQDB * kWave + lane) * 4);   // + b * 1 KiB
+    const uint32_t o_off = 4 * (2 * kWH + (b0 * kWave + lane) * 4);   // + b * 1 KiB
     if (wave == 0 && g == 0) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m_run), rec_rs, rec0 + 4 * c, 0, kSc1);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_run), rec_rs, rec0 + 4 * (kWH + c), 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(l_tot), rec_rs, rec0 + 4 * (kWH + c), 0, kSc1);
     }
 #pragma unroll
     for (int b = 0; b < kQDB; ++b)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, o[b]), rec_rs, rec0 + o_off + b * 1024, 0, kSc1);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, om[b]), rec_rs, rec0 + o_off + b * 1024, 0, kSc1);
     asm volatile("s_waitcnt vmcnt(0)" : : : "memory");   // this wave's record stores are done
     __syncthreads();                                      // ... and every wave's
     uint32_t *s_flag = reinterpret_cast<uint32_t *>(s_xch);
