@@ -31,9 +31,10 @@ constexpr int kFBpi = 2;
 constexpr int64_t kFCUs = 256;
 constexpr int64_t kFSlots = 2 * kFCUs;
 
-// A chunk of up to EPT * 512 rows (`rows` per chunk): each thread selects over EPT keys.
+// A chunk of up to EPT * 512 rows (`rows` per chunk): each thread selects over EPT keys.  Two
+// workgroups share a CU (4 waves per SIMD: at most 128 VGPRs).
 template <int EPT, bool FP8>
-__global__ __launch_bounds__(kNT) void indexer_select_kernel(
+__global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
     int T, int64_t N, int K, int rows, int64_t chunks,
     const uint16_t *__restrict__ qI, const float *__restrict__ w, KeyRows keys,
     const int32_t *__restrict__ n_vis, int32_t *__restrict__ out, uint32_t *__restrict__ out_keys)

@@ -5,6 +5,8 @@
 
 #include "common.hpp"
 
+#include <type_traits>
+
 namespace ds4a {
 
 namespace {
@@ -20,12 +22,13 @@ constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4
 constexpr int kMaxK = 2048;
 
 struct SelectShared {
-    uint32_t hist[kBins];
-    uint32_t wave_a[kNW];
-    uint32_t wave_b[kNW];
-    uint32_t res[4];
-    int32_t sel_id[kMaxK];      // the selected set, in row order, before the coalesced copy-out
-    uint32_t sel_key[kMaxK];
+    uint32_t hist[2][kBins];    // digit histograms of alternate passes
+    alignas(16) uint32_t wave_a[kNW];
+    uint32_t wave_mn[kNW];
+    uint32_t wave_mx[kNW];
+    uint32_t res[2][4];         // boundary bin of alternate passes
+    int32_t sel_id[kMaxK + kWave];   // the selected set, in row order, before the coalesced copy-out;
+    uint32_t sel_key[kMaxK + kWave]; // slots from kMaxK on take the stores of keys not taken
 };
 
 // Chunk sizes of the levels that produced a candidate list, first level on rows.
@@ -35,76 +38,64 @@ struct Levels {
 };
 
 // Valid candidates of a query with nv visible rows after the given levels: each chunk of
-// a level keeps min(K, its size), and the kept ones are stored contiguously.
+// a level keeps min(K, its size), and the kept ones are stored contiguously.  In 32 bits: nv
+// < 2^31, and a merged level's chunks hold at least 4K rows, so every count stays below 2^30.
 __device__ __forceinline__ int64_t cand_count(int64_t nv, int K, const Levels &lv) {
-    int64_t c = nv;
+    uint32_t c = (uint32_t)nv;
     for (int l = 0; l < lv.n; ++l) {
-        const int64_t m = c % lv.ch[l];
-        c = (c / lv.ch[l]) * K + (m < K ? m : K);
+        const uint32_t ch = (uint32_t)lv.ch[l];
+        const uint32_t m = c % ch;
+        c = (c / ch) * (uint32_t)K + (m < (uint32_t)K ? m : (uint32_t)K);
     }
-    return c;
+    return (int64_t)c;
 }
 
-// Thread t receives src_a/src_b[t*EPT .. t*EPT + EPT - 1] (0 past n, n <= EPT*kNT, n uniform
-// across the workgroup) through LDS stages of EPT*kNT words each: the global loads of both
-// arrays are lane-consecutive (one 256-byte run per wave instruction) and all issued before
-// any is used; indices past n are clamped to n - 1, so no load is conditional.  Every thread
-// of the workgroup calls it.
-template <int EPT>
-__device__ __forceinline__ void load_blocked2(const uint32_t *__restrict__ src_a, const uint32_t *__restrict__ src_b,
-                                              int n, uint32_t (&va)[EPT], uint32_t (&vb)[EPT], uint32_t *stage_a,
-                                              uint32_t *stage_b) {
-    if (n > 0) {
-        uint32_t xa[EPT], xb[EPT];
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const int j = (int)threadIdx.x + i * kNT;
-            xa[i] = src_a[j < n ? j : n - 1];
-            xb[i] = src_b[j < n ? j : n - 1];
-        }
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            stage_a[(int)threadIdx.x + i * kNT] = xa[i];
-            stage_b[(int)threadIdx.x + i * kNT] = xb[i];
-        }
-    }
-    __syncthreads();
-    const int j0 = (int)threadIdx.x * EPT;
-#pragma unroll
-    for (int i = 0; i < EPT; ++i) {
-        va[i] = j0 + i < n ? stage_a[j0 + i] : 0u;
-        vb[i] = j0 + i < n ? stage_b[j0 + i] : 0u;
-    }
+// A buffer resource over `bytes` bytes at p (wave-uniform): loads past its end return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t list_rsrc(const void *p, uint32_t bytes) {
+    const uint64_t a = reinterpret_cast<uintptr_t>(p);
+    const uint64_t au = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>(au), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
 }
 
-// Exclusive prefix sum over the workgroup.
+// Exclusive prefix sum over the workgroup (kNW waves: the totals are read at once, not one
+// dependent read per earlier wave).
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
+    static_assert(kNW == 8, "two 16-byte reads cover the wave totals");
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const uint32_t incl = wave_incl_scan_dpp(v);
     if (lane == kWave - 1) wave_sums[wave] = incl;
     __syncthreads();
+    const u32x4 s0 = *reinterpret_cast<const u32x4 *>(wave_sums);
+    const u32x4 s1 = *reinterpret_cast<const u32x4 *>(wave_sums + 4);
     uint32_t off = 0;
-    for (int i = 0; i < wave; ++i) off += wave_sums[i];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        off += i < wave ? s0[i] : 0u;
+        off += i + 4 < wave ? s1[i] : 0u;
+    }
     __syncthreads();
     return off + incl - v;
 }
 
+// Min and max over the workgroup.  Its slots are used once per select, so no barrier follows.
 template <int NT>
 __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     wave_minmax_u32(kmin, kmax);
     if (lane == 0) {
-        sm.wave_a[wave] = kmin;
-        sm.wave_b[wave] = kmax;
+        sm.wave_mn[wave] = kmin;
+        sm.wave_mx[wave] = kmax;
     }
     __syncthreads();
     kmin = 0xFFFFFFFFu;
     kmax = 0u;
+#pragma unroll
     for (int i = 0; i < NT / kWave; ++i) {
-        kmin = sm.wave_a[i] < kmin ? sm.wave_a[i] : kmin;
-        kmax = sm.wave_b[i] > kmax ? sm.wave_b[i] : kmax;
+        kmin = sm.wave_mn[i] < kmin ? sm.wave_mn[i] : kmin;
+        kmax = sm.wave_mx[i] > kmax ? sm.wave_mx[i] : kmax;
     }
-    __syncthreads();
 }
 
 // Selects the `need` largest of the n keys held in registers (thread t holds positions
@@ -127,49 +118,55 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
                 kmax = key[i] > kmax ? key[i] : kmax;
             }
         }
-        static_assert(NT % kWave == 0 && NT <= kNT && NT >= kWave * 2, "workgroup size");
+        static_assert(NT % kWave == 0 && NT <= kNT && NT >= kWave * 2 && kBins <= NT - kWave, "workgroup size");
+        for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[0][b] = 0;   // published by the next barrier
         block_minmax<NT>(kmin, kmax, sm);
         int bit = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
         uint32_t pmask = bit >= 32 ? 0u : ~((1u << bit) - 1u);
         uint32_t prefix = kmin & pmask;
         uint32_t remaining = (uint32_t)need;
         bool whole_bin = false;
+        // Passes alternate between two histograms and two result slots: while wave 0 scans this
+        // pass's histogram, the other waves clear the one the next pass counts into (last read
+        // by the previous pass's scan), so each pass needs two barriers.
+        int pb = 0;
         while (bit > 0) {
             const int width = bit < 8 ? bit : 8;
             const int shift = bit - width;
             const uint32_t dmask = (1u << width) - 1u;
-            for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[b] = 0;
-            __syncthreads();
+            uint32_t *hist = sm.hist[pb];
 #pragma unroll
             for (int i = 0; i < EPT; ++i)
-                if (j0 + i < n && (key[i] & pmask) == prefix) atomicAdd(&sm.hist[(key[i] >> shift) & dmask], 1u);
+                if (j0 + i < n && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
             __syncthreads();
             if (threadIdx.x < kWave) {
                 // lane l owns bins 255-4l .. 252-4l, highest first
                 uint32_t v[4], s = 0;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    v[i] = sm.hist[kBins - 1 - (4 * lane + i)];
+                    v[i] = hist[kBins - 1 - (4 * lane + i)];
                     s += v[i];
                 }
                 uint32_t cum = wave_incl_scan_dpp(s) - s;
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     if (cum < remaining && remaining <= cum + v[i]) {
-                        sm.res[0] = (uint32_t)(kBins - 1 - (4 * lane + i));
-                        sm.res[1] = cum;
-                        sm.res[2] = v[i];
+                        sm.res[pb][0] = (uint32_t)(kBins - 1 - (4 * lane + i));
+                        sm.res[pb][1] = cum;
+                        sm.res[pb][2] = v[i];
                     }
                     cum += v[i];
                 }
+            } else if (threadIdx.x < kWave + kBins) {
+                sm.hist[pb ^ 1][threadIdx.x - kWave] = 0;
             }
             __syncthreads();
-            remaining -= sm.res[1];
-            prefix |= sm.res[0] << shift;
+            remaining -= sm.res[pb][1];
+            prefix |= sm.res[pb][0] << shift;
             pmask |= dmask << shift;
             bit = shift;
-            whole_bin = sm.res[2] == remaining;   // the whole boundary bin is taken
-            __syncthreads();
+            whole_bin = sm.res[pb][2] == remaining;   // the whole boundary bin is taken
+            pb ^= 1;
             if (whole_bin) break;
         }
         T = prefix;
@@ -191,24 +188,26 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
     const uint32_t packed = block_excl_scan((gt << 16) | eq, sm.wave_a);
     uint32_t tie_rank = packed & 0xFFFFu;
     uint32_t pos = (packed >> 16) + (tie_rank < ties ? tie_rank : ties);
-    if (need > 0) {
+    // Branch-free: a key not taken is stored to this lane's spare slot past kMaxK.  Exactly
+    // need <= K keys are taken, so a taken key's position is below K.
+    auto collect = [&](auto keys_tag) __attribute__((always_inline)) {
+        constexpr bool KEYS = decltype(keys_tag)::value;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            if (j0 + i < n) {
-                bool take = key[i] > T;
-                if (key[i] == T) {
-                    take = tie_rank < ties;
-                    ++tie_rank;
-                }
-                if (take && pos < (uint32_t)K) {
-                    sm.sel_id[pos] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
-                    sm.sel_key[pos] = key[i];
-                    ++pos;
-                }
-            }
+            const bool valid = j0 + i < n;
+            const bool eqk = valid && key[i] == T;
+            const bool take = (valid && key[i] > T) || (eqk && tie_rank < ties);
+            tie_rank += eqk ? 1u : 0u;
+            const uint32_t dst = take ? pos : (uint32_t)(kMaxK + lane);
+            sm.sel_id[dst] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
+            if (KEYS) sm.sel_key[dst] = key[i];
+            pos += take ? 1u : 0u;
         }
+    };
+    if (need > 0) {
+        if (out_keys) collect(std::true_type{});
+        else collect(std::false_type{});
     }
-    (void)lane;
     __syncthreads();
     const int taken = need > 0 ? need : 0;
     for (int i = threadIdx.x; i < K; i += NT) {

@@ -91,14 +91,32 @@ __global__ __launch_bounds__(kNT) void topk_cand_kernel(int64_t N, int K, Levels
     const int n = rem <= 0 ? 0 : (rem < chunk ? (int)rem : chunk);
     const uint32_t *ik = in_keys + q * in_stride + c0;
     const int32_t *ii = in_ids + q * in_stride + c0;
-    __shared__ uint32_t stage[2][EPT * kNT];
+    // Thread t's contiguous run of candidates straight into registers, 16 bytes per load when
+    // both lists start 16-byte aligned (K a multiple of 4), else 4; the buffers end at the list's
+    // n entries, so positions past it read as zeros.
+    static_assert(EPT % 4 == 0, "candidates are loaded four at a time");
+    const __amdgpu_buffer_rsrc_t rk = list_rsrc(ik, (uint32_t)n * 4u), ri = list_rsrc(ii, (uint32_t)n * 4u);
+    const int j0 = threadIdx.x * EPT;
     uint32_t key[EPT];
     int32_t id[EPT];
-    {
-        uint32_t tmp[EPT];
-        load_blocked2<EPT>(ik, reinterpret_cast<const uint32_t *>(ii), n, key, tmp, stage[0], stage[1]);
+    if (((reinterpret_cast<uintptr_t>(ik) | reinterpret_cast<uintptr_t>(ii)) & 15u) == 0) {
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) id[i] = (int32_t)tmp[i];
+        for (int v = 0; v < EPT / 4; ++v) {
+            const uint32_t off = (uint32_t)(j0 + 4 * v) * 4u;
+            const u32x4 a = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+            const u32x4 b = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off, 0, 0));
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                key[4 * v + e] = a[e];
+                id[4 * v + e] = (int32_t)b[e];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            key[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)(j0 + i) * 4u, 0, 0);
+            id[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j0 + i) * 4u, 0, 0);
+        }
     }
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + c) * K;
