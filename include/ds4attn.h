@@ -37,7 +37,8 @@
 extern "C" {
 #endif
 
-#define DS4A_VERSION 2
+/* 2: raw_vis in the attention calls; 3: ds4a_indexer_topk_mqa(_fp8) */
+#define DS4A_VERSION 3
 
 typedef enum {
     DS4A_OK = 0,
@@ -198,6 +199,41 @@ int ds4a_sparse_mqa_noalloc(int U, int T, int H, int D, int n_rot, int W, int64_
                             const void *raw_kv, const int32_t *raw_vis, const void *comp_kv,
                             const int32_t *idx, float scale, float *out, void *stream);
 
+/* A1 + A2 + A3-A6 in one call: ds4a_indexer_topk on (idx_q, idx_w, idx_k, n_vis) followed by
+ * ds4a_sparse_mqa on the selected rows, with the same results bit for bit (sections 3-1 to 3-3
+ * of "Reading the architecture of DwarfStar (ds4.c), part 1/8": the indexer picks the rows
+ * that the main attention then reads).  In decode shapes (T < 4, at least 128 chunk
+ * workgroups for the fused select, few enough queries that the attention keeps each union
+ * whole) the last merge level of the top-k runs inside the attention kernel: each workgroup
+ * selects its query's rows from the chunks' candidates itself, so the selection needs no
+ * launch and no round trip through memory of its own.  Otherwise the call launches what the
+ * two calls would.
+ * Arguments as for ds4a_indexer_topk (Hi, Di, K, idx_q, idx_w, idx_k, n_vis) and
+ * ds4a_sparse_mqa (H, D, n_rot, W, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis, comp_kv,
+ * scale, out), with N the rows of both caches, and
+ *   idx      : int32 [U][T][K] receiving the selected rows, or NULL
+ *   workspace: ds4a_workspace_bytes(4, U, T, N, K, H, W) bytes, zero-filled before its first
+ *              use (it holds the attention's arrival counters, which every call leaves zero);
+ *              calls that share a workspace must be ordered on one stream
+ */
+int ds4a_indexer_topk_mqa(int U, int T, int64_t N, int Hi, int Di, int K,
+                          const void *idx_q, const float *idx_w, const void *idx_k,
+                          const int32_t *n_vis, int H, int D, int n_rot, int W,
+                          const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                          const void *raw_kv, const int32_t *raw_vis, const void *comp_kv,
+                          float scale, int32_t *idx, float *out,
+                          void *workspace, size_t workspace_bytes, void *stream);
+/* The same on FP8-stored indexer keys and compressed rows (formats as at ds4a_indexer_topk_fp8
+ * and ds4a_sparse_mqa_fp8); the results are those of those two calls, bit for bit. */
+int ds4a_indexer_topk_mqa_fp8(int U, int T, int64_t N, int Hi, int Di, int K,
+                              const void *idx_q, const float *idx_w, const uint8_t *idx_k8,
+                              const float *idx_k_scale, const int32_t *n_vis, int H, int D,
+                              int n_rot, int W, const void *q, int q_dtype, const int64_t *q_pos,
+                              double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+                              const uint8_t *comp_kv8, const float *comp_scale, float scale,
+                              int32_t *idx, float *out,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
 /* Dense attention for the layers that have no indexer (section 3-2 of the same
  * page: ratio-128 layers fold 128 tokens into one row and are few enough to be
  * read whole; ratio-0 layers, the first two of Flash, keep only the raw window).
@@ -331,9 +367,10 @@ int ds4a_rope_q(int U, int T, int H, int D, int n_rot, const void *q, int q_dtyp
                 const int64_t *q_pos, double rope_theta, float *q_out, void *stream);
 
 /* Workspace bytes for `which` = 0 (ds4a_topk_select; H and W ignored),
- * 1 (ds4a_sparse_mqa), 2 (ds4a_indexer_topk; H and W ignored) or 3
- * (ds4a_dense_mqa; K ignored, N may be 0).  0 means no workspace is needed
- * (NULL is accepted), or that the arguments are invalid.
+ * 1 (ds4a_sparse_mqa), 2 (ds4a_indexer_topk; H and W ignored), 3
+ * (ds4a_dense_mqa; K ignored, N may be 0) or 4 (ds4a_indexer_topk_mqa and its FP8
+ * form; never 0 for valid arguments).  0 means no workspace is needed (NULL is
+ * accepted), or that the arguments are invalid.
  * Host-only, never touches the GPU. */
 size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, int W);
 

@@ -86,6 +86,22 @@ int hip_status(const char *fn, hipError_t e) {
     return fail(DS4A_E_HIP, "%s: HIP error %d (%s)", fn, (int)e, hipGetErrorString(e));
 }
 
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Workspace of ds4a_indexer_topk_mqa: idx when the caller passes none, then the top-k's, then
+// the attention's (whose counters must start at zero).
+struct StepLayout {
+    size_t idx, topk, attn, total;
+};
+StepLayout step_layout(int U, int T, int64_t N, int K, int H, int W) {
+    StepLayout l;
+    l.idx = round256((size_t)U * (size_t)T * (size_t)K * 4);
+    l.topk = round256(ds4a::indexer_topk_workspace_bytes(U, T, N, K));
+    l.attn = ds4a::plan_attn(U, T, H, W, K).workspace_bytes;
+    l.total = l.idx + l.topk + l.attn;
+    return l;
+}
+
 }  // namespace
 
 extern "C" {
@@ -103,6 +119,10 @@ size_t ds4a_workspace_bytes(int which, int U, int T, int64_t N, int K, int H, in
     if (U < 1 || T < 1 || N < 1 || N > kMaxRows || K < 1 || K > DS4A_MAX_TOPK) return 0;
     if (which == 0) return ds4a::topk_workspace_bytes((int64_t)U * T, N, K);
     if (which == 2) return ds4a::indexer_topk_workspace_bytes(U, T, N, K);
+    if (which == 4) {
+        if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW) return 0;
+        return step_layout(U, T, N, K, H, W).total;
+    }
     if (which == 1) {
         if (H < 16 || H % 16 || H > DS4A_MAX_HEADS || W < 0 || W % 32 || W > DS4A_MAX_WINDOW) return 0;
         return ds4a::plan_attn(U, T, H, W, K).workspace_bytes;
@@ -352,6 +372,89 @@ int ds4a_sparse_mqa_fp8(int U, int T, int H, int D, int n_rot, int W, int64_t N,
                         float scale, float *out, void *workspace, size_t workspace_bytes, void *stream) {
     return sparse_mqa("ds4a_sparse_mqa_fp8", U, T, H, D, n_rot, W, N, K, q, q_dtype, q_pos, rope_theta, raw_kv,
                       raw_vis, comp_kv8, comp_scale, true, idx, scale, out, workspace, workspace_bytes, stream);
+}
+
+namespace {
+
+// A1 + A2 + A3-A6 in one call.  Where the fused select runs with several chunks per query and
+// the attention's 16-head kernel takes whole unions, the last merge level runs inside the
+// attention kernel; otherwise the two calls' launches, one after the other.
+static int indexer_topk_mqa(const char *fn, int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q,
+                            const float *idx_w, ds4a::KeyRows idx_k, bool fp8k, const int32_t *n_vis, int H, int D,
+                            int n_rot, int W, const void *q, int q_dtype, const int64_t *q_pos, double rope_theta,
+                            const void *raw_kv, const int32_t *raw_vis, const void *comp_kv, const float *comp_scale,
+                            bool fp8r, float scale, int32_t *idx, float *out, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+    if (int rc = check_attn_shape(fn, U, T, H, D, n_rot, W, N, K, q_dtype, rope_theta)) return rc;
+    if (Hi != DS4A_INDEXER_HEADS || Di != DS4A_INDEXER_DIM)
+        return fail(DS4A_E_UNSUPPORTED, "%s: Hi=%d Di=%d (only %d x %d)", fn, Hi, Di, DS4A_INDEXER_HEADS,
+                    DS4A_INDEXER_DIM);
+    if (!(scale == scale) || scale == INFINITY || scale == -INFINITY)
+        return fail(DS4A_E_SHAPE, "%s: scale must be finite", fn);
+    if (N > DS4A_MAX_ATTN_ROWS)
+        return fail(DS4A_E_UNSUPPORTED, "%s: N=%lld (at most %d rows per unit)", fn, (long long)N, DS4A_MAX_ATTN_ROWS);
+    REQUIRE_PTR(idx_q);
+    REQUIRE_PTR(idx_w);
+    REQUIRE_KEYS(idx_k, fp8k);
+    OPTIONAL_PTR(n_vis);
+    REQUIRE_PTR(q);
+    REQUIRE_PTR(q_pos);
+    if (W > 0) REQUIRE_PTR(raw_kv);
+    OPTIONAL_PTR(raw_vis);
+    REQUIRE_COMP(comp_kv, comp_scale, fp8r);
+    OPTIONAL_PTR(idx);
+    REQUIRE_PTR(out);
+    const StepLayout l = step_layout(U, T, N, K, H, W);
+    if (!workspace || workspace_bytes < l.total)
+        return fail(DS4A_E_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, l.total,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (misaligned(workspace)) return fail(DS4A_E_ALIGN, "%s: workspace is not 16-byte aligned", fn);
+    char *ws = static_cast<char *>(workspace);
+    void *ws_topk = ws + l.idx;
+    void *ws_attn = ws + l.idx + l.topk;
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const uint16_t *iq = static_cast<const uint16_t *>(idx_q);
+    const uint16_t *raw = static_cast<const uint16_t *>(raw_kv);
+    const float *cs = fp8r ? comp_scale : nullptr;
+    const ds4a::AttnPlan plan = ds4a::plan_attn(U, T, H, W, K);
+    if (ds4a::indexer_candidates_apply(U, T, N, K) && ds4a::attn_dq_merge_apply(plan, 0)) {
+        ds4a::CandList cl;
+        hipError_t e = ds4a::launch_indexer_candidates(U, T, N, K, iq, idx_w, idx_k, n_vis, ws_topk,
+                                                       ds4a::kAttnMergeMax, &cl, st);
+        if (e != hipSuccess) return hip_status(fn, e);
+        return hip_status(fn, ds4a::launch_attn_dq_merge(plan, U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos,
+                                                         rope_theta, raw, comp_kv, cs, cl, n_vis, raw_vis, scale, idx,
+                                                         out, st));
+    }
+    int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(ws);
+    hipError_t e = ds4a::launch_indexer_topk(U, T, N, K, iq, idx_w, idx_k, n_vis, ix, ws_topk, st);
+    if (e != hipSuccess) return hip_status(fn, e);
+    return hip_status(fn, ds4a::launch_attn(U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos, rope_theta, raw, comp_kv,
+                                           cs, ix, nullptr, raw_vis, scale, out, ws_attn, st));
+}
+
+}  // namespace
+
+int ds4a_indexer_topk_mqa(int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q, const float *idx_w,
+                          const void *idx_k, const int32_t *n_vis, int H, int D, int n_rot, int W, const void *q,
+                          int q_dtype, const int64_t *q_pos, double rope_theta, const void *raw_kv,
+                          const int32_t *raw_vis, const void *comp_kv, float scale, int32_t *idx, float *out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    return indexer_topk_mqa("ds4a_indexer_topk_mqa", U, T, N, Hi, Di, K, idx_q, idx_w, ds4a::KeyRows{idx_k, nullptr},
+                            false, n_vis, H, D, n_rot, W, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis, comp_kv,
+                            nullptr, false, scale, idx, out, workspace, workspace_bytes, stream);
+}
+
+int ds4a_indexer_topk_mqa_fp8(int U, int T, int64_t N, int Hi, int Di, int K, const void *idx_q,
+                              const float *idx_w, const uint8_t *idx_k8, const float *idx_k_scale,
+                              const int32_t *n_vis, int H, int D, int n_rot, int W, const void *q, int q_dtype,
+                              const int64_t *q_pos, double rope_theta, const void *raw_kv, const int32_t *raw_vis,
+                              const uint8_t *comp_kv8, const float *comp_scale, float scale, int32_t *idx, float *out,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+    return indexer_topk_mqa("ds4a_indexer_topk_mqa_fp8", U, T, N, Hi, Di, K, idx_q, idx_w,
+                            ds4a::KeyRows{idx_k8, idx_k_scale}, true, n_vis, H, D, n_rot, W, q, q_dtype, q_pos,
+                            rope_theta, raw_kv, raw_vis, comp_kv8, comp_scale, true, scale, idx, out, workspace,
+                            workspace_bytes, stream);
 }
 
 int ds4a_dense_mqa(int U, int T, int H, int D, int n_rot, int W, int64_t N, const void *q, int q_dtype,

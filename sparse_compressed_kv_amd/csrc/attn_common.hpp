@@ -46,6 +46,15 @@ struct AttnArgs {
     uint32_t *count;                         // split unions: arrivals per (query, 16-head group)
     float *part;                             // split unions: records
     double log2_theta;
+    // Last top-k merge level inside the 16-head kernel (unsplit unions): each query's final
+    // candidate list, selected by the workgroup itself into its row table.
+    const uint32_t *cand_keys;
+    const int32_t *cand_ids;
+    int64_t cand_stride;
+    const int32_t *cand_nvis;                // the indexer's visible rows per query, or NULL
+    int32_t *idx_out;                        // the selected rows [U][T][K], or NULL
+    int lv_n;                                // levels that produced the list, and their chunk rows
+    int lv_ch[12];
 };
 
 // Wait until at most N vector-memory operations of this wave are in flight.  The row loads

@@ -42,6 +42,7 @@
 #include "attn_common.hpp"
 #include "launch.hpp"
 #include "rope.hpp"
+#include "select.hpp"
 
 #include <math.h>
 #include <mutex>
@@ -72,6 +73,10 @@ template <bool E8> constexpr int kDqMaxLds = kDqRowTabOff<E8> + 4 * kSR * kDqMax
 static_assert(kDqMaxLds<false> <= 160 * 1024 && kDqMaxLds<true> <= 160 * 1024, "LDS of one workgroup");
 static_assert(kDqMaxChunkSteps * kSR % kAT == 0, "row table fill");
 constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[quarter][block][lane][4]
+constexpr int kMEpt = 16;                     // last merge level in the kernel: candidates per thread
+constexpr int kDqMergeMax = kMEpt * kDqT;     // ... and per query (6,144)
+static_assert(sizeof(SelectShared) <= kBuf, "the selection's scratch fits in one ring slot");
+static_assert(kDqMergeMax == kAttnMergeMax, "the host's bound on the in-kernel merge");
 static_assert(kAW * kQDB * kWave * 16 <= kDqNB * kBuf, "row-half merge fits in the ring");
 static_assert(kAW * kQKs * 2 * kWave * 16 <= kBuf, "query quarters fit in one ring slot");
 constexpr float kLazy = 8.f;                  // reference slack (log2 units): P stays below 2^8
@@ -181,9 +186,14 @@ struct DqProducer {
     }
 };
 
-template <bool QF32, bool DENSE, bool E8>
+// MERGE (sparse, unsplit unions): the workgroup selects the query's K rows from the last
+// candidate list of the chunked top-k itself (every wave: kMEpt candidates per thread, the same
+// workgroup radix select as the top-k kernels, so the set is the same), straight into its row
+// table; the workgroup of head group 0 also writes them out.
+template <bool QF32, bool DENSE, bool E8, bool MERGE = false>
 __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
 {
+    static_assert(!(MERGE && DENSE), "the merge feeds the sparse union");
     constexpr int NB = kDqNB;
     extern __shared__ __align__(16) unsigned char smem[];
     unsigned char *ring = smem;
@@ -228,6 +238,46 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     const int raw_lim = a.raw_vis ? (int)clamp_nvis(a.raw_vis, q, a.W) : a.W;
     const int64_t j_lim = DENSE ? clamp_nvis(a.n_vis, q, a.N) : a.N;
 
+    // The last merge level (every thread of the workgroup): the selection lands in s_row[W ..
+    // W + K) in ascending row order, -1 past the selected; ring slot 3 holds the select's
+    // scratch (no rows reach it before the barrier of step -2).
+    auto select_final = [&]() __attribute__((always_inline)) {
+        Levels lv = {};
+        lv.n = a.lv_n;
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) lv.ch[l] = a.lv_ch[l];
+        int64_t count = cand_count(clamp_nvis(a.cand_nvis, q, a.N), a.K, lv);
+        if (count > a.cand_stride) count = a.cand_stride;
+        const int nc = (int)count;
+        const uint32_t *ik = a.cand_keys + q * a.cand_stride;
+        const int32_t *ii = a.cand_ids + q * a.cand_stride;
+        const __amdgpu_buffer_rsrc_t rk = list_rsrc(ik, (uint32_t)nc * 4u), ri = list_rsrc(ii, (uint32_t)nc * 4u);
+        const int j0 = tid * kMEpt;
+        uint32_t key[kMEpt];
+        int32_t id[kMEpt];
+        if (((reinterpret_cast<uintptr_t>(ik) | reinterpret_cast<uintptr_t>(ii)) & 15u) == 0) {
+#pragma unroll
+            for (int v = 0; v < kMEpt / 4; ++v) {
+                const uint32_t off = (uint32_t)(j0 + 4 * v) * 4u;
+                const u32x4 x = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, off, 0, 0));
+                const u32x4 y = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off, 0, 0));
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    key[4 * v + e] = x[e];
+                    id[4 * v + e] = (int32_t)y[e];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < kMEpt; ++i) {
+                key[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)(j0 + i) * 4u, 0, 0);
+                id[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j0 + i) * 4u, 0, 0);
+            }
+        }
+        SelectShared &sm = *reinterpret_cast<SelectShared *>(ring + (NB - 1) * kBuf);
+        block_select<kMEpt, true, kDqT>(key, id, 0, nc, a.K < nc ? a.K : nc, a.K, s_row + (a.W - rho0), nullptr, sm);
+    };
+
     if (wave >= kAW) {
         // ---- producer wave: raw steps' loads at once (they need no index), the first
         // compressed steps' after the row table, then per step: wait for step k+2's loads
@@ -247,6 +297,10 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         i32x4 ent[4];
         ld.entries(-1, ent);                  // no entries (raw steps)
         if (n_raw > 0) ld.issue(0, ent);
+        if (MERGE) {
+            select_final();
+            __syncthreads();                  // the selection is in the row table
+        }
         __syncthreads();                      // row table
 #pragma unroll
         for (int j = 0; j < NB - 1; ++j)
@@ -287,7 +341,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     const int64_t pos = a.pos[q];             // first: the rotation angles need only it
     constexpr int kPer = kDqMaxChunkSteps * kSR / kAT;        // index entries per thread (6)
     int32_t v_idx[kPer];
-    if (!DENSE) {
+    if (!DENSE && !MERGE) {
         const int32_t *idx_q = a.idx + q * (int64_t)a.K;
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
@@ -316,13 +370,30 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
     }
+    if (MERGE) {
+        select_final();
+        __syncthreads();                      // the selection is in the row table
+        if (a.idx_out && hg == 0) {
+            int32_t *dst = a.idx_out + q * (int64_t)a.K;
+            for (int k = tid; k < a.K; k += kAT) dst[k] = s_row[a.W - rho0 + k];
+        }
+    }
     if (!DENSE) {
         // row table (local union row -> compressed row or -1) and per-step validity masks
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
             const int i = tid + r * kAT;
-            const int32_t e = (v_idx[r] >= 0 && (int64_t)v_idx[r] < a.N) ? v_idx[r] : -1;
-            if (i < n * kSR) s_row[i] = e;
+            int32_t e;
+            if (MERGE) {
+                // the selection's entries, -1 outside them (raw rows, the last step's tail)
+                const int k = rho0 + i - a.W;
+                e = (i < n * kSR && k >= 0 && k < a.K) ? s_row[i] : -1;
+                e = (e >= 0 && (int64_t)e < a.N) ? e : -1;
+                if (i < n * kSR && (k < 0 || k >= a.K)) s_row[i] = e;
+            } else {
+                e = (v_idx[r] >= 0 && (int64_t)v_idx[r] < a.N) ? v_idx[r] : -1;
+                if (i < n * kSR) s_row[i] = e;
+            }
             const int rho = rho0 + i;
             const bool ok = i < n * kSR && (rho < a.W ? rho < raw_lim : e >= 0);
             const uint64_t bits = __builtin_amdgcn_ballot_w64(ok);
@@ -708,6 +779,49 @@ hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t
     a.count = count;
     a.part = part;
     a.log2_theta = log2(theta);
+    hipLaunchKernelGGL(fn, dim3((unsigned)p.blocks), dim3(kDqT), lds, stream, a);
+    return hipGetLastError();
+}
+
+bool attn_dq_merge_apply(const AttnPlan &p, int64_t list_stride) {
+    return p.dq && p.n_chunks == 1 && list_stride <= kDqMergeMax;
+}
+
+hipError_t launch_attn_dq_merge(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q,
+                                int q_bf16, const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                                const float *comp_scale, const CandList &cl, const int32_t *cand_nvis,
+                                const int32_t *raw_vis, float scale, int32_t *idx_out, float *out, hipStream_t stream)
+{
+    if (!attn_dq_merge_apply(p, cl.stride) || cl.n_levels < 1 || cl.n_levels > kMaxLevels) return hipErrorInvalidValue;
+    const bool e8 = comp_scale != nullptr && N > 0;
+    using Fn = void (*)(AttnArgs);
+    const int variant = (q_bf16 ? 1 : 0) + (e8 ? 2 : 0);
+    static const Fn kernels[4] = {attn_dq_kernel<true, false, false, true>, attn_dq_kernel<false, false, false, true>,
+                                  attn_dq_kernel<true, false, true, true>, attn_dq_kernel<false, false, true, true>};
+    static std::once_flag attr_once[4];
+    static hipError_t attr_err[4];
+    const Fn fn = kernels[variant];
+    std::call_once(attr_once[variant], [&] {
+        attr_err[variant] = hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                                                hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                e8 ? kDqMaxLds<true> : kDqMaxLds<false>);
+    });
+    if (attr_err[variant] != hipSuccess) return attr_err[variant];
+    const int lds = (e8 ? kDqRowTabOff<true> : kDqRowTabOff<false>) + 4 * kSR * p.steps_per_chunk;
+    AttnArgs a = {};
+    a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_chunks = p.n_chunks;
+    a.steps_per_chunk = p.steps_per_chunk; a.n_steps = p.n_steps;
+    a.n_items = (int)((int64_t)U * T * p.n_hg * p.n_chunks);
+    a.N = N;
+    a.q = q; a.pos = q_pos; a.raw = raw; a.comp = comp;
+    a.comp_scale = e8 ? comp_scale : nullptr;
+    a.raw_vis = W > 0 ? raw_vis : nullptr;
+    a.scale = scale; a.out = out;
+    a.log2_theta = log2(theta);
+    a.cand_keys = cl.keys; a.cand_ids = cl.ids; a.cand_stride = cl.stride; a.cand_nvis = cand_nvis;
+    a.idx_out = idx_out;
+    a.lv_n = cl.n_levels;
+    for (int l = 0; l < cl.n_levels; ++l) a.lv_ch[l] = cl.level_rows[l];
     hipLaunchKernelGGL(fn, dim3((unsigned)p.blocks), dim3(kDqT), lds, stream, a);
     return hipGetLastError();
 }

@@ -180,4 +180,30 @@ hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *i
     return launch_topk_merge(Q, N, K, fs.rows, fs.chunks, n_vis, idx, workspace, stream);
 }
 
+bool indexer_candidates_apply(int U, int T, int64_t N, int K) {
+    const int64_t Q = (int64_t)U * T;
+    return use_fused(T, Q, N, K) && fused_shape(Q, N, K).chunks > 1;
+}
+
+hipError_t launch_indexer_candidates(int U, int T, int64_t N, int K, const uint16_t *idx_q, const float *idx_w,
+                                     KeyRows idx_k, const int32_t *n_vis, void *workspace, int64_t max_last,
+                                     CandList *list, hipStream_t stream)
+{
+    const int64_t Q = (int64_t)U * T;
+    const FusedShape fs = fused_shape(Q, N, K);
+    uint32_t *keys = nullptr;
+    int32_t *ids = nullptr;
+    topk_level1_buffers(workspace, Q, fs.chunks, K, &keys, &ids);
+    const int64_t grid = Q * fs.chunks;
+    switch (fs.ept) {
+    case 4: launch_select<4>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    case 8: launch_select<8>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    case 12: launch_select<12>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    default: launch_select<16>(grid, T, N, K, fs.rows, fs.chunks, idx_q, idx_w, idx_k, n_vis, ids, keys, stream); break;
+    }
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_topk_merge_levels(Q, N, K, fs.rows, fs.chunks, n_vis, workspace, max_last, list, stream);
+}
+
 }  // namespace ds4a

@@ -33,6 +33,21 @@ size_t topk_cand_workspace_bytes(int64_t Q, int64_t chunks, int K);
 void topk_level1_buffers(void *workspace, int64_t Q, int64_t chunks, int K, uint32_t **keys, int32_t **ids);
 hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chunks, const int32_t *n_vis,
                              int32_t *idx, void *workspace, hipStream_t stream);
+// A candidate list per query: query q's candidates are the first count(n_vis[q]) entries of
+// keys/ids[q * stride ...], where count follows the chunk sizes of the levels that produced the
+// list (first level on rows: each chunk of a level keeps min(K, its size)).
+struct CandList {
+    static constexpr int kMaxLevels = 12;
+    const uint32_t *keys;
+    const int32_t *ids;
+    int64_t stride;
+    int n_levels;
+    int level_rows[kMaxLevels];
+};
+// The merge levels of the chunked select short of the last one: stops at the first list of
+// at most max_last slots per query and describes it.
+hipError_t launch_topk_merge_levels(int64_t Q, int64_t N, int K, int chunk, int64_t chunks, const int32_t *n_vis,
+                                    void *workspace, int64_t max_last, CandList *list, hipStream_t stream);
 
 // A1 + A2 fused: the selected set without materialising scores (decode shapes), or through
 // scores kept in the workspace (many queries per unit).
@@ -40,6 +55,13 @@ size_t indexer_topk_workspace_bytes(int U, int T, int64_t N, int K);
 hipError_t launch_indexer_topk(int U, int T, int64_t N, int K, const uint16_t *idx_q, const float *idx_w,
                                KeyRows idx_k, const int32_t *n_vis, int32_t *idx, void *workspace,
                                hipStream_t stream);
+// A1 + A2 short of the last merge level, for a consumer that selects from the final list
+// itself: only where the fused select runs with more than one chunk per query (same workspace
+// as launch_indexer_topk).
+bool indexer_candidates_apply(int U, int T, int64_t N, int K);
+hipError_t launch_indexer_candidates(int U, int T, int64_t N, int K, const uint16_t *idx_q, const float *idx_w,
+                                     KeyRows idx_k, const int32_t *n_vis, void *workspace, int64_t max_last,
+                                     CandList *list, hipStream_t stream);
 
 // A3-A6
 // A3-A6.  Two kernels: attn.hip, workgroups of (query, 64-head group, union chunk), for many
@@ -70,6 +92,16 @@ hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t
                           const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                           const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
                           float scale, float *out, uint32_t *count, float *part, hipStream_t stream);
+// The 16-head kernel with the last top-k merge level inside (sparse, unsplit unions, lists of
+// at most 6,144 candidates per query): the rows of each query are selected from cl by the
+// workgroups themselves (the set the top-k kernels would write), and written to idx_out when
+// it is not null.  cand_nvis: the indexer's visible rows per query (NULL: all N).
+constexpr int64_t kAttnMergeMax = 6144;      // candidates per query the in-kernel merge takes
+bool attn_dq_merge_apply(const AttnPlan &p, int64_t list_stride);
+hipError_t launch_attn_dq_merge(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q,
+                                int q_bf16, const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
+                                const float *comp_scale, const CandList &cl, const int32_t *cand_nvis,
+                                const int32_t *raw_vis, float scale, int32_t *idx_out, float *out, hipStream_t stream);
 // As launch_attn with the counters and the records given apart (count: plan.count_bytes,
 // zero before the call and left zero; part: plan.workspace_bytes - plan.count_bytes).
 hipError_t launch_attn_parts(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,

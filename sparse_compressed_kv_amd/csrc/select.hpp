@@ -42,10 +42,13 @@ struct Levels {
 // < 2^31, and a merged level's chunks hold at least 4K rows, so every count stays below 2^30.
 __device__ __forceinline__ int64_t cand_count(int64_t nv, int K, const Levels &lv) {
     uint32_t c = (uint32_t)nv;
-    for (int l = 0; l < lv.n; ++l) {
-        const uint32_t ch = (uint32_t)lv.ch[l];
-        const uint32_t m = c % ch;
-        c = (c / ch) * (uint32_t)K + (m < (uint32_t)K ? m : (uint32_t)K);
+#pragma unroll
+    for (int l = 0; l < kMaxLevels; ++l) {    // constant indices: the levels stay in registers
+        if (l < lv.n) {
+            const uint32_t ch = (uint32_t)lv.ch[l];
+            const uint32_t m = c % ch;
+            c = (c / ch) * (uint32_t)K + (m < (uint32_t)K ? m : (uint32_t)K);
+        }
     }
     return (int64_t)c;
 }
@@ -135,9 +138,13 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
             const int shift = bit - width;
             const uint32_t dmask = (1u << width) - 1u;
             uint32_t *hist = sm.hist[pb];
+            // After the first pass few keys still match the prefix: a wave with none skips the
+            // atomic (each costs about the same with or without active lanes).
 #pragma unroll
-            for (int i = 0; i < EPT; ++i)
-                if (j0 + i < n && (key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
+            for (int i = 0; i < EPT; ++i) {
+                const bool m = j0 + i < n && (key[i] & pmask) == prefix;
+                if (__builtin_amdgcn_ballot_w64(m) != 0 && m) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
+            }
             __syncthreads();
             if (threadIdx.x < kWave) {
                 // lane l owns bins 255-4l .. 252-4l, highest first
@@ -173,14 +180,22 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
         ties = whole_bin ? 0xFFFFFFFFu : remaining;
     }
 
-    // Index-ordered collection over each thread's contiguous positions.
+    // Index-ordered collection over each thread's contiguous positions.  When every key equal
+    // to T is taken (the boundary bin was taken whole, as with distinct keys), a key is taken iff
+    // it is >= T and the ties need no ranks.
+    const bool all_ties = ties == 0xFFFFFFFFu;        // uniform
     uint32_t gt = 0, eq = 0;
     if (need > 0) {
+        if (all_ties) {
 #pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            if (j0 + i < n) {
-                gt += key[i] > T;
-                eq += key[i] == T;
+            for (int i = 0; i < EPT; ++i) gt += (j0 + i < n && key[i] >= T) ? 1u : 0u;
+        } else {
+#pragma unroll
+            for (int i = 0; i < EPT; ++i) {
+                if (j0 + i < n) {
+                    gt += key[i] > T;
+                    eq += key[i] == T;
+                }
             }
         }
     }
@@ -204,9 +219,25 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
             pos += take ? 1u : 0u;
         }
     };
+    auto collect_all = [&](auto keys_tag) __attribute__((always_inline)) {
+        constexpr bool KEYS = decltype(keys_tag)::value;
+#pragma unroll
+        for (int i = 0; i < EPT; ++i) {
+            const bool take = j0 + i < n && key[i] >= T;
+            const uint32_t dst = take ? pos : (uint32_t)(kMaxK + lane);
+            sm.sel_id[dst] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
+            if (KEYS) sm.sel_key[dst] = key[i];
+            pos += take ? 1u : 0u;
+        }
+    };
     if (need > 0) {
-        if (out_keys) collect(std::true_type{});
-        else collect(std::false_type{});
+        if (all_ties) {
+            if (out_keys) collect_all(std::true_type{});
+            else collect_all(std::false_type{});
+        } else {
+            if (out_keys) collect(std::true_type{});
+            else collect(std::false_type{});
+        }
     }
     __syncthreads();
     const int taken = need > 0 ? need : 0;

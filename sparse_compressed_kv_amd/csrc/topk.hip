@@ -152,9 +152,10 @@ size_t topk_workspace_bytes(int64_t Q, int64_t N, int K) {
     return topk_cand_workspace_bytes(Q, (N + ch - 1) / ch, K);
 }
 
-hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chunks, const int32_t *n_vis,
-                             int32_t *idx, void *workspace, hipStream_t stream)
+hipError_t launch_topk_merge_levels(int64_t Q, int64_t N, int K, int chunk, int64_t chunks, const int32_t *n_vis,
+                                    void *workspace, int64_t max_last, CandList *list, hipStream_t stream)
 {
+    static_assert(kMaxLevels <= CandList::kMaxLevels, "level chunk sizes fit the host list");
     const size_t per = (size_t)Q * (size_t)chunks * (size_t)K;
     char *p = static_cast<char *>(workspace);
     uint32_t *keys_a = reinterpret_cast<uint32_t *>(p);
@@ -165,7 +166,7 @@ hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chu
     lv.n = 1;
     lv.ch[0] = chunk;
     int64_t stride = chunks * K;                 // candidate slots per query in the current list
-    while (stride > kMergeMax && lv.n < kMaxLevels) {
+    while (stride > max_last && lv.n < kMaxLevels) {
         const int64_t chunks2 = (stride + kLevelChunk - 1) / kLevelChunk;
         hipLaunchKernelGGL(topk_cand_kernel<16>, dim3((unsigned)(Q * chunks2)), dim3(kNT), 0, stream, N, K, lv,
                            stride, kLevelChunk, chunks2, keys_a, ids_a, n_vis, ids_b, keys_b);
@@ -174,7 +175,28 @@ hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chu
         uint32_t *tk = keys_a; keys_a = keys_b; keys_b = tk;
         int32_t *ti = ids_a; ids_a = ids_b; ids_b = ti;
     }
-    if (stride > kMergeMax) return hipErrorInvalidValue;
+    if (stride > max_last) return hipErrorInvalidValue;
+    list->keys = keys_a;
+    list->ids = ids_a;
+    list->stride = stride;
+    list->n_levels = lv.n;
+    for (int l = 0; l < lv.n; ++l) list->level_rows[l] = lv.ch[l];
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_merge(int64_t Q, int64_t N, int K, int chunk, int64_t chunks, const int32_t *n_vis,
+                             int32_t *idx, void *workspace, hipStream_t stream)
+{
+    CandList cl;
+    if (hipError_t e = launch_topk_merge_levels(Q, N, K, chunk, chunks, n_vis, workspace, kMergeMax, &cl, stream);
+        e != hipSuccess)
+        return e;
+    const uint32_t *keys_a = cl.keys;
+    const int32_t *ids_a = cl.ids;
+    const int64_t stride = cl.stride;
+    Levels lv = {};
+    lv.n = cl.n_levels;
+    for (int l = 0; l < lv.n; ++l) lv.ch[l] = cl.level_rows[l];
     // The last level: one workgroup per query, with as few candidates per thread as the list
     // needs (each select pass walks every thread's EPT keys).
     const auto last = [&](auto ept_tag) {

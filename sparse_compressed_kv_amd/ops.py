@@ -63,6 +63,13 @@ def lib() -> ctypes.CDLL:
     L.ds4a_sparse_mqa.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt, P, P, sz,
                                   P]
     L.ds4a_sparse_mqa.restype = i32
+    # U T N Hi Di K idx_q idx_w idx_k n_vis H D n_rot W q q_dtype q_pos theta raw raw_vis comp scale idx out ws nb s
+    L.ds4a_indexer_topk_mqa.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, i32, i32, i32, i32, P, i32, P, dbl,
+                                        P, P, P, flt, P, P, P, sz, P]
+    L.ds4a_indexer_topk_mqa.restype = i32
+    L.ds4a_indexer_topk_mqa_fp8.argtypes = [i32, i32, i64, i32, i32, i32, P, P, P, P, P, i32, i32, i32, i32, P, i32,
+                                            P, dbl, P, P, P, P, flt, P, P, P, sz, P]
+    L.ds4a_indexer_topk_mqa_fp8.restype = i32
     L.ds4a_sparse_mqa_noalloc.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32, P, i32, P, dbl, P, P, P, P, flt,
                                           P, P]
     L.ds4a_sparse_mqa_noalloc.restype = i32
@@ -309,6 +316,56 @@ def sparse_mqa(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 1000
     return out
 
 
+def indexer_topk_mqa(idx_q, idx_w, idx_k, K: int, q, q_pos, raw_kv, comp_kv, scale: float,
+                     theta: float = 10000.0, W: int = 128, n_vis=None, raw_vis=None, idx=None, out=None,
+                     workspace=None, stream=None, idx_k_scale=None, comp_scale=None):
+    """A1 + A2 + A3-A6 in one call: (idx i32 [U,T,K], out f32 [U,T,H,512]) as indexer_topk then
+    sparse_mqa would give.  FP8 storage: idx_k as E4M3 codes with idx_k_scale and comp_kv as E4M3
+    codes with comp_scale (both, or neither)."""
+    if not isinstance(q, torch.Tensor):
+        raise TypeError("q must be a torch.Tensor")
+    U, T, Hi, Di = idx_q.shape
+    _, _, H, D = q.shape
+    _need(idx_q, "idx_q", torch.bfloat16)
+    _need(idx_w, "idx_w", torch.float32, (U, T, Hi))
+    fp8 = idx_k_scale is not None
+    if fp8 != (comp_scale is not None):
+        raise ValueError("FP8 keys and FP8 rows go together (idx_k_scale and comp_scale)")
+    if fp8:
+        idx_k, N = _fp8_keys(idx_k, idx_k_scale, U, Di)
+    else:
+        N = idx_k.shape[1]
+        _need(idx_k, "idx_k", torch.bfloat16, (U, N, Di))
+    if n_vis is not None:
+        _need(n_vis, "n_vis", torch.int32, (U, T))
+    _need(q, "q", q.dtype, (U, T, H, D))
+    qd = _q_dtype(q)
+    _need(q_pos, "q_pos", torch.int64, (U, T))
+    if W > 0:
+        _need(raw_kv, "raw_kv", torch.float16, (U, T + W - 1, D))
+    comp_kv, _ = _comp_rows(comp_kv, comp_scale, U, N, D)
+    if idx is None:
+        idx = torch.empty((U, T, K), dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32, (U, T, K))
+    if out is None:
+        out = torch.empty((U, T, H, D), dtype=torch.float32, device=q.device)
+    _need(out, "out", torch.float32, (U, T, H, D))
+    ws, nb = _workspace(workspace_bytes(4, U, T, N, K, H, W), q.device, workspace)
+    raw = _ptr(raw_kv) if W > 0 else None
+    rv = _ptr(_raw_vis(raw_vis, U, T, W))
+    if fp8:
+        _check("ds4a_indexer_topk_mqa_fp8", lib().ds4a_indexer_topk_mqa_fp8(
+            U, T, N, Hi, Di, K, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k), _ptr(idx_k_scale), _ptr(n_vis), H, D, 64, W,
+            _ptr(q), qd, _ptr(q_pos), float(theta), raw, rv, _ptr(comp_kv), _ptr(comp_scale), float(scale),
+            _ptr(idx), _ptr(out), _ptr(ws), nb, _stream(stream)))
+    else:
+        _check("ds4a_indexer_topk_mqa", lib().ds4a_indexer_topk_mqa(
+            U, T, N, Hi, Di, K, _ptr(idx_q), _ptr(idx_w), _ptr(idx_k), _ptr(n_vis), H, D, 64, W, _ptr(q), qd,
+            _ptr(q_pos), float(theta), raw, rv, _ptr(comp_kv), float(scale), _ptr(idx), _ptr(out), _ptr(ws), nb,
+            _stream(stream)))
+    return idx, out
+
+
 def sparse_mqa_noalloc(q, q_pos, raw_kv, comp_kv, idx, scale: float, theta: float = 10000.0, W: int = 128,
                        out=None, stream=None, raw_vis=None):
     """sparse_mqa without a workspace: split unions use the library's own device scratch
@@ -473,19 +530,25 @@ class Step:
     """The whole hot path for fixed shapes: indexer -> top-k -> attention, with every
     intermediate, output and workspace allocated once up front.  fused=True runs A1 + A2
     as ds4a_indexer_topk (no score buffer in decode shapes); fused=False runs the separate
-    calls and keeps the scores in self.scores."""
+    calls and keeps the scores in self.scores; one_call=True runs the whole path as
+    ds4a_indexer_topk_mqa (same idx and out, bit for bit)."""
 
-    def __init__(self, U, T, N, H=64, K=512, W=128, q_dtype=torch.float32, device="cuda", fused=False):
+    def __init__(self, U, T, N, H=64, K=512, W=128, q_dtype=torch.float32, device="cuda", fused=False,
+                 one_call=False):
         self.U, self.T, self.N, self.H, self.K, self.W = U, T, N, H, K, W
-        self.fused = fused
+        self.fused = fused or one_call
+        self.one_call = one_call
         dev = torch.device(device)
-        self.scores = None if fused else torch.empty((U, T, N), dtype=torch.float32, device=dev)
+        self.scores = None if self.fused else torch.empty((U, T, N), dtype=torch.float32, device=dev)
         self.idx = torch.empty((U, T, K), dtype=torch.int32, device=dev)
         self.out = torch.empty((U, T, H, 512), dtype=torch.float32, device=dev)
-        nb0 = workspace_bytes(2 if fused else 0, U, T, N, K)
+        nb0 = workspace_bytes(2 if self.fused else 0, U, T, N, K)
         nb1 = workspace_bytes(1, U, T, N, K, H, W)
         self.ws_topk = torch.zeros(max(nb0, 1), dtype=torch.uint8, device=dev)
         self.ws_mqa = torch.zeros(max(nb1, 1), dtype=torch.uint8, device=dev)   # counters start at zero
+        self.ws_step = None
+        if one_call:
+            self.ws_step = torch.zeros(workspace_bytes(4, U, T, N, K, H, W), dtype=torch.uint8, device=dev)
 
     def select(self, x: dict, n_vis=None, stream=None):
         """A1 + A2 into self.idx."""
@@ -499,6 +562,11 @@ class Step:
 
     def __call__(self, x: dict, n_vis=None, scale=1.0 / 512 ** 0.5, theta=10000.0, stream=None, raw_vis=None):
         """raw_vis: int32 [U, T] raw-window rows that take part (a window not yet full), or None."""
+        if self.one_call:
+            indexer_topk_mqa(x["idx_q"], x["idx_w"], x["idx_k"], self.K, x["q"], x["pos"], x["raw"], x["comp"],
+                             scale, theta, W=self.W, n_vis=n_vis, raw_vis=raw_vis, idx=self.idx, out=self.out,
+                             workspace=self.ws_step, stream=stream)
+            return self.out
         self.select(x, n_vis=n_vis, stream=stream)
         sparse_mqa(x["q"], x["pos"], x["raw"], x["comp"], self.idx, scale, theta, W=self.W, out=self.out,
                    workspace=self.ws_mqa, stream=stream, raw_vis=raw_vis)

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(L):
     assert {"ds4a_indexer_score", "ds4a_topk_select", "ds4a_indexer_topk", "ds4a_sparse_mqa", "ds4a_dense_mqa",
             "ds4a_compress_rows", "ds4a_rope_q", "ds4a_indexer_score_fp8", "ds4a_indexer_topk_fp8",
             "ds4a_compress_append", "ds4a_push_raw", "ds4a_frontier_push", "ds4a_sparse_mqa_fp8",
-            "ds4a_dense_mqa_fp8", "ds4a_workspace_bytes", "ds4a_last_error", "ds4a_version"} <= set(names)
+            "ds4a_dense_mqa_fp8", "ds4a_indexer_topk_mqa", "ds4a_indexer_topk_mqa_fp8", "ds4a_workspace_bytes",
+            "ds4a_last_error", "ds4a_version"} <= set(names)
     for n in names:
         assert hasattr(L, n), n
 
@@ -42,7 +43,7 @@ def test_ceiling_validation(L):
 
 
 def test_version(L):
-    assert L.ds4a_version() == 2
+    assert L.ds4a_version() == 3
 
 
 def test_indexer_validation(L):
@@ -185,6 +186,48 @@ def test_mqa_validation(L):
     assert _mqa(L, ws=None, ws_bytes=0) == -5
     assert _mqa(L, ws_bytes=need - 1) == -5
     assert _mqa(L, U=1 << 16, T=1 << 9) == -2     # U*T above 2^24 (keeps every grid below 2^31)
+
+
+def test_indexer_topk_mqa_validation(L):
+    """A1 + A2 + A3-A6 in one call validates both halves' arguments before anything is enqueued,
+    and always needs a workspace (the top-k's and the attention's)."""
+    def st(fp8=False, **kw):
+        a = dict(U=43, T=1, N=65536, Hi=64, Di=128, K=512, iq=A, iw=A, ik=A, iks=A, n_vis=None, H=64, D=512,
+                 n_rot=64, W=128, q=A, q_dtype=0, q_pos=A, theta=10000.0, raw=A, raw_vis=None, comp=A, cs=A,
+                 scale=0.044, idx=A, out=A, ws=A, ws_bytes=1 << 40)
+        a.update(kw)
+        if fp8:
+            return L.ds4a_indexer_topk_mqa_fp8(
+                a["U"], a["T"], a["N"], a["Hi"], a["Di"], a["K"], a["iq"], a["iw"], a["ik"], a["iks"], a["n_vis"],
+                a["H"], a["D"], a["n_rot"], a["W"], a["q"], a["q_dtype"], a["q_pos"], a["theta"], a["raw"],
+                a["raw_vis"], a["comp"], a["cs"], a["scale"], a["idx"], a["out"], a["ws"], a["ws_bytes"], S)
+        return L.ds4a_indexer_topk_mqa(
+            a["U"], a["T"], a["N"], a["Hi"], a["Di"], a["K"], a["iq"], a["iw"], a["ik"], a["n_vis"], a["H"], a["D"],
+            a["n_rot"], a["W"], a["q"], a["q_dtype"], a["q_pos"], a["theta"], a["raw"], a["raw_vis"], a["comp"],
+            a["scale"], a["idx"], a["out"], a["ws"], a["ws_bytes"], S)
+
+    assert st(Hi=32) == -3 and "ds4a_indexer_topk_mqa" in ops.last_error()
+    assert st(D=256) == -3
+    assert st(K=0) == -2
+    assert st(K=4096) == -3
+    assert st(W=100) == -3
+    assert st(N=0) == -2
+    assert st(scale=float("inf")) == -2
+    assert st(iq=None) == -1 and "idx_q" in ops.last_error()
+    assert st(ik=MIS) == -4
+    assert st(comp=None) == -1 and "comp_kv" in ops.last_error()
+    assert st(out=None) == -1
+    assert st(raw_vis=MIS) == -4
+    assert st(idx=MIS) == -4                  # idx may be NULL, but not misaligned
+    need = ops.workspace_bytes(4, 43, 1, 65536, 512, 64, 128)
+    assert need >= ops.workspace_bytes(2, 43, 1, 65536, 512, 0, 0) + 43 * 512 * 4
+    assert st(ws=None, ws_bytes=0) == -5 and "workspace" in ops.last_error()
+    assert st(ws_bytes=need - 1) == -5
+    assert st(ws=MIS) == -4
+    assert st(fp8=True, ik=None) == -1 and "idx_k8" in ops.last_error()
+    assert st(fp8=True, iks=None) == -1 and "idx_k_scale" in ops.last_error()
+    assert st(fp8=True, cs=None) == -1 and "comp_scale" in ops.last_error()
+    assert ops.workspace_bytes(4, 1, 1, 1000, 512, 48 + 1, 128) == 0
 
 
 def test_mqa_noalloc_validation(L):
