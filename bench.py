@@ -1,9 +1,11 @@
 #!/usr/bin/env python3
 """Benchmark of one layer's compressed sparse attention step on one MI355X.
 
-One step = the whole hot path over one batch: indexer scores + top-k (one
-ds4a_indexer_topk call) -> RoPE + sparse multi-query attention (ds4a_sparse_mqa),
-for every unit of the workload.
+One step = the whole hot path over one batch: indexer scores + top-k -> RoPE + sparse
+multi-query attention, for every unit of the workload, as one ds4a_indexer_topk_mqa call
+(the same results as ds4a_indexer_topk followed by ds4a_sparse_mqa, bit for bit; in decode
+shapes the last top-k merge level runs inside the attention kernel).  The two calls are
+also timed one by one for the per-call figures.
 
 Main line: decode at the DeepSeek V4 Flash shape, 43 independent layers with
 N = 65,536 compressed rows each (64 query heads x 512 dims, one KV head,
@@ -108,10 +110,10 @@ def upload(x: dict) -> dict:
 
 
 class Bench:
-    """Device-resident replicas of one workload, and timed steps over them.  A step is
-    ds4a_indexer_topk (A1 + A2) then ds4a_sparse_mqa (A3-A6); with `fp8_keys` (the indexer keys
-    as E4M3 codes and row scales, synth.make_indexer_fp8_config) the select is
-    ds4a_indexer_topk_fp8."""
+    """Device-resident replicas of one workload, and timed steps over them.  A step is one
+    ds4a_indexer_topk_mqa call (A1 + A2 + A3-A6), or ds4a_indexer_topk_mqa_fp8 with `fp8_keys`
+    (the indexer keys as E4M3 codes and row scales, synth.make_indexer_fp8_config) and
+    `fp8_rows`; with FP8 keys and bf16 rows it is ds4a_indexer_topk_fp8 then ds4a_sparse_mqa."""
 
     def __init__(self, w, x, replicas: int, fp8_keys=None, fp8_rows: bool = False):
         import torch
@@ -133,14 +135,27 @@ class Bench:
         self.step = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=True)
         self.sep = ops.Step(w.U, w.T, w.N, H=w.H, K=w.K, W=w.W, fused=False)
         self.nvis = w.vis_base is not None
+        self.one_call = self.fp8 == fp8_rows
+        self.ws_step = torch.zeros(ops.workspace_bytes(4, w.U, w.T, w.N, w.K, w.H, w.W), dtype=torch.uint8,
+                                   device="cuda") if self.one_call else None
 
     def one(self, i: int, stream):
-        """Step i: both calls on `stream`, over input replica i mod replicas."""
+        """Step i on `stream`, over input replica i mod replicas."""
         w, st = self.w, self.step
         d = self.reps[i % len(self.reps)]
         nv = d["n_vis"] if self.nvis else None
-        self.select(d, nv, stream)
-        self.attend(d, stream)
+        if not self.one_call:
+            self.select(d, nv, stream)
+            self.attend(d, stream)
+        elif self.fp8:
+            self.ops.indexer_topk_mqa(d["idx_q"], d["idx_w"], d["k8"], w.K, d["q"], d["pos"], d["raw"], d["comp8"],
+                                      w.scale, w.theta, W=w.W, n_vis=nv, idx=st.idx, out=st.out,
+                                      workspace=self.ws_step, stream=stream, idx_k_scale=d["sc"],
+                                      comp_scale=d["comp_s"])
+        else:
+            self.ops.indexer_topk_mqa(d["idx_q"], d["idx_w"], d["idx_k"], w.K, d["q"], d["pos"], d["raw"], d["comp"],
+                                      w.scale, w.theta, W=w.W, n_vis=nv, idx=st.idx, out=st.out,
+                                      workspace=self.ws_step, stream=stream)
 
     def attend(self, d, stream):
         w, st = self.w, self.step
@@ -385,7 +400,7 @@ def full_schedule(steps: int, warmup: int):
     """Attention of one whole Flash decode step, all 43 layers, at 262,144 tokens of context,
     with the layer schedule of "Reading the architecture of DwarfStar (ds4.c), part 1/8",
     section 3-2: layers 0-1 keep only the raw window (ds4a_dense_mqa with N = 0), even layers
-    from 2 on are ratio 4 (65,536 rows: ds4a_indexer_topk + ds4a_sparse_mqa, top-512) and odd
+    from 2 on are ratio 4 (65,536 rows: ds4a_indexer_topk_mqa, top-512) and odd
     layers from 3 on ratio 128 (2,048 rows, all of them: ds4a_dense_mqa)."""
     import torch
 
@@ -401,7 +416,7 @@ def full_schedule(steps: int, warmup: int):
     r128 = [upload(x128) for _ in range(2)]
     x0 = gen.make_config(w0)
     r0 = [upload(x0) for _ in range(2)]
-    st4 = ops.Step(w4.U, 1, w4.N, fused=True)
+    st4 = ops.Step(w4.U, 1, w4.N, one_call=True)
     out128 = torch.empty((w128.U, 1, 64, 512), dtype=torch.float32, device="cuda")
     ws128 = torch.zeros(max(ops.workspace_bytes(3, w128.U, 1, w128.N, 0, 64, 128), 1), dtype=torch.uint8,
                         device="cuda")
@@ -411,10 +426,7 @@ def full_schedule(steps: int, warmup: int):
     scale, theta = w4.scale, w4.theta
 
     def g4(i):
-        d = r4[i % len(r4)]
-        st4.select(d, stream=stream)
-        ops.sparse_mqa(d["q"], d["pos"], d["raw"], d["comp"], st4.idx, scale, theta, W=128, out=st4.out,
-                       workspace=st4.ws_mqa, stream=stream)
+        st4(r4[i % len(r4)], scale=scale, theta=theta, stream=stream)
 
     def g128(i):
         d = r128[i % len(r128)]

@@ -109,8 +109,8 @@ __device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
 // -0 is folded onto +0 so that equal floats give equal keys.
 __device__ __forceinline__ uint32_t float_key(float f) {
     uint32_t u = __float_as_uint(f);
-    if (u == 0x80000000u) u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    u = u == 0x80000000u ? 0u : u;                 // -0 ties with +0
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);   // negative: all bits flip; else the sign bit
 }
 
 // ---- DPP (data-parallel primitives on VALU lanes, no LDS round trip)

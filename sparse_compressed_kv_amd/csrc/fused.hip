@@ -42,8 +42,9 @@ __global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
     __shared__ u32x4 sq[kHeads * kDim / 8];
     constexpr int kRows = EPT * kNT;
     static_assert(EPT % 4 == 0, "scores are read from LDS four at a time");
-    __shared__ __align__(16) float s_sc[kRows];
+    __shared__ __align__(16) float s_sc[kRows];    // keys of the chunk's rows (float_key of the scores)
     __shared__ SelectShared sm;
+    __shared__ uint32_t s_claim;                  // next unclaimed group of rows
 
     const int64_t q = blockIdx.x / chunks;
     const int64_t ch = blockIdx.x % chunks;
@@ -55,6 +56,8 @@ __global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
     const int64_t rem = nv - c0;
     const int n = rem <= 0 ? 0 : (rem < rows ? (int)rem : rows);     // visible rows of this chunk
 
+    // Positions past the last 16-row block of scores hold 0, the absent key.
+    for (int j = (n + 15) / 16 * 16 + (int)threadIdx.x; j < kRows; j += kNT) reinterpret_cast<uint32_t *>(s_sc)[j] = 0u;
     if (n > 0) {                                  // uniform across the workgroup
         const KeyRows unit = {static_cast<const char *>(keys.k) + u * N * kKeyRowBytes<FP8>,
                               FP8 ? keys.scale + u * N : nullptr};
@@ -62,11 +65,12 @@ __global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
         KeyBlock<FP8> kb[kFBpi];
         indexer_first_keys<kFBpi, FP8>(st, wave, g, c, kb);   // in flight during the query set-up
         bf16x8 aq[4][4];
+        if (threadIdx.x == 0) s_claim = kFWaves;  // published by the query set-up's barrier
         indexer_query_frags<kNT>(qI, q, sq, g, c, aq);
         float wh[4];
 #pragma unroll
         for (int ht = 0; ht < 4; ++ht) wh[ht] = w[q * kHeads + 16 * ht + c];
-        indexer_score_rows<kFWaves, kFBpi, FP8>(aq, wh, st, n, wave, g, c, s_sc, kb);
+        indexer_score_rows<kFWaves, kFBpi, FP8, true>(aq, wh, st, n, wave, g, c, s_sc, kb, &s_claim);
     }
     __syncthreads();
 
@@ -75,10 +79,10 @@ __global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
     int32_t id[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; i += 4) {
-        const f32x4 v = *reinterpret_cast<const f32x4 *>(s_sc + j0 + i);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(s_sc + j0 + i);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            key[i + e] = j0 + i + e < n ? float_key(v[e]) : 0u;
+            key[i + e] = v[e];
             id[i + e] = 0;
         }
     }

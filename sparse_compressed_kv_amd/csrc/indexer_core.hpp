@@ -143,19 +143,34 @@ __device__ __forceinline__ void indexer_first_keys(const KeyStream<FP8> &st, int
 // query.  A block's registers are refilled with the same block of the next iteration as soon
 // as its MFMAs are issued (its scale once the score is stored), so BPI blocks stay in flight
 // while the epilogues run; loads complete in issue order, the order the blocks are used in.
-// A row's score does not depend on WAVES or BPI.  E4M3 keys: the products use the code values
-// and the row's score is multiplied by its scale at the end (scale > 0 commutes with the
-// ReLU); with power-of-two scales the score is bit-identical to that of the bf16 keys
-// code * scale.
-template <int WAVES, int BPI, bool FP8>
+// A row's score does not depend on WAVES, BPI or which wave computes it.  E4M3 keys: the
+// products use the code values and the row's score is multiplied by its scale at the end
+// (scale > 0 commutes with the ReLU); with power-of-two scales the score is bit-identical to
+// that of the bf16 keys code * scale.
+// KEYS: s_out receives float_key of each score (as uint32), and 0 for the rows of the last
+// 16-row block past n, the form the workgroup select takes.
+// Wave w starts with rows 16*BPI*w ..; its next 16*BPI rows are WAVES*16*BPI further on, or,
+// with a claim counter (LDS, set to WAVES before any wave reaches the loop), the next unclaimed
+// group of 16*BPI rows: waves that the hardware serves first take more of them, so the waves
+// of a workgroup finish together and all of them keep streaming until the end.
+template <int WAVES, int BPI, bool FP8, bool KEYS = false>
 __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], const float (&wh)[4],
                                                    const KeyStream<FP8> &st, int n, int wave, int g, int c,
-                                                   float *s_out, KeyBlock<FP8> (&kb)[BPI]) {
-    constexpr int kRowsPerIter = 16 * BPI * WAVES;
+                                                   float *s_out, KeyBlock<FP8> (&kb)[BPI],
+                                                   uint32_t *claim = nullptr) {
+    constexpr int kWaveRows = 16 * BPI;
+    constexpr int kRowsPerIter = kWaveRows * WAVES;
     // The head weights arrive before the loop: a wait for them inside it would also wait for
     // every key load issued after them.
     asm volatile("" : : "v"(wh[0]), "v"(wh[1]), "v"(wh[2]), "v"(wh[3]));
-    for (int base = 16 * BPI * wave; base < n; base += kRowsPerIter) {
+    for (int base = kWaveRows * wave, next; base < n; base = next) {
+        if (claim) {                                  // the result is first needed after 16 MFMAs
+            uint32_t v = 0;
+            if ((threadIdx.x & (kWave - 1)) == 0) v = atomicAdd(claim, 1u);
+            next = kWaveRows * (int)__builtin_amdgcn_readfirstlane(v);
+        } else {
+            next = base + kRowsPerIter;
+        }
 #pragma unroll
         for (int bi = 0; bi < BPI; ++bi) {
             // Every block is computed, also past n (its keys read as zero): a branch here would
@@ -178,7 +193,7 @@ __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], con
 #pragma unroll
                 for (int r = 0; r < 4; ++r) acc[r] += wh[ht] * relu(d[r]);
             }
-            indexer_load_block<FP8>(st, blk + kRowsPerIter, g, c, kb[bi]);
+            indexer_load_block<FP8>(st, next + 16 * bi, g, c, kb[bi]);
             // Sum over the 16 heads of each row: the 16 lanes of a DPP row.
 #pragma unroll
             for (int r = 0; r < 4; ++r) acc[r] = row16_sum(acc[r]);
@@ -189,10 +204,23 @@ __device__ __forceinline__ void indexer_score_rows(const bf16x8 (&aq)[4][4], con
                 v = r == 1 ? acc[1] : v;
                 v = r == 2 ? acc[2] : v;
                 v = r == 3 ? acc[3] : v;
-                if (live && c < 4) s_out[blk + 4 * g + r] = v * kb[bi].sc;
-                kb[bi].sc = indexer_load_scale<FP8>(st, blk + kRowsPerIter, g, c);
+                v *= kb[bi].sc;
+                if constexpr (KEYS) {
+                    const uint32_t kv = blk + 4 * g + r < n ? float_key(v) : 0u;
+                    if (live && c < 4) reinterpret_cast<uint32_t *>(s_out)[blk + 4 * g + r] = kv;
+                } else {
+                    if (live && c < 4) s_out[blk + 4 * g + r] = v;
+                }
+                kb[bi].sc = indexer_load_scale<FP8>(st, next + 16 * bi, g, c);
             } else {
-                if (live && c == 0) *reinterpret_cast<f32x4 *>(s_out + blk + 4 * g) = acc;
+                if constexpr (KEYS) {
+                    u32x4 kv;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) kv[r] = blk + 4 * g + r < n ? float_key(acc[r]) : 0u;
+                    if (live && c == 0) *reinterpret_cast<u32x4 *>(s_out + blk + 4 * g) = kv;
+                } else {
+                    if (live && c == 0) *reinterpret_cast<f32x4 *>(s_out + blk + 4 * g) = acc;
+                }
             }
         }
     }

@@ -22,11 +22,10 @@ constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4
 constexpr int kMaxK = 2048;
 
 struct SelectShared {
-    uint32_t hist[2][kBins];    // digit histograms of alternate passes
+    alignas(16) uint32_t hist[3][kBins];     // digit histograms, used by turns (pass p counts into p % 3)
     alignas(16) uint32_t wave_a[kNW];
     uint32_t wave_mn[kNW];
     uint32_t wave_mx[kNW];
-    uint32_t res[2][4];         // boundary bin of alternate passes
     int32_t sel_id[kMaxK + kWave];   // the selected set, in row order, before the coalesced copy-out;
     uint32_t sel_key[kMaxK + kWave]; // slots from kMaxK on take the stores of keys not taken
 };
@@ -63,7 +62,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t list_rsrc(const void *p, uint3
 }
 
 // Exclusive prefix sum over the workgroup (kNW waves: the totals are read at once, not one
-// dependent read per earlier wave).
+// dependent read per earlier wave).  Once per workgroup: wave_sums is not reused.
 __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
     static_assert(kNW == 8, "two 16-byte reads cover the wave totals");
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
@@ -78,8 +77,7 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
         off += i < wave ? s0[i] : 0u;
         off += i + 4 < wave ? s1[i] : 0u;
     }
-    __syncthreads();
-    return off + incl - v;
+    return off + incl - v;           // wave_sums is not written again: no barrier after the reads
 }
 
 // Min and max over the workgroup.  Its slots are used once per select, so no barrier follows.
@@ -105,75 +103,90 @@ __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
 // t*EPT .. t*EPT+EPT-1; ties go to the lower position) and writes their rows (id[i] if IDS, else
 // row0 + position) in ascending position order to out[0..need), then -1 up to K.  If out_keys,
 // the selected keys go there too.  Every thread of the NT-thread workgroup calls it.
+// Positions 0 .. n-1 hold present keys, which are never 0 (float_key maps no float to 0), and
+// every later position holds 0; need = min(K, n).  A key of 0 is thus absent, and no step tests
+// positions against n: absent keys stay below every threshold, and the one histogram bin they can
+// reach (bin 0) is corrected by their number.
 template <int EPT, bool IDS, int NT = kNT>
 __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int64_t row0, int n, int need,
                              int K, int32_t *out, uint32_t *out_keys, SelectShared &sm)
 {
-    const int lane = threadIdx.x & (kWave - 1);
+    static_assert(NT % kWave == 0 && NT <= kNT && NT >= 2 * kWave && kBins == 4 * kWave, "workgroup size");
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int j0 = threadIdx.x * EPT;
-    uint32_t T = 0, ties = 0xFFFFFFFFu;       // take key > T, and the first `ties` keys == T
-    if (need > 0 && need < n) {
+    uint32_t T = 1u, ties = 0xFFFFFFFFu;      // take keys > T and the first `ties` keys == T (T = 1: all present)
+    if (need < n) {                           // uniform; implies n > 0 and need > 0
+        // min over present keys: key - 1 takes absent keys (0) to the top of the range
         uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            if (j0 + i < n) {
-                kmin = key[i] < kmin ? key[i] : kmin;
-                kmax = key[i] > kmax ? key[i] : kmax;
-            }
+            const uint32_t k1 = key[i] - 1u;
+            kmin = k1 < kmin ? k1 : kmin;
+            kmax = key[i] > kmax ? key[i] : kmax;
         }
-        static_assert(NT % kWave == 0 && NT <= kNT && NT >= kWave * 2 && kBins <= NT - kWave, "workgroup size");
-        for (int b = threadIdx.x; b < kBins; b += NT) sm.hist[0][b] = 0;   // published by the next barrier
+        // the first two histograms, cleared before the barrier of the min/max
+        if (threadIdx.x < 2 * kBins / 4)
+            reinterpret_cast<u32x4 *>(&sm.hist[0][0])[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
         block_minmax<NT>(kmin, kmax, sm);
+        kmin += 1u;
         int bit = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
         uint32_t pmask = bit >= 32 ? 0u : ~((1u << bit) - 1u);
         uint32_t prefix = kmin & pmask;
         uint32_t remaining = (uint32_t)need;
+        const uint32_t absent = (uint32_t)(NT * EPT - n);
         bool whole_bin = false;
-        // Passes alternate between two histograms and two result slots: while wave 0 scans this
-        // pass's histogram, the other waves clear the one the next pass counts into (last read
-        // by the previous pass's scan), so each pass needs two barriers.
-        int pb = 0;
+        // One histogram per pass, three in turn: after pass p's barrier every wave reads
+        // hist[p % 3] and finds the boundary bin itself (no second barrier), and wave 0 clears
+        // hist[(p + 2) % 3], last read before that barrier and next counted into after the next.
+        int h = 0;
+        bool first = true;
         while (bit > 0) {
             const int width = bit < 8 ? bit : 8;
             const int shift = bit - width;
             const uint32_t dmask = (1u << width) - 1u;
-            uint32_t *hist = sm.hist[pb];
-            // After the first pass few keys still match the prefix: a wave with none skips the
-            // atomic (each costs about the same with or without active lanes).
+            uint32_t *hist = sm.hist[h];
+            // Absent keys reach bin 0 when they match the prefix: in the first pass, which tests no
+            // prefix (every present key shares it), or when the prefix is 0.
+            const bool absent_in_0 = first || prefix == 0u;
+            if (first) {
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                const bool m = j0 + i < n && (key[i] & pmask) == prefix;
-                if (__builtin_amdgcn_ballot_w64(m) != 0 && m) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
+                for (int i = 0; i < EPT; ++i) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
+            } else {
+#pragma unroll
+                for (int i = 0; i < EPT; ++i)
+                    if ((key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
             }
             __syncthreads();
-            if (threadIdx.x < kWave) {
-                // lane l owns bins 255-4l .. 252-4l, highest first
-                uint32_t v[4], s = 0;
+            const int hc = h == 0 ? 2 : h - 1;            // (h + 2) % 3
+            if (wave == 0) reinterpret_cast<u32x4 *>(sm.hist[hc])[lane] = u32x4{0u, 0u, 0u, 0u};
+            // lane l owns bins 255-4l .. 252-4l, highest first
+            const u32x4 hv = reinterpret_cast<const u32x4 *>(hist)[kWave - 1 - lane];
+            uint32_t v[4] = {hv[3], hv[2], hv[1], hv[0]};
+            if (absent_in_0 && lane == kWave - 1) v[3] -= absent;
+            const uint32_t s = v[0] + v[1] + v[2] + v[3];
+            uint32_t cum = wave_incl_scan_dpp(s) - s;
+            uint32_t f_bin = 0, f_cum = 0, f_cnt = 0;
+            bool found = false;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[i] = hist[kBins - 1 - (4 * lane + i)];
-                    s += v[i];
+            for (int i = 0; i < 4; ++i) {
+                if (cum < remaining && remaining <= cum + v[i]) {
+                    found = true;
+                    f_bin = (uint32_t)(kBins - 1 - (4 * lane + i));
+                    f_cum = cum;
+                    f_cnt = v[i];
                 }
-                uint32_t cum = wave_incl_scan_dpp(s) - s;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    if (cum < remaining && remaining <= cum + v[i]) {
-                        sm.res[pb][0] = (uint32_t)(kBins - 1 - (4 * lane + i));
-                        sm.res[pb][1] = cum;
-                        sm.res[pb][2] = v[i];
-                    }
-                    cum += v[i];
-                }
-            } else if (threadIdx.x < kWave + kBins) {
-                sm.hist[pb ^ 1][threadIdx.x - kWave] = 0;
+                cum += v[i];
             }
-            __syncthreads();
-            remaining -= sm.res[pb][1];
-            prefix |= sm.res[pb][0] << shift;
+            const uint64_t fb = __builtin_amdgcn_ballot_w64(found);   // exactly one lane
+            const int src = (int)__builtin_ctzll(fb);
+            const uint32_t bin = __builtin_amdgcn_readlane(f_bin, src);
+            remaining -= __builtin_amdgcn_readlane(f_cum, src);
+            prefix |= bin << shift;
             pmask |= dmask << shift;
             bit = shift;
-            whole_bin = sm.res[pb][2] == remaining;   // the whole boundary bin is taken
-            pb ^= 1;
+            whole_bin = __builtin_amdgcn_readlane(f_cnt, src) == remaining;   // the whole boundary bin is taken
+            h = h == 2 ? 0 : h + 1;
+            first = false;
             if (whole_bin) break;
         }
         T = prefix;
@@ -185,18 +198,14 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
     // it is >= T and the ties need no ranks.
     const bool all_ties = ties == 0xFFFFFFFFu;        // uniform
     uint32_t gt = 0, eq = 0;
-    if (need > 0) {
-        if (all_ties) {
+    if (all_ties) {
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) gt += (j0 + i < n && key[i] >= T) ? 1u : 0u;
-        } else {
+        for (int i = 0; i < EPT; ++i) gt += key[i] >= T ? 1u : 0u;
+    } else {
 #pragma unroll
-            for (int i = 0; i < EPT; ++i) {
-                if (j0 + i < n) {
-                    gt += key[i] > T;
-                    eq += key[i] == T;
-                }
-            }
+        for (int i = 0; i < EPT; ++i) {
+            gt += key[i] > T ? 1u : 0u;
+            eq += key[i] == T ? 1u : 0u;
         }
     }
     // gt and eq totals stay below 2^16 (n <= 16384), so one scan carries both.
@@ -205,45 +214,36 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
     uint32_t pos = (packed >> 16) + (tie_rank < ties ? tie_rank : ties);
     // Branch-free: a key not taken is stored to this lane's spare slot past kMaxK.  Exactly
     // need <= K keys are taken, so a taken key's position is below K.
-    auto collect = [&](auto keys_tag) __attribute__((always_inline)) {
+    auto collect = [&](auto keys_tag, auto all_tag) __attribute__((always_inline)) {
         constexpr bool KEYS = decltype(keys_tag)::value;
+        constexpr bool ALL = decltype(all_tag)::value;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
-            const bool valid = j0 + i < n;
-            const bool eqk = valid && key[i] == T;
-            const bool take = (valid && key[i] > T) || (eqk && tie_rank < ties);
-            tie_rank += eqk ? 1u : 0u;
+            bool take;
+            if (ALL) {
+                take = key[i] >= T;
+            } else {
+                const bool eqk = key[i] == T;
+                take = key[i] > T || (eqk && tie_rank < ties);
+                tie_rank += eqk ? 1u : 0u;
+            }
             const uint32_t dst = take ? pos : (uint32_t)(kMaxK + lane);
             sm.sel_id[dst] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
             if (KEYS) sm.sel_key[dst] = key[i];
             pos += take ? 1u : 0u;
         }
     };
-    auto collect_all = [&](auto keys_tag) __attribute__((always_inline)) {
-        constexpr bool KEYS = decltype(keys_tag)::value;
-#pragma unroll
-        for (int i = 0; i < EPT; ++i) {
-            const bool take = j0 + i < n && key[i] >= T;
-            const uint32_t dst = take ? pos : (uint32_t)(kMaxK + lane);
-            sm.sel_id[dst] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
-            if (KEYS) sm.sel_key[dst] = key[i];
-            pos += take ? 1u : 0u;
-        }
-    };
-    if (need > 0) {
-        if (all_ties) {
-            if (out_keys) collect_all(std::true_type{});
-            else collect_all(std::false_type{});
-        } else {
-            if (out_keys) collect(std::true_type{});
-            else collect(std::false_type{});
-        }
+    if (all_ties) {
+        if (out_keys) collect(std::true_type{}, std::true_type{});
+        else collect(std::false_type{}, std::true_type{});
+    } else {
+        if (out_keys) collect(std::true_type{}, std::false_type{});
+        else collect(std::false_type{}, std::false_type{});
     }
     __syncthreads();
-    const int taken = need > 0 ? need : 0;
     for (int i = threadIdx.x; i < K; i += NT) {
-        out[i] = i < taken ? sm.sel_id[i] : -1;
-        if (out_keys) out_keys[i] = i < taken ? sm.sel_key[i] : 0u;
+        out[i] = i < need ? sm.sel_id[i] : -1;
+        if (out_keys) out_keys[i] = i < need ? sm.sel_key[i] : 0u;
     }
 }
 

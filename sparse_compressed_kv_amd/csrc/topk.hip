@@ -8,13 +8,13 @@
 //
 // Core: block_select, one workgroup radix-selecting `need` of n keys held in
 // registers (each thread a contiguous run of up to 32 keys, all loaded before
-// first use); LDS holds only the 256-bin histogram and scan scratch:
+// first use); LDS holds only 256-bin histograms and scan scratch:
 //   1. min/max of the keys; the bits above their highest differing bit are
 //      common to all keys and are skipped;
-//   2. 8-bit digit passes: LDS histogram of the keys that match the prefix so
-//      far, then wave 0 scans the 256 bins (descending, DPP wavefront scan)
-//      for the bin holding the need-th key; stop early once a whole bin is
-//      taken;
+//   2. 8-bit digit passes: each wave histograms its keys that match the prefix
+//      so far, then every wave sums the per-wave histograms and scans the 256
+//      bins (descending, DPP wavefront scan) for the bin holding the need-th
+//      key, one barrier per pass; stop early once a whole bin is taken;
 //   3. the result is a threshold key T plus a number of ties (keys == T) to
 //      take in row order; one block scan of packed (above, tie) counts gives
 //      every thread its output offset, so the set is written in ascending row
@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(int64_t N, int K, int ch
     int32_t id[EPT];
 #pragma unroll
     for (int i = 0; i < EPT; ++i) {
-        key[i] = float_key(v[i]);
+        key[i] = j0 + i < n ? float_key(v[i]) : 0u;   // absent positions hold 0
         id[i] = 0;
     }
     const int need = K < n ? K : n;

@@ -119,6 +119,11 @@ def _scores(pattern, n, rng):
         s[rng.random(n) < 0.5] = -0.0
         s[rng.random(n) < 0.01] = 1.0
         return s
+    if pattern == "low":     # keys with a zero top byte (large negative scores) hold the boundary
+        s = np.float32(-3e38) * (np.float32(1.0) - rng.random(n).astype(np.float32) * np.float32(1e-3))
+        few = rng.random(n) < 0.05
+        s[few] = rng.standard_normal(int(few.sum())).astype(np.float32) * np.float32(50.0)
+        return s
     if pattern == "heavy":
         s = np.abs(rng.standard_normal(n)).astype(np.float32) * np.float32(100.0) + np.float32(10.0)
         s[rng.choice(n, max(1, n // 100), replace=False)] *= np.float32(4.0)
@@ -131,6 +136,7 @@ TOPK_CASES = [
     (1, 512, 512, "equal"), (2, 513, 512, "ties"), (2, 4095, 512, "zeros"), (2, 16384, 512, "heavy"),
     (2, 16384, 2048, "ties"), (2, 16385, 512, "normal"), (2, 40961, 1024, "heavy"), (1, 65537, 512, "equal"),
     (2, 65537, 1024, "ties"), (1, 262144, 512, "normal"), (1, 100000, 2048, "zeros"), (3, 20000, 7, "normal"),
+    (3, 4095, 512, "low"), (3, 40000, 1024, "low"),
 ]
 
 
