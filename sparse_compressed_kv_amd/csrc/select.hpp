@@ -19,15 +19,12 @@ constexpr int kLevelChunk = 8192;             // candidates per workgroup in int
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4x
 
-constexpr int kMaxK = 2048;
 
 struct SelectShared {
     alignas(16) uint32_t hist[3][kBins];     // digit histograms, used by turns (pass p counts into p % 3)
     alignas(16) uint32_t wave_a[kNW];
-    uint32_t wave_mn[kNW];
-    uint32_t wave_mx[kNW];
-    int32_t sel_id[kMaxK + kWave];   // the selected set, in row order, before the coalesced copy-out;
-    uint32_t sel_key[kMaxK + kWave]; // slots from kMaxK on take the stores of keys not taken
+    alignas(16) uint32_t wave_mn[kNW];       // per wave: min over present keys of (key - 1), max of keys
+    alignas(16) uint32_t wave_mx[kNW];
 };
 
 // Chunk sizes of the levels that produced a candidate list, first level on rows.
@@ -80,14 +77,14 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
     return off + incl - v;           // wave_sums is not written again: no barrier after the reads
 }
 
-// Min and max over the workgroup.  Its slots are used once per select, so no barrier follows.
+// Min over present keys and max over the workgroup, from each thread's min of (key - 1) and max
+// of key.  Its slots are used once per select, so no barrier follows the reads.
 template <int NT>
-__device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
-    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-    wave_minmax_u32(kmin, kmax);
-    if (lane == 0) {
-        sm.wave_mn[wave] = kmin;
-        sm.wave_mx[wave] = kmax;
+__device__ void block_minmax(uint32_t kmin1, uint32_t kmax1, uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
+    wave_minmax_u32(kmin1, kmax1);
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+        sm.wave_mn[threadIdx.x / kWave] = kmin1;
+        sm.wave_mx[threadIdx.x / kWave] = kmax1;
     }
     __syncthreads();
     kmin = 0xFFFFFFFFu;
@@ -97,6 +94,7 @@ __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
         kmin = sm.wave_mn[i] < kmin ? sm.wave_mn[i] : kmin;
         kmax = sm.wave_mx[i] > kmax ? sm.wave_mx[i] : kmax;
     }
+    kmin += 1u;
 }
 
 // Selects the `need` largest of the n keys held in registers (thread t holds positions
@@ -107,6 +105,7 @@ __device__ void block_minmax(uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
 // every later position holds 0; need = min(K, n).  A key of 0 is thus absent, and no step tests
 // positions against n: absent keys stay below every threshold, and the one histogram bin they can
 // reach (bin 0) is corrected by their number.
+// The selection goes from registers straight to out / out_keys: a taken key's slot is its rank.
 template <int EPT, bool IDS, int NT = kNT>
 __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int64_t row0, int n, int need,
                              int K, int32_t *out, uint32_t *out_keys, SelectShared &sm)
@@ -117,18 +116,17 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
     uint32_t T = 1u, ties = 0xFFFFFFFFu;      // take keys > T and the first `ties` keys == T (T = 1: all present)
     if (need < n) {                           // uniform; implies n > 0 and need > 0
         // min over present keys: key - 1 takes absent keys (0) to the top of the range
-        uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
+        uint32_t kmin1 = 0xFFFFFFFFu, kmax1 = 0u;
 #pragma unroll
         for (int i = 0; i < EPT; ++i) {
             const uint32_t k1 = key[i] - 1u;
-            kmin = k1 < kmin ? k1 : kmin;
-            kmax = key[i] > kmax ? key[i] : kmax;
+            kmin1 = k1 < kmin1 ? k1 : kmin1;
+            kmax1 = key[i] > kmax1 ? key[i] : kmax1;
         }
         // the first two histograms, cleared before the barrier of the min/max
-        if (threadIdx.x < 2 * kBins / 4)
-            reinterpret_cast<u32x4 *>(&sm.hist[0][0])[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
-        block_minmax<NT>(kmin, kmax, sm);
-        kmin += 1u;
+        if (threadIdx.x < 2 * kBins / 4) reinterpret_cast<u32x4 *>(&sm.hist[0][0])[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+        uint32_t kmin, kmax;
+        block_minmax<NT>(kmin1, kmax1, kmin, kmax, sm);
         int bit = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
         uint32_t pmask = bit >= 32 ? 0u : ~((1u << bit) - 1u);
         uint32_t prefix = kmin & pmask;
@@ -152,9 +150,16 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
 #pragma unroll
                 for (int i = 0; i < EPT; ++i) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
             } else {
+                // Few keys still match: a wave with none branches over the atomic (an LDS atomic
+                // costs the same with or without active lanes).
 #pragma unroll
-                for (int i = 0; i < EPT; ++i)
-                    if ((key[i] & pmask) == prefix) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
+                for (int i = 0; i < EPT; ++i) {
+                    const bool m = (key[i] & pmask) == prefix;
+                    if (__builtin_amdgcn_ballot_w64(m) != 0) {
+                        asm volatile("" ::: "memory");     // keeps the uniform branch a branch
+                        if (m) atomicAdd(&hist[(key[i] >> shift) & dmask], 1u);
+                    }
+                }
             }
             __syncthreads();
             const int hc = h == 0 ? 2 : h - 1;            // (h + 2) % 3
@@ -212,8 +217,7 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
     const uint32_t packed = block_excl_scan((gt << 16) | eq, sm.wave_a);
     uint32_t tie_rank = packed & 0xFFFFu;
     uint32_t pos = (packed >> 16) + (tie_rank < ties ? tie_rank : ties);
-    // Branch-free: a key not taken is stored to this lane's spare slot past kMaxK.  Exactly
-    // need <= K keys are taken, so a taken key's position is below K.
+    // A taken key's slot is its rank; waves with no taken key at a position branch over the store.
     auto collect = [&](auto keys_tag, auto all_tag) __attribute__((always_inline)) {
         constexpr bool KEYS = decltype(keys_tag)::value;
         constexpr bool ALL = decltype(all_tag)::value;
@@ -227,9 +231,13 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
                 take = key[i] > T || (eqk && tie_rank < ties);
                 tie_rank += eqk ? 1u : 0u;
             }
-            const uint32_t dst = take ? pos : (uint32_t)(kMaxK + lane);
-            sm.sel_id[dst] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
-            if (KEYS) sm.sel_key[dst] = key[i];
+            if (__builtin_amdgcn_ballot_w64(take) != 0) {
+                asm volatile("" ::: "memory");         // keeps the uniform branch a branch
+                if (take) {
+                    out[pos] = IDS ? id[i] : (int32_t)(row0 + j0 + i);
+                    if (KEYS) out_keys[pos] = key[i];
+                }
+            }
             pos += take ? 1u : 0u;
         }
     };
@@ -240,10 +248,9 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
         if (out_keys) collect(std::true_type{}, std::false_type{});
         else collect(std::false_type{}, std::false_type{});
     }
-    __syncthreads();
-    for (int i = threadIdx.x; i < K; i += NT) {
-        out[i] = i < need ? sm.sel_id[i] : -1;
-        if (out_keys) out_keys[i] = i < need ? sm.sel_key[i] : 0u;
+    for (int i = need + (int)threadIdx.x; i < K; i += NT) {
+        out[i] = -1;
+        if (out_keys) out_keys[i] = 0u;
     }
 }
 
