@@ -25,11 +25,16 @@ constexpr int kFWaves = kNT / kWave;
 // 16-row blocks in flight per wave, for both key formats (3 or 4 blocks of E4M3 rows measured
 // no faster on MI355X: their loads are limited by request rate, not by bytes in flight).
 constexpr int kFBpi = 2;
-// Device figures behind the chunk rule (MI355X): 256 CUs, each holding two chunk workgroups
-// at once (the row loop keeps the query in VGPRs, 125 per lane: 4 waves per SIMD).  Fixed,
-// so that workspace sizes do not depend on the device a call runs on.
+// Device figures behind the chunk rule (MI355X, measured with bf16 keys): a chunk workgroup
+// alone on a CU streams its keys at ~23 GB/s (its loads in flight set the rate), two on one CU
+// at ~26 GB/s together, and all of them at most at the device's read rate, ~6.1 TB/s; 256 CUs
+// hold two chunk workgroups each (the row loop keeps the query in VGPRs, 125 per lane: 4 waves
+// per SIMD).  Fixed, so that workspace sizes do not depend on the device a call runs on.
 constexpr int64_t kFCUs = 256;
 constexpr int64_t kFSlots = 2 * kFCUs;
+constexpr double kFRate1 = 23.0;              // bytes per ns: one chunk workgroup on a CU
+constexpr double kFRate2 = 26.0;              // two on a CU, together
+constexpr double kFRateAll = 6100.0;          // the device
 
 // A chunk of up to EPT * 512 rows (`rows` per chunk): each thread selects over EPT keys.  Two
 // workgroups share a CU (4 waves per SIMD: at most 128 VGPRs).
@@ -97,30 +102,37 @@ struct FusedShape {
     int64_t chunks;                           // chunks per query
 };
 
-// Chunk rule.  Every CU gets about the same share of HBM bandwidth, so a chunk workgroup
-// streams at a rate set by how many share its CU, and the call lasts as long as its busiest
-// CU: (workgroups per CU) x (rows per chunk), plus a select and the query set-up per
-// resident round, plus the merge: ~0.6 ns per candidate and ~10 us per extra level.  Costs
-// are in rows (one 256-byte key row at a CU's share of the bandwidth, ~10 ns): a select +
-// set-up costs 370 + 24 * ept, a merge candidate 1/16.
-// Chunks hold at most 8192 rows (16 keys per thread) and at least 4 rows per candidate.
+// Chunk rule: the chunk count with the least modelled time, in ns.  A call streams for as long
+// as its busiest CU needs (one or two chunk workgroups per CU per resident round, at the rates
+// above) and at least as long as the device needs for all the keys; each resident round ends
+// with a select (~3 us + 0.15 us per key per thread); a merge (more than one chunk) costs ~3 us
+// + 0.6 ns per candidate, plus ~8 us per extra level, and a final list longer than the attention
+// kernel merges itself costs the one-call step that extra level too.  Chunks hold at most 8192 rows (16 keys per thread)
+// and at least 2 rows per candidate.
 FusedShape fused_shape(int64_t Q, int64_t N, int K) {
     const int64_t cmin = (N + 8191) / 8192 > 0 ? (N + 8191) / 8192 : 1;
-    int64_t cmax = N / (4 * (int64_t)K);
-    if (cmax > cmin + 32) cmax = cmin + 32;
+    int64_t cmax = N / (2 * (int64_t)K);
+    if (cmax > cmin + 64) cmax = cmin + 64;
     if (cmax < cmin) cmax = cmin;
     FusedShape best = {16, 8192, cmin};
-    int64_t best_cost = -1;
+    double best_cost = -1.0;
     for (int64_t c = cmin; c <= cmax; ++c) {
         const int64_t rows = ((N + c - 1) / c + 15) / 16 * 16;
         const int ept = (int)((rows + 2047) / 2048 * 4);
         const int64_t wgs = Q * c;
+        const int64_t rounds = (wgs + kFSlots - 1) / kFSlots;
+        const int64_t last = wgs - (rounds - 1) * kFSlots;          // workgroups of the last round
+        const double chunk_bytes = (double)rows * 256.0;
+        double cu_ns = (double)(rounds - 1) * 2.0 * chunk_bytes / kFRate2;
+        cu_ns += last <= kFCUs ? chunk_bytes / kFRate1 : 2.0 * chunk_bytes / kFRate2;
+        const double all_ns = (double)Q * (double)N * 256.0 / kFRateAll;
         int64_t levels = 0;
-        for (int64_t stride = c * K; stride > kMergeMax; stride = (stride + kLevelChunk - 1) / kLevelChunk * K)
-            ++levels;
-        const int64_t cost = (wgs + kFCUs - 1) / kFCUs * rows + (wgs + kFSlots - 1) / kFSlots * (370 + 24 * ept) +
-                             c * K / 16 + 1000 * levels;
-        if (best_cost < 0 || cost < best_cost) {
+        int64_t stride = c * K;
+        for (; stride > kMergeMax; stride = (stride + kLevelChunk - 1) / kLevelChunk * K) ++levels;
+        if (stride > kAttnMergeMax) ++levels;
+        const double merge_ns = c > 1 ? 3000.0 + 0.6 * (double)stride + 8000.0 * (double)levels : 0.0;
+        const double cost = (cu_ns > all_ns ? cu_ns : all_ns) + (double)rounds * (3000.0 + 150.0 * ept) + merge_ns;
+        if (best_cost < 0.0 || cost < best_cost) {
             best_cost = cost;
             best = {ept, (int)rows, c};
         }
@@ -128,11 +140,17 @@ FusedShape fused_shape(int64_t Q, int64_t N, int K) {
     return best;
 }
 
-// The fused kernel needs enough chunk workgroups to stream the keys at full rate; with fewer
-// (a handful of units) the score kernel's smaller 1024-row chunks plus the separate top-k
-// are faster, and so are many queries per unit (prefill shapes).
+// The fused kernel needs enough chunk workgroups to stream the keys at full rate while its
+// chunks keep at least 4 rows per candidate; with fewer (a handful of units) the score kernel's
+// smaller 1024-row chunks plus the separate top-k are faster, and so are many queries per unit
+// (prefill shapes).
 bool use_fused(int T, int64_t Q, int64_t N, int K) {
-    return T < kIndexerManyQueries && Q * fused_shape(Q, N, K).chunks >= 128;
+    if (T >= kIndexerManyQueries) return false;
+    const int64_t cmin = (N + 8191) / 8192 > 0 ? (N + 8191) / 8192 : 1;
+    int64_t c4 = N / (4 * (int64_t)K);
+    if (c4 > cmin + 32) c4 = cmin + 32;
+    if (c4 < cmin) c4 = cmin;
+    return Q * c4 >= 128;
 }
 
 template <int EPT>

@@ -362,7 +362,7 @@ def test_workspace_bytes(L):
     assert ops.workspace_bytes(3, 1, 1, 10, 10) == 0                  # unknown `which`
     assert ops.workspace_bytes(1, 1, 2048, 8192, 512, 64, 128) == 0   # prefill: no split
     assert ops.workspace_bytes(1, 1, 1, 10, 512, 64, 100) == 0        # invalid W
-    assert ops.workspace_bytes(2, 300, 1, 2048, 512) == 0            # fused: one chunk, no candidates
+    assert ops.workspace_bytes(2, 256, 1, 2048, 512) == 0            # fused: one chunk, no candidates
     assert ops.workspace_bytes(2, 4, 1, 65536, 1024) >= 4 * 65536 * 4  # too few chunks: scores kept
     assert ops.workspace_bytes(2, 43, 1, 65536, 512) >= 2 * 43 * 11 * 512 * 8  # 11 chunks of candidates
     assert ops.workspace_bytes(2, 1, 2048, 8192, 512) >= 2048 * 8192 * 4       # many queries: scores

@@ -167,12 +167,15 @@ FUSED_CASES = [
     dict(U=3, T=1, N=8193, K=512, nv=[[8193], [0], [300]], ept=None),
     dict(U=1, T=2, N=100000, K=2048, nv=[[100000, 2047]], ept=None),
     # fused: every chunk size, one chunk (direct output) to two merge levels
+    dict(U=200, T=1, N=2048, K=512, nv="edges", ept=4),        # one chunk
     dict(U=100, T=3, N=2048, K=512, nv="edges", ept=4),
-    dict(U=200, T=1, N=8197, K=512, nv="edges", ept=12),
+    dict(U=200, T=1, N=8197, K=512, nv="edges", ept=4),
     dict(U=43, T=1, N=65536, K=512, nv=None, heavy=0.01, ept=12),
-    dict(U=43, T=1, N=65537, K=1024, nv="edges", ept=12),
-    dict(U=8, T=1, N=262144, K=512, nv="edges", ept=16),
-    dict(U=40, T=1, N=100000, K=2048, nv="edges", ept=16),
+    dict(U=43, T=1, N=65537, K=1024, nv="edges", ept=8),
+    dict(U=8, T=1, N=262144, K=512, nv="edges", ept=8),
+    dict(U=8, T=1, N=262144, K=2048, nv="edges", ept=16),      # two merge levels
+    dict(U=64, T=1, N=50000, K=512, nv="edges", ept=16),
+    dict(U=40, T=1, N=100000, K=2048, nv="edges", ept=12),
     dict(U=50, T=3, N=20000, K=7, nv=None, ept=8),
     dict(U=64, T=1, N=4096, K=512, nv="edges", ept=4),
     dict(U=70, T=2, N=3000, K=64, nv="edges", ept=4),
@@ -221,7 +224,7 @@ def test_indexer_topk_equals_separate_calls(case):
 def test_indexer_topk_all_tied():
     """Every score equal (zero query): the set is rows 0..K-1 across chunk boundaries."""
     w = gen.Workload("fut", 106, U=130, T=1, N=9000, H=16, K=512)
-    assert routing.uses_fused(w.U, w.T, w.N, w.K) and routing.fused_shape(w.U, w.N, w.K) == (8, 3008, 3)
+    assert routing.uses_fused(w.U, w.T, w.N, w.K) and routing.fused_shape(w.U, w.N, w.K) == (4, 1296, 7)
     x = gen.make_indexer_config(w, seed=3)
     x["idx_q"][:] = 0
     got = ops.indexer_topk(bits_to_torch(x["idx_q"], torch.bfloat16), torch.from_numpy(x["idx_w"]).cuda(),
@@ -286,9 +289,10 @@ FP8_TOPK_CASES = [
     dict(U=3, T=1, N=8193, K=512, nv=[[8193], [0], [300]], ept=None),        # scores through the workspace
     dict(U=2, T=16, N=3000, K=512, nv="edges", ept=None),                    # many queries per unit
     dict(U=100, T=3, N=2048, K=512, nv="edges", ept=4),
-    dict(U=200, T=1, N=8197, K=512, nv="edges", ept=12),
+    dict(U=200, T=1, N=8197, K=512, nv="edges", ept=4),
     dict(U=43, T=1, N=65536, K=512, nv=None, heavy=0.01, ept=12),
-    dict(U=8, T=1, N=262144, K=512, nv="edges", ept=16),
+    dict(U=8, T=1, N=262144, K=512, nv="edges", ept=8),
+    dict(U=64, T=1, N=50000, K=512, nv="edges", ept=16),
     dict(U=70, T=2, N=3000, K=64, nv="edges", ept=4),
 ]
 

@@ -44,8 +44,8 @@ def _inputs(U, T, N, H, W, qdt, seed, ragged):
 
 CASES = [
     # name, U, T, N, H, K, W, q dtype, ragged.  Routes (tests/routing.py and the attention's
-    # plan): the first five select inside the attention kernel (5, 7, 11, 11 and 11 chunks per
-    # query; the K = 768 case after one intermediate merge level of 8,448 candidates), the last
+    # plan): the first five select inside the attention kernel (11, 11, 7, 11 and 22 chunks per
+    # query; the K = 768 case after one intermediate merge level of 16,896 candidates), the last
     # two launch the two calls (few queries: the union is split; four queries per unit).
     ("decode_merge", 43, 1, 16384, 64, 512, 128, torch.float32, False),
     ("decode_merge_ragged", 43, 1, 16384, 64, 512, 128, torch.float32, True),
