@@ -75,7 +75,8 @@ static_assert(kDqMaxChunkSteps * kSR % kAT == 0, "row table fill");
 constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[quarter][block][lane][4]
 constexpr int kMEpt = 16;                     // last merge level in the kernel: candidates per thread
 constexpr int kDqMergeMax = kMEpt * kDqT;     // ... and per query (6,144)
-static_assert(sizeof(SelectShared) <= kBuf, "the selection's scratch fits in one ring slot");
+constexpr int kSelCopies = 8;                 // histogram copies of the in-kernel select (merge candidates crowd into few bins)
+static_assert(sizeof(SelectSharedT<kSelCopies>) <= kBuf, "the selection's scratch fits in one ring slot");
 static_assert(kDqMergeMax == kAttnMergeMax, "the host's bound on the in-kernel merge");
 static_assert(kAW * kQDB * kWave * 16 <= kDqNB * kBuf, "row-half merge fits in the ring");
 static_assert(kAW * kQKs * 2 * kWave * 16 <= kBuf, "query quarters fit in one ring slot");
@@ -239,22 +240,25 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     const int64_t j_lim = DENSE ? clamp_nvis(a.n_vis, q, a.N) : a.N;
 
     // The last merge level (every thread of the workgroup): the selection lands in s_row[W ..
-    // W + K) in ascending row order, -1 past the selected; ring slot 3 holds the select's
-    // scratch (no rows reach it before the barrier of step -2).
-    auto select_final = [&]() __attribute__((always_inline)) {
+    // W + K) in ascending row order, -1 past the selected.  Its candidates are loaded first of
+    // all (cand_load), so their latency overlaps the query set-up and the first raw rows' loads;
+    // ring slot 2 holds the select's scratch (slots 0 and 1 take raw rows meanwhile, slot 3 the
+    // query quarters), free again after the barrier that follows the select.
+    uint32_t ckey[kMEpt];
+    int32_t cid[kMEpt];
+    int cand_n = 0;
+    auto cand_load = [&]() __attribute__((always_inline)) {
         Levels lv = {};
         lv.n = a.lv_n;
 #pragma unroll
         for (int l = 0; l < kMaxLevels; ++l) lv.ch[l] = a.lv_ch[l];
         int64_t count = cand_count(clamp_nvis(a.cand_nvis, q, a.N), a.K, lv);
         if (count > a.cand_stride) count = a.cand_stride;
-        const int nc = (int)count;
+        cand_n = (int)count;
         const uint32_t *ik = a.cand_keys + q * a.cand_stride;
         const int32_t *ii = a.cand_ids + q * a.cand_stride;
-        const __amdgpu_buffer_rsrc_t rk = list_rsrc(ik, (uint32_t)nc * 4u), ri = list_rsrc(ii, (uint32_t)nc * 4u);
+        const __amdgpu_buffer_rsrc_t rk = list_rsrc(ik, (uint32_t)cand_n * 4u), ri = list_rsrc(ii, (uint32_t)cand_n * 4u);
         const int j0 = tid * kMEpt;
-        uint32_t key[kMEpt];
-        int32_t id[kMEpt];
         if (((reinterpret_cast<uintptr_t>(ik) | reinterpret_cast<uintptr_t>(ii)) & 15u) == 0) {
 #pragma unroll
             for (int v = 0; v < kMEpt / 4; ++v) {
@@ -263,20 +267,28 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
                 const u32x4 y = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(ri, off, 0, 0));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    key[4 * v + e] = x[e];
-                    id[4 * v + e] = (int32_t)y[e];
+                    ckey[4 * v + e] = x[e];
+                    cid[4 * v + e] = (int32_t)y[e];
                 }
             }
         } else {
 #pragma unroll
             for (int i = 0; i < kMEpt; ++i) {
-                key[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)(j0 + i) * 4u, 0, 0);
-                id[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j0 + i) * 4u, 0, 0);
+                ckey[i] = __builtin_amdgcn_raw_buffer_load_b32(rk, (uint32_t)(j0 + i) * 4u, 0, 0);
+                cid[i] = (int32_t)__builtin_amdgcn_raw_buffer_load_b32(ri, (uint32_t)(j0 + i) * 4u, 0, 0);
             }
         }
-        SelectShared &sm = *reinterpret_cast<SelectShared *>(ring + (NB - 1) * kBuf);
-        block_select<kMEpt, true, kDqT>(key, id, 0, nc, a.K < nc ? a.K : nc, a.K, s_row + (a.W - rho0), nullptr, sm);
     };
+    auto cand_select = [&]() __attribute__((always_inline)) {
+        SelectSharedT<kSelCopies> &sm = *reinterpret_cast<SelectSharedT<kSelCopies> *>(ring + (NB - 2) * kBuf);
+        block_select<kMEpt, true, kDqT, kSelCopies>(ckey, cid, 0, cand_n, a.K < cand_n ? a.K : cand_n, a.K,
+                                                    s_row + (a.W - rho0), nullptr, sm);
+    };
+    // Raw steps whose loads go out before the row table: with the merge, as many as the slots
+    // the select leaves free (its own slot and the query quarters' stay untouched); without it,
+    // step 0 only (a cold start's loads are slow to issue, and the computing waves would wait
+    // for them at the row table's barrier).
+    const int n_pre = MERGE ? min(n_raw, NB - 2) : min(n_raw, 1);
 
     if (wave >= kAW) {
         // ---- producer wave: raw steps' loads at once (they need no index), the first
@@ -292,19 +304,18 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         ld.scale_rs = rsrc(cscale_u, E8 ? (uint32_t)a.N * 4u : 0u);
         ld.step0 = step0; ld.n = n; ld.n_raw = n_raw; ld.rho0 = rho0; ld.W = a.W;
         ld.p = wave - kAW; ld.lane = lane; ld.j_lim = j_lim;
-        // Only step 0 goes out before the row table's barrier: the loads of a cold start are
-        // slow to issue, and the computing waves would wait for them at that barrier.
+        if (MERGE) cand_load();
         i32x4 ent[4];
         ld.entries(-1, ent);                  // no entries (raw steps)
-        if (n_raw > 0) ld.issue(0, ent);
+        for (int j = 0; j < n_pre; ++j) ld.issue(j, ent);
         if (MERGE) {
-            select_final();
+            cand_select();
             __syncthreads();                  // the selection is in the row table
         }
         __syncthreads();                      // row table
 #pragma unroll
         for (int j = 0; j < NB - 1; ++j)
-            if ((j > 0 || n_raw == 0) && j < n) {
+            if (j >= n_pre && j < n) {
                 ld.entries(j, ent);
                 ld.issue(j, ent);
             }
@@ -339,6 +350,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
 
     // ---- computing waves: set-up (index entries, query, row table), then the steps.
     const int64_t pos = a.pos[q];             // first: the rotation angles need only it
+    if (MERGE) cand_load();
     constexpr int kPer = kDqMaxChunkSteps * kSR / kAT;        // index entries per thread (6)
     int32_t v_idx[kPer];
     if (!DENSE && !MERGE) {
@@ -370,13 +382,49 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
     }
+    // The rotated tail (dims 448..511) is quarter 3's k-steps 2 and 3: pair 16(s - 2) + 4g + e/2,
+    // rotated in fp64 and rounded once to f32 (rope.hpp, as the compressor rotates its rows).
+    // The angles need only the position, so they are formed while the loads are in flight.
+    if (qq == kAW - 1 && lane < kRot / 2) {
+        double cs, sn;
+        rope_angle(a.log2_theta, lane, pos, cs, sn);
+        s_ang_all[2 * lane] = cs;
+        s_ang_all[2 * lane + 1] = sn;
+    }
     if (MERGE) {
-        select_final();
+        cand_select();                        // waits for the candidates only (loaded before the query)
         __syncthreads();                      // the selection is in the row table
         if (a.idx_out && hg == 0) {
             int32_t *dst = a.idx_out + q * (int64_t)a.K;
             for (int k = tid; k < a.K; k += kAT) dst[k] = s_row[a.W - rho0 + k];
         }
+    }
+    if (qq == kAW - 1) {
+        wait_lds();                           // this wave's angles
+#pragma unroll
+        for (int s = kQKs - 2; s < kQKs; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                const int pr = 16 * (s - (kQKs - 2)) + 4 * g + e / 2;
+                rope_rotate(s_ang_all[2 * pr], s_ang_all[2 * pr + 1], qv[s][e], qv[s][e + 1]);
+            }
+    }
+    // Query fragments: f16 pair while the steps are raw, bf16 pair after (a bf16 query's
+    // unrotated dims have lo = 0).  Each wave publishes its quarter's pairs in ring slot 3, which
+    // takes rows only after the barrier of step -2, and reads its partner's after the row
+    // table's barrier.  Without the merge all of this comes before the row table, whose index
+    // entries it waits for.
+    u32x4 qh_m[kQKs], ql_m[kQKs];
+#pragma unroll
+    for (int s = 0; s < kQKs; ++s) {
+        if (n_raw > 0) split8<true>(qv[s], qh_m[s], ql_m[s]);
+        else split8<false>(qv[s], qh_m[s], ql_m[s]);
+    }
+    u32x4 *xq = reinterpret_cast<u32x4 *>(ring + (NB - 1) * kBuf);      // [wave][k-step][hi, lo][lane]
+#pragma unroll
+    for (int s = 0; s < kQKs; ++s) {
+        xq[((wave * kQKs + s) * 2) * kWave + lane] = qh_m[s];
+        xq[((wave * kQKs + s) * 2 + 1) * kWave + lane] = ql_m[s];
     }
     if (!DENSE) {
         // row table (local union row -> compressed row or -1) and per-step validity masks
@@ -402,39 +450,6 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
                 s_mask[(r * kAT + wave * kWave) / kSR + 1] = (uint32_t)(bits >> 32);
             }
         }
-    }
-    // The rotated tail (dims 448..511) is quarter 3's k-steps 2 and 3: pair 16(s - 2) + 4g + e/2,
-    // rotated in fp64 and rounded once to f32 (rope.hpp, as the compressor rotates its rows).
-    if (qq == kAW - 1) {
-        double *s_ang = s_ang_all;
-        if (lane < kRot / 2) {
-            double cs, sn;
-            rope_angle(a.log2_theta, lane, pos, cs, sn);
-            s_ang[2 * lane] = cs;
-            s_ang[2 * lane + 1] = sn;
-        }
-#pragma unroll
-        for (int s = kQKs - 2; s < kQKs; ++s)
-#pragma unroll
-            for (int e = 0; e < 8; e += 2) {
-                const int pr = 16 * (s - (kQKs - 2)) + 4 * g + e / 2;
-                rope_rotate(s_ang[2 * pr], s_ang[2 * pr + 1], qv[s][e], qv[s][e + 1]);
-            }
-    }
-    // Query fragments: f16 pair while the steps are raw, bf16 pair after (a bf16 query's
-    // unrotated dims have lo = 0).  Each wave publishes its quarter's pairs in ring slot 3, which
-    // takes rows only after the barrier of step -2, and reads its partner's after the next one.
-    u32x4 qh_m[kQKs], ql_m[kQKs];
-#pragma unroll
-    for (int s = 0; s < kQKs; ++s) {
-        if (n_raw > 0) split8<true>(qv[s], qh_m[s], ql_m[s]);
-        else split8<false>(qv[s], qh_m[s], ql_m[s]);
-    }
-    u32x4 *xq = reinterpret_cast<u32x4 *>(ring + (NB - 1) * kBuf);      // [wave][k-step][hi, lo][lane]
-#pragma unroll
-    for (int s = 0; s < kQKs; ++s) {
-        xq[((wave * kQKs + s) * 2) * kWave + lane] = qh_m[s];
-        xq[((wave * kQKs + s) * 2 + 1) * kWave + lane] = ql_m[s];
     }
     __syncthreads();                          // row table, query quarters
     u32x4 qh[kHKs], ql[kHKs];
@@ -517,17 +532,9 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         const uint32_t mask = step_mask(j) >> (16 * rh);
         const float *src = s_xch + (j & 1) * (kXchBuf / 4) + ((2 * rh) * kWave + lane) * 4;
         const f32x4 sl = *reinterpret_cast<const f32x4 *>(src) + *reinterpret_cast<const f32x4 *>(src + kWave * 4);
-        // QK of step jq (independent of the softmax)
-        if (QK) {
-            acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc[1] = acc[0];
-#pragma unroll
-            for (int s = 0; s < kHKs; ++s) {
-                acc[s & 1] = mma<FQ>(x[s], qh[s], acc[s & 1]);
-                acc[s & 1] = mma<FQ>(x[s], ql[s], acc[s & 1]);
-            }
-        }
-        // softmax of step j against the lazy reference
+        // softmax of step j against the lazy reference: logits, the row half's maximum, and the
+        // rare rescale first, so that the rest of it (exponentials, the sum, the hi + lo split)
+        // can be issued between the QK MFMAs of step jq, which do not depend on it
         float lg[4];
         float tmax = -INFINITY;
 #pragma unroll
@@ -546,6 +553,15 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             m_ref = m_new;
         }
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        if (QK) {
+            acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+            acc[1] = acc[0];
+#pragma unroll
+            for (int s = 0; s < kHKs; ++s) {
+                acc[s & 1] = mma<FQ>(x[s], qh[s], acc[s & 1]);
+                acc[s & 1] = mma<FQ>(x[s], ql[s], acc[s & 1]);
+            }
+        }
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -554,6 +570,15 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             pv[e] = p * rs_cur[e];
         }
         const u32x4 pp = split4_fold<FP>(pv);
+        if (QK && !E8) {
+            // one QK MFMA, then two VALU instructions of the softmax, in turn (E4M3 rows keep the
+            // compiler's order: their row scales leave no registers for it)
+#pragma unroll
+            for (int i = 0; i < 2 * kHKs; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                __builtin_amdgcn_sched_group_barrier(0x402, 2, 0);
+            }
+        }
         // PV of step j; V^T of step jq in place
 #pragma unroll
         for (int i = 0; i < kHDB; ++i) {

@@ -20,12 +20,21 @@ constexpr int kBins = 256;
 constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4x
 
 
-struct SelectShared {
-    alignas(16) uint32_t hist[3][kBins];     // digit histograms, used by turns (pass p counts into p % 3)
+// Histogram scratch of the select.  CP > 1 splits every histogram into CP copies, lane l
+// counting into copy l % CP: a wave's lanes whose keys fall into one bin then add to CP
+// addresses instead of one (an LDS atomic serialises lanes on one address), which matters when
+// the keys crowd into a few bins, as merge candidates do.  Copy c's row starts 4c banks after
+// copy c - 1's (rows of kBins + 4 words), so lanes of different copies never meet in a bank on
+// one bin.
+template <int CP>
+struct SelectSharedT {
+    static constexpr int kRow = CP > 1 ? kBins + 4 : kBins;
+    alignas(16) uint32_t hist[3][CP][kRow];  // digit histograms, used by turns (pass p counts into p % 3)
     alignas(16) uint32_t wave_a[kNW];
     alignas(16) uint32_t wave_mn[kNW];       // per wave: min over present keys of (key - 1), max of keys
     alignas(16) uint32_t wave_mx[kNW];
 };
+using SelectShared = SelectSharedT<1>;
 
 // Chunk sizes of the levels that produced a candidate list, first level on rows.
 struct Levels {
@@ -79,8 +88,8 @@ __device__ uint32_t block_excl_scan(uint32_t v, uint32_t *wave_sums) {
 
 // Min over present keys and max over the workgroup, from each thread's min of (key - 1) and max
 // of key.  Its slots are used once per select, so no barrier follows the reads.
-template <int NT>
-__device__ void block_minmax(uint32_t kmin1, uint32_t kmax1, uint32_t &kmin, uint32_t &kmax, SelectShared &sm) {
+template <int NT, int CP>
+__device__ void block_minmax(uint32_t kmin1, uint32_t kmax1, uint32_t &kmin, uint32_t &kmax, SelectSharedT<CP> &sm) {
     wave_minmax_u32(kmin1, kmax1);
     if ((threadIdx.x & (kWave - 1)) == 0) {
         sm.wave_mn[threadIdx.x / kWave] = kmin1;
@@ -106,10 +115,14 @@ __device__ void block_minmax(uint32_t kmin1, uint32_t kmax1, uint32_t &kmin, uin
 // positions against n: absent keys stay below every threshold, and the one histogram bin they can
 // reach (bin 0) is corrected by their number.
 // The selection goes from registers straight to out / out_keys: a taken key's slot is its rank.
-template <int EPT, bool IDS, int NT = kNT>
-__device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int64_t row0, int n, int need,
-                             int K, int32_t *out, uint32_t *out_keys, SelectShared &sm)
+// CP: copies of each histogram (SelectSharedT).
+template <int EPT, bool IDS, int NT = kNT, int CP = 1>
+__device__ __forceinline__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT], int64_t row0, int n, int need,
+                             int K, int32_t *out, uint32_t *out_keys, SelectSharedT<CP> &sm)
 {
+    static_assert(CP >= 1 && CP <= 8 && (CP & (CP - 1)) == 0, "histogram copies");
+    constexpr int kRow = SelectSharedT<CP>::kRow;
+    constexpr int kHistV4 = CP * kRow / 4;    // one histogram (all copies) as 16-byte words
     static_assert(NT % kWave == 0 && NT <= kNT && NT >= 2 * kWave && kBins == 4 * kWave, "workgroup size");
     const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
     const int j0 = threadIdx.x * EPT;
@@ -124,9 +137,10 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
             kmax1 = key[i] > kmax1 ? key[i] : kmax1;
         }
         // the first two histograms, cleared before the barrier of the min/max
-        if (threadIdx.x < 2 * kBins / 4) reinterpret_cast<u32x4 *>(&sm.hist[0][0])[threadIdx.x] = u32x4{0u, 0u, 0u, 0u};
+        for (int i = (int)threadIdx.x; i < 2 * kHistV4; i += NT)
+            reinterpret_cast<u32x4 *>(&sm.hist[0][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
         uint32_t kmin, kmax;
-        block_minmax<NT>(kmin1, kmax1, kmin, kmax, sm);
+        block_minmax<NT, CP>(kmin1, kmax1, kmin, kmax, sm);
         int bit = kmin == kmax ? 0 : 32 - __clz(kmin ^ kmax);
         uint32_t pmask = bit >= 32 ? 0u : ~((1u << bit) - 1u);
         uint32_t prefix = kmin & pmask;
@@ -142,7 +156,7 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
             const int width = bit < 8 ? bit : 8;
             const int shift = bit - width;
             const uint32_t dmask = (1u << width) - 1u;
-            uint32_t *hist = sm.hist[h];
+            uint32_t *hist = sm.hist[h][CP > 1 ? (lane & (CP - 1)) : 0];   // this lane's copy
             // Absent keys reach bin 0 when they match the prefix: in the first pass, which tests no
             // prefix (every present key shares it), or when the prefix is 0.
             const bool absent_in_0 = first || prefix == 0u;
@@ -163,9 +177,16 @@ __device__ void block_select(const uint32_t (&key)[EPT], const int32_t (&id)[EPT
             }
             __syncthreads();
             const int hc = h == 0 ? 2 : h - 1;            // (h + 2) % 3
-            if (wave == 0) reinterpret_cast<u32x4 *>(sm.hist[hc])[lane] = u32x4{0u, 0u, 0u, 0u};
-            // lane l owns bins 255-4l .. 252-4l, highest first
-            const u32x4 hv = reinterpret_cast<const u32x4 *>(hist)[kWave - 1 - lane];
+            if (CP == 1) {
+                if (wave == 0) reinterpret_cast<u32x4 *>(&sm.hist[hc][0][0])[lane] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                for (int i = (int)threadIdx.x; i < kHistV4; i += NT)
+                    reinterpret_cast<u32x4 *>(&sm.hist[hc][0][0])[i] = u32x4{0u, 0u, 0u, 0u};
+            }
+            // lane l owns bins 255-4l .. 252-4l, highest first (summed over the copies)
+            u32x4 hv = reinterpret_cast<const u32x4 *>(sm.hist[h][0])[kWave - 1 - lane];
+#pragma unroll
+            for (int cp = 1; cp < CP; ++cp) hv += reinterpret_cast<const u32x4 *>(sm.hist[h][cp])[kWave - 1 - lane];
             uint32_t v[4] = {hv[3], hv[2], hv[1], hv[0]};
             if (absent_in_0 && lane == kWave - 1) v[3] -= absent;
             const uint32_t s = v[0] + v[1] + v[2] + v[3];
