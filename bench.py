@@ -861,8 +861,12 @@ def main():
         w3 = gen.CONFIGS["prefill_2048q_n8192"]
         x3 = gen.make_config(w3)
         b3 = Bench(w3, x3, 2)
-        steps3 = max(5, args.steps // 10)
-        r3 = b3.run(steps3, max(2, args.warmup // 10))
+        # A prefill step is ~0.5 ms: half the main line's step count, and more warm-up steps than
+        # the decode lines (the first steps over freshly allocated 128 MB query and 256 MB
+        # output tensors run slower: their pages are first touched there).
+        steps3 = max(5, args.steps // 2)
+        warm3 = max(2, args.warmup // 2)
+        r3 = b3.run(steps3, warm3)
         log(f"[bench] {w3.name}: {r3}")
         fl = prefill_flops(w3)
         tf = fl / (r3["ms_per_step"] / 1e3) / 1e12
@@ -878,7 +882,7 @@ def main():
         # ---- the same prefill over E4M3 indexer keys and E4M3 attention rows (half the gathered
         # bytes); flops as above
         b38 = Bench(w3, x3, 2, fp8_keys=gen.make_indexer_fp8_config(w3), fp8_rows=True)
-        r38 = b38.run(steps3, max(2, args.warmup // 10))
+        r38 = b38.run(steps3, warm3)
         log(f"[bench] {w3.name} fp8 keys + fp8 rows: {r38}")
         tf8 = fl / (r38["ms_per_step"] / 1e3) / 1e12
         rec["prefill_fp8_keys_rows"] = {

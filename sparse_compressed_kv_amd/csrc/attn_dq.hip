@@ -75,7 +75,6 @@ static_assert(kDqMaxChunkSteps * kSR % kAT == 0, "row table fill");
 constexpr int kDqRec = 2 * kWH + kWH * kD;    // record: m[16], l[16], O[quarter][block][lane][4]
 constexpr int kMEpt = 16;                     // last merge level in the kernel: candidates per thread
 constexpr int kDqMergeMax = kMEpt * kDqT;     // ... and per query (6,144)
-constexpr int kSelCopies = 8;                 // histogram copies of the in-kernel select (merge candidates crowd into few bins)
 static_assert(sizeof(SelectSharedT<kSelCopies>) <= kBuf, "the selection's scratch fits in one ring slot");
 static_assert(kDqMergeMax == kAttnMergeMax, "the host's bound on the in-kernel merge");
 static_assert(kAW * kQDB * kWave * 16 <= kDqNB * kBuf, "row-half merge fits in the ring");
@@ -279,6 +278,12 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             }
         }
     };
+    // The candidates are waited for here, while nothing else is in flight: the rows' and the
+    // query's loads go out after them, during the select's passes, and do not delay them.
+    auto cand_wait = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < kMEpt; ++i) asm volatile("" : : "v"(ckey[i]), "v"(cid[i]));
+    };
     auto cand_select = [&]() __attribute__((always_inline)) {
         SelectSharedT<kSelCopies> &sm = *reinterpret_cast<SelectSharedT<kSelCopies> *>(ring + (NB - 2) * kBuf);
         block_select<kMEpt, true, kDqT, kSelCopies>(ckey, cid, 0, cand_n, a.K < cand_n ? a.K : cand_n, a.K,
@@ -304,7 +309,10 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         ld.scale_rs = rsrc(cscale_u, E8 ? (uint32_t)a.N * 4u : 0u);
         ld.step0 = step0; ld.n = n; ld.n_raw = n_raw; ld.rho0 = rho0; ld.W = a.W;
         ld.p = wave - kAW; ld.lane = lane; ld.j_lim = j_lim;
-        if (MERGE) cand_load();
+        if (MERGE) {
+            cand_load();
+            cand_wait();
+        }
         i32x4 ent[4];
         ld.entries(-1, ent);                  // no entries (raw steps)
         for (int j = 0; j < n_pre; ++j) ld.issue(j, ent);
@@ -350,7 +358,10 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
 
     // ---- computing waves: set-up (index entries, query, row table), then the steps.
     const int64_t pos = a.pos[q];             // first: the rotation angles need only it
-    if (MERGE) cand_load();
+    if (MERGE) {
+        cand_load();
+        cand_wait();
+    }
     constexpr int kPer = kDqMaxChunkSteps * kSR / kAT;        // index entries per thread (6)
     int32_t v_idx[kPer];
     if (!DENSE && !MERGE) {

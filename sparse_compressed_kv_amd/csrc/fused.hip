@@ -48,7 +48,7 @@ __global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
     constexpr int kRows = EPT * kNT;
     static_assert(EPT % 4 == 0, "scores are read from LDS four at a time");
     __shared__ __align__(16) float s_sc[kRows];    // keys of the chunk's rows (float_key of the scores)
-    __shared__ SelectShared sm;
+    __shared__ SelectShared sm;                   // one copy: eight measured slower here (LDS, scan reads)
     __shared__ uint32_t s_claim;                  // next unclaimed group of rows
 
     const int64_t q = blockIdx.x / chunks;

@@ -18,6 +18,7 @@ constexpr int kMergeMax = 12288;              // candidates per workgroup (expli
 constexpr int kLevelChunk = 8192;             // candidates per workgroup in intermediate levels
 constexpr int kBins = 256;
 constexpr int kMaxLevels = 12;              // each level shrinks a list by >= 4x
+constexpr int kSelCopies = 8;               // histogram copies (SelectSharedT) where keys crowd into few bins
 
 
 // Histogram scratch of the select.  CP > 1 splits every histogram into CP copies, lane l

@@ -46,7 +46,7 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(int64_t N, int K, int ch
                                                         const int32_t *__restrict__ n_vis,
                                                         int32_t *__restrict__ out, uint32_t *__restrict__ out_keys)
 {
-    __shared__ SelectShared sm;
+    __shared__ SelectSharedT<kSelCopies> sm;       // copies: later passes crowd into the boundary bin
     const int64_t q = blockIdx.x / chunks;
     const int64_t c = blockIdx.x % chunks;
     const int64_t nv = clamp_nvis(n_vis, q, N);
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kNT) void topk_rows_kernel(int64_t N, int K, int ch
     }
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + c) * K;
-    block_select<EPT, false>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
+    block_select<EPT, false, kNT, kSelCopies>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
 }
 
 // One workgroup per (query, chunk of `chunk` <= EPT*kNT candidates).  The candidates of query q
