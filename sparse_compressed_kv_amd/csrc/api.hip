@@ -422,9 +422,11 @@ static int indexer_topk_mqa(const char *fn, int U, int T, int64_t N, int Hi, int
         hipError_t e = ds4a::launch_indexer_candidates(U, T, N, K, iq, idx_w, idx_k, n_vis, ws_topk,
                                                        ds4a::kAttnMergeMax, &cl, st);
         if (e != hipSuccess) return hip_status(fn, e);
+        uint32_t *count = static_cast<uint32_t *>(ws_attn);
+        float *part = reinterpret_cast<float *>(static_cast<char *>(ws_attn) + plan.count_bytes);
         return hip_status(fn, ds4a::launch_attn_dq_merge(plan, U, T, H, W, N, K, q, q_dtype == DS4A_BF16, q_pos,
                                                          rope_theta, raw, comp_kv, cs, cl, n_vis, raw_vis, scale, idx,
-                                                         out, st));
+                                                         out, count, part, st));
     }
     int32_t *ix = idx ? idx : reinterpret_cast<int32_t *>(ws);
     hipError_t e = ds4a::launch_indexer_topk(U, T, N, K, iq, idx_w, idx_k, n_vis, ix, ws_topk, st);

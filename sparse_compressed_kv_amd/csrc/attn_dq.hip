@@ -287,7 +287,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     auto cand_select = [&]() __attribute__((always_inline)) {
         SelectSharedT<kSelCopies> &sm = *reinterpret_cast<SelectSharedT<kSelCopies> *>(ring + (NB - 2) * kBuf);
         block_select<kMEpt, true, kDqT, kSelCopies>(ckey, cid, 0, cand_n, a.K < cand_n ? a.K : cand_n, a.K,
-                                                    s_row + (a.W - rho0), nullptr, sm);
+                                                    s_row + a.W, nullptr, sm);
     };
     // Raw steps whose loads go out before the row table: with the merge, as many as the slots
     // the select leaves free (its own slot and the query quarters' stay untouched); without it,
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         ld.ring = ring;
         ld.ring_a = lds_addr(ring);
         ld.scale_a = lds_addr(s_scale);
-        ld.s_row = s_row;
+        ld.s_row = MERGE ? s_row + rho0 : s_row;   // merge: the row table covers the whole union
         ld.raw_rs = rsrc(raw_q, (uint32_t)raw_lim * (2 * kD));
         ld.comp_rs = rsrc(comp_u, (uint32_t)((uint64_t)a.N * kCompRowBytes));
         ld.scale_rs = rsrc(cscale_u, E8 ? (uint32_t)a.N * 4u : 0u);
@@ -405,9 +405,9 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
     if (MERGE) {
         cand_select();                        // waits for the candidates only (loaded before the query)
         __syncthreads();                      // the selection is in the row table
-        if (a.idx_out && hg == 0) {
+        if (a.idx_out && hg == 0 && chunk == 0) {
             int32_t *dst = a.idx_out + q * (int64_t)a.K;
-            for (int k = tid; k < a.K; k += kAT) dst[k] = s_row[a.W - rho0 + k];
+            for (int k = tid; k < a.K; k += kAT) dst[k] = s_row[a.W + k];
         }
     }
     if (qq == kAW - 1) {
@@ -444,11 +444,12 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             const int i = tid + r * kAT;
             int32_t e;
             if (MERGE) {
-                // the selection's entries, -1 outside them (raw rows, the last step's tail)
+                // the selection's entries, -1 outside them (raw rows, the last step's tail); the
+                // table is indexed by union row, so this chunk's rows start at rho0
                 const int k = rho0 + i - a.W;
-                e = (i < n * kSR && k >= 0 && k < a.K) ? s_row[i] : -1;
+                e = (i < n * kSR && k >= 0 && k < a.K) ? s_row[rho0 + i] : -1;
                 e = (e >= 0 && (int64_t)e < a.N) ? e : -1;
-                if (i < n * kSR && (k < 0 || k >= a.K)) s_row[i] = e;
+                if (i < n * kSR && (k < 0 || k >= a.K)) s_row[rho0 + i] = e;
             } else {
                 e = (v_idx[r] >= 0 && (int64_t)v_idx[r] < a.N) ? v_idx[r] : -1;
                 if (i < n * kSR) s_row[i] = e;
@@ -820,13 +821,14 @@ hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t
 }
 
 bool attn_dq_merge_apply(const AttnPlan &p, int64_t list_stride) {
-    return p.dq && p.n_chunks == 1 && list_stride <= kDqMergeMax;
+    return p.dq && p.n_steps <= kDqMaxChunkSteps && list_stride <= kDqMergeMax;
 }
 
 hipError_t launch_attn_dq_merge(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q,
                                 int q_bf16, const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                                 const float *comp_scale, const CandList &cl, const int32_t *cand_nvis,
-                                const int32_t *raw_vis, float scale, int32_t *idx_out, float *out, hipStream_t stream)
+                                const int32_t *raw_vis, float scale, int32_t *idx_out, float *out, uint32_t *count,
+                                float *part, hipStream_t stream)
 {
     if (!attn_dq_merge_apply(p, cl.stride) || cl.n_levels < 1 || cl.n_levels > kMaxLevels) return hipErrorInvalidValue;
     const bool e8 = comp_scale != nullptr && N > 0;
@@ -843,7 +845,7 @@ hipError_t launch_attn_dq_merge(const AttnPlan &p, int U, int T, int H, int W, i
                                                 e8 ? kDqMaxLds<true> : kDqMaxLds<false>);
     });
     if (attr_err[variant] != hipSuccess) return attr_err[variant];
-    const int lds = (e8 ? kDqRowTabOff<true> : kDqRowTabOff<false>) + 4 * kSR * p.steps_per_chunk;
+    const int lds = (e8 ? kDqRowTabOff<true> : kDqRowTabOff<false>) + 4 * kSR * p.n_steps;   // the whole union's rows
     AttnArgs a = {};
     a.T = T; a.H = H; a.W = W; a.K = K; a.n_hg = p.n_hg; a.n_chunks = p.n_chunks;
     a.steps_per_chunk = p.steps_per_chunk; a.n_steps = p.n_steps;
@@ -856,6 +858,8 @@ hipError_t launch_attn_dq_merge(const AttnPlan &p, int U, int T, int H, int W, i
     a.log2_theta = log2(theta);
     a.cand_keys = cl.keys; a.cand_ids = cl.ids; a.cand_stride = cl.stride; a.cand_nvis = cand_nvis;
     a.idx_out = idx_out;
+    a.count = count;
+    a.part = part;
     a.lv_n = cl.n_levels;
     for (int l = 0; l < cl.n_levels; ++l) a.lv_ch[l] = cl.level_rows[l];
     hipLaunchKernelGGL(fn, dim3((unsigned)p.blocks), dim3(kDqT), lds, stream, a);

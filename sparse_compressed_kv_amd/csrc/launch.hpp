@@ -92,16 +92,19 @@ hipError_t launch_attn_dq(const AttnPlan &p, int U, int T, int H, int W, int64_t
                           const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                           const float *comp_scale, const int32_t *idx, const int32_t *n_vis, const int32_t *raw_vis,
                           float scale, float *out, uint32_t *count, float *part, hipStream_t stream);
-// The 16-head kernel with the last top-k merge level inside (sparse, unsplit unions, lists of
-// at most 6,144 candidates per query): the rows of each query are selected from cl by the
-// workgroups themselves (the set the top-k kernels would write), and written to idx_out when
-// it is not null.  cand_nvis: the indexer's visible rows per query (NULL: all N).
+// The 16-head kernel with the last top-k merge level inside (sparse unions of at most 48 steps,
+// lists of at most 6,144 candidates per query): the rows of each query are selected from cl by
+// the workgroups themselves (the set the top-k kernels would write; a workgroup of a split
+// union selects them all and attends its chunk's), and written to idx_out when it is not null.
+// cand_nvis: the indexer's visible rows per query (NULL: all N).  count, part: as for
+// launch_attn_parts (used when the union is split).
 constexpr int64_t kAttnMergeMax = 6144;      // candidates per query the in-kernel merge takes
 bool attn_dq_merge_apply(const AttnPlan &p, int64_t list_stride);
 hipError_t launch_attn_dq_merge(const AttnPlan &p, int U, int T, int H, int W, int64_t N, int K, const void *q,
                                 int q_bf16, const int64_t *q_pos, double theta, const uint16_t *raw, const void *comp,
                                 const float *comp_scale, const CandList &cl, const int32_t *cand_nvis,
-                                const int32_t *raw_vis, float scale, int32_t *idx_out, float *out, hipStream_t stream);
+                                const int32_t *raw_vis, float scale, int32_t *idx_out, float *out, uint32_t *count,
+                                float *part, hipStream_t stream);
 // As launch_attn with the counters and the records given apart (count: plan.count_bytes,
 // zero before the call and left zero; part: plan.workspace_bytes - plan.count_bytes).
 hipError_t launch_attn_parts(int U, int T, int H, int W, int64_t N, int K, const void *q, int q_bf16,

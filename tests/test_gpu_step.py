@@ -44,14 +44,18 @@ def _inputs(U, T, N, H, W, qdt, seed, ragged):
 
 CASES = [
     # name, U, T, N, H, K, W, q dtype, ragged.  Routes (tests/routing.py and the attention's
-    # plan): the first five select inside the attention kernel (11, 11, 7, 11 and 22 chunks per
-    # query; the K = 768 case after one intermediate merge level of 16,896 candidates), the last
-    # two launch the two calls (few queries: the union is split; four queries per unit).
+    # plan): the first seven select inside the attention kernel (11, 11, 7, 11 and 22 chunks per
+    # query; the K = 768 case after one intermediate merge level of 16,896 candidates; the two
+    # split_union cases with the union split over several workgroups per head group, each of
+    # which selects the whole set and attends its part), the last two launch the two calls
+    # (too few chunk workgroups for the fused select; four queries per unit).
     ("decode_merge", 43, 1, 16384, 64, 512, 128, torch.float32, False),
     ("decode_merge_ragged", 43, 1, 16384, 64, 512, 128, torch.float32, True),
     ("decode_merge_bf16q", 36, 1, 20000, 64, 512, 96, torch.bfloat16, True),
     ("decode_main_shape", 43, 1, 65536, 64, 512, 128, torch.float32, True),
     ("decode_merge_after_a_level", 43, 1, 40000, 64, 768, 128, torch.float32, True),
+    ("split_union_merge", 8, 1, 65536, 64, 512, 128, torch.float32, True),
+    ("split_union_merge_w64", 12, 1, 30000, 64, 512, 64, torch.bfloat16, True),
     ("pro_split_union", 4, 1, 16384, 128, 1024, 128, torch.float32, True),
     ("many_queries", 2, 4, 8192, 64, 512, 128, torch.bfloat16, True),
 ]
