@@ -544,9 +544,22 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         const uint32_t mask = step_mask(j) >> (16 * rh);
         const float *src = s_xch + (j & 1) * (kXchBuf / 4) + ((2 * rh) * kWave + lane) * 4;
         const f32x4 sl = *reinterpret_cast<const f32x4 *>(src) + *reinterpret_cast<const f32x4 *>(src + kWave * 4);
-        // softmax of step j against the lazy reference: logits, the row half's maximum, and the
-        // rare rescale first, so that the rest of it (exponentials, the sum, the hi + lo split)
-        // can be issued between the QK MFMAs of step jq, which do not depend on it
+        // QK of step jq: independent of the softmax of step j.  Without E4M3 rows it comes after
+        // the softmax's logits, the row half's maximum and the rare rescale, so that the rest of
+        // the softmax (exponentials, the sum, the hi + lo split) is issued between its MFMAs;
+        // with them it comes first (the other order leaves their row scales no registers).
+        auto qk_mfmas = [&]() __attribute__((always_inline)) {
+            if (QK) {
+                acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+                acc[1] = acc[0];
+#pragma unroll
+                for (int s = 0; s < kHKs; ++s) {
+                    acc[s & 1] = mma<FQ>(x[s], qh[s], acc[s & 1]);
+                    acc[s & 1] = mma<FQ>(x[s], ql[s], acc[s & 1]);
+                }
+            }
+        };
+        if (E8) qk_mfmas();
         float lg[4];
         float tmax = -INFINITY;
 #pragma unroll
@@ -565,15 +578,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
             m_ref = m_new;
         }
         const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
-        if (QK) {
-            acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-            acc[1] = acc[0];
-#pragma unroll
-            for (int s = 0; s < kHKs; ++s) {
-                acc[s & 1] = mma<FQ>(x[s], qh[s], acc[s & 1]);
-                acc[s & 1] = mma<FQ>(x[s], ql[s], acc[s & 1]);
-            }
-        }
+        if (!E8) qk_mfmas();
         float pv[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -583,8 +588,7 @@ __global__ __launch_bounds__(kDqT, 1) void attn_dq_kernel(AttnArgs a)
         }
         const u32x4 pp = split4_fold<FP>(pv);
         if (QK && !E8) {
-            // one QK MFMA, then two VALU instructions of the softmax, in turn (E4M3 rows keep the
-            // compiler's order: their row scales leave no registers for it)
+            // one QK MFMA, then two VALU instructions of the softmax, in turn
 #pragma unroll
             for (int i = 0; i < 2 * kHKs; ++i) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
