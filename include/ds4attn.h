@@ -203,11 +203,12 @@ int ds4a_sparse_mqa_noalloc(int U, int T, int H, int D, int n_rot, int W, int64_
  * ds4a_sparse_mqa on the selected rows, with the same results bit for bit (sections 3-1 to 3-3
  * of "Reading the architecture of DwarfStar (ds4.c), part 1/8": the indexer picks the rows
  * that the main attention then reads).  In decode shapes (T < 4, at least 128 chunk
- * workgroups for the fused select, few enough queries that the attention keeps each union
- * whole) the last merge level of the top-k runs inside the attention kernel: each workgroup
- * selects its query's rows from the chunks' candidates itself, so the selection needs no
- * launch and no round trip through memory of its own.  Otherwise the call launches what the
- * two calls would.
+ * workgroups for the fused select, few enough queries for the 16-head attention kernel, and a
+ * union of at most 1,536 rows) the last merge level of the top-k runs inside the attention
+ * kernel: each workgroup selects its query's rows from the chunks' candidates itself (when the
+ * union is split over several workgroups, each selects the whole set and attends its part), so
+ * the selection needs no launch and no round trip through memory of its own.  Otherwise the
+ * call launches what the two calls would.
  * Arguments as for ds4a_indexer_topk (Hi, Di, K, idx_q, idx_w, idx_k, n_vis) and
  * ds4a_sparse_mqa (H, D, n_rot, W, q, q_dtype, q_pos, rope_theta, raw_kv, raw_vis, comp_kv,
  * scale, out), with N the rows of both caches, and
