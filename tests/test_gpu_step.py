@@ -108,8 +108,19 @@ def _e4m3(g, shape):
     return c
 
 
-def test_one_call_fp8_equals_two_calls():
-    U, T, N, H, K, W = 43, 1, 16384, 64, 512, 128
+FP8_CASES = [
+    # name, U, N: the union kept whole (43 queries) and split over several workgroups per head
+    # group (8 queries), both with the final merge inside the attention kernel
+    ("fp8_whole_union", 43, 16384),
+    ("fp8_split_union", 8, 65536),
+]
+
+
+@pytest.mark.parametrize("case", FP8_CASES, ids=[c[0] for c in FP8_CASES])
+def test_one_call_fp8_equals_two_calls(case):
+    name, U, N = case
+    T, H, K, W = 1, 64, 512, 128
+    print(f"[one call] {name}", flush=True)
     x, n_vis, raw_vis = _inputs(U, T, N, H, W, torch.float32, seed=21, ragged=True)
     g = torch.Generator(device="cuda").manual_seed(22)
     k8 = _e4m3(g, (U, N, 128))
