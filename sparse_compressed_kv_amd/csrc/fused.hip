@@ -93,7 +93,21 @@ __global__ __launch_bounds__(kNT, 4) void indexer_select_kernel(
     }
     const int need = K < n ? K : n;
     const int64_t slot = (q * chunks + ch) * K;
-    block_select<EPT, false>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
+    if (2 * K > kRows) {                          // uniform; chunks of fewer than 2K key slots
+        block_select<EPT, false>(key, id, c0, n, need, K, out + slot, out_keys ? out_keys + slot : nullptr, sm);
+        return;
+    }
+    // The selection is gathered in LDS (the scores' buffer, K ids then K keys) and leaves in one
+    // coalesced pass instead of the collection's scattered stores.
+    __syncthreads();                              // every thread holds its keys: s_sc is free
+    int32_t *g_id = reinterpret_cast<int32_t *>(s_sc);
+    uint32_t *g_key = reinterpret_cast<uint32_t *>(s_sc) + K;
+    block_select<EPT, false>(key, id, c0, n, need, K, g_id, out_keys ? g_key : nullptr, sm);
+    __syncthreads();
+    for (int i = (int)threadIdx.x; i < K; i += kNT) {
+        out[slot + i] = g_id[i];
+        if (out_keys) out_keys[slot + i] = g_key[i];
+    }
 }
 
 struct FusedShape {
