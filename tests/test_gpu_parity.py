@@ -179,6 +179,7 @@ FUSED_CASES = [
     dict(U=50, T=3, N=20000, K=7, nv=None, ept=8),
     dict(U=64, T=1, N=4096, K=512, nv="edges", ept=4),
     dict(U=70, T=2, N=3000, K=64, nv="edges", ept=4),
+    dict(U=128, T=1, N=2000, K=2048, nv="edges", ept=4),      # chunks of fewer than 2K key slots
 ]
 
 
